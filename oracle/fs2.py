@@ -1,0 +1,184 @@
+"""Multiscale pipeline: Morton cells, coarse annealed Sinkhorn on cell records,
+lift to points, and the sparse fine loop with a certified stop.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+FlashSinkhorn 2:
+  * §3 and §B.1: cells are Morton-prefix groups, at most twice as many cells
+    as blocks; read here as the prefix of p = floor(log2(2 * max(NB, MB))) bits.
+  * §3.1 and §B.2: the coarse stage anneals on cell records (centroid, mass),
+    then lifts the potentials to points; extra centroid updates run until the
+    coarse error stalls or 2048 updates.
+  * §1, §A.1: the lift of centroid potentials to the points is a log-sum-exp
+    against the other side's centroids (worked example: two points at -h, h
+    per side in one cell give lifted residual cosh(2h^2/eps) - 1).
+  * §3.2: every fine update rebuilds the mask at the current potentials and
+    runs both sparse half-steps on it.
+  * §C.4: the stop certificate is the admitted-plan residual plus a bound on
+    the omitted mass. Read here as R_A + Omega <= tol with
+    Omega = max(NB, MB) * delta_rel, the a-priori total omitted-mass bound
+    of the threshold rule (§3.2).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .blocks import (
+    block_summaries,
+    screen,
+    screen_transpose,
+    sparse_halfstep_f,
+    sparse_halfstep_g,
+    sparse_residuals,
+)
+from .dense import Schedule, annealing_stages, halfstep_f, halfstep_g, marginal_residuals
+from .morton import BITS, morton_order
+
+
+def cells(codes_sorted, P_sorted, w_sorted, p_bits: int):
+    """Cells = runs of equal Morton prefix (top ``p_bits`` bits of the d*21-bit
+    code). Returns offsets int64 [C+1], centroids [C,d] = sum w x / sum w
+    (plain mean for a massless cell) and masses [C] = sum w, in float64."""
+    codes = np.asarray(codes_sorted, dtype=np.uint64)
+    P = np.asarray(P_sorted, dtype=np.float64)
+    w = np.asarray(w_sorted, dtype=np.float64)
+    d = P.shape[1]
+    shift = np.uint64(d * BITS - p_bits)
+    prefix = codes >> shift
+    starts = np.concatenate([[0], np.nonzero(prefix[1:] != prefix[:-1])[0] + 1])
+    offsets = np.concatenate([starts, [len(codes)]]).astype(np.int64)
+    C = len(starts)
+    cent = np.empty((C, d))
+    mass = np.empty(C)
+    for c in range(C):
+        s, e = offsets[c], offsets[c + 1]
+        ws = w[s:e]
+        mass[c] = ws.sum()
+        if mass[c] > 0:
+            cent[c] = (ws[:, None] * P[s:e]).sum(axis=0) / mass[c]
+        else:
+            cent[c] = P[s:e].mean(axis=0)
+    return offsets, cent, mass
+
+
+def lift(P, cent_q, mass_q, G, eps: float, scale: float) -> np.ndarray:
+    """Point potentials from the other side's centroid potentials:
+    f_i = -eps * LSE_J(log M_J + (G_J - s ||p_i - c_J||^2)/eps)."""
+    return halfstep_f(P, cent_q, mass_q, G, eps, scale)
+
+
+@dataclass
+class FS2Params:
+    B: int = 128
+    eps: float = 1e-4
+    tol: float = 1e-2
+    delta_scale: float = 1e-3  # delta_rel = delta_scale / max(NB, MB)
+    coarse_eps_start: float = 1.0
+    coarse_factor: float = 0.5
+    coarse_iters_per_stage: int = 10
+    coarse_tol: float = 1e-3
+    coarse_max: int = 2048
+    stall_window: int = 10
+    stall_rel: float = 0.01
+    max_fine: int = 8192
+    p_bits: int = -1  # -1: floor(log2(2 * max(NB, MB)))
+    scale: float = 1.0
+
+
+@dataclass
+class FS2Result:
+    f: np.ndarray  # user order
+    g: np.ndarray
+    coarse_iters: int
+    fine_updates: int
+    R_A_row: float
+    R_A_col: float
+    omega: float
+    certified: bool
+    ncells_x: int
+    ncells_y: int
+    tiles_history: list = field(default_factory=list)
+
+
+def prefix_bits(NB: int, MB: int, d: int) -> int:
+    return min(d * BITS, int(math.floor(math.log2(2 * max(NB, MB)))))
+
+
+def coarse_solve(cx, cy, mx, my, prm: FS2Params):
+    """Annealed dense Sinkhorn between centroid clouds, then iterations at the
+    target eps until R <= coarse_tol, a stall, or coarse_max updates."""
+    F = np.zeros(len(cx))
+    G = np.zeros(len(cy))
+    iters = 0
+    sched = Schedule(prm.coarse_eps_start, prm.eps, prm.coarse_factor, prm.coarse_iters_per_stage)
+    for eps in annealing_stages(sched):
+        for _ in range(prm.coarse_iters_per_stage):
+            F = halfstep_f(cx, cy, my, G, eps, prm.scale)
+            G = halfstep_g(cx, cy, mx, F, eps, prm.scale)
+            iters += 1
+    hist = []
+    for _ in range(prm.coarse_max):
+        F = halfstep_f(cx, cy, my, G, prm.eps, prm.scale)
+        G = halfstep_g(cx, cy, mx, F, prm.eps, prm.scale)
+        iters += 1
+        R = max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale))
+        hist.append(R)
+        if R <= prm.coarse_tol:
+            break
+        w = prm.stall_window
+        if len(hist) > w and hist[-1] > (1.0 - prm.stall_rel) * hist[-1 - w]:
+            break
+    return F, G, iters
+
+
+def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
+    x = np.asarray(x, np.float32)
+    y = np.asarray(y, np.float32)
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    n, d = x.shape
+    m = len(y)
+    B = prm.B
+    NB, MB = (n + B - 1) // B, (m + B - 1) // B
+    delta = prm.delta_scale / max(NB, MB)
+    omega = max(NB, MB) * delta
+    p_bits = prm.p_bits if prm.p_bits > 0 else prefix_bits(NB, MB, d)
+
+    cxs, px, cys, py = morton_order(x, y)
+    X, Y, A, Bw = x[px], y[py], a[px], b[py]
+    offx, centx, massx = cells(cxs, X, A, p_bits)
+    offy, centy, massy = cells(cys, Y, Bw, p_bits)
+
+    F, G, coarse_iters = coarse_solve(centx, centy, massx, massy, prm)
+    f = lift(X, centy, massy, G, prm.eps, prm.scale)
+    g = lift(Y, centx, massx, F, prm.eps, prm.scale)
+
+    tiles = []
+    certified = False
+    R_row = R_col = math.nan
+    updates = 0
+    while updates < prm.max_fine:
+        f32 = f.astype(np.float32)
+        g32 = g.astype(np.float32)
+        sx = block_summaries(X, A, f32, B)
+        sy = block_summaries(Y, Bw, g32, B)
+        ptr, col = screen(sx, sy, prm.eps, prm.scale, delta)
+        ptrT, rowT = screen_transpose(sx, sy, prm.eps, prm.scale, delta)
+        tiles.append(int(ptr[-1]))
+        R_row, R_col = sparse_residuals(X, Y, A, Bw, f, g, prm.eps, prm.scale, ptr, col, ptrT, rowT, B)
+        if max(R_row, R_col) + omega <= prm.tol:
+            certified = True
+            break
+        f = sparse_halfstep_f(X, Y, Bw, g, prm.eps, prm.scale, ptr, col, B)
+        g = sparse_halfstep_g(X, Y, A, f, prm.eps, prm.scale, ptrT, rowT, B)
+        updates += 1
+
+    fu = np.empty(n)
+    gu = np.empty(m)
+    fu[px] = f
+    gu[py] = g
+    return FS2Result(fu, gu, coarse_iters, updates, R_row, R_col, omega, certified,
+                     len(centx), len(centy), tiles)
