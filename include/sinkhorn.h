@@ -1,0 +1,253 @@
+/*
+ * sinkhorn.h - C ABI of the MI355X (gfx950) online log-domain Sinkhorn library.
+ *
+ * Problem (FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport, §2.1):
+ * entropic optimal transport between source points x (n x d) with weights a
+ * and target points y (m x d) with weights b under the squared-Euclidean
+ * cost C_ij = s * ||x_i - y_j||^2, where the cost scale s is a number resolved
+ * once by the caller (moscot pull request #846, "Two correctness traps": the
+ * scale travels as a resolved value, never re-derived from a subset).
+ *
+ * Conventions shared by every entry point:
+ *   plan      pi_ij = a_i b_j exp((f_i + g_j - C_ij) / eps)
+ *   f-step    f_i = -eps * LSE_j( log b_j + (g_j - C_ij) / eps )
+ *   g-step    g_j = -eps * LSE_i( log a_i + (f_i - C_ij) / eps )
+ *   residual  R_row = sum_i |sum_j pi_ij - a_i|,  R_col = sum_j |sum_i pi_ij - b_j|
+ * The cost is recomputed on the fly and never stored; working memory is
+ * O((n + m) d) (FlashSinkhorn 2, §2.1).
+ *
+ * Memory and streams:
+ *   - Every float / int array argument is a DEVICE pointer unless marked
+ *     "host". Arrays are contiguous; points are row-major [count][d]; weights
+ *     and potentials are [count] in the caller's point order.
+ *   - The caller owns all argument buffers. A problem handle copies x, y, a, b
+ *     at init (the caller may free them afterwards) and owns only its
+ *     O((n + m) d) workspace.
+ *   - All device work is enqueued on the stream given at init (a hipStream_t
+ *     passed as void*; NULL means the null stream). Calls that return host
+ *     values (residuals, counts, thresholds, reports) synchronize that stream.
+ *   - A handle must not be used from two host threads at once.
+ *
+ * Errors: every function returns an int status. 0 = SINKHORN_OK, positive =
+ * success with a note, negative = error. No exception or abort crosses the
+ * ABI. sinkhorn_last_error() gives a detail string for the calling thread.
+ * Index arithmetic is 64-bit throughout (n * m may exceed 2^31).
+ */
+#ifndef SINKHORN_H
+#define SINKHORN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINKHORN_OK 0
+#define SINKHORN_NOT_CONVERGED 1      /* iteration cap reached; outputs are valid */
+#define SINKHORN_ERR_INVALID_ARG (-1) /* bad size, null pointer, eps or scale not finite and > 0 */
+#define SINKHORN_ERR_OOM (-2)         /* device or pinned host allocation failed */
+#define SINKHORN_ERR_HIP (-3)         /* HIP runtime or launch error (detail in sinkhorn_last_error) */
+#define SINKHORN_ERR_CAPACITY (-4)    /* output list too small; *nnz_out holds the required count */
+#define SINKHORN_ERR_NONFINITE (-5)   /* a potential or residual came out NaN or infinite */
+#define SINKHORN_ERR_MASS (-6)        /* sum(a) and sum(b) differ by more than 1e-5 relative */
+#define SINKHORN_ERR_UNSUPPORTED (-7) /* valid request this build does not implement */
+
+typedef struct sinkhorn_problem sinkhorn_problem; /* opaque handle */
+
+/* Annealing schedule (FlashSinkhorn 2, §3.1 and §B.2: annealing in eps with
+ * warm starts). Stages eps_start, eps_start*eps_factor, ... while above
+ * eps_target, each running iters_per_stage full iterations (f-step then
+ * g-step). Then at eps_target: exactly fixed_iters iterations if fixed_iters > 0;
+ * otherwise iterate until max(R_row, R_col) <= tol (tested after every full
+ * iteration when check_every <= 1, else after every check_every-th), at most
+ * max_iters iterations. */
+typedef struct {
+  double eps_start;
+  double eps_target;
+  double eps_factor;      /* in (0, 1) */
+  int32_t iters_per_stage;
+  int32_t fixed_iters;
+  double tol;
+  int32_t max_iters;
+  int32_t check_every;
+} sinkhorn_schedule;
+
+/* Filled by sinkhorn_solve / sinkhorn_solve_multiscale (host struct). */
+typedef struct {
+  int64_t halfsteps;       /* dense or sparse potential updates launched */
+  int64_t iters;           /* full iterations, all stages */
+  int64_t final_iters;     /* full iterations at eps_target */
+  double pairs_evaluated;  /* point pairs visited by all half-steps */
+  double row_l1;           /* R_row of the returned potentials */
+  double col_l1;           /* R_col of the returned potentials */
+  double seconds;          /* host wall time of the call */
+  int32_t stages;          /* annealing stages run (eps_target not counted) */
+  int32_t converged;       /* 1 if the stop test passed */
+} sinkhorn_report;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* sinkhorn_strerror(int code);
+/* Detail of the last error raised on the calling host thread ("" if none). */
+const char* sinkhorn_last_error(void);
+
+/* Unweighted mean of ||x_i - y_j||^2 over all n*m pairs, computed on the device
+ * in fp64 through mean||x||^2 + mean||y||^2 - 2 mean(x) . mean(y). This is the
+ * "mean" cost scaling that moscot #846 resolves once over the full clouds
+ * ("Two correctness traps"); pass 1 / mean as cost_scale. x [n][d], y [m][d]
+ * device; mean_out host. Synchronizes the stream. */
+int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
+                           void* stream, double* mean_out);
+
+/* Create a problem handle: copies x [n][d], y [m][d] (device) and the weights
+ * a [n], b [m] (device; NULL = uniform 1/n, 1/m) into device-resident layouts.
+ * Requires n, m >= 1, 1 <= d <= 1024, cost_scale finite and > 0, weights >= 0
+ * (negative weights are not checked and give undefined results); returns
+ * SINKHORN_ERR_MASS if |sum a - sum b| > 1e-5 * max(sum a, sum b), and
+ * SINKHORN_ERR_NONFINITE if a coordinate or weight is NaN or infinite.
+ * The handle (host pointer) is written to *out. The moscot #846 materializer is
+ * "a callable over row indices built once per call", with geometry resolution
+ * hoisted out of the row loop; the handle plays that role. */
+int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const float* a,
+                  const float* b, int64_t n, int64_t m, int32_t d, double cost_scale,
+                  void* stream);
+
+/* Release the handle and its workspace (synchronizes its stream). NULL is a no-op. */
+int sinkhorn_destroy(sinkhorn_problem* p);
+
+/* Sizes of a handle (host outputs; any may be NULL). */
+int sinkhorn_problem_info(const sinkhorn_problem* p, int64_t* n, int64_t* m, int32_t* d,
+                          double* cost_scale);
+
+/* One dense f-step (FlashSinkhorn 2, §2.1: the source dual update as a tiled
+ * streaming log-sum-exp; the cost is recomputed per pair and never stored):
+ *   f_out_i = -eps * LSE_j( log b_j + (g_j - C_ij) / eps ),  g [m] -> f_out [n].
+ * If f_prev [n] and row_l1 (host) are both non-NULL, also returns the row
+ * residual of the state (f_prev, g), which equals
+ *   sum_i a_i |exp((f_prev_i - f_out_i) / eps) - 1|
+ * because the f-step makes every row sum to a_i (and synchronizes).
+ * f_out may not alias g or f_prev. An all -inf row (every b_j = 0) gives
+ * f_out = +inf and SINKHORN_ERR_NONFINITE. */
+int sinkhorn_halfstep_f(sinkhorn_problem* p, double eps, const float* g, float* f_out,
+                        const float* f_prev, double* row_l1);
+
+/* The g-step, the same reduction with the roles of the sides swapped:
+ *   g_out_j = -eps * LSE_i( log a_i + (f_i - C_ij) / eps ),  f [n] -> g_out [m];
+ * col_l1 (host, with g_prev) is the column residual of the state (f, g_prev). */
+int sinkhorn_halfstep_g(sinkhorn_problem* p, double eps, const float* f, float* g_out,
+                        const float* g_prev, double* col_l1);
+
+/* Exact L1 marginal residuals of (f, g) (FlashSinkhorn 2, §3.1: the exact
+ * residual is an O(nm) pass): one row pass and one column pass over all pairs,
+ * writing no potential. row_l1 and col_l1 are host pointers (either may be NULL). */
+int sinkhorn_marginal_residual(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                               double* row_l1, double* col_l1);
+
+/* Annealed dense solve (FlashSinkhorn 2, §2.1 alternating updates, §3.1
+ * annealing). f [n], g [m] are in/out warm starts (zeros for a cold start);
+ * on return they hold the potentials whose residual passed the stop test (the
+ * last full iteration when fixed_iters > 0). rep (host) may be NULL.
+ * Returns SINKHORN_NOT_CONVERGED when max_iters ran out. */
+int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sched, float* f, float* g,
+                   sinkhorn_report* rep);
+
+/* Entropic transport-plan rows (moscot #846, "Fix": T[rows] = exp((f + g - C)/eps)
+ * built directly from the potentials, never through an n x m x k tensor):
+ *   T[r][j] = a_i b_j exp((f_i + g_j - C_ij) / eps),  i = rows[r],
+ * rows int64 [k] device (0 <= rows[r] < n), T [k][m] device fp32 row-major,
+ * row_max [k] device (may be NULL) = max_j T[r][j]. */
+int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                              const int64_t* rows, int64_t k, float* T, float* row_max);
+
+/* min over rows with a_i > 0 of max_j T_ij (moscot #846, "Behavioural changes":
+ * the largest threshold that keeps every row non-empty, exact and independent
+ * of the batch; rows without mass take no part). Computed in row batches
+ * without storing T. out (host) is NaN when every a_i is 0. */
+int sinkhorn_min_row(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                     float* out);
+
+/* Morton (Z-order) codes and a stable Morton order of both clouds
+ * (FlashSinkhorn 2, §3: Morton sorting makes cells and blocks of consecutive
+ * points spatially compact). d <= 3; 21 bits per axis over the bounding box of
+ * x and y together, q_k = min(2^21 - 1, floor((p_k - lo_k) * (2^21 / (hi_k - lo_k))))
+ * in fp64 (0 on a flat axis), bit b of axis k at position d*b + k; ties keep
+ * the original order. Outputs (device): codes_x [n] / codes_y [m] sorted codes,
+ * perm_x [n] / perm_y [m] original index of each sorted point. */
+int sinkhorn_morton_order(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
+                          void* stream, uint64_t* codes_x, int32_t* perm_x, uint64_t* codes_y,
+                          int32_t* perm_y);
+
+/* Block-pair screen (FlashSinkhorn 2, §3.2 and §B.3: block-level potential
+ * maxima and bounding boxes; §A.3: an omitted tile drops at most
+ * delta_rel * a_i per row and delta_rel * b_j per column). Blocks are B
+ * consecutive points of the handle's clouds in their stored order (sort them
+ * first). Tile (I, J) is omitted iff, in fp64,
+ *   (F_I + G_J) - D_IJ <= eps * (log(delta_rel) - max(log W^a_I, log W^b_J))
+ * with F_I = max f over I, G_J = max g over J, D_IJ = s * sum_k gap_k^2,
+ * gap_k = max(0, lo_Jk - hi_Ik, lo_Ik - hi_Jk), W = points * max weight of the
+ * block. transpose = 0 gives the row-major list (ptr [NB+1] over source blocks,
+ * idx = admitted target blocks in increasing order); transpose = 1 the
+ * column-major list of the same tiles (ptr [MB+1], idx = source blocks).
+ * ptr int64 and idx int32 are device arrays; cap is idx's capacity. *nnz_out
+ * (host) gets the tile count; if it exceeds cap the call returns
+ * SINKHORN_ERR_CAPACITY and idx is not written. 1 <= B <= 1024. */
+int sinkhorn_block_screen(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                          int32_t B, double delta_rel, int32_t transpose, int64_t* ptr,
+                          int32_t* idx, int64_t cap, int64_t* nnz_out);
+
+/* Sparse f-step on a row-major tile list (FlashSinkhorn 2, §3.2: log-sum-exp
+ * over admitted tiles only; a block with no admitted tile takes a dense
+ * update). Same outputs as sinkhorn_halfstep_f, with the residual (when
+ * f_prev and row_l1 are given) taken over the same support. */
+int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, int32_t B,
+                               const int64_t* ptr, const int32_t* idx, float* f_out,
+                               const float* f_prev, double* row_l1);
+
+/* Sparse g-step on the column-major list of the same tiles. */
+int sinkhorn_sparse_halfstep_g(sinkhorn_problem* p, double eps, const float* f, int32_t B,
+                               const int64_t* ptr, const int32_t* idx, float* g_out,
+                               const float* g_prev, double* col_l1);
+
+/* Multiscale solve parameters (FlashSinkhorn 2, §1, §3, §3.1, §3.2, §B.1, §B.2). */
+typedef struct {
+  int32_t B;                /* block size (points per block) */
+  int32_t p_bits;           /* Morton prefix bits of a cell; <= 0: floor(log2(2 max(NB, MB))) */
+  double eps;               /* target eps */
+  double tol;               /* stop when max(R_A,row, R_A,col) + Omega <= tol */
+  double delta_scale;       /* delta_rel = delta_scale / max(NB, MB); Omega = delta_scale */
+  double coarse_eps_start;  /* coarse annealing start */
+  double coarse_factor;     /* coarse annealing factor */
+  int32_t coarse_iters_per_stage;
+  double coarse_tol;        /* coarse stop: R <= coarse_tol, ... */
+  int32_t coarse_max;       /* ... or this many iterations at the target eps, ... */
+  int32_t stall_window;     /* ... or R > (1 - stall_rel) * R of stall_window iterations before */
+  double stall_rel;
+  int32_t max_fine;         /* cap on fine updates */
+} sinkhorn_multiscale_params;
+
+typedef struct {
+  int64_t coarse_iters;
+  int64_t fine_updates;
+  int64_t ncells_x, ncells_y;
+  int64_t last_tiles;       /* admitted tiles of the last mask */
+  double pairs_evaluated;   /* all point pairs visited (coarse, lift, fine, checks) */
+  double R_A_row, R_A_col;  /* admitted-plan residuals of the returned potentials */
+  double omega;             /* a-priori omitted-mass bound */
+  double seconds_total, seconds_sort, seconds_coarse, seconds_lift, seconds_fine;
+  int32_t certified;
+} sinkhorn_multiscale_report;
+
+/* Block-sparse multiscale solve for d <= 3 (FlashSinkhorn 2): Morton sort,
+ * Morton-prefix cells with mass-weighted centroids, annealed coarse Sinkhorn
+ * on the cells, lift of the coarse potentials to the points, then fine updates
+ * that each rebuild the block-pair mask and run the sparse f- and g-steps,
+ * stopping when the certificate max(R_A,row, R_A,col) + Omega <= tol holds.
+ * f [n], g [m] (device) receive the potentials in the caller's order;
+ * rep (host) may be NULL. Returns SINKHORN_NOT_CONVERGED at the fine cap. */
+int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
+                              float* f, float* g, sinkhorn_multiscale_report* rep);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKHORN_H */

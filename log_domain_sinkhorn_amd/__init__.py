@@ -1,0 +1,428 @@
+"""Python binding of the MI355X online log-domain Sinkhorn library.
+
+Thin ctypes wrappers around the C ABI declared in ``include/sinkhorn.h``: the
+functions here only marshal arguments (torch device tensors -> raw pointers,
+the current HIP stream -> ``void*``) and turn status codes into exceptions.
+Every step of the computation runs in the HIP kernels of ``libsinkhorn.so``.
+PyTorch provides device memory and streams only.
+
+The library must have been built (``python -m log_domain_sinkhorn_amd.build``);
+every entry point raises ``ImportError`` without it: there is no CPU or
+PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch  # loads the HIP runtime the library links against
+
+__all__ = [
+    "SinkhornError",
+    "Schedule",
+    "MultiscaleParams",
+    "Problem",
+    "mean_sqeuclid",
+    "morton_order",
+    "lib",
+    "LIB_PATH",
+    "OK",
+    "NOT_CONVERGED",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsinkhorn.so")
+
+OK = 0
+NOT_CONVERGED = 1
+ERR_INVALID_ARG = -1
+ERR_OOM = -2
+ERR_HIP = -3
+ERR_CAPACITY = -4
+ERR_NONFINITE = -5
+ERR_MASS = -6
+ERR_UNSUPPORTED = -7
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f64 = ctypes.c_double
+
+
+class _ScheduleC(ctypes.Structure):
+    _fields_ = [
+        ("eps_start", _f64),
+        ("eps_target", _f64),
+        ("eps_factor", _f64),
+        ("iters_per_stage", _i32),
+        ("fixed_iters", _i32),
+        ("tol", _f64),
+        ("max_iters", _i32),
+        ("check_every", _i32),
+    ]
+
+
+class _ReportC(ctypes.Structure):
+    _fields_ = [
+        ("halfsteps", _i64),
+        ("iters", _i64),
+        ("final_iters", _i64),
+        ("pairs_evaluated", _f64),
+        ("row_l1", _f64),
+        ("col_l1", _f64),
+        ("seconds", _f64),
+        ("stages", _i32),
+        ("converged", _i32),
+    ]
+
+
+class _MultiscaleParamsC(ctypes.Structure):
+    _fields_ = [
+        ("B", _i32),
+        ("p_bits", _i32),
+        ("eps", _f64),
+        ("tol", _f64),
+        ("delta_scale", _f64),
+        ("coarse_eps_start", _f64),
+        ("coarse_factor", _f64),
+        ("coarse_iters_per_stage", _i32),
+        ("coarse_tol", _f64),
+        ("coarse_max", _i32),
+        ("stall_window", _i32),
+        ("stall_rel", _f64),
+        ("max_fine", _i32),
+    ]
+
+
+class _MultiscaleReportC(ctypes.Structure):
+    _fields_ = [
+        ("coarse_iters", _i64),
+        ("fine_updates", _i64),
+        ("ncells_x", _i64),
+        ("ncells_y", _i64),
+        ("last_tiles", _i64),
+        ("pairs_evaluated", _f64),
+        ("R_A_row", _f64),
+        ("R_A_col", _f64),
+        ("omega", _f64),
+        ("seconds_total", _f64),
+        ("seconds_sort", _f64),
+        ("seconds_coarse", _f64),
+        ("seconds_lift", _f64),
+        ("seconds_fine", _f64),
+        ("certified", _i32),
+    ]
+
+
+# name -> argtypes (every entry point declared in include/sinkhorn.h)
+_SIGS = {
+    "sinkhorn_strerror": ([_i32], ctypes.c_char_p),
+    "sinkhorn_last_error": ([], ctypes.c_char_p),
+    "sinkhorn_mean_sqeuclid": ([_p, _p, _i64, _i64, _i32, _p, _p], _i32),
+    "sinkhorn_init": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f64, _p], _i32),
+    "sinkhorn_destroy": ([_p], _i32),
+    "sinkhorn_problem_info": ([_p, _p, _p, _p, _p], _i32),
+    "sinkhorn_halfstep_f": ([_p, _f64, _p, _p, _p, _p], _i32),
+    "sinkhorn_halfstep_g": ([_p, _f64, _p, _p, _p, _p], _i32),
+    "sinkhorn_marginal_residual": ([_p, _f64, _p, _p, _p, _p], _i32),
+    "sinkhorn_solve": ([_p, _p, _p, _p, _p], _i32),
+    "sinkhorn_materialize_rows": ([_p, _f64, _p, _p, _p, _i64, _p, _p], _i32),
+    "sinkhorn_min_row": ([_p, _f64, _p, _p, _p], _i32),
+    "sinkhorn_morton_order": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p], _i32),
+    "sinkhorn_block_screen": ([_p, _f64, _p, _p, _i32, _f64, _i32, _p, _p, _i64, _p], _i32),
+    "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
+    "sinkhorn_sparse_halfstep_g": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
+    "sinkhorn_solve_multiscale": ([_p, _p, _p, _p, _p], _i32),
+}
+
+EXPORTED = tuple(_SIGS)
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises ImportError if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing; build it with `python -m log_domain_sinkhorn_amd.build`"
+            )
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = handle
+    return _LIB
+
+
+class SinkhornError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        L = lib()
+        detail = L.sinkhorn_last_error().decode()
+        name = L.sinkhorn_strerror(code).decode()
+        super().__init__(f"{where}: {name} ({code}){': ' + detail if detail else ''}")
+        self.code = code
+
+
+def _check(code: int, where: str) -> int:
+    if code < 0:
+        raise SinkhornError(code, where)
+    return code
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclass
+class Schedule:
+    eps_start: float
+    eps_target: float
+    eps_factor: float = 0.5
+    iters_per_stage: int = 10
+    fixed_iters: int = 0
+    tol: float = 1e-3
+    max_iters: int = 10000
+    check_every: int = 1
+
+    def _c(self) -> _ScheduleC:
+        return _ScheduleC(self.eps_start, self.eps_target, self.eps_factor, self.iters_per_stage,
+                          self.fixed_iters, self.tol, self.max_iters, self.check_every)
+
+
+@dataclass
+class MultiscaleParams:
+    B: int = 128
+    p_bits: int = 0
+    eps: float = 1e-4
+    tol: float = 1e-2
+    delta_scale: float = 1e-3
+    coarse_eps_start: float = 1.0
+    coarse_factor: float = 0.5
+    coarse_iters_per_stage: int = 10
+    coarse_tol: float = 1e-3
+    coarse_max: int = 2048
+    stall_window: int = 10
+    stall_rel: float = 0.01
+    max_fine: int = 8192
+
+    def _c(self) -> _MultiscaleParamsC:
+        return _MultiscaleParamsC(self.B, self.p_bits, self.eps, self.tol, self.delta_scale,
+                                  self.coarse_eps_start, self.coarse_factor,
+                                  self.coarse_iters_per_stage, self.coarse_tol, self.coarse_max,
+                                  self.stall_window, self.stall_rel, self.max_fine)
+
+
+def _struct_dict(s) -> dict:
+    return {name: getattr(s, name) for name, _ in s._fields_}
+
+
+def mean_sqeuclid(x: torch.Tensor, y: torch.Tensor) -> float:
+    """Unweighted mean of ||x_i - y_j||^2 over all pairs (device fp64)."""
+    _dev(x, torch.float32, "x")
+    _dev(y, torch.float32, "y")
+    out = _f64()
+    _check(lib().sinkhorn_mean_sqeuclid(_ptr(x), _ptr(y), x.shape[0], y.shape[0], x.shape[1],
+                                        _stream(x.device), ctypes.byref(out)), "mean_sqeuclid")
+    return out.value
+
+
+def morton_order(x: torch.Tensor, y: torch.Tensor):
+    """(codes_x, perm_x, codes_y, perm_y): sorted Morton codes (int64 tensors
+    holding the uint64 bits) and the original index of each sorted point."""
+    _dev(x, torch.float32, "x")
+    _dev(y, torch.float32, "y")
+    n, d = x.shape
+    m = y.shape[0]
+    cx = torch.empty(n, dtype=torch.int64, device=x.device)
+    cy = torch.empty(m, dtype=torch.int64, device=x.device)
+    px = torch.empty(n, dtype=torch.int32, device=x.device)
+    py = torch.empty(m, dtype=torch.int32, device=x.device)
+    _check(lib().sinkhorn_morton_order(_ptr(x), _ptr(y), n, m, d, _stream(x.device), _ptr(cx),
+                                       _ptr(px), _ptr(cy), _ptr(py)), "morton_order")
+    return cx, px, cy, py
+
+
+class Problem:
+    """A problem handle (``sinkhorn_init``) over device clouds x [n,d], y [m,d]."""
+
+    def __init__(self, x, y, a=None, b=None, cost_scale: float = 1.0):
+        _dev(x, torch.float32, "x")
+        _dev(y, torch.float32, "y")
+        if x.dim() != 2 or y.dim() != 2 or x.shape[1] != y.shape[1]:
+            raise ValueError("x and y must be [n,d] and [m,d]")
+        self.n, self.d = x.shape
+        self.m = y.shape[0]
+        if a is not None:
+            _dev(a, torch.float32, "a", (self.n,))
+        if b is not None:
+            _dev(b, torch.float32, "b", (self.m,))
+        self.device = x.device
+        self.cost_scale = float(cost_scale)
+        h = ctypes.c_void_p()
+        _check(lib().sinkhorn_init(ctypes.byref(h), _ptr(x), _ptr(y), _ptr(a), _ptr(b), self.n,
+                                   self.m, self.d, self.cost_scale, _stream(self.device)), "init")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().sinkhorn_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _pot(self, t, k, name):
+        return _dev(t, torch.float32, name, (k,))
+
+    def _new(self, k):
+        return torch.empty(k, dtype=torch.float32, device=self.device)
+
+    def halfstep_f(self, eps, g, out=None, f_prev=None):
+        """f = f-step(g). Returns (f, R_row of (f_prev, g) or None)."""
+        self._pot(g, self.m, "g")
+        out = self._new(self.n) if out is None else self._pot(out, self.n, "out")
+        res = _f64() if f_prev is not None else None
+        if f_prev is not None:
+            self._pot(f_prev, self.n, "f_prev")
+        _check(lib().sinkhorn_halfstep_f(self._h, float(eps), _ptr(g), _ptr(out), _ptr(f_prev),
+                                         ctypes.byref(res) if res is not None else None), "halfstep_f")
+        return out, (res.value if res is not None else None)
+
+    def halfstep_g(self, eps, f, out=None, g_prev=None):
+        """g = g-step(f). Returns (g, R_col of (f, g_prev) or None)."""
+        self._pot(f, self.n, "f")
+        out = self._new(self.m) if out is None else self._pot(out, self.m, "out")
+        res = _f64() if g_prev is not None else None
+        if g_prev is not None:
+            self._pot(g_prev, self.m, "g_prev")
+        _check(lib().sinkhorn_halfstep_g(self._h, float(eps), _ptr(f), _ptr(out), _ptr(g_prev),
+                                         ctypes.byref(res) if res is not None else None), "halfstep_g")
+        return out, (res.value if res is not None else None)
+
+    def marginal_residual(self, eps, f, g):
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        r, c = _f64(), _f64()
+        _check(lib().sinkhorn_marginal_residual(self._h, float(eps), _ptr(f), _ptr(g),
+                                                ctypes.byref(r), ctypes.byref(c)), "marginal_residual")
+        return r.value, c.value
+
+    def solve(self, sched: Schedule, f=None, g=None):
+        """Annealed dense solve. Returns (f, g, report dict); report['status']
+        is OK or NOT_CONVERGED."""
+        f = torch.zeros(self.n, dtype=torch.float32, device=self.device) if f is None else self._pot(f, self.n, "f")
+        g = torch.zeros(self.m, dtype=torch.float32, device=self.device) if g is None else self._pot(g, self.m, "g")
+        sc = sched._c()
+        rep = _ReportC()
+        st = _check(lib().sinkhorn_solve(self._h, ctypes.byref(sc), _ptr(f), _ptr(g), ctypes.byref(rep)),
+                    "solve")
+        out = _struct_dict(rep)
+        out["status"] = st
+        return f, g, out
+
+    def materialize_rows(self, eps, f, g, rows, T=None, row_max=None):
+        """T[r] = plan row rows[r] (fp32 [k, m]); row_max optional [k]."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        _dev(rows, torch.int64, "rows")
+        k = rows.shape[0]
+        T = torch.empty((k, self.m), dtype=torch.float32, device=self.device) if T is None else \
+            _dev(T, torch.float32, "T", (k, self.m))
+        if row_max is not None:
+            _dev(row_max, torch.float32, "row_max", (k,))
+        _check(lib().sinkhorn_materialize_rows(self._h, float(eps), _ptr(f), _ptr(g), _ptr(rows), k,
+                                               _ptr(T), _ptr(row_max)), "materialize_rows")
+        return T, row_max
+
+    def min_row(self, eps, f, g) -> float:
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        out = ctypes.c_float()
+        _check(lib().sinkhorn_min_row(self._h, float(eps), _ptr(f), _ptr(g), ctypes.byref(out)),
+               "min_row")
+        return out.value
+
+    def block_screen(self, eps, f, g, B, delta_rel, transpose=False, cap=None):
+        """Admitted tiles as (ptr int64, idx int32) device tensors."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        nb = (self.m + B - 1) // B if transpose else (self.n + B - 1) // B
+        ptr = torch.empty(nb + 1, dtype=torch.int64, device=self.device)
+        nnz = _i64()
+        if cap is None:
+            code = lib().sinkhorn_block_screen(self._h, float(eps), _ptr(f), _ptr(g), B,
+                                               float(delta_rel), int(transpose), _ptr(ptr), None, 0,
+                                               ctypes.byref(nnz))
+            if code not in (OK, ERR_CAPACITY):
+                _check(code, "block_screen")
+            cap = nnz.value
+        idx = torch.empty(max(1, cap), dtype=torch.int32, device=self.device)
+        _check(lib().sinkhorn_block_screen(self._h, float(eps), _ptr(f), _ptr(g), B, float(delta_rel),
+                                           int(transpose), _ptr(ptr), _ptr(idx), cap,
+                                           ctypes.byref(nnz)), "block_screen")
+        return ptr, idx[: nnz.value]
+
+    def sparse_halfstep_f(self, eps, g, B, ptr, idx, out=None, f_prev=None):
+        self._pot(g, self.m, "g")
+        out = self._new(self.n) if out is None else self._pot(out, self.n, "out")
+        res = _f64() if f_prev is not None else None
+        _check(lib().sinkhorn_sparse_halfstep_f(self._h, float(eps), _ptr(g), B, _ptr(ptr), _ptr(idx),
+                                                _ptr(out), _ptr(f_prev),
+                                                ctypes.byref(res) if res is not None else None),
+               "sparse_halfstep_f")
+        return out, (res.value if res is not None else None)
+
+    def sparse_halfstep_g(self, eps, f, B, ptr, idx, out=None, g_prev=None):
+        self._pot(f, self.n, "f")
+        out = self._new(self.m) if out is None else self._pot(out, self.m, "out")
+        res = _f64() if g_prev is not None else None
+        _check(lib().sinkhorn_sparse_halfstep_g(self._h, float(eps), _ptr(f), B, _ptr(ptr), _ptr(idx),
+                                                _ptr(out), _ptr(g_prev),
+                                                ctypes.byref(res) if res is not None else None),
+               "sparse_halfstep_g")
+        return out, (res.value if res is not None else None)
+
+    def solve_multiscale(self, prm: MultiscaleParams, f=None, g=None):
+        f = self._new(self.n) if f is None else self._pot(f, self.n, "f")
+        g = self._new(self.m) if g is None else self._pot(g, self.m, "g")
+        c = prm._c()
+        rep = _MultiscaleReportC()
+        st = _check(lib().sinkhorn_solve_multiscale(self._h, ctypes.byref(c), _ptr(f), _ptr(g),
+                                                    ctypes.byref(rep)), "solve_multiscale")
+        out = _struct_dict(rep)
+        out["status"] = st
+        return f, g, out
+

@@ -1,0 +1,378 @@
+// C ABI entry points: argument checks, handle life cycle, half-steps, the
+// exact residual and the annealed dense solve driver.
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace sk {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+void fail(int code, const std::string& msg) { throw Failure{code, msg}; }
+
+void check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    fail(SINKHORN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  }
+}
+
+namespace {
+
+template <class F>
+int guard(F&& body) {
+  try {
+    g_last_error.clear();
+    return body();
+  } catch (const Failure& f) {
+    g_last_error = f.msg;
+    return f.code;
+  } catch (const std::bad_alloc&) {
+    g_last_error = "host allocation failed";
+    return SINKHORN_ERR_OOM;
+  } catch (...) {
+    g_last_error = "unexpected exception";
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+inline void require(bool ok, const char* what) {
+  if (!ok) fail(SINKHORN_ERR_INVALID_ARG, what);
+}
+
+inline void require_eps(double eps) {
+  require(std::isfinite(eps) && eps > 0.0, "eps must be finite and > 0");
+}
+
+void problem_free(sinkhorn_problem* p) {
+  if (!p) return;
+  if (p->stream) (void)hipStreamSynchronize(p->stream);
+  side_free(p->X);
+  side_free(p->Y);
+  dev_free(p->Mpart);
+  dev_free(p->Spart);
+  dev_free(p->red_part);
+  dev_free(p->red_out);
+  dev_free(p->nonfinite);
+  host_free(p->host_red);
+  for (int k = 0; k < 2; ++k) {
+    dev_free(p->fbuf[k]);
+    dev_free(p->gbuf[k]);
+  }
+  if (p->ev) (void)hipEventDestroy(p->ev);
+  delete p;
+}
+
+// f-step (rows = X) or g-step (rows = Y) with caller buffers.
+void halfstep(sinkhorn_problem* p, bool fside, double eps, const float* other, float* out,
+              const float* prev, double* l1) {
+  require(p != nullptr, "null handle");
+  require_eps(eps);
+  require(other != nullptr && out != nullptr, "null potential");
+  require(out != other && (prev == nullptr || out != prev), "output aliases an input");
+  Side& rows = fside ? p->X : p->Y;
+  Side& cols = fside ? p->Y : p->X;
+  prep_column_term(p, cols, other, eps, cols.H);
+  zero_i32(p->nonfinite, 1, p->stream);
+  HalfStep hs{&rows, &cols, cols.H, out, prev, nullptr, eps, eps, prev != nullptr && l1 != nullptr};
+  dense_halfstep(p, hs);
+  if (l1) {
+    double v = 0.0;
+    int32_t bad = 0;
+    read_reduction(p, &v, &bad);
+    *l1 = hs.residual ? v : NAN;
+    if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in half-step");
+  }
+}
+
+double seconds_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+}
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+const char* sinkhorn_strerror(int code) {
+  switch (code) {
+    case SINKHORN_OK: return "ok";
+    case SINKHORN_NOT_CONVERGED: return "not converged (iteration cap reached)";
+    case SINKHORN_ERR_INVALID_ARG: return "invalid argument";
+    case SINKHORN_ERR_OOM: return "out of memory";
+    case SINKHORN_ERR_HIP: return "HIP runtime error";
+    case SINKHORN_ERR_CAPACITY: return "output capacity too small";
+    case SINKHORN_ERR_NONFINITE: return "non-finite value";
+    case SINKHORN_ERR_MASS: return "unbalanced masses";
+    case SINKHORN_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* sinkhorn_last_error(void) { return g_last_error.c_str(); }
+
+int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
+                           void* stream, double* mean_out) {
+  return guard([&] {
+    require(x && y && mean_out, "null pointer");
+    require(n >= 1 && m >= 1 && d >= 1 && d <= 1024, "bad sizes");
+    *mean_out = device_mean_sqeuclid(x, y, n, m, d, (hipStream_t)stream);
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const float* a,
+                  const float* b, int64_t n, int64_t m, int32_t d, double cost_scale,
+                  void* stream) {
+  return guard([&] {
+    require(out != nullptr, "null output handle");
+    *out = nullptr;
+    require(x && y, "null coordinates");
+    require(n >= 1 && m >= 1, "n and m must be >= 1");
+    require(d >= 1 && d <= 1024, "d must be in [1, 1024]");
+    require(std::isfinite(cost_scale) && cost_scale > 0.0, "cost_scale must be finite and > 0");
+    sinkhorn_problem* p = new sinkhorn_problem();
+    try {
+      p->n = n;
+      p->m = m;
+      p->d = d;
+      p->scale = cost_scale;
+      p->stream = (hipStream_t)stream;
+      p->red_out = (double*)dev_alloc(sizeof(double) * 4);
+      p->nonfinite = (int32_t*)dev_alloc(sizeof(int32_t) * 4);
+      p->host_red = (double*)host_alloc(sizeof(double) * 8);
+      side_init(p, p->X, x, a, n);
+      side_init(p, p->Y, y, b, m);
+      const double sa = p->X.wsum, sb = p->Y.wsum;
+      if (std::fabs(sa - sb) > 1e-5 * std::fmax(sa, sb))
+        fail(SINKHORN_ERR_MASS, "sum(a) = " + std::to_string(sa) + " differs from sum(b) = " +
+                                    std::to_string(sb));
+      if (d > kMaxValuD) setup_mfma(p, x, y);
+      p->part_cap = std::max(partial_floats_needed(p, n, p->X.padded, m),
+                             partial_floats_needed(p, m, p->Y.padded, n));
+      p->Mpart = (float*)dev_alloc(sizeof(float) * p->part_cap);
+      p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
+      p->red_cap = std::max((n + 255) / 256, (m + 255) / 256) + 16;
+      p->red_part = (double*)dev_alloc(sizeof(double) * p->red_cap);
+      for (int k = 0; k < 2; ++k) {
+        p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);
+        p->gbuf[k] = (float*)dev_alloc(sizeof(float) * m);
+      }
+      SK_HIP(hipEventCreateWithFlags(&p->ev, hipEventDisableTiming));
+      SK_HIP(hipStreamSynchronize(p->stream));
+    } catch (...) {
+      problem_free(p);
+      throw;
+    }
+    *out = p;
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_destroy(sinkhorn_problem* p) {
+  return guard([&] {
+    problem_free(p);
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_problem_info(const sinkhorn_problem* p, int64_t* n, int64_t* m, int32_t* d,
+                          double* cost_scale) {
+  return guard([&] {
+    require(p != nullptr, "null handle");
+    if (n) *n = p->n;
+    if (m) *m = p->m;
+    if (d) *d = p->d;
+    if (cost_scale) *cost_scale = p->scale;
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_halfstep_f(sinkhorn_problem* p, double eps, const float* g, float* f_out,
+                        const float* f_prev, double* row_l1) {
+  return guard([&] {
+    halfstep(p, true, eps, g, f_out, f_prev, row_l1);
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_halfstep_g(sinkhorn_problem* p, double eps, const float* f, float* g_out,
+                        const float* g_prev, double* col_l1) {
+  return guard([&] {
+    halfstep(p, false, eps, f, g_out, g_prev, col_l1);
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_marginal_residual(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                               double* row_l1, double* col_l1) {
+  return guard([&] {
+    require(p && f && g, "null pointer");
+    double r = NAN, c = NAN;
+    halfstep(p, true, eps, g, p->fbuf[0], f, &r);
+    halfstep(p, false, eps, f, p->gbuf[0], g, &c);
+    if (row_l1) *row_l1 = r;
+    if (col_l1) *col_l1 = c;
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, float* g,
+                   sinkhorn_report* rep) {
+  return guard([&] {
+    require(p && sc && f && g, "null pointer");
+    const sinkhorn_schedule s = *sc;
+    require_eps(s.eps_target);
+    require(std::isfinite(s.eps_start) && s.eps_start >= s.eps_target, "eps_start must be >= eps_target");
+    require(s.eps_start == s.eps_target || (s.eps_factor > 0.0 && s.eps_factor < 1.0),
+            "eps_factor must be in (0, 1)");
+    require(s.iters_per_stage >= 0 && s.fixed_iters >= 0, "negative iteration count");
+    require(s.fixed_iters > 0 || (s.max_iters >= 1 && s.tol >= 0.0), "need max_iters >= 1 and tol >= 0");
+    const auto t0 = std::chrono::steady_clock::now();
+    hipStream_t st = p->stream;
+    const double pairs = (double)p->n * (double)p->m;
+    float* F[2] = {p->fbuf[0], p->fbuf[1]};
+    float* G[2] = {p->gbuf[0], p->gbuf[1]};
+    copy_f32(f, p->n, F[0], st);
+    copy_f32(g, p->m, G[0], st);
+    zero_i32(p->nonfinite, 1, st);
+    int cur = 0;
+    int64_t halfsteps = 0, iters = 0, final_iters = 0;
+    int32_t stages = 0;
+
+    // one full iteration from state `cur`; eps_next is the eps of the f-step that follows
+    auto iterate = [&](double eps, double eps_next, bool residual) {
+      HalfStep fs{&p->X, &p->Y, p->Y.H, F[1 - cur], F[cur], p->X.H, eps, eps, residual};
+      dense_halfstep(p, fs);
+      if (residual) {
+        SK_HIP(hipMemcpyAsync(p->host_red, p->red_out, sizeof(double), hipMemcpyDeviceToHost, st));
+        SK_HIP(hipMemcpyAsync(p->host_red + 1, p->nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+        SK_HIP(hipEventRecord(p->ev, st));
+      }
+      HalfStep gs{&p->Y, &p->X, p->X.H, G[1 - cur], G[cur], p->Y.H, eps, eps_next, false};
+      dense_halfstep(p, gs);
+      halfsteps += 2;
+      cur = 1 - cur;
+    };
+    auto nonfinite_now = [&]() {
+      int32_t bad;
+      memcpy(&bad, p->host_red + 1, sizeof(int32_t));
+      return bad;
+    };
+
+    // annealing stages
+    double eps = s.eps_start;
+    bool first = true;
+    while (eps > s.eps_target) {
+      double nxt = eps * s.eps_factor;
+      const double eps_after = nxt > s.eps_target ? nxt : s.eps_target;
+      if (s.iters_per_stage > 0) {
+        if (first) prep_column_term(p, p->Y, G[cur], eps, p->Y.H);
+        first = false;
+        for (int32_t k = 0; k < s.iters_per_stage; ++k) {
+          const bool last = k + 1 == s.iters_per_stage;
+          iterate(eps, last ? eps_after : eps, false);
+          ++iters;
+        }
+      }
+      ++stages;
+      eps = nxt;
+    }
+    eps = s.eps_target;
+    if (first) prep_column_term(p, p->Y, G[cur], eps, p->Y.H);
+
+    int status = SINKHORN_OK;
+    double row_l1 = NAN, col_l1 = NAN, seconds = 0.0;
+    int32_t converged = 0;
+    int ret = cur;
+    if (s.fixed_iters > 0) {
+      for (int32_t k = 0; k < s.fixed_iters; ++k) {
+        iterate(eps, eps, false);
+        ++iters;
+        ++final_iters;
+      }
+      ret = cur;
+      converged = 1;
+    } else {
+      const int32_t every = s.check_every > 1 ? s.check_every : 1;
+      // iteration k checks the state left by iteration k-1
+      for (int64_t k = 1;; ++k) {
+        const int64_t prev_done = k - 1;
+        const bool check = prev_done >= 1 && prev_done % every == 0;
+        const bool last_allowed = prev_done >= s.max_iters;
+        if (last_allowed) {
+          // only the residual of the final state is still needed
+          HalfStep fs{&p->X, &p->Y, p->Y.H, F[1 - cur], F[cur], nullptr, eps, eps, true};
+          dense_halfstep(p, fs);
+          ++halfsteps;
+          double v;
+          int32_t bad;
+          read_reduction(p, &v, &bad);
+          if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
+          row_l1 = v;
+          ret = cur;
+          converged = v <= s.tol ? 1 : 0;
+          seconds = seconds_since(t0);
+          break;
+        }
+        const int state = cur;
+        iterate(eps, eps, check);
+        if (check) {
+          SK_HIP(hipEventSynchronize(p->ev));
+          if (nonfinite_now()) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
+          const double v = p->host_red[0];
+          if (v <= s.tol) {
+            row_l1 = v;
+            ret = state;
+            converged = 1;
+            seconds = seconds_since(t0);
+            break;
+          }
+        }
+        ++iters;
+        ++final_iters;
+      }
+      if (!converged) status = SINKHORN_NOT_CONVERGED;
+    }
+    // residuals of the returned state (the row side is known in the tol mode)
+    {
+      double r = NAN, c = NAN;
+      if (std::isnan(row_l1)) {
+        halfstep(p, true, eps, G[ret], F[1 - ret], F[ret], &r);
+        row_l1 = r;
+        ++halfsteps;
+      }
+      halfstep(p, false, eps, F[ret], G[1 - ret], G[ret], &c);
+      col_l1 = c;
+      ++halfsteps;
+    }
+    if (seconds == 0.0) seconds = seconds_since(t0);
+    copy_f32(F[ret], p->n, f, st);
+    copy_f32(G[ret], p->m, g, st);
+    SK_HIP(hipStreamSynchronize(st));
+    if (rep) {
+      rep->halfsteps = halfsteps;
+      rep->iters = iters;
+      rep->final_iters = final_iters;
+      rep->pairs_evaluated = pairs * (double)halfsteps;
+      rep->row_l1 = row_l1;
+      rep->col_l1 = col_l1;
+      rep->seconds = seconds;
+      rep->stages = stages;
+      rep->converged = converged;
+    }
+    return status;
+  });
+}
+
+}  // extern "C"

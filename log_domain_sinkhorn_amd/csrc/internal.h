@@ -1,0 +1,124 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "sinkhorn.h"
+
+namespace sk {
+
+// ---------------------------------------------------------------- errors
+struct Failure {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const std::string& msg);
+void check_hip(hipError_t e, const char* what);
+void set_last_error(const std::string& msg);
+
+#define SK_HIP(call) ::sk::check_hip((call), #call)
+#define SK_LAUNCH_CHECK() ::sk::check_hip(hipGetLastError(), "kernel launch")
+
+// ---------------------------------------------------------------- constants
+constexpr double kLog2e = 1.4426950408889634074;  // 1 / ln 2
+constexpr double kLn2 = 0.69314718055994530942;
+// Every side is stored padded to a multiple of this many points; padding has
+// zero coordinates and a -inf column term, so it never contributes.
+constexpr int64_t kPad = 1024;
+// Points per column chunk of the VALU kernel (one scalar load per array).
+constexpr int kChunk = 16;
+// Largest d served by the VALU difference-form kernel; above it the cross
+// term runs on MFMA.
+constexpr int kMaxValuD = 8;
+// Row tiles per MFMA kernel uses 32-point tiles, K padded to a multiple of 4.
+constexpr int kMfmaTile = 32;
+
+inline int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
+
+// ---------------------------------------------------------------- device memory
+void* dev_alloc(size_t bytes);
+void dev_free(void* p);
+void* host_alloc(size_t bytes);  // pinned
+void host_free(void* p);
+
+// One cloud as stored by a handle.
+struct Side {
+  int64_t count = 0;   // points
+  int64_t padded = 0;  // round_up(count, kPad)
+  float* soa = nullptr;    // [d][padded] coordinates (VALU path), zero padding
+  float* rowmaj = nullptr; // [padded][kpad] centred coordinates (MFMA path), zero padding
+  float* norm2 = nullptr;  // [padded] ||centred point||^2 (MFMA path)
+  float* w = nullptr;      // [count] weights
+  float* H = nullptr;      // [padded] column term of this side, -inf padding
+  double wsum = 0.0;
+};
+
+// Per-launch description of one dense half-step "rows against columns".
+struct HalfStep {
+  const Side* rows;
+  const Side* cols;
+  const float* Hcols;      // column term (log2 units) of the column side
+  float* pot_out;          // [rows.count]
+  const float* pot_prev;   // nullable, for the residual
+  float* H_next;           // nullable: column term of the row side for the next step
+  double eps;              // eps of this half-step
+  double eps_next;         // eps used for H_next
+  bool residual;
+};
+
+}  // namespace sk
+
+struct sinkhorn_problem {
+  int64_t n = 0, m = 0;
+  int32_t d = 0;
+  int32_t kpad = 0;  // MFMA K (d rounded up to a multiple of 4), 0 on the VALU path
+  double scale = 1.0;
+  hipStream_t stream = nullptr;
+  sk::Side X, Y;
+  // split-m partials of the row reduction: [max_split][max(npad, mpad)] each
+  float* Mpart = nullptr;
+  float* Spart = nullptr;
+  int64_t part_cap = 0;  // floats per partial array
+  // residual block partials and the reduced values
+  double* red_part = nullptr;
+  int64_t red_cap = 0;
+  double* red_out = nullptr;     // [4] device
+  int32_t* nonfinite = nullptr;  // [1] device counter
+  double* host_red = nullptr;    // [8] pinned
+  // solve scratch: double-buffered potentials
+  float* fbuf[2] = {nullptr, nullptr};
+  float* gbuf[2] = {nullptr, nullptr};
+  hipEvent_t ev = nullptr;
+};
+
+namespace sk {
+
+// setup.hip helpers
+void zero_i32(int32_t* v, int32_t count, hipStream_t st);
+void fill_f32(float* v, int64_t count, float value, hipStream_t st);
+void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st);
+
+// dense.hip
+int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
+                              int64_t ncols);
+void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
+                      float* H);
+void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs);
+// returns (residual sum, nonfinite count) after a synchronizing read
+void read_reduction(sinkhorn_problem* p, double* value, int32_t* nonfinite);
+void reset_nonfinite(sinkhorn_problem* p);
+
+// setup.hip
+void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count);
+void side_free(Side& s);
+// mfma.hip (d > kMaxValuD)
+void setup_mfma(sinkhorn_problem* p, const float* x, const float* y);
+
+double device_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
+                            hipStream_t st);
+
+}  // namespace sk

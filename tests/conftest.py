@@ -14,8 +14,9 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU test")
 
 
-@pytest.fixture(scope="session")
+@pytest.fixture
 def rng():
+    """A fresh seeded generator per test, so no test depends on test order."""
     import numpy as np
 
     return np.random.default_rng(12345)

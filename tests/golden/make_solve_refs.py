@@ -1,0 +1,52 @@
+"""Write the oracle's annealed-solve results used by the GPU solve-parity tests.
+
+Calls only ``oracle`` and ``synth`` (the seeded generators). Each case stores
+the fp64 potentials, the iteration counts and the residuals of the oracle run
+in ``tests/golden/solve_<name>.npz``. Regenerate with
+
+    python tests/golden/make_solve_refs.py [name ...]
+"""
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+# name: (workload, n, m, schedule kwargs, cost scale rule)
+CASES = {
+    "w1_full_fixed200": (1, None, None, dict(eps_start=0.01, eps_target=0.01, fixed_iters=200), "one"),
+    "w2_n1000_tol": (2, 1000, 1000, dict(eps_start=1.0, eps_target=1e-3, tol=1e-3, max_iters=5000), "one"),
+    "w4_n1000_tol": (4, 1000, 1000, dict(eps_start=1.0, eps_target=1e-4, tol=1e-3, max_iters=5000), "one"),
+    "w3_n1500_tol": (3, 1500, 1800, dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=5000), "mean"),
+}
+
+
+def run(name):
+    w, n, m, kw, rule = CASES[name]
+    c = synth.make(w, n=n, m=m)
+    scale = 1.0 if rule == "one" else 1.0 / oracle.mean_sqeuclid(c.x, c.y)
+    sched = oracle.Schedule(**kw)
+    t = time.time()
+    r = oracle.solve(c.x, c.y, c.a, c.b, scale, sched)
+    out = os.path.join(HERE, f"solve_{name}.npz")
+    np.savez_compressed(
+        out, f=r.f, g=r.g, iters=r.iters, final_iters=r.final_iters, R_row=r.R_row, R_col=r.R_col,
+        converged=r.converged, scale=scale, workload=w, n=c.n, m=c.m,
+        eps_start=sched.eps_start, eps_target=sched.eps_target, eps_factor=sched.eps_factor,
+        iters_per_stage=sched.iters_per_stage, fixed_iters=sched.fixed_iters, tol=sched.tol,
+        max_iters=sched.max_iters,
+    )
+    print(f"{name}: iters {r.iters} (final {r.final_iters}) R {r.R_row:.3e}/{r.R_col:.3e} "
+          f"converged {r.converged} in {time.time() - t:.1f}s -> {out}", flush=True)
+
+
+if __name__ == "__main__":
+    for name in sys.argv[1:] or list(CASES):
+        run(name)

@@ -1,0 +1,249 @@
+"""GPU parity of the dense online half-steps, the residual and the annealed
+solve against the fp64 oracle (same seeded inputs on both sides).
+
+Tolerances (stated with the workloads): one half-step from identical
+potentials within 1e-5 * max(eps, |f|) per entry; final potentials within
+1e-3 * eps after the same number of iterations.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _skip_without_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def sk():
+    _skip_without_gpu()
+    import log_domain_sinkhorn_amd as sk
+
+    return sk
+
+
+DEV = "cuda:0"
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _problem(sk, c, scale=1.0, uniform=False):
+    return sk.Problem(_t(c.x), _t(c.y), None if uniform else _t(c.a), None if uniform else _t(c.b), scale)
+
+
+def _assert_halfstep(got, ref, eps, what):
+    err = np.abs(got.astype(np.float64) - ref) / np.maximum(eps, np.abs(ref))
+    worst = int(np.argmax(err))
+    assert err.max() <= 1e-5, f"{what}: max rel err {err.max():.3e} at {worst} (got {got[worst]}, ref {ref[worst]})"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize(
+    "workload,n,m,eps_list",
+    [
+        (1, None, None, [0.01, 1.0]),
+        (2, None, None, [1e-3, 0.125]),
+        (2, 1, 1, [1e-2]),
+        (2, 37, 1029, [1e-3]),
+        (2, 1029, 37, [1e-3]),
+        (1, 3001, 517, [1e-2]),
+        (4, 4096, 4096, [1e-4, 1e-2]),
+    ],
+)
+def test_single_halfsteps_match_oracle(sk, workload, n, m, eps_list):
+    c = synth.make(workload, n=n, m=m)
+    _log(f"halfstep parity workload={workload} n={c.n} m={c.m}")
+    rng = np.random.default_rng(100 + workload)
+    with _problem(sk, c) as P:
+        for eps in eps_list:
+            g0 = (rng.normal(0, 1, c.m) * eps).astype(np.float32)
+            f, _ = P.halfstep_f(eps, _t(g0))
+            f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, 1.0)
+            _assert_halfstep(f.cpu().numpy(), f_ref, eps, f"f-step eps={eps}")
+            f32 = f_ref.astype(np.float32)
+            g, _ = P.halfstep_g(eps, _t(f32))
+            g_ref = oracle.halfstep_g(c.x, c.y, c.a, f32, eps, 1.0)
+            _assert_halfstep(g.cpu().numpy(), g_ref, eps, f"g-step eps={eps}")
+
+
+def test_full_size_sampled_rows_workload4(sk):
+    """n = m = 10^6 at eps = 1e-4: every row on the GPU, 256 sampled rows and
+    columns recomputed by the oracle one by one."""
+    c = synth.make(4)
+    eps = 1e-4
+    rng = np.random.default_rng(44)
+    g0 = (rng.normal(0, 1, c.m) * eps).astype(np.float32)
+    _log("workload 4 full-size halfstep")
+    with _problem(sk, c, uniform=True) as P:
+        f, _ = P.halfstep_f(eps, _t(g0))
+        f = f.cpu().numpy()
+        rows = rng.choice(c.n, 256, replace=False)
+        f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, 1.0, rows=rows)
+        _assert_halfstep(f[rows], f_ref, eps, "f-step sampled rows")
+        g, _ = P.halfstep_g(eps, _t(f))
+        g = g.cpu().numpy()
+        cols = rng.choice(c.m, 256, replace=False)
+        g_ref = oracle.halfstep_g(c.x, c.y, c.a, f, eps, 1.0, cols=cols)
+        _assert_halfstep(g[cols], g_ref, eps, "g-step sampled cols")
+
+
+def test_massless_points_and_all_massless_side(sk):
+    c = synth.make(2, n=300, m=400)
+    b = c.b.copy()
+    b[::3] = 0.0
+    b = (b / b.astype(np.float64).sum()).astype(np.float32)
+    a = c.a.copy()
+    a[:50] = 0.0
+    a = (a / a.astype(np.float64).sum()).astype(np.float32)
+    eps = 1e-2
+    with sk.Problem(_t(c.x), _t(c.y), _t(a), _t(b), 1.0) as P:
+        g0 = np.zeros(c.m, np.float32)
+        f, _ = P.halfstep_f(eps, _t(g0))
+        _assert_halfstep(f.cpu().numpy(), oracle.halfstep_f(c.x, c.y, b, g0, eps, 1.0), eps, "f with b_j = 0")
+        f32 = f.cpu().numpy()
+        g, _ = P.halfstep_g(eps, _t(f32))
+        _assert_halfstep(g.cpu().numpy(), oracle.halfstep_g(c.x, c.y, a, f32, eps, 1.0), eps, "g with a_i = 0")
+    # every exponent -C/eps overflows to -inf: an all -inf row, so f = +inf
+    x = np.zeros((3, 2), np.float32)
+    y = np.full((2, 2), 10.0, np.float32)  # |x - y|^2 = 200: 200 * s * log2(e) / eps overflows
+    with sk.Problem(_t(x), _t(y), None, None, 1.0) as P:
+        out = torch.empty(3, device=DEV)
+        prev = torch.zeros(3, device=DEV)
+        with pytest.raises(sk.SinkhornError) as ei:
+            P.halfstep_f(1e-38, _t(np.zeros(2, np.float32)), out=out, f_prev=prev)
+        assert ei.value.code == sk.ERR_NONFINITE
+        assert torch.isinf(out).all()
+
+
+def test_init_errors(sk):
+    c = synth.make(1, n=10, m=12)
+    with pytest.raises(sk.SinkhornError) as ei:
+        sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b * 2), 1.0)
+    assert ei.value.code == sk.ERR_MASS
+    xb = c.x.copy()
+    xb[3, 1] = np.nan
+    with pytest.raises(sk.SinkhornError) as ei:
+        sk.Problem(_t(xb), _t(c.y), _t(c.a), _t(c.b), 1.0)
+    assert ei.value.code == sk.ERR_NONFINITE
+
+
+def test_fused_row_residual_matches_explicit_plan(sk):
+    c = synth.make(2, n=1500, m=1300)
+    eps = 5e-3
+    rng = np.random.default_rng(3)
+    f0 = (rng.normal(0, 1, c.n) * eps).astype(np.float32)
+    g0 = (rng.normal(0, 1, c.m) * eps).astype(np.float32)
+    with _problem(sk, c) as P:
+        _, r = P.halfstep_f(eps, _t(g0), f_prev=_t(f0))
+        _, cr = P.halfstep_g(eps, _t(f0), g_prev=_t(g0))
+        R_row, R_col = oracle.marginal_residuals(c.x, c.y, c.a, c.b, f0, g0, eps, 1.0)
+        # error of the half-step (1e-5 max(eps,|f|)) propagated through exp(./eps)
+        f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, 1.0)
+        bound = (c.a * np.exp((f0 - f_ref) / eps) * 1e-5 * np.maximum(eps, np.abs(f_ref)) / eps).sum()
+        assert abs(r - R_row) <= bound + 1e-12, (r, R_row, bound)
+        g_ref = oracle.halfstep_g(c.x, c.y, c.a, f0, eps, 1.0)
+        bound = (c.b * np.exp((g0 - g_ref) / eps) * 1e-5 * np.maximum(eps, np.abs(g_ref)) / eps).sum()
+        assert abs(cr - R_col) <= bound + 1e-12, (cr, R_col, bound)
+        rr, cc = P.marginal_residual(eps, _t(f0), _t(g0))
+        assert rr == r and cc == cr  # the same kernels, deterministic
+
+
+def test_mean_sqeuclid(sk):
+    c = synth.make(3, n=3000, m=2000)
+    got = sk.mean_sqeuclid(_t(c.x), _t(c.y))
+    assert got == pytest.approx(oracle.mean_sqeuclid(c.x, c.y), rel=1e-10)
+
+
+def test_bit_reproducible(sk):
+    c = synth.make(2, n=5000, m=7000)
+    g0 = np.zeros(c.m, np.float32)
+    with _problem(sk, c) as P:
+        f1, _ = P.halfstep_f(1e-3, _t(g0))
+        f2, _ = P.halfstep_f(1e-3, _t(g0))
+        assert torch.equal(f1, f2)
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    path = os.path.join(GOLDEN, f"solve_{name}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_solve_refs.py")
+    return dict(np.load(path))
+
+
+def _schedule(sk, ref, **over):
+    kw = dict(eps_start=float(ref["eps_start"]), eps_target=float(ref["eps_target"]),
+              eps_factor=float(ref["eps_factor"]), iters_per_stage=int(ref["iters_per_stage"]),
+              fixed_iters=int(ref["fixed_iters"]), tol=float(ref["tol"]), max_iters=int(ref["max_iters"]))
+    kw.update(over)
+    return sk.Schedule(**kw)
+
+
+def _golden_problem(sk, ref):
+    c = synth.make(int(ref["workload"]), n=int(ref["n"]), m=int(ref["m"]))
+    return c, sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), float(ref["scale"]))
+
+
+def _potentials_close(f, g, ref, eps):
+    df = np.abs(f.cpu().numpy().astype(np.float64) - ref["f"]).max()
+    dg = np.abs(g.cpu().numpy().astype(np.float64) - ref["g"]).max()
+    assert df <= 1e-3 * eps and dg <= 1e-3 * eps, (df, dg, 1e-3 * eps)
+
+
+@pytest.mark.parametrize("name", ["w1_full_fixed200", "w2_n1000_tol", "w4_n1000_tol"])
+def test_solve_same_iteration_count_gives_same_potentials(sk, name):
+    """Run exactly the oracle's iteration count, then compare the potentials."""
+    ref = _golden(name)
+    eps = float(ref["eps_target"])
+    _log(f"solve parity {name} ({int(ref['iters'])} iterations)")
+    c, P = _golden_problem(sk, ref)
+    with P:
+        f, g, rep = P.solve(_schedule(sk, ref, fixed_iters=int(ref["final_iters"])))
+        assert rep["status"] == sk.OK and rep["iters"] == int(ref["iters"])
+        _potentials_close(f, g, ref, eps)
+        # a residual computed from fp32 potentials carries the half-step
+        # tolerance through exp(./eps): sum_i a_i 1e-5 max(eps, |f_i|) / eps
+        floor = float((c.a * 1e-5 * np.maximum(eps, np.abs(ref["f"])) / eps).sum())
+        assert abs(rep["row_l1"] - float(ref["R_row"])) <= 2e-2 * float(ref["R_row"]) + floor
+
+
+@pytest.mark.parametrize("name", ["w2_n1000_tol", "w4_n1000_tol"])
+def test_solve_stops_at_the_oracles_iteration(sk, name):
+    """Tolerance mode: the residual test fires at the oracle's iteration (one
+    iteration of slack, since both residuals sit within rounding of tol there)."""
+    ref = _golden(name)
+    c, P = _golden_problem(sk, ref)
+    with P:
+        f, g, rep = P.solve(_schedule(sk, ref))
+    assert rep["status"] == sk.OK and rep["converged"] == 1
+    assert abs(rep["iters"] - int(ref["iters"])) <= 1, (rep["iters"], int(ref["iters"]))
+    assert rep["row_l1"] <= float(ref["tol"])
+    if rep["iters"] == int(ref["iters"]):
+        _potentials_close(f, g, ref, float(ref["eps_target"]))
+
+
+def test_solve_not_converged_returns_valid_potentials(sk):
+    c = synth.make(2, n=800, m=900)
+    with _problem(sk, c) as P:
+        f, g, rep = P.solve(sk.Schedule(1e-3, 1e-3, tol=1e-12, max_iters=5))
+    assert rep["status"] == sk.NOT_CONVERGED and rep["final_iters"] == 5
+    ref = oracle.solve(c.x, c.y, c.a, c.b, 1.0, oracle.Schedule(1e-3, 1e-3, fixed_iters=5))
+    assert np.abs(f.cpu().numpy() - ref.f).max() <= 1e-3 * 1e-3
