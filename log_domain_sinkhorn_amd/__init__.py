@@ -134,6 +134,8 @@ _SIGS = {
     "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_g": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_solve_multiscale": ([_p, _p, _p, _p, _p], _i32),
+    "sinkhorn_profile_enable": ([_p, _i32], _i32),
+    "sinkhorn_profile_read": ([_p, _p, _p, _p], _i32),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -414,6 +416,17 @@ class Problem:
                                                 ctypes.byref(res) if res is not None else None),
                "sparse_halfstep_g")
         return out, (res.value if res is not None else None)
+
+    def profile_enable(self, enable: bool = True):
+        """Bracket every later pair-loop kernel launch with HIP events."""
+        _check(lib().sinkhorn_profile_enable(self._h, int(bool(enable))), "profile_enable")
+
+    def profile_read(self):
+        """(kernel_ms, launches, pairs) recorded since the last read (syncs)."""
+        ms, n, pairs = _f64(), _i64(), _f64()
+        _check(lib().sinkhorn_profile_read(self._h, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(pairs)),
+               "profile_read")
+        return ms.value, n.value, pairs.value
 
     def solve_multiscale(self, prm: MultiscaleParams, f=None, g=None):
         f = self._new(self.n) if f is None else self._pot(f, self.n, "f")

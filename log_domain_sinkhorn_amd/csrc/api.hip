@@ -25,6 +25,25 @@ void check_hip(hipError_t e, const char* what) {
   }
 }
 
+void prof_begin(sinkhorn_problem* p) {
+  if (!p->prof) return;
+  if (p->prof_ev.size() < 2 * (p->prof_used + 1)) {
+    for (int k = 0; k < 2; ++k) {
+      hipEvent_t e;
+      SK_HIP(hipEventCreate(&e));
+      p->prof_ev.push_back(e);
+    }
+  }
+  SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used], p->stream));
+}
+
+void prof_end(sinkhorn_problem* p, double pairs) {
+  if (!p->prof) return;
+  SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used + 1], p->stream));
+  ++p->prof_used;
+  p->prof_pairs += pairs;
+}
+
 namespace {
 
 template <class F>
@@ -60,14 +79,16 @@ void problem_free(sinkhorn_problem* p) {
   dev_free(p->Mpart);
   dev_free(p->Spart);
   dev_free(p->red_part);
-  dev_free(p->red_out);
-  dev_free(p->nonfinite);
-  host_free(p->host_red);
+  dev_free(p->cnt);
+  dev_free(p->ctl);
+  host_free(p->host_ctl);
+  host_free(p->host_tmp);
   for (int k = 0; k < 2; ++k) {
     dev_free(p->fbuf[k]);
     dev_free(p->gbuf[k]);
   }
   if (p->ev) (void)hipEventDestroy(p->ev);
+  for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   delete p;
 }
 
@@ -81,7 +102,7 @@ void halfstep(sinkhorn_problem* p, bool fside, double eps, const float* other, f
   Side& rows = fside ? p->X : p->Y;
   Side& cols = fside ? p->Y : p->X;
   prep_column_term(p, cols, other, eps, cols.H);
-  zero_i32(p->nonfinite, 1, p->stream);
+  reset_nonfinite(p);
   HalfStep hs{&rows, &cols, cols.H, out, prev, nullptr, eps, eps, prev != nullptr && l1 != nullptr};
   dense_halfstep(p, hs);
   if (l1) {
@@ -148,9 +169,9 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       p->d = d;
       p->scale = cost_scale;
       p->stream = (hipStream_t)stream;
-      p->red_out = (double*)dev_alloc(sizeof(double) * 4);
-      p->nonfinite = (int32_t*)dev_alloc(sizeof(int32_t) * 4);
-      p->host_red = (double*)host_alloc(sizeof(double) * 8);
+      p->ctl = (Ctl*)dev_alloc(sizeof(Ctl));
+      p->host_ctl = (Ctl*)host_alloc(sizeof(Ctl));
+      p->host_tmp = (double*)host_alloc(sizeof(double) * 8);
       side_init(p, p->X, x, a, n);
       side_init(p, p->Y, y, b, m);
       const double sa = p->X.wsum, sb = p->Y.wsum;
@@ -162,8 +183,11 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
                              partial_floats_needed(p, m, p->Y.padded, n));
       p->Mpart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
-      p->red_cap = std::max((n + 255) / 256, (m + 255) / 256) + 16;
+      p->red_cap = std::max(row_groups(n), row_groups(m)) + 16;
       p->red_part = (double*)dev_alloc(sizeof(double) * p->red_cap);
+      p->cnt = (uint32_t*)dev_alloc(sizeof(uint32_t) * (p->red_cap + 1));
+      zero_i32((int32_t*)p->cnt, (int32_t)(p->red_cap + 1), p->stream);
+      reset_nonfinite(p);
       for (int k = 0; k < 2; ++k) {
         p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);
         p->gbuf[k] = (float*)dev_alloc(sizeof(float) * m);
@@ -245,7 +269,7 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
     float* G[2] = {p->gbuf[0], p->gbuf[1]};
     copy_f32(f, p->n, F[0], st);
     copy_f32(g, p->m, G[0], st);
-    zero_i32(p->nonfinite, 1, st);
+    reset_nonfinite(p);
     int cur = 0;
     int64_t halfsteps = 0, iters = 0, final_iters = 0;
     int32_t stages = 0;
@@ -255,8 +279,7 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
       HalfStep fs{&p->X, &p->Y, p->Y.H, F[1 - cur], F[cur], p->X.H, eps, eps, residual};
       dense_halfstep(p, fs);
       if (residual) {
-        SK_HIP(hipMemcpyAsync(p->host_red, p->red_out, sizeof(double), hipMemcpyDeviceToHost, st));
-        SK_HIP(hipMemcpyAsync(p->host_red + 1, p->nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+        copy_ctl(p);
         SK_HIP(hipEventRecord(p->ev, st));
       }
       HalfStep gs{&p->Y, &p->X, p->X.H, G[1 - cur], G[cur], p->Y.H, eps, eps_next, false};
@@ -264,11 +287,7 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
       halfsteps += 2;
       cur = 1 - cur;
     };
-    auto nonfinite_now = [&]() {
-      int32_t bad;
-      memcpy(&bad, p->host_red + 1, sizeof(int32_t));
-      return bad;
-    };
+    auto nonfinite_now = [&]() { return p->host_ctl->nonfinite; };
 
     // annealing stages
     double eps = s.eps_start;
@@ -330,7 +349,7 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
         if (check) {
           SK_HIP(hipEventSynchronize(p->ev));
           if (nonfinite_now()) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
-          const double v = p->host_red[0];
+          const double v = p->host_ctl->residual;
           if (v <= s.tol) {
             row_l1 = v;
             ret = state;
@@ -372,6 +391,38 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
       rep->converged = converged;
     }
     return status;
+  });
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t enable) {
+  return guard([&] {
+    require(p != nullptr, "null handle");
+    p->prof = enable != 0;
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launches,
+                          double* pairs) {
+  return guard([&] {
+    require(p != nullptr, "null handle");
+    SK_HIP(hipStreamSynchronize(p->stream));
+    double total = 0.0;
+    for (size_t k = 0; k < p->prof_used; ++k) {
+      float ms = 0.0f;
+      SK_HIP(hipEventElapsedTime(&ms, p->prof_ev[2 * k], p->prof_ev[2 * k + 1]));
+      total += (double)ms;
+    }
+    if (kernel_ms) *kernel_ms = total;
+    if (launches) *launches = (int64_t)p->prof_used;
+    if (pairs) *pairs = p->prof_pairs;
+    p->prof_used = 0;
+    p->prof_pairs = 0.0;
+    return SINKHORN_OK;
   });
 }
 

@@ -1,13 +1,25 @@
-// Dense online half-step for small d (difference form on VALU), its finalize
-// step (split merge, potential, fused residual, next column term) and the
-// deterministic reductions.
+// Dense online half-step for small d: difference-form pair loop on the VALU.
 //
 // FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport, §2.1: a half-step
 // is a tiled streaming log-sum-exp over all pairs that never stores the cost.
-// Here one lane owns R rows; the column tile (coordinates and column term) is
-// wave-uniform and arrives through scalar loads, so every pair costs d subs,
-// d squares (1 mul + d-1 fma), one fma for the exponent, one max, one sub, one
-// exp2 and one add, all on the vector ALU.
+//
+// Layout and mapping:
+//   * a lane owns R rows (row side SoA, coalesced loads); the column tile
+//     (coordinates and column term of kChunk points) is wave-uniform and
+//     arrives through scalar loads, so each pair costs d subs, 1 mul +
+//     (d-1) fma for the squared distance, 1 fma for the exponent, a max, a
+//     sub, an exp2 and an add on the vector ALU;
+//   * a workgroup holds W waves on the SAME 64R rows, each wave a contiguous
+//     slice of the workgroup's columns; the W partial (max, sum) pairs are
+//     merged through LDS in wave order;
+//   * when the rows alone give too few workgroups, G workgroups per row tile
+//     split the columns further and a small merge kernel combines their
+//     partials in split order; otherwise the workgroup finalizes in place.
+// Finalizing writes the potential, optionally the next column term of the row
+// side (log2 w_i + pot_i log2(e)/eps_next) and the residual terms
+// w_i |exp((prev_i - new_i)/eps) - 1|, summed per workgroup and then, on
+// request, in workgroup order by a one-block kernel. Results are
+// bit-reproducible.
 #include <cfloat>
 #include <cmath>
 #include <cstring>
@@ -17,40 +29,82 @@
 namespace sk {
 namespace {
 
-// Base-2 exponential of the hardware (v_exp_f32). Arguments are <= 0 or -inf
-// here, where it is accurate to about 1 ulp; -inf gives +0.
+// Base-2 exponential of the hardware (v_exp_f32). Arguments here are <= 0 or
+// -inf, where it is accurate to about 1 ulp; -inf gives +0.
 __device__ __forceinline__ float ex2(float v) { return __builtin_amdgcn_exp2f(v); }
 
-// One wave = 64 lanes x R rows against the column range of one split.
-// Block = 4 waves on 4 consecutive row tiles, all on the same split so the
-// scalar-loaded column tile is shared through the scalar cache.
-template <int D, int R>
-__global__ __launch_bounds__(256) void k_lse_valu(
-    const float* __restrict__ P, int64_t pstride,      // row side, SoA [D][pstride]
-    const float* __restrict__ Q, int64_t qstride,      // column side, SoA [D][qstride]
-    const float* __restrict__ H,                       // column term, log2 units
-    float nkappa,                                      // -s * log2(e) / eps
-    int64_t nchunks, int64_t chunks_per_split, int32_t nsplit, int64_t np,
-    float* __restrict__ Mp, float* __restrict__ Sp, int64_t part_stride) {
-  const int32_t s = (int32_t)(blockIdx.x % (uint32_t)nsplit);
-  const int64_t rg = blockIdx.x / (uint32_t)nsplit;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t row0 = (rg * 4 + wave) * (64 * R) + lane;
+constexpr int kR = 2;                // rows per lane
+constexpr int kW = 8;                // waves per workgroup
+constexpr int kRowsPerTile = 64 * kR;
+constexpr int kThreads = 64 * kW;
 
-  float x[R][D];
-  float M[R], S[R];
+struct LseArgs {
+  const float* P;       // row side SoA [D][pstride]
+  int64_t pstride;
+  const float* Q;       // column side SoA [D][qstride]
+  int64_t qstride;
+  const float* H;       // column term of the column side, log2 units, -inf padding
+  float nkappa;         // -s log2(e) / eps
+  int32_t G;            // workgroups per row tile (global column splits)
+  int64_t nchunks;      // column chunks of kChunk points
+  int64_t cps;          // chunks per global split
+  int64_t np;           // rows
+  float* Mp;            // [G][np] partial max (G > 1)
+  float* Sp;            // [G][np] partial sum (G > 1)
+  // finalize (G == 1)
+  const float* w;       // row weights [np]
+  float* out;           // new potentials [np]
+  const float* prev;    // previous potentials [np] for the residual, or null
+  float* Hnext;         // next column term of the row side, or null
+  double neg_eps_ln2;   // -eps ln 2
+  double inv_eps;
+  double lam_next;      // log2(e) / eps_next
+  double* red_part;     // [tiles] residual per workgroup (if prev)
+  Ctl* ctl;
+};
+
+// Potential, next column term and residual term of row i from its merged
+// (max, sum); returns the residual term.
+__device__ __forceinline__ double finalize_row(const LseArgs& A, int64_t i, float mx, double sum,
+                                               int* bad) {
+  const double v = A.neg_eps_ln2 * ((double)mx + log2(sum));  // sum == 0 -> +inf
+  const float v32 = (float)v;
+  A.out[i] = v32;
+  if (!isfinite(v32)) ++*bad;
+  const double wi = (double)A.w[i];
+  if (A.Hnext) A.Hnext[i] = (float)(log2(wi) + (double)v32 * A.lam_next);
+  if (A.prev && wi > 0.0) return wi * fabs(expm1(((double)A.prev[i] - v) * A.inv_eps));
+  return 0.0;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
+  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)A.G);
+  const int64_t tile = blockIdx.x / (uint32_t)A.G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = tile * kRowsPerTile + lane;
+
+  float x[kR][D];
+  float M[kR], S[kR];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < kR; ++r) {
 #pragma unroll
-    for (int k = 0; k < D; ++k) x[r][k] = P[k * pstride + row0 + 64 * r];
+    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
     M[r] = -FLT_MAX;
     S[r] = 0.0f;
   }
-  const float nk = nkappa;
+  const float nk = A.nkappa;
+  const float* __restrict__ Q = A.Q;
+  const float* __restrict__ H = A.H;
+  const int64_t qs = A.qstride;
 
-  const int64_t c0 = (int64_t)s * chunks_per_split;
-  const int64_t c1 = c0 + chunks_per_split < nchunks ? c0 + chunks_per_split : nchunks;
+  // this wave's slice of this workgroup's column range
+  const int64_t g0 = (int64_t)gs * A.cps;
+  const int64_t g1 = g0 + A.cps < A.nchunks ? g0 + A.cps : A.nchunks;
+  const int64_t per = (g1 - g0 + kW - 1) / kW;
+  const int64_t c0 = g0 + wave * per;
+  const int64_t c1 = c0 + per < g1 ? c0 + per : g1;
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t j0 = c * kChunk;
     float yv[D][kChunk];
@@ -58,12 +112,12 @@ __global__ __launch_bounds__(256) void k_lse_valu(
 #pragma unroll
     for (int k = 0; k < D; ++k)
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qstride + j0 + jj];
+      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qs + j0 + jj];
 #pragma unroll
     for (int jj = 0; jj < kChunk; ++jj) hv[jj] = H[j0 + jj];
 
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < kR; ++r) {
       float z[kChunk];
 #pragma unroll
       for (int jj = 0; jj < kChunk; ++jj) {
@@ -87,62 +141,95 @@ __global__ __launch_bounds__(256) void k_lse_valu(
       M[r] = Mn;
     }
   }
+
+  // ---- merge the W waves through LDS (wave order)
+  __shared__ float sM[kW][kRowsPerTile];
+  __shared__ float sS[kW][kRowsPerTile];
+  __shared__ double sRed[kThreads];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t i = row0 + 64 * r;
-    if (i < np) {
-      Mp[(int64_t)s * part_stride + i] = M[r];
-      Sp[(int64_t)s * part_stride + i] = S[r];
+  for (int r = 0; r < kR; ++r) {
+    sM[wave][lane + 64 * r] = M[r];
+    sS[wave][lane + 64 * r] = S[r];
+  }
+  __syncthreads();
+  double term = 0.0;
+  int bad = 0;
+  if (threadIdx.x < kRowsPerTile) {
+    const int t = threadIdx.x;
+    float mx = -FLT_MAX;
+#pragma unroll
+    for (int v = 0; v < kW; ++v) mx = fmaxf(mx, sM[v][t]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kW; ++v) sum = __builtin_fmaf(sS[v][t], ex2(sM[v][t] - mx), sum);
+    const int64_t i = tile * kRowsPerTile + t;
+    if (i < A.np) {
+      if (A.G > 1) {
+        A.Mp[(int64_t)gs * A.np + i] = mx;
+        A.Sp[(int64_t)gs * A.np + i] = sum;
+      } else {
+        term = finalize_row(A, i, mx, (double)sum, &bad);
+      }
+    }
+  }
+  if (A.G == 1) {
+    if (bad) atomicAdd(&A.ctl->nonfinite, bad);
+    if (A.prev) {
+      sRed[threadIdx.x] = term;
+      __syncthreads();
+#pragma unroll
+      for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
+        __syncthreads();
+      }
+      if (threadIdx.x == 0) A.red_part[tile] = sRed[0];
     }
   }
 }
 
-// Deterministic block sum of one double per thread (256 threads).
-__device__ double block_sum_256(double v) {
+// Merge of the G global splits of each row (split order), then finalize.
+__global__ __launch_bounds__(256) void k_merge(LseArgs A) {
+  __shared__ double sRed[256];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double term = 0.0;
+  int bad = 0;
+  if (i < A.np) {
+    float mx = -FLT_MAX;
+    for (int32_t t = 0; t < A.G; ++t) mx = fmaxf(mx, A.Mp[(int64_t)t * A.np + i]);
+    double sum = 0.0;
+    for (int32_t t = 0; t < A.G; ++t) {
+      const int64_t o = (int64_t)t * A.np + i;
+      sum += (double)A.Sp[o] * (double)ex2(A.Mp[o] - mx);
+    }
+    term = finalize_row(A, i, mx, sum, &bad);
+  }
+  if (bad) atomicAdd(&A.ctl->nonfinite, bad);
+  if (A.prev) {
+    sRed[threadIdx.x] = term;
+    __syncthreads();
+#pragma unroll
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) A.red_part[blockIdx.x] = sRed[0];
+  }
+}
+
+// Sum of count doubles in a fixed order into ctl->residual (one block).
+__global__ __launch_bounds__(256) void k_reduce(const double* __restrict__ part, int64_t count,
+                                                Ctl* ctl) {
   __shared__ double sh[256];
-  sh[threadIdx.x] = v;
+  double acc = 0.0;
+  for (int64_t k = threadIdx.x; k < count; k += 256) acc += part[k];
+  sh[threadIdx.x] = acc;
   __syncthreads();
 #pragma unroll
   for (int w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
     __syncthreads();
   }
-  return sh[0];
-}
-
-// Merge the split partials of each row (fp64), write the potential, optionally
-// the next column term of this side and the residual term
-//   w_i |exp((prev_i - new_i)/eps) - 1|,
-// summed per block into red_part.
-__global__ __launch_bounds__(256) void k_finalize(
-    const float* __restrict__ Mp, const float* __restrict__ Sp, int64_t part_stride,
-    int32_t nsplit, int64_t np, double neg_eps_ln2, float* __restrict__ out,
-    const float* __restrict__ prev, const float* __restrict__ w, double inv_eps,
-    float* __restrict__ Hnext, double lam_next, double* __restrict__ red_part,
-    int32_t* __restrict__ nonfinite) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  double term = 0.0;
-  if (i < np) {
-    double mx = -INFINITY;
-    for (int32_t s = 0; s < nsplit; ++s) mx = fmax(mx, (double)Mp[(int64_t)s * part_stride + i]);
-    double sum = 0.0;
-    for (int32_t s = 0; s < nsplit; ++s) {
-      const int64_t o = (int64_t)s * part_stride + i;
-      sum += (double)Sp[o] * exp2((double)Mp[o] - mx);
-    }
-    const double L = mx + log2(sum);  // sum == 0 -> -inf -> potential +inf
-    const double v = neg_eps_ln2 * L;
-    const float v32 = (float)v;
-    out[i] = v32;
-    if (!isfinite(v32)) atomicAdd(nonfinite, 1);
-    const double wi = (double)w[i];
-    if (Hnext) Hnext[i] = (float)(log2(wi) + (double)v32 * lam_next);
-    if (prev && wi > 0.0) term = wi * fabs(expm1(((double)prev[i] - v) * inv_eps));
-  }
-  if (red_part) {
-    const double b = block_sum_256(term);
-    if (threadIdx.x == 0) red_part[blockIdx.x] = b;
-  }
+  if (threadIdx.x == 0) ctl->residual = sh[0];
 }
 
 // Column term H_j = log2 w_j + pot_j * log2(e) / eps, rounded once to fp32.
@@ -154,59 +241,58 @@ __global__ __launch_bounds__(256) void k_column_term(const float* __restrict__ w
   if (j < count) H[j] = (float)(log2((double)w[j]) + (double)pot[j] * lam);
 }
 
-// Sum of count doubles in a fixed order (one block of 256 threads).
-__global__ __launch_bounds__(256) void k_reduce(const double* __restrict__ part, int64_t count,
-                                                double* __restrict__ out) {
-  double acc = 0.0;
-  for (int64_t k = threadIdx.x; k < count; k += 256) acc += part[k];
-  const double s = block_sum_256(acc);
-  if (threadIdx.x == 0) out[0] = s;
+__global__ void k_reset_ctl(Ctl* ctl) {
+  if (threadIdx.x == 0) {
+    ctl->residual = 0.0;
+    ctl->nonfinite = 0;
+  }
 }
 
 struct SplitPlan {
-  int R;
-  int32_t nsplit;
-  int64_t cps;  // chunks per split
+  int32_t G;
+  int64_t cps;
   int64_t nchunks;
-  int64_t groups;  // row groups of 4 waves
+  int64_t tiles;
 };
-
-constexpr int kRowsPerLane = 2;
 
 SplitPlan plan_split(int64_t nrows, int64_t ncols) {
   SplitPlan sp;
-  sp.R = kRowsPerLane;
   sp.nchunks = (ncols + kChunk - 1) / kChunk;
-  sp.groups = (nrows + 256 * sp.R - 1) / (256 * sp.R);
-  // aim at ~1024 workgroups (4096 waves) so all 256 CUs stay busy
-  int64_t want = (1024 + sp.groups - 1) / sp.groups;
-  int64_t maxsplit = sp.nchunks / 4 > 1 ? sp.nchunks / 4 : 1;  // >= 4 chunks per split
+  sp.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
+  // aim at >= 2048 workgroups (8 per CU, so the last round is short) with at
+  // least 4 chunks per wave
+  int64_t want = (2048 + sp.tiles - 1) / sp.tiles;
+  const int64_t maxsplit = sp.nchunks / (4 * kW) > 1 ? sp.nchunks / (4 * kW) : 1;
   if (want > 64) want = 64;
   if (want > maxsplit) want = maxsplit;
   if (want < 1) want = 1;
-  if (want > 8) want = (want + 7) / 8 * 8;  // split -> XCD alignment
   sp.cps = (sp.nchunks + want - 1) / want;
-  sp.nsplit = (int32_t)((sp.nchunks + sp.cps - 1) / sp.cps);
+  sp.G = (int32_t)((sp.nchunks + sp.cps - 1) / sp.cps);
   return sp;
 }
 
 template <int D>
-void launch_lse(sinkhorn_problem* p, const Side& rows, const Side& cols, const float* H,
-                float nkappa, const SplitPlan& sp) {
-  const dim3 grid((uint32_t)(sp.groups * sp.nsplit));
-  hipLaunchKernelGGL((k_lse_valu<D, kRowsPerLane>), grid, dim3(256), 0, p->stream, rows.soa,
-                     rows.padded, cols.soa, cols.padded, H, nkappa, sp.nchunks, sp.cps,
-                     sp.nsplit, rows.count, p->Mpart, p->Spart, rows.padded);
+void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, double pairs) {
+  prof_begin(p);
+  hipLaunchKernelGGL((k_lse_valu<D>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream, A);
   SK_LAUNCH_CHECK();
+  prof_end(p, pairs);
 }
 
 }  // namespace
 
+int64_t row_groups(int64_t rows) {
+  const int64_t tiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
+  const int64_t merge_blocks = (rows + 255) / 256;
+  return tiles > merge_blocks ? tiles : merge_blocks;
+}
+
 int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols) {
   (void)p;
+  (void)rows_padded;
   const SplitPlan sp = plan_split(nrows, ncols);
-  return (int64_t)sp.nsplit * rows_padded;
+  return sp.G > 1 ? (int64_t)sp.G * nrows : 1;
 }
 
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
@@ -218,49 +304,76 @@ void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, d
 }
 
 void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
+  if (p->d > kMaxValuD) {
+    mfma_halfstep(p, hs);
+    return;
+  }
   const Side& rows = *hs.rows;
   const Side& cols = *hs.cols;
   const SplitPlan sp = plan_split(rows.count, cols.count);
-  if ((int64_t)sp.nsplit * rows.padded > p->part_cap) fail(SINKHORN_ERR_HIP, "partial buffer too small");
-  const float nkappa = (float)(-p->scale * kLog2e / hs.eps);
+  if (sp.G > 1 && (int64_t)sp.G * rows.count > p->part_cap) fail(SINKHORN_ERR_HIP, "partial buffer too small");
+  if (row_groups(rows.count) > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
+  LseArgs A;
+  A.P = rows.soa;
+  A.pstride = rows.padded;
+  A.Q = cols.soa;
+  A.qstride = cols.padded;
+  A.H = hs.Hcols;
+  A.nkappa = (float)(-p->scale * kLog2e / hs.eps);
+  A.G = sp.G;
+  A.nchunks = sp.nchunks;
+  A.cps = sp.cps;
+  A.np = rows.count;
+  A.Mp = p->Mpart;
+  A.Sp = p->Spart;
+  A.w = rows.w;
+  A.out = hs.pot_out;
+  A.prev = hs.residual ? hs.pot_prev : nullptr;
+  A.Hnext = hs.H_next;
+  A.neg_eps_ln2 = -hs.eps * kLn2;
+  A.inv_eps = 1.0 / hs.eps;
+  A.lam_next = kLog2e / hs.eps_next;
+  A.red_part = p->red_part;
+  A.ctl = p->ctl;
+  const int64_t blocks = sp.tiles * sp.G;
+  const double pairs = (double)rows.count * (double)cols.count;
   switch (p->d) {
-    case 1: launch_lse<1>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 2: launch_lse<2>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 3: launch_lse<3>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 4: launch_lse<4>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 5: launch_lse<5>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 6: launch_lse<6>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 7: launch_lse<7>(p, rows, cols, hs.Hcols, nkappa, sp); break;
-    case 8: launch_lse<8>(p, rows, cols, hs.Hcols, nkappa, sp); break;
+    case 1: launch_lse<1>(p, A, blocks, pairs); break;
+    case 2: launch_lse<2>(p, A, blocks, pairs); break;
+    case 3: launch_lse<3>(p, A, blocks, pairs); break;
+    case 4: launch_lse<4>(p, A, blocks, pairs); break;
+    case 5: launch_lse<5>(p, A, blocks, pairs); break;
+    case 6: launch_lse<6>(p, A, blocks, pairs); break;
+    case 7: launch_lse<7>(p, A, blocks, pairs); break;
+    case 8: launch_lse<8>(p, A, blocks, pairs); break;
     default: fail(SINKHORN_ERR_UNSUPPORTED, "VALU half-step supports d <= 8");
   }
-  const int64_t fblocks = (rows.count + 255) / 256;
-  if (hs.residual && fblocks > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
-  hipLaunchKernelGGL(k_finalize, dim3((uint32_t)fblocks), dim3(256), 0, p->stream, p->Mpart,
-                     p->Spart, rows.padded, sp.nsplit, rows.count, -hs.eps * kLn2, hs.pot_out,
-                     hs.residual ? hs.pot_prev : nullptr, rows.w, 1.0 / hs.eps, hs.H_next,
-                     kLog2e / hs.eps_next, hs.residual ? p->red_part : nullptr, p->nonfinite);
-  SK_LAUNCH_CHECK();
-  if (hs.residual) {
-    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, fblocks,
-                       p->red_out);
+  int64_t nred = sp.tiles;
+  if (sp.G > 1) {
+    nred = (rows.count + 255) / 256;
+    hipLaunchKernelGGL(k_merge, dim3((uint32_t)nred), dim3(256), 0, p->stream, A);
+    SK_LAUNCH_CHECK();
+  }
+  if (A.prev) {
+    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, nred, p->ctl);
     SK_LAUNCH_CHECK();
   }
 }
 
-void reset_nonfinite(sinkhorn_problem* p) { zero_i32(p->nonfinite, 1, p->stream); }
+void reset_nonfinite(sinkhorn_problem* p) {
+  hipLaunchKernelGGL(k_reset_ctl, dim3(1), dim3(64), 0, p->stream, p->ctl);
+  SK_LAUNCH_CHECK();
+}
+
+void copy_ctl(sinkhorn_problem* p) {
+  SK_HIP(hipMemcpyAsync(p->host_ctl, p->ctl, sizeof(Ctl), hipMemcpyDeviceToHost, p->stream));
+}
 
 void read_reduction(sinkhorn_problem* p, double* value, int32_t* nonfinite) {
-  SK_HIP(hipMemcpyAsync(p->host_red, p->red_out, sizeof(double), hipMemcpyDeviceToHost, p->stream));
-  SK_HIP(hipMemcpyAsync(p->host_red + 1, p->nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost,
-                        p->stream));
+  copy_ctl(p);
   SK_HIP(hipStreamSynchronize(p->stream));
-  if (value) *value = p->host_red[0];
-  if (nonfinite) {
-    int32_t v;
-    memcpy(&v, p->host_red + 1, sizeof(int32_t));
-    *nonfinite = v;
-  }
+  if (value) *value = p->host_ctl->residual;
+  if (nonfinite) *nonfinite = p->host_ctl->nonfinite;
 }
 
 }  // namespace sk

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "sinkhorn.h"
 
@@ -57,6 +58,13 @@ struct Side {
   double wsum = 0.0;
 };
 
+// Results a half-step leaves on the device; read back with one copy.
+struct Ctl {
+  double residual;     // last fused residual (sum over rows of w_i |exp((prev_i - new_i)/eps) - 1|)
+  int32_t nonfinite;   // non-finite potentials written since the last reset
+  int32_t pad;
+};
+
 // Per-launch description of one dense half-step "rows against columns".
 struct HalfStep {
   const Side* rows;
@@ -83,16 +91,22 @@ struct sinkhorn_problem {
   float* Mpart = nullptr;
   float* Spart = nullptr;
   int64_t part_cap = 0;  // floats per partial array
-  // residual block partials and the reduced values
-  double* red_part = nullptr;
+  // residual block partials, arrival counters and the reduced values
+  double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
-  double* red_out = nullptr;     // [4] device
-  int32_t* nonfinite = nullptr;  // [1] device counter
-  double* host_red = nullptr;    // [8] pinned
+  uint32_t* cnt = nullptr;      // [red_cap + 1] arrival counters, zero between launches
+  sk::Ctl* ctl = nullptr;       // device control block
+  sk::Ctl* host_ctl = nullptr;  // pinned mirror
+  double* host_tmp = nullptr;   // [8] pinned scratch
   // solve scratch: double-buffered potentials
   float* fbuf[2] = {nullptr, nullptr};
   float* gbuf[2] = {nullptr, nullptr};
   hipEvent_t ev = nullptr;
+  // measurement hook: event pairs around pair-loop kernel launches
+  bool prof = false;
+  std::vector<hipEvent_t> prof_ev;  // 2 per launch, reused across reads
+  size_t prof_used = 0;             // launches recorded since the last read
+  double prof_pairs = 0.0;
 };
 
 namespace sk {
@@ -102,21 +116,30 @@ void zero_i32(int32_t* v, int32_t count, hipStream_t st);
 void fill_f32(float* v, int64_t count, float value, hipStream_t st);
 void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st);
 
+// measurement hook (api.hip): call around a pair-loop kernel launch
+void prof_begin(sinkhorn_problem* p);
+void prof_end(sinkhorn_problem* p, double pairs);
+
 // dense.hip
 int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols);
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
                       float* H);
 void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs);
+// enqueue the copy of the control block to its pinned mirror
+void copy_ctl(sinkhorn_problem* p);
 // returns (residual sum, nonfinite count) after a synchronizing read
 void read_reduction(sinkhorn_problem* p, double* value, int32_t* nonfinite);
 void reset_nonfinite(sinkhorn_problem* p);
+// row groups of the pair kernel for a side of `rows` points (for buffer sizing)
+int64_t row_groups(int64_t rows);
 
 // setup.hip
 void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count);
 void side_free(Side& s);
 // mfma.hip (d > kMaxValuD)
 void setup_mfma(sinkhorn_problem* p, const float* x, const float* y);
+void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs);
 
 double device_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
                             hipStream_t st);

@@ -4,6 +4,9 @@
 
 namespace sk {
 void setup_mfma(sinkhorn_problem*, const float*, const float*) {}
+void mfma_halfstep(sinkhorn_problem*, const HalfStep&) {
+  fail(SINKHORN_ERR_UNSUPPORTED, "d > 8 needs the MFMA half-step");
+}
 }  // namespace sk
 
 extern "C" {

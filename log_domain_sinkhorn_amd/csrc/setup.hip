@@ -213,19 +213,21 @@ void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, i
   const uint32_t nb = blocks_for(count);
   double* part = (double*)dev_alloc(sizeof(double) * nb);
   double* out = (double*)dev_alloc(sizeof(double));
-  zero_i32(p->nonfinite, 1, st);
-  hipLaunchKernelGGL(k_check, dim3(nb), dim3(256), 0, st, pts, s.w, count, d, part, p->nonfinite);
+  int32_t* badc = (int32_t*)dev_alloc(sizeof(int32_t));
+  zero_i32(badc, 1, st);
+  hipLaunchKernelGGL(k_check, dim3(nb), dim3(256), 0, st, pts, s.w, count, d, part, badc);
   SK_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_sum_blocks, dim3(1), dim3(256), 0, st, part, (int64_t)nb, out);
   SK_LAUNCH_CHECK();
-  SK_HIP(hipMemcpyAsync(p->host_red, out, sizeof(double), hipMemcpyDeviceToHost, st));
-  SK_HIP(hipMemcpyAsync(p->host_red + 1, p->nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  SK_HIP(hipMemcpyAsync(p->host_tmp, out, sizeof(double), hipMemcpyDeviceToHost, st));
+  SK_HIP(hipMemcpyAsync(p->host_tmp + 1, badc, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   SK_HIP(hipStreamSynchronize(st));
   dev_free(part);
   dev_free(out);
-  s.wsum = p->host_red[0];
+  dev_free(badc);
+  s.wsum = p->host_tmp[0];
   int32_t bad;
-  memcpy(&bad, p->host_red + 1, sizeof(int32_t));
+  memcpy(&bad, p->host_tmp + 1, sizeof(int32_t));
   if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite coordinate or weight at init");
   if (!(s.wsum > 0.0) || !std::isfinite(s.wsum)) fail(SINKHORN_ERR_INVALID_ARG, "weights must have a positive finite sum");
 }
