@@ -100,7 +100,8 @@ int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m,
 
 /* Create a problem handle: copies x [n][d], y [m][d] (device) and the weights
  * a [n], b [m] (device; NULL = uniform 1/n, 1/m) into device-resident layouts.
- * Requires n, m >= 1, 1 <= d <= 1024, cost_scale finite and > 0, weights >= 0
+ * Requires n, m >= 1, 1 <= d <= 63 (d <= 8 runs the difference form on the
+ * vector ALU, larger d the MFMA cross term on centred clouds), cost_scale finite and > 0, weights >= 0
  * (negative weights are not checked and give undefined results); returns
  * SINKHORN_ERR_MASS if |sum a - sum b| > 1e-5 * max(sum a, sum b), and
  * SINKHORN_ERR_NONFINITE if a coordinate or weight is NaN or infinite.

@@ -160,7 +160,7 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
     *out = nullptr;
     require(x && y, "null coordinates");
     require(n >= 1 && m >= 1, "n and m must be >= 1");
-    require(d >= 1 && d <= 1024, "d must be in [1, 1024]");
+    require(d >= 1 && d <= kMaxMfmaD, "d must be in [1, 63]");
     require(std::isfinite(cost_scale) && cost_scale > 0.0, "cost_scale must be finite and > 0");
     sinkhorn_problem* p = new sinkhorn_problem();
     try {

@@ -16,15 +16,13 @@
 //     split the columns further and a small merge kernel combines their
 //     partials in split order; otherwise the workgroup finalizes in place.
 // Finalizing writes the potential, optionally the next column term of the row
-// side (log2 w_i + pot_i log2(e)/eps_next) and the residual terms
-// w_i |exp((prev_i - new_i)/eps) - 1|, summed per workgroup and then, on
-// request, in workgroup order by a one-block kernel. Results are
-// bit-reproducible.
+// side and the residual terms, summed per workgroup and then, on request, in
+// workgroup order by a one-block kernel. Results are bit-reproducible.
 #include <cfloat>
 #include <cmath>
 #include <cstring>
 
-#include "internal.h"
+#include "rowfinal.h"
 
 namespace sk {
 namespace {
@@ -48,34 +46,10 @@ struct LseArgs {
   int32_t G;            // workgroups per row tile (global column splits)
   int64_t nchunks;      // column chunks of kChunk points
   int64_t cps;          // chunks per global split
-  int64_t np;           // rows
   float* Mp;            // [G][np] partial max (G > 1)
   float* Sp;            // [G][np] partial sum (G > 1)
-  // finalize (G == 1)
-  const float* w;       // row weights [np]
-  float* out;           // new potentials [np]
-  const float* prev;    // previous potentials [np] for the residual, or null
-  float* Hnext;         // next column term of the row side, or null
-  double neg_eps_ln2;   // -eps ln 2
-  double inv_eps;
-  double lam_next;      // log2(e) / eps_next
-  double* red_part;     // [tiles] residual per workgroup (if prev)
-  Ctl* ctl;
+  RowFinal F;
 };
-
-// Potential, next column term and residual term of row i from its merged
-// (max, sum); returns the residual term.
-__device__ __forceinline__ double finalize_row(const LseArgs& A, int64_t i, float mx, double sum,
-                                               int* bad) {
-  const double v = A.neg_eps_ln2 * ((double)mx + log2(sum));  // sum == 0 -> +inf
-  const float v32 = (float)v;
-  A.out[i] = v32;
-  if (!isfinite(v32)) ++*bad;
-  const double wi = (double)A.w[i];
-  if (A.Hnext) A.Hnext[i] = (float)(log2(wi) + (double)v32 * A.lam_next);
-  if (A.prev && wi > 0.0) return wi * fabs(expm1(((double)A.prev[i] - v) * A.inv_eps));
-  return 0.0;
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
@@ -163,18 +137,18 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
 #pragma unroll
     for (int v = 0; v < kW; ++v) sum = __builtin_fmaf(sS[v][t], ex2(sM[v][t] - mx), sum);
     const int64_t i = tile * kRowsPerTile + t;
-    if (i < A.np) {
+    if (i < A.F.np) {
       if (A.G > 1) {
-        A.Mp[(int64_t)gs * A.np + i] = mx;
-        A.Sp[(int64_t)gs * A.np + i] = sum;
+        A.Mp[(int64_t)gs * A.F.np + i] = mx;
+        A.Sp[(int64_t)gs * A.F.np + i] = sum;
       } else {
-        term = finalize_row(A, i, mx, (double)sum, &bad);
+        term = finalize_row(A.F, i, mx, (double)sum, &bad);
       }
     }
   }
   if (A.G == 1) {
-    if (bad) atomicAdd(&A.ctl->nonfinite, bad);
-    if (A.prev) {
+    if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
+    if (A.F.prev) {
       sRed[threadIdx.x] = term;
       __syncthreads();
 #pragma unroll
@@ -182,29 +156,30 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
         if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
         __syncthreads();
       }
-      if (threadIdx.x == 0) A.red_part[tile] = sRed[0];
+      if (threadIdx.x == 0) A.F.red_part[tile] = sRed[0];
     }
   }
 }
 
 // Merge of the G global splits of each row (split order), then finalize.
-__global__ __launch_bounds__(256) void k_merge(LseArgs A) {
+__global__ __launch_bounds__(256) void k_merge(RowFinal F, int32_t G, const float* __restrict__ Mp,
+                                               const float* __restrict__ Sp) {
   __shared__ double sRed[256];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   double term = 0.0;
   int bad = 0;
-  if (i < A.np) {
+  if (i < F.np) {
     float mx = -FLT_MAX;
-    for (int32_t t = 0; t < A.G; ++t) mx = fmaxf(mx, A.Mp[(int64_t)t * A.np + i]);
+    for (int32_t t = 0; t < G; ++t) mx = fmaxf(mx, Mp[(int64_t)t * F.np + i]);
     double sum = 0.0;
-    for (int32_t t = 0; t < A.G; ++t) {
-      const int64_t o = (int64_t)t * A.np + i;
-      sum += (double)A.Sp[o] * (double)ex2(A.Mp[o] - mx);
+    for (int32_t t = 0; t < G; ++t) {
+      const int64_t o = (int64_t)t * F.np + i;
+      sum += (double)Sp[o] * (double)ex2(Mp[o] - mx);
     }
-    term = finalize_row(A, i, mx, sum, &bad);
+    term = finalize_row(F, i, mx, sum, &bad);
   }
-  if (bad) atomicAdd(&A.ctl->nonfinite, bad);
-  if (A.prev) {
+  if (bad) atomicAdd(&F.ctl->nonfinite, bad);
+  if (F.prev) {
     sRed[threadIdx.x] = term;
     __syncthreads();
 #pragma unroll
@@ -212,7 +187,7 @@ __global__ __launch_bounds__(256) void k_merge(LseArgs A) {
       if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
       __syncthreads();
     }
-    if (threadIdx.x == 0) A.red_part[blockIdx.x] = sRed[0];
+    if (threadIdx.x == 0) F.red_part[blockIdx.x] = sRed[0];
   }
 }
 
@@ -281,6 +256,39 @@ void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, double pa
 
 }  // namespace
 
+RowFinal make_rowfinal(sinkhorn_problem* p, const HalfStep& hs) {
+  RowFinal F;
+  F.np = hs.rows->count;
+  F.w = hs.rows->w;
+  F.out = hs.pot_out;
+  F.prev = hs.residual ? hs.pot_prev : nullptr;
+  F.norm2 = nullptr;
+  F.row_scale = 0.0;
+  F.Hnext = hs.H_next;
+  F.hstride = 1;
+  F.lam_next = kLog2e / hs.eps_next;
+  F.hmul = 1.0;
+  F.hnorm = 0.0;
+  F.neg_eps_ln2 = -hs.eps * kLn2;
+  F.inv_eps = 1.0 / hs.eps;
+  F.red_part = p->red_part;
+  F.ctl = p->ctl;
+  return F;
+}
+
+void launch_merge(sinkhorn_problem* p, const RowFinal& F, int32_t G, const float* Mp,
+                  const float* Sp) {
+  const int64_t nblocks = (F.np + 255) / 256;
+  hipLaunchKernelGGL(k_merge, dim3((uint32_t)nblocks), dim3(256), 0, p->stream, F, G, Mp, Sp);
+  SK_LAUNCH_CHECK();
+  if (F.prev) launch_reduce(p, nblocks);
+}
+
+void launch_reduce(sinkhorn_problem* p, int64_t count) {
+  hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, count, p->ctl);
+  SK_LAUNCH_CHECK();
+}
+
 int64_t row_groups(int64_t rows) {
   const int64_t tiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
   const int64_t merge_blocks = (rows + 255) / 256;
@@ -289,14 +297,18 @@ int64_t row_groups(int64_t rows) {
 
 int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols) {
-  (void)p;
   (void)rows_padded;
+  if (p->d > kMaxValuD) return mfma_partial_floats(nrows, ncols);
   const SplitPlan sp = plan_split(nrows, ncols);
   return sp.G > 1 ? (int64_t)sp.G * nrows : 1;
 }
 
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
                       float* H) {
+  if (p->d > kMaxValuD) {
+    mfma_column_term(p, side, pot, eps);
+    return;
+  }
   const int64_t blocks = (side.count + 255) / 256;
   hipLaunchKernelGGL(k_column_term, dim3((uint32_t)blocks), dim3(256), 0, p->stream, side.w, pot,
                      side.count, kLog2e / eps, H);
@@ -323,18 +335,9 @@ void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
   A.G = sp.G;
   A.nchunks = sp.nchunks;
   A.cps = sp.cps;
-  A.np = rows.count;
   A.Mp = p->Mpart;
   A.Sp = p->Spart;
-  A.w = rows.w;
-  A.out = hs.pot_out;
-  A.prev = hs.residual ? hs.pot_prev : nullptr;
-  A.Hnext = hs.H_next;
-  A.neg_eps_ln2 = -hs.eps * kLn2;
-  A.inv_eps = 1.0 / hs.eps;
-  A.lam_next = kLog2e / hs.eps_next;
-  A.red_part = p->red_part;
-  A.ctl = p->ctl;
+  A.F = make_rowfinal(p, hs);
   const int64_t blocks = sp.tiles * sp.G;
   const double pairs = (double)rows.count * (double)cols.count;
   switch (p->d) {
@@ -348,16 +351,10 @@ void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
     case 8: launch_lse<8>(p, A, blocks, pairs); break;
     default: fail(SINKHORN_ERR_UNSUPPORTED, "VALU half-step supports d <= 8");
   }
-  int64_t nred = sp.tiles;
-  if (sp.G > 1) {
-    nred = (rows.count + 255) / 256;
-    hipLaunchKernelGGL(k_merge, dim3((uint32_t)nred), dim3(256), 0, p->stream, A);
-    SK_LAUNCH_CHECK();
-  }
-  if (A.prev) {
-    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, nred, p->ctl);
-    SK_LAUNCH_CHECK();
-  }
+  if (sp.G > 1)
+    launch_merge(p, A.F, sp.G, p->Mpart, p->Spart);
+  else if (A.F.prev)
+    launch_reduce(p, sp.tiles);
 }
 
 void reset_nonfinite(sinkhorn_problem* p) {

@@ -35,6 +35,8 @@ constexpr int kChunk = 16;
 // Largest d served by the VALU difference-form kernel; above it the cross
 // term runs on MFMA.
 constexpr int kMaxValuD = 8;
+// Largest d served by the MFMA kernel (K = d + 1 rounded up to 4 stays <= 64).
+constexpr int kMaxMfmaD = 63;
 // Row tiles per MFMA kernel uses 32-point tiles, K padded to a multiple of 4.
 constexpr int kMfmaTile = 32;
 
@@ -137,9 +139,13 @@ int64_t row_groups(int64_t rows);
 // setup.hip
 void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count);
 void side_free(Side& s);
+// per-dimension (sum, sum of squares) of a device cloud [count][d] -> host [d][2]
+void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double* host_out);
 // mfma.hip (d > kMaxValuD)
 void setup_mfma(sinkhorn_problem* p, const float* x, const float* y);
 void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs);
+void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps);
+int64_t mfma_partial_floats(int64_t nrows, int64_t ncols);
 
 double device_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
                             hipStream_t st);

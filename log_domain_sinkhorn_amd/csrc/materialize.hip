@@ -1,0 +1,438 @@
+// Transport-plan rows and the min_row threshold.
+//
+// moscot pull request #846, "Fix": entropic rows are built directly from the
+// potentials, T[rows] = exp((f_i + g_j - C_ij)/eps) with the weights carried
+// by the plan (T_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) here), never through
+// an n x m x k tensor; "Behavioural changes": min_row = min over rows with
+// a_i > 0 of max_j T_ij, exact and independent of the row batch.
+//
+// The exponent E_ij = log2 T_ij is assembled in fp64 from per-row and
+// per-column terms and rounded once before the fp32 exp2, so a row entry
+// carries about |E| 2^-24 ln 2 relative error. Row maxima are exact: each
+// workgroup reduces its share and merges it with an atomic max on an
+// order-preserving integer key of E (max is order independent).
+#include <cfloat>
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+namespace sk {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float ex2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Monotone map float -> uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t okey(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float okey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Row terms for the selected rows: P_i = log2 a_i + lam f_i [- kappa ||x_i||^2].
+__global__ __launch_bounds__(256) void k_row_terms(const int64_t* __restrict__ rows, int64_t row0,
+                                                   int64_t k, const float* __restrict__ a,
+                                                   const float* __restrict__ f,
+                                                   const float* __restrict__ norm2, double lam,
+                                                   double kappa, double* __restrict__ P,
+                                                   int32_t* __restrict__ live,
+                                                   uint32_t* __restrict__ keys) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= k) return;
+  const int64_t i = rows ? rows[r] : row0 + r;
+  double v = log2((double)a[i]) + lam * (double)f[i];
+  if (norm2) v -= kappa * (double)norm2[i];
+  P[r] = v;
+  if (live) live[r] = a[i] > 0.0f ? 1 : 0;
+  keys[r] = 0u;  // below every finite key
+}
+
+// Column terms (VALU path): Hd_j = log2 b_j + lam g_j in fp64.
+__global__ __launch_bounds__(256) void k_col_terms(const float* __restrict__ b,
+                                                  const float* __restrict__ g, int64_t m,
+                                                  double lam, double* __restrict__ Hd) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < m) Hd[j] = log2((double)b[j]) + lam * (double)g[j];
+}
+
+constexpr int kRB = 8;  // rows per workgroup (VALU materializer)
+
+// VALU path (d <= 8): thread = column j (coalesced stores), kRB rows per block.
+template <int D>
+__global__ __launch_bounds__(256) void k_materialize_valu(
+    const float* __restrict__ X, int64_t xs, const float* __restrict__ Y, int64_t ys, int64_t m,
+    const int64_t* __restrict__ rows, int64_t row0, int64_t k, const double* __restrict__ P,
+    const double* __restrict__ Hd, double kappa, float* __restrict__ T,
+    uint32_t* __restrict__ keys) {
+  __shared__ uint32_t sKey[256];
+  const int64_t j = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t rb = (int64_t)blockIdx.x * kRB;
+  float yv[D];
+  double hj = -INFINITY;
+  if (j < m) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) yv[q] = Y[q * ys + j];
+    hj = Hd[j];
+  } else {
+#pragma unroll
+    for (int q = 0; q < D; ++q) yv[q] = 0.0f;
+  }
+  for (int r = 0; r < kRB; ++r) {
+    const int64_t rr = rb + r;
+    if (rr >= k) break;  // uniform
+    const int64_t i = rows ? rows[rr] : row0 + rr;
+    // fp64 difference form: the fp32 coordinates subtract exactly, so the
+    // exponent of a far entry (large kappa q) keeps full relative accuracy
+    double dd = (double)X[i] - (double)yv[0];
+    double q = dd * dd;
+#pragma unroll
+    for (int c = 1; c < D; ++c) {
+      dd = (double)X[c * xs + i] - (double)yv[c];
+      q = __builtin_fma(dd, dd, q);
+    }
+    const double E = __builtin_fma(-kappa, q, P[rr] + hj);
+    const float e32 = (float)E;
+    if (T && j < m) T[rr * m + j] = ex2(e32);
+    sKey[threadIdx.x] = j < m ? okey(e32) : 0u;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sKey[threadIdx.x] = max(sKey[threadIdx.x], sKey[threadIdx.x + w]);
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) atomicMax(&keys[rr], sKey[0]);
+    __syncthreads();
+  }
+}
+
+// MFMA path (9 <= d <= 63): A = selected x rows (slot d := 1), B = column tile
+// of y from LDS (slot d = H'_j), D[i][j] = x_i . y_j + H'_j, E = 2 kappa D + P_i.
+// A wave owns 2 tiles of 32 rows; lane (l32, kh) holds rows 8(r/4) + 4kh + r%4
+// of each tile at column l32, so the T stores are 128-byte row segments.
+template <int KP>
+__global__ __launch_bounds__(256) void k_materialize_mfma(
+    const float* __restrict__ X, const float* __restrict__ Y, int32_t d, int64_t m,
+    const int64_t* __restrict__ rows, int64_t row0, int64_t k, const double* __restrict__ P,
+    double twokappa, int32_t G, int64_t ntiles, int64_t tps, float* __restrict__ T,
+    uint32_t* __restrict__ keys) {
+  constexpr int KH = KP / 2;
+  constexpr int LW = KP + 1;
+  constexpr int NV4 = 32 * KP / 4;
+  constexpr int PER = (NV4 + 255) / 256;
+  __shared__ float sY[2][32 * LW];
+  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)G);
+  const int64_t rt = blockIdx.x / (uint32_t)G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t rbase = rt * 256 + wave * 64;  // first selected row of this wave
+
+  float ax[2][KH];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int64_t rr = rbase + it * 32 + l32;
+    const int64_t i = rr < k ? (rows ? rows[rr] : row0 + rr) : -1;
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const int c = 2 * kk + kh;
+      ax[it][kk] = i < 0 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
+    }
+  }
+  double prow[2][16];
+  float emax[2][16];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+      prow[it][r] = rr < k ? P[rr] : -INFINITY;
+      emax[it][r] = -INFINITY;
+    }
+
+  const int64_t t0 = (int64_t)gs * tps;
+  const int64_t t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
+  float4 pre[PER];
+  auto gload = [&](int64_t t) {
+    const float4* src = reinterpret_cast<const float4*>(Y + t * 32 * KP);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      if (idx < NV4) pre[q] = src[idx];
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      if (idx < NV4) {
+        const int e = idx * 4;
+        float* dst = &sY[buf][(e / KP) * LW + (e % KP)];
+        dst[0] = pre[q].x;
+        dst[1] = pre[q].y;
+        dst[2] = pre[q].z;
+        dst[3] = pre[q].w;
+      }
+    }
+  };
+  if (t0 < t1) {
+    gload(t0);
+    lstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    const bool more = t + 1 < t1;
+    if (more) gload(t + 1);
+    v16f acc[2];
+    acc[0] = (v16f){};
+    acc[1] = (v16f){};
+    const float* ys = &sY[buf][l32 * LW + kh];
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      const float bv = ys[2 * kk];
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[0][kk], bv, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[1][kk], bv, acc[1], 0, 0, 0);
+    }
+    const int64_t j = t * 32 + l32;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+        const float e32 = (float)__builtin_fma(twokappa, (double)acc[it][r], prow[it][r]);
+        if (j < m && rr < k) {
+          if (T) T[rr * m + j] = ex2(e32);
+          emax[it][r] = fmaxf(emax[it][r], e32);
+        }
+      }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // max over the 32 columns held by the lanes of each half
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = emax[it][r];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+      if (l32 == 0 && rr < k && v > -INFINITY) atomicMax(&keys[rr], okey(v));
+    }
+}
+
+// row_max[r] = exp2(E max) from the keys (0 key: no column -> 0).
+__global__ __launch_bounds__(256) void k_keys_to_max(const uint32_t* __restrict__ keys, int64_t k,
+                                                     float* __restrict__ row_max) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r < k) row_max[r] = keys[r] == 0u ? 0.0f : ex2(okey_inv(keys[r]));
+}
+
+// min over live rows of exp2(E max), into one key slot (order independent).
+__global__ __launch_bounds__(256) void k_min_live(const uint32_t* __restrict__ keys,
+                                                  const int32_t* __restrict__ live, int64_t k,
+                                                  uint32_t* __restrict__ out_key) {
+  __shared__ uint32_t sm[256];
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t v = 0xffffffffu;
+  if (r < k && live[r]) v = keys[r];
+  sm[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sm[threadIdx.x] = min(sm[threadIdx.x], sm[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMin(out_key, sm[0]);
+}
+
+__global__ void k_set_u32(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
+// Count of row indices outside [0, n).
+__global__ __launch_bounds__(256) void k_check_rows(const int64_t* __restrict__ rows, int64_t k,
+                                                    int64_t n, uint32_t* __restrict__ bad) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r < k && (rows[r] < 0 || rows[r] >= n)) atomicAdd(bad, 1u);
+}
+
+template <int D>
+void launch_valu(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t k,
+                 const double* P, const double* Hd, double kappa, float* T, uint32_t* keys) {
+  const dim3 grid((uint32_t)((k + kRB - 1) / kRB), (uint32_t)((p->m + 255) / 256));
+  hipLaunchKernelGGL((k_materialize_valu<D>), grid, dim3(256), 0, p->stream, p->X.soa, p->X.padded,
+                     p->Y.soa, p->Y.padded, p->m, rows, row0, k, P, Hd, kappa, T, keys);
+  SK_LAUNCH_CHECK();
+}
+
+template <int KP>
+void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t k,
+                 const double* P, double twokappa, float* T, uint32_t* keys) {
+  const int64_t rtiles = (k + 255) / 256;
+  const int64_t ntiles = (p->m + 31) / 32;
+  int64_t want = (1024 + rtiles - 1) / rtiles;
+  const int64_t maxsplit = ntiles / 4 > 1 ? ntiles / 4 : 1;
+  if (want > maxsplit) want = maxsplit;
+  if (want < 1) want = 1;
+  const int64_t tps = (ntiles + want - 1) / want;
+  const int32_t G = (int32_t)((ntiles + tps - 1) / tps);
+  hipLaunchKernelGGL((k_materialize_mfma<KP>), dim3((uint32_t)(rtiles * G)), dim3(256), 0,
+                     p->stream, p->X.rowmaj, p->Y.rowmaj, p->d, p->m, rows, row0, k, P, twokappa,
+                     G, ntiles, tps, T, keys);
+  SK_LAUNCH_CHECK();
+}
+
+// Rows [row0, row0 + k) (rows == null) or rows[0..k): T (nullable) and keys.
+void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* rows, int64_t row0,
+               int64_t k, double* P, int32_t* live, uint32_t* keys, const double* Hd, float* T) {
+  const double lam = kLog2e / eps;
+  const double kappa = p->scale * lam;
+  const bool mf = p->d > kMaxValuD;
+  hipLaunchKernelGGL(k_row_terms, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream, rows,
+                     row0, k, p->X.w, f, mf ? p->X.norm2 : nullptr, lam, kappa, P, live, keys);
+  SK_LAUNCH_CHECK();
+  prof_begin(p);
+  if (mf) {
+    switch (p->kpad) {
+#define SK_KP(v) case v: launch_mfma<v>(p, rows, row0, k, P, 2.0 * kappa, T, keys); break;
+      SK_KP(12) SK_KP(16) SK_KP(20) SK_KP(24) SK_KP(28) SK_KP(32) SK_KP(36)
+      SK_KP(40) SK_KP(44) SK_KP(48) SK_KP(52) SK_KP(56) SK_KP(60) SK_KP(64)
+#undef SK_KP
+      default: fail(SINKHORN_ERR_UNSUPPORTED, "materializer: unsupported K");
+    }
+  } else {
+    switch (p->d) {
+      case 1: launch_valu<1>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 2: launch_valu<2>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 3: launch_valu<3>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 4: launch_valu<4>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 5: launch_valu<5>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 6: launch_valu<6>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 7: launch_valu<7>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 8: launch_valu<8>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      default: fail(SINKHORN_ERR_UNSUPPORTED, "materializer: unsupported d");
+    }
+  }
+  prof_end(p, (double)k * (double)p->m);
+}
+
+// Column terms for this eps and g: the MFMA path writes H'_j into slot d of y,
+// the VALU path fills Hd (fp64, caller-owned).
+void column_terms(sinkhorn_problem* p, double eps, const float* g, double* Hd) {
+  if (p->d > kMaxValuD) {
+    mfma_column_term(p, p->Y, g, eps);
+  } else {
+    hipLaunchKernelGGL(k_col_terms, dim3((uint32_t)((p->m + 255) / 256)), dim3(256), 0, p->stream,
+                       p->Y.w, g, p->m, kLog2e / eps, Hd);
+    SK_LAUNCH_CHECK();
+  }
+}
+
+struct Scratch {
+  double* P = nullptr;
+  double* Hd = nullptr;
+  int32_t* live = nullptr;
+  uint32_t* keys = nullptr;
+  ~Scratch() {
+    dev_free(P);
+    dev_free(Hd);
+    dev_free(live);
+    dev_free(keys);
+  }
+};
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                              const int64_t* rows, int64_t k, float* T, float* row_max) {
+  try {
+    if (!p || !f || !g || !rows || !T) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (k < 0) fail(SINKHORN_ERR_INVALID_ARG, "k must be >= 0");
+    if (k == 0) return SINKHORN_OK;
+    Scratch s;
+    s.P = (double*)dev_alloc(sizeof(double) * k);
+    s.keys = (uint32_t*)dev_alloc(sizeof(uint32_t) * (k + 1));
+    hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(64), 0, p->stream, s.keys + k, 0u);
+    SK_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_check_rows, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+                       rows, k, p->n, s.keys + k);
+    SK_LAUNCH_CHECK();
+    SK_HIP(hipMemcpyAsync(p->host_tmp, s.keys + k, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+    SK_HIP(hipStreamSynchronize(p->stream));
+    uint32_t nbad;
+    memcpy(&nbad, p->host_tmp, sizeof(uint32_t));
+    if (nbad) fail(SINKHORN_ERR_INVALID_ARG, "row index outside [0, n)");
+    if (p->d <= kMaxValuD) s.Hd = (double*)dev_alloc(sizeof(double) * p->m);
+    column_terms(p, eps, g, s.Hd);
+    rows_pass(p, eps, f, rows, 0, k, s.P, nullptr, s.keys, s.Hd, T);
+    if (row_max) {
+      hipLaunchKernelGGL(k_keys_to_max, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+                         s.keys, k, row_max);
+      SK_LAUNCH_CHECK();
+    }
+    SK_HIP(hipStreamSynchronize(p->stream));
+    return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+int sinkhorn_min_row(sinkhorn_problem* p, double eps, const float* f, const float* g, float* out) {
+  try {
+    if (!p || !f || !g || !out) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    const int64_t batch = 16384;
+    const int64_t kb = p->n < batch ? p->n : batch;
+    Scratch s;
+    s.P = (double*)dev_alloc(sizeof(double) * kb);
+    s.keys = (uint32_t*)dev_alloc(sizeof(uint32_t) * (kb + 1));
+    s.live = (int32_t*)dev_alloc(sizeof(int32_t) * kb);
+    if (p->d <= kMaxValuD) s.Hd = (double*)dev_alloc(sizeof(double) * p->m);
+    column_terms(p, eps, g, s.Hd);
+    uint32_t* best = s.keys + kb;
+    hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(64), 0, p->stream, best, 0xffffffffu);
+    SK_LAUNCH_CHECK();
+    for (int64_t r0 = 0; r0 < p->n; r0 += kb) {
+      const int64_t k = p->n - r0 < kb ? p->n - r0 : kb;
+      rows_pass(p, eps, f, nullptr, r0, k, s.P, s.live, s.keys, s.Hd, nullptr);
+      hipLaunchKernelGGL(k_min_live, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+                         s.keys, s.live, k, best);
+      SK_LAUNCH_CHECK();
+    }
+    uint32_t key = 0;
+    SK_HIP(hipMemcpyAsync(p->host_tmp, best, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+    SK_HIP(hipStreamSynchronize(p->stream));
+    memcpy(&key, p->host_tmp, sizeof(uint32_t));
+    if (key == 0xffffffffu) {
+      *out = NAN;  // no row carries mass
+    } else {
+      const float e = (key & 0x80000000u) ? __builtin_bit_cast(float, key & 0x7fffffffu)
+                                          : __builtin_bit_cast(float, ~key);
+      *out = key == 0u ? 0.0f : std::exp2(e);
+    }
+    return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -2,21 +2,8 @@
 // and report SINKHORN_ERR_UNSUPPORTED.
 #include "internal.h"
 
-namespace sk {
-void setup_mfma(sinkhorn_problem*, const float*, const float*) {}
-void mfma_halfstep(sinkhorn_problem*, const HalfStep&) {
-  fail(SINKHORN_ERR_UNSUPPORTED, "d > 8 needs the MFMA half-step");
-}
-}  // namespace sk
 
 extern "C" {
-int sinkhorn_materialize_rows(sinkhorn_problem*, double, const float*, const float*,
-                              const int64_t*, int64_t, float*, float*) {
-  return SINKHORN_ERR_UNSUPPORTED;
-}
-int sinkhorn_min_row(sinkhorn_problem*, double, const float*, const float*, float*) {
-  return SINKHORN_ERR_UNSUPPORTED;
-}
 int sinkhorn_morton_order(const float*, const float*, int64_t, int64_t, int32_t, void*, uint64_t*,
                           int32_t*, uint64_t*, int32_t*) {
   return SINKHORN_ERR_UNSUPPORTED;

@@ -124,6 +124,8 @@ __global__ __launch_bounds__(256) void k_moments_reduce(const double* __restrict
 
 inline uint32_t blocks_for(int64_t count) { return (uint32_t)((count + 255) / 256); }
 
+}  // namespace
+
 // Per-dimension (sum, sum of squares) of a cloud, on the host after a sync.
 void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double* host_out) {
   const int64_t nchunk = count < 256 * 64 ? 1 : (count + 256 * 64 - 1) / (256 * 64);
@@ -141,8 +143,6 @@ void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double*
   dev_free(part);
   dev_free(out);
 }
-
-}  // namespace
 
 void* dev_alloc(size_t bytes) {
   void* p = nullptr;

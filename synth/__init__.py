@@ -138,11 +138,13 @@ def _w5(rng, n, m):
 _GEN = {1: _w1, 2: _w2, 3: _w3, 4: _w4, 5: _w5}
 
 
-def make(workload: int, n: int | None = None, m: int | None = None, seed: int | None = None) -> Clouds:
+def make(workload: int, n: int | None = None, m: int | None = None, seed: int | None = None,
+         d: int | None = None) -> Clouds:
     """Return the seeded clouds of ``workload`` (1..5), optionally resized.
 
     The seed defaults to the workload number. Resized clouds keep the same
-    recipe (distribution, structure and weight law) at the smaller size.
+    recipe (distribution, structure and weight law) at the smaller size;
+    ``d`` changes the dimension of workload 3 only (default 50).
     """
     if workload not in _GEN:
         raise ValueError(f"unknown workload {workload}")
@@ -151,7 +153,12 @@ def make(workload: int, n: int | None = None, m: int | None = None, seed: int | 
     m = dm if m is None else int(m)
     seed = workload if seed is None else int(seed)
     rng = np.random.default_rng(seed)
-    x, y, a, b = _GEN[workload](rng, n, m)
+    if d is not None and workload != 3:
+        raise ValueError("only workload 3 takes a dimension")
+    if workload == 3 and d is not None:
+        x, y, a, b = _w3(rng, n, m, d=int(d))
+    else:
+        x, y, a, b = _GEN[workload](rng, n, m)
     return Clouds(
         x=np.ascontiguousarray(x, dtype=np.float32),
         y=np.ascontiguousarray(y, dtype=np.float32),
