@@ -119,6 +119,142 @@ double seconds_since(std::chrono::steady_clock::time_point t0) {
 }
 
 }  // namespace
+
+SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, float* F[2],
+                     float* G[2], const sinkhorn_schedule& s, int32_t stall_window,
+                     double stall_rel) {
+  if (!(std::isfinite(s.eps_target) && s.eps_target > 0.0))
+    fail(SINKHORN_ERR_INVALID_ARG, "eps_target must be finite and > 0");
+  if (!(std::isfinite(s.eps_start) && s.eps_start >= s.eps_target))
+    fail(SINKHORN_ERR_INVALID_ARG, "eps_start must be >= eps_target");
+  if (!(s.eps_start == s.eps_target || (s.eps_factor > 0.0 && s.eps_factor < 1.0)))
+    fail(SINKHORN_ERR_INVALID_ARG, "eps_factor must be in (0, 1)");
+  if (s.iters_per_stage < 0 || s.fixed_iters < 0) fail(SINKHORN_ERR_INVALID_ARG, "negative iteration count");
+  if (!(s.fixed_iters > 0 || (s.max_iters >= 1 && s.tol >= 0.0)))
+    fail(SINKHORN_ERR_INVALID_ARG, "need max_iters >= 1 and tol >= 0");
+  const auto t0 = std::chrono::steady_clock::now();
+  hipStream_t st = p->stream;
+  const double pairs = (double)X.count * (double)Y.count;
+  copy_f32(f, X.count, F[0], st);
+  copy_f32(g, Y.count, G[0], st);
+  reset_nonfinite(p);
+  int cur = 0;
+  SolveOut o;
+
+  // one full iteration from state `cur`; eps_next is the eps of the f-step that follows
+  auto iterate = [&](double eps, double eps_next, bool residual) {
+    HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], X.H, eps, eps, residual};
+    dense_halfstep(p, fs);
+    if (residual) {
+      copy_ctl(p);
+      SK_HIP(hipEventRecord(p->ev, st));
+    }
+    HalfStep gs{&Y, &X, X.H, G[1 - cur], G[cur], Y.H, eps, eps_next, false};
+    dense_halfstep(p, gs);
+    o.halfsteps += 2;
+    cur = 1 - cur;
+  };
+
+  // annealing stages
+  double eps = s.eps_start;
+  bool first = true;
+  while (eps > s.eps_target) {
+    const double nxt = eps * s.eps_factor;
+    const double eps_after = nxt > s.eps_target ? nxt : s.eps_target;
+    if (s.iters_per_stage > 0) {
+      if (first) prep_column_term(p, Y, G[cur], eps, Y.H);
+      first = false;
+      for (int32_t k = 0; k < s.iters_per_stage; ++k) {
+        const bool last = k + 1 == s.iters_per_stage;
+        iterate(eps, last ? eps_after : eps, false);
+        ++o.iters;
+      }
+    }
+    ++o.stages;
+    eps = nxt;
+  }
+  eps = s.eps_target;
+  if (first) prep_column_term(p, Y, G[cur], eps, Y.H);
+
+  int ret = cur;
+  if (s.fixed_iters > 0) {
+    for (int32_t k = 0; k < s.fixed_iters; ++k) {
+      iterate(eps, eps, false);
+      ++o.iters;
+      ++o.final_iters;
+    }
+    ret = cur;
+    o.converged = 1;
+  } else {
+    const int32_t every = s.check_every > 1 ? s.check_every : 1;
+    std::vector<double> hist;
+    // iteration k checks the state left by iteration k-1
+    for (int64_t k = 1;; ++k) {
+      const int64_t prev_done = k - 1;
+      const bool check = prev_done >= 1 && prev_done % every == 0;
+      if (prev_done >= s.max_iters) {
+        // only the residual of the final state is still needed
+        HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], nullptr, eps, eps, true};
+        dense_halfstep(p, fs);
+        ++o.halfsteps;
+        double v;
+        int32_t bad;
+        read_reduction(p, &v, &bad);
+        if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
+        o.row_l1 = v;
+        ret = cur;
+        o.converged = v <= s.tol ? 1 : 0;
+        o.seconds = seconds_since(t0);
+        break;
+      }
+      const int state = cur;
+      iterate(eps, eps, check);
+      if (check) {
+        SK_HIP(hipEventSynchronize(p->ev));
+        if (p->host_ctl->nonfinite) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
+        const double v = p->host_ctl->residual;
+        hist.push_back(v);
+        const bool stalled = stall_window > 0 && (int64_t)hist.size() > stall_window &&
+                             v > (1.0 - stall_rel) * hist[hist.size() - 1 - stall_window];
+        if (v <= s.tol || stalled) {
+          o.row_l1 = v;
+          ret = state;
+          o.converged = v <= s.tol ? 1 : 0;
+          o.stalled = stalled && v > s.tol;
+          o.seconds = seconds_since(t0);
+          break;
+        }
+      }
+      ++o.iters;
+      ++o.final_iters;
+    }
+    if (!o.converged && !o.stalled) o.status = SINKHORN_NOT_CONVERGED;
+  }
+  // residuals of the returned state (the row side is known in the tol mode)
+  {
+    if (std::isnan(o.row_l1)) {
+      prep_column_term(p, Y, G[ret], eps, Y.H);
+      reset_nonfinite(p);
+      HalfStep fs{&X, &Y, Y.H, F[1 - ret], F[ret], nullptr, eps, eps, true};
+      dense_halfstep(p, fs);
+      read_reduction(p, &o.row_l1, nullptr);
+      ++o.halfsteps;
+    }
+    prep_column_term(p, X, F[ret], eps, X.H);
+    reset_nonfinite(p);
+    HalfStep gs{&Y, &X, X.H, G[1 - ret], G[ret], nullptr, eps, eps, true};
+    dense_halfstep(p, gs);
+    read_reduction(p, &o.col_l1, nullptr);
+    ++o.halfsteps;
+  }
+  if (o.seconds == 0.0) o.seconds = seconds_since(t0);
+  copy_f32(F[ret], X.count, f, st);
+  copy_f32(G[ret], Y.count, g, st);
+  SK_HIP(hipStreamSynchronize(st));
+  o.pairs = pairs * (double)o.halfsteps;
+  return o;
+}
+
 }  // namespace sk
 
 using namespace sk;
@@ -255,142 +391,21 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
                    sinkhorn_report* rep) {
   return guard([&] {
     require(p && sc && f && g, "null pointer");
-    const sinkhorn_schedule s = *sc;
-    require_eps(s.eps_target);
-    require(std::isfinite(s.eps_start) && s.eps_start >= s.eps_target, "eps_start must be >= eps_target");
-    require(s.eps_start == s.eps_target || (s.eps_factor > 0.0 && s.eps_factor < 1.0),
-            "eps_factor must be in (0, 1)");
-    require(s.iters_per_stage >= 0 && s.fixed_iters >= 0, "negative iteration count");
-    require(s.fixed_iters > 0 || (s.max_iters >= 1 && s.tol >= 0.0), "need max_iters >= 1 and tol >= 0");
-    const auto t0 = std::chrono::steady_clock::now();
-    hipStream_t st = p->stream;
-    const double pairs = (double)p->n * (double)p->m;
     float* F[2] = {p->fbuf[0], p->fbuf[1]};
     float* G[2] = {p->gbuf[0], p->gbuf[1]};
-    copy_f32(f, p->n, F[0], st);
-    copy_f32(g, p->m, G[0], st);
-    reset_nonfinite(p);
-    int cur = 0;
-    int64_t halfsteps = 0, iters = 0, final_iters = 0;
-    int32_t stages = 0;
-
-    // one full iteration from state `cur`; eps_next is the eps of the f-step that follows
-    auto iterate = [&](double eps, double eps_next, bool residual) {
-      HalfStep fs{&p->X, &p->Y, p->Y.H, F[1 - cur], F[cur], p->X.H, eps, eps, residual};
-      dense_halfstep(p, fs);
-      if (residual) {
-        copy_ctl(p);
-        SK_HIP(hipEventRecord(p->ev, st));
-      }
-      HalfStep gs{&p->Y, &p->X, p->X.H, G[1 - cur], G[cur], p->Y.H, eps, eps_next, false};
-      dense_halfstep(p, gs);
-      halfsteps += 2;
-      cur = 1 - cur;
-    };
-    auto nonfinite_now = [&]() { return p->host_ctl->nonfinite; };
-
-    // annealing stages
-    double eps = s.eps_start;
-    bool first = true;
-    while (eps > s.eps_target) {
-      double nxt = eps * s.eps_factor;
-      const double eps_after = nxt > s.eps_target ? nxt : s.eps_target;
-      if (s.iters_per_stage > 0) {
-        if (first) prep_column_term(p, p->Y, G[cur], eps, p->Y.H);
-        first = false;
-        for (int32_t k = 0; k < s.iters_per_stage; ++k) {
-          const bool last = k + 1 == s.iters_per_stage;
-          iterate(eps, last ? eps_after : eps, false);
-          ++iters;
-        }
-      }
-      ++stages;
-      eps = nxt;
-    }
-    eps = s.eps_target;
-    if (first) prep_column_term(p, p->Y, G[cur], eps, p->Y.H);
-
-    int status = SINKHORN_OK;
-    double row_l1 = NAN, col_l1 = NAN, seconds = 0.0;
-    int32_t converged = 0;
-    int ret = cur;
-    if (s.fixed_iters > 0) {
-      for (int32_t k = 0; k < s.fixed_iters; ++k) {
-        iterate(eps, eps, false);
-        ++iters;
-        ++final_iters;
-      }
-      ret = cur;
-      converged = 1;
-    } else {
-      const int32_t every = s.check_every > 1 ? s.check_every : 1;
-      // iteration k checks the state left by iteration k-1
-      for (int64_t k = 1;; ++k) {
-        const int64_t prev_done = k - 1;
-        const bool check = prev_done >= 1 && prev_done % every == 0;
-        const bool last_allowed = prev_done >= s.max_iters;
-        if (last_allowed) {
-          // only the residual of the final state is still needed
-          HalfStep fs{&p->X, &p->Y, p->Y.H, F[1 - cur], F[cur], nullptr, eps, eps, true};
-          dense_halfstep(p, fs);
-          ++halfsteps;
-          double v;
-          int32_t bad;
-          read_reduction(p, &v, &bad);
-          if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
-          row_l1 = v;
-          ret = cur;
-          converged = v <= s.tol ? 1 : 0;
-          seconds = seconds_since(t0);
-          break;
-        }
-        const int state = cur;
-        iterate(eps, eps, check);
-        if (check) {
-          SK_HIP(hipEventSynchronize(p->ev));
-          if (nonfinite_now()) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
-          const double v = p->host_ctl->residual;
-          if (v <= s.tol) {
-            row_l1 = v;
-            ret = state;
-            converged = 1;
-            seconds = seconds_since(t0);
-            break;
-          }
-        }
-        ++iters;
-        ++final_iters;
-      }
-      if (!converged) status = SINKHORN_NOT_CONVERGED;
-    }
-    // residuals of the returned state (the row side is known in the tol mode)
-    {
-      double r = NAN, c = NAN;
-      if (std::isnan(row_l1)) {
-        halfstep(p, true, eps, G[ret], F[1 - ret], F[ret], &r);
-        row_l1 = r;
-        ++halfsteps;
-      }
-      halfstep(p, false, eps, F[ret], G[1 - ret], G[ret], &c);
-      col_l1 = c;
-      ++halfsteps;
-    }
-    if (seconds == 0.0) seconds = seconds_since(t0);
-    copy_f32(F[ret], p->n, f, st);
-    copy_f32(G[ret], p->m, g, st);
-    SK_HIP(hipStreamSynchronize(st));
+    const SolveOut o = dense_solve(p, p->X, p->Y, f, g, F, G, *sc, 0, 0.0);
     if (rep) {
-      rep->halfsteps = halfsteps;
-      rep->iters = iters;
-      rep->final_iters = final_iters;
-      rep->pairs_evaluated = pairs * (double)halfsteps;
-      rep->row_l1 = row_l1;
-      rep->col_l1 = col_l1;
-      rep->seconds = seconds;
-      rep->stages = stages;
-      rep->converged = converged;
+      rep->halfsteps = o.halfsteps;
+      rep->iters = o.iters;
+      rep->final_iters = o.final_iters;
+      rep->pairs_evaluated = o.pairs;
+      rep->row_l1 = o.row_l1;
+      rep->col_l1 = o.col_l1;
+      rep->seconds = o.seconds;
+      rep->stages = o.stages;
+      rep->converged = o.converged;
     }
-    return status;
+    return o.status;
   });
 }
 

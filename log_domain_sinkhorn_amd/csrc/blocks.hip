@@ -1,0 +1,579 @@
+// Block summaries, the block-pair screen and sparse half-steps on its mask.
+//
+// FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport, §3.2 and §B.3:
+// fine updates screen block pairs with block-level potential maxima and
+// bounding boxes, keep admitted tiles in CSR form and stream them through the
+// log-sum-exp; a block with no admitted tile takes a dense update; both sparse
+// half-steps run on the same mask (the g-step on its transpose). §A.3: a tile
+// whose mass bound is at most its threshold omits at most delta_rel a_i per
+// row and delta_rel b_j per column.
+//
+// Blocks are B consecutive points of a side in its stored order. A tile
+// (I, J) is omitted iff, in fp64 with this exact operation order and no fused
+// multiply-adds,
+//   gap_k = max(max(lo_Jk - hi_Ik, lo_Ik - hi_Jk), 0),
+//   D     = s * ((gap_0^2 + gap_1^2) + gap_2^2),
+//   (F_I + G_J) - D  <=  eps * (log(delta_rel) - max(log W_I, log W_J)),
+// F/G = block maxima of the fp32 potentials, W = points * max weight of the
+// block, every log taken on the host by the C library. The test is symmetric
+// in I and J, so the column-major list is the same screen with the roles
+// swapped. Lists are written in increasing block order: bit-exact and
+// deterministic.
+#include <cfloat>
+#include <cmath>
+#include <vector>
+
+#include <rocprim/device/device_scan.hpp>
+
+#include "rowfinal.h"
+
+namespace sk {
+namespace {
+
+__device__ __forceinline__ float ex2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// One wave per block: min / max of each axis and the max weight.
+__global__ __launch_bounds__(64) void k_block_static(const float* __restrict__ soa, int64_t stride,
+                                                     int32_t d, const float* __restrict__ w,
+                                                     int64_t count, int32_t B,
+                                                     double* __restrict__ lo,
+                                                     double* __restrict__ hi,
+                                                     double* __restrict__ Wout, int64_t nb) {
+  const int64_t I = blockIdx.x;
+  const int64_t s = I * B;
+  const int64_t e = s + B < count ? s + B : count;
+  float l[3] = {FLT_MAX, FLT_MAX, FLT_MAX}, h[3] = {-FLT_MAX, -FLT_MAX, -FLT_MAX};
+  float wm = -FLT_MAX;
+  for (int64_t i = s + threadIdx.x; i < e; i += 64) {
+    for (int k = 0; k < d; ++k) {
+      const float v = soa[k * stride + i];
+      l[k] = fminf(l[k], v);
+      h[k] = fmaxf(h[k], v);
+    }
+    wm = fmaxf(wm, w[i]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    for (int k = 0; k < d; ++k) {
+      l[k] = fminf(l[k], __shfl_xor(l[k], o, 64));
+      h[k] = fmaxf(h[k], __shfl_xor(h[k], o, 64));
+    }
+    wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+  }
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < d; ++k) {
+      lo[k * nb + I] = (double)l[k];
+      hi[k * nb + I] = (double)h[k];
+    }
+    Wout[I] = (double)(e - s) * (double)wm;
+  }
+}
+
+// Block maxima of a potential (fp32 values widened exactly).
+__global__ __launch_bounds__(64) void k_block_max(const float* __restrict__ pot, int64_t count,
+                                                  int32_t B, double* __restrict__ F) {
+  const int64_t I = blockIdx.x;
+  const int64_t s = I * B;
+  const int64_t e = s + B < count ? s + B : count;
+  float v = -INFINITY;
+  for (int64_t i = s + threadIdx.x; i < e; i += 64) v = fmaxf(v, pot[i]);
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if (threadIdx.x == 0) F[I] = (double)v;
+}
+
+struct ScreenArgs {
+  const double* rlo;  // row side summaries [d][nr]
+  const double* rhi;
+  const double* rF;
+  const double* rlw;
+  int64_t nr;
+  const double* clo;  // column side summaries [d][nc]
+  const double* chi;
+  const double* cF;
+  const double* clw;
+  int64_t nc;
+  double scale;
+  double eps;
+  double log_delta;
+  int64_t* counts;    // count pass
+  const int64_t* ptr; // fill pass
+  int32_t* idx;
+};
+
+// Thread = row block I; the column blocks stream through as wave-uniform
+// scalar loads. FILL = false counts admitted tiles, FILL = true writes them.
+template <int D, bool FILL>
+__global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
+  const int64_t I = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = I < A.nr;
+  const int64_t Ir = live ? I : 0;
+  double lo[D], hi[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    lo[k] = A.rlo[k * A.nr + Ir];
+    hi[k] = A.rhi[k * A.nr + Ir];
+  }
+  const double FI = A.rF[Ir];
+  const double lwI = A.rlw[Ir];
+  int64_t cnt = 0;
+  int64_t out = (FILL && live) ? A.ptr[I] : 0;
+  const double* __restrict__ clo = A.clo;
+  const double* __restrict__ chi = A.chi;
+  const double* __restrict__ cF = A.cF;
+  const double* __restrict__ clw = A.clw;
+  for (int64_t J = 0; J < A.nc; ++J) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      const double a = __dsub_rn(clo[k * A.nc + J], hi[k]);
+      const double b = __dsub_rn(lo[k], chi[k * A.nc + J]);
+      const double gap = fmax(fmax(a, b), 0.0);
+      const double sq = __dmul_rn(gap, gap);
+      acc = k == 0 ? sq : __dadd_rn(acc, sq);
+    }
+    const double Dst = __dmul_rn(A.scale, acc);
+    const double lhs = __dsub_rn(__dadd_rn(FI, cF[J]), Dst);
+    const double rhs = __dmul_rn(A.eps, __dsub_rn(A.log_delta, fmax(lwI, clw[J])));
+    if (lhs > rhs) {
+      if (FILL) {
+        if (live) A.idx[out] = (int32_t)J;
+        ++out;
+      } else {
+        ++cnt;
+      }
+    }
+  }
+  if (!FILL && live) A.counts[I] = cnt;
+}
+
+constexpr int kSW = 8;   // waves per workgroup of the sparse half-step
+constexpr int kSR = 2;   // rows per lane
+constexpr int kSRows = 64 * kSR;
+
+struct SparseArgs {
+  const float* P;      // row side SoA [D][pstride]
+  int64_t pstride;
+  const float* Q;      // column side SoA [D][qstride]
+  int64_t qstride;
+  const float* H;      // column term of the column side
+  float nkappa;
+  int64_t nchunks;     // column chunks of kChunk points (all columns)
+  int32_t B;           // block size (multiple of kSRows)
+  const int64_t* ptr;  // [row blocks + 1]
+  const int32_t* idx;  // admitted column blocks
+  RowFinal F;
+};
+
+// Workgroup = one 128-row tile of row block I = tile * 128 / B; its waves
+// share out the admitted column blocks (or, for an empty list, all column
+// chunks) and merge through LDS in wave order.
+template <int D>
+__global__ __launch_bounds__(64 * kSW) void k_lse_sparse(SparseArgs A) {
+  const int64_t tile = blockIdx.x;
+  const int64_t I = tile * kSRows / A.B;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = tile * kSRows + lane;
+  float x[kSR][D];
+  float M[kSR], S[kSR];
+#pragma unroll
+  for (int r = 0; r < kSR; ++r) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
+    M[r] = -FLT_MAX;
+    S[r] = 0.0f;
+  }
+  const float nk = A.nkappa;
+  const float* __restrict__ Q = A.Q;
+  const float* __restrict__ H = A.H;
+  const int64_t qs = A.qstride;
+  const int64_t p0 = A.ptr[I];
+  const int64_t p1 = A.ptr[I + 1];
+  const int64_t cpb = A.B / kChunk;  // chunks per column block
+
+  auto run = [&](int64_t c0, int64_t c1) {
+    for (int64_t c = c0; c < c1; ++c) {
+      const int64_t j0 = c * kChunk;
+      float yv[D][kChunk];
+      float hv[kChunk];
+#pragma unroll
+      for (int k = 0; k < D; ++k)
+#pragma unroll
+        for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qs + j0 + jj];
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) hv[jj] = H[j0 + jj];
+#pragma unroll
+      for (int r = 0; r < kSR; ++r) {
+        float z[kChunk];
+#pragma unroll
+        for (int jj = 0; jj < kChunk; ++jj) {
+          float dd = x[r][0] - yv[0][jj];
+          float q = dd * dd;
+#pragma unroll
+          for (int k = 1; k < D; ++k) {
+            dd = x[r][k] - yv[k][jj];
+            q = __builtin_fmaf(dd, dd, q);
+          }
+          z[jj] = __builtin_fmaf(nk, q, hv[jj]);
+        }
+        float cm = z[0];
+#pragma unroll
+        for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
+        const float Mn = fmaxf(M[r], cm);
+        float acc = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kChunk; ++jj) acc += ex2(z[jj] - Mn);
+        S[r] = __builtin_fmaf(S[r], ex2(M[r] - Mn), acc);
+        M[r] = Mn;
+      }
+    }
+  };
+
+  if (p1 > p0) {
+    for (int64_t q = p0 + wave; q < p1; q += kSW) {
+      const int64_t J = A.idx[q];
+      const int64_t c0 = J * cpb;
+      const int64_t c1 = c0 + cpb < A.nchunks ? c0 + cpb : A.nchunks;
+      run(c0, c1);
+    }
+  } else {
+    const int64_t per = (A.nchunks + kSW - 1) / kSW;
+    const int64_t c0 = wave * per;
+    const int64_t c1 = c0 + per < A.nchunks ? c0 + per : A.nchunks;
+    run(c0, c1);
+  }
+
+  __shared__ float sM[kSW][kSRows];
+  __shared__ float sS[kSW][kSRows];
+  __shared__ double sRed[64 * kSW];
+#pragma unroll
+  for (int r = 0; r < kSR; ++r) {
+    sM[wave][lane + 64 * r] = M[r];
+    sS[wave][lane + 64 * r] = S[r];
+  }
+  __syncthreads();
+  double term = 0.0;
+  int bad = 0;
+  if (threadIdx.x < kSRows) {
+    const int t = threadIdx.x;
+    float mx = -FLT_MAX;
+#pragma unroll
+    for (int v = 0; v < kSW; ++v) mx = fmaxf(mx, sM[v][t]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kSW; ++v) sum = __builtin_fmaf(sS[v][t], ex2(sM[v][t] - mx), sum);
+    const int64_t i = tile * kSRows + t;
+    if (i < A.F.np) term = finalize_row(A.F, i, mx, (double)sum, &bad);
+  }
+  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
+  if (A.F.prev) {
+    sRed[threadIdx.x] = term;
+    __syncthreads();
+#pragma unroll
+    for (int w = 64 * kSW / 2; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) A.F.red_part[tile] = sRed[0];
+  }
+}
+
+// Counts entries of idx outside [0, nc) and rows whose ptr decreases.
+__global__ __launch_bounds__(256) void k_check_csr(const int64_t* __restrict__ ptr, int64_t nr,
+                                                   const int32_t* __restrict__ idx, int64_t nc,
+                                                   uint32_t* __restrict__ bad) {
+  const int64_t I = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (I >= nr) return;
+  const int64_t a = ptr[I], b = ptr[I + 1];
+  if (b < a || a < 0) {
+    atomicAdd(bad, 1u);
+    return;
+  }
+  for (int64_t q = a; q < b; ++q)
+    if (idx[q] < 0 || idx[q] >= nc) atomicAdd(bad, 1u);
+}
+
+// number of row blocks with an empty list
+__global__ __launch_bounds__(256) void k_count_empty(const int64_t* __restrict__ ptr, int64_t nr,
+                                                     uint32_t* __restrict__ out) {
+  const int64_t I = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (I < nr && ptr[I + 1] == ptr[I]) atomicAdd(out, 1u);
+}
+
+template <int D>
+void launch_screen(hipStream_t st, const ScreenArgs& A, bool fill) {
+  const dim3 grid((uint32_t)((A.nr + 255) / 256));
+  if (fill)
+    hipLaunchKernelGGL((k_screen<D, true>), grid, dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL((k_screen<D, false>), grid, dim3(256), 0, st, A);
+  SK_LAUNCH_CHECK();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- summaries
+void BlockSummary::release() {
+  dev_free(lo);
+  dev_free(hi);
+  dev_free(lw);
+  dev_free(F);
+  lo = hi = lw = F = nullptr;
+  nb = 0;
+}
+
+void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& out) {
+  out.release();
+  out.nb = (s.count + B - 1) / B;
+  out.B = B;
+  out.lo = (double*)dev_alloc(sizeof(double) * 3 * out.nb);
+  out.hi = (double*)dev_alloc(sizeof(double) * 3 * out.nb);
+  out.lw = (double*)dev_alloc(sizeof(double) * out.nb);
+  out.F = (double*)dev_alloc(sizeof(double) * out.nb);
+  double* W = (double*)dev_alloc(sizeof(double) * out.nb);
+  hipLaunchKernelGGL(k_block_static, dim3((uint32_t)out.nb), dim3(64), 0, p->stream, s.soa,
+                     s.padded, p->d, s.w, s.count, B, out.lo, out.hi, W, out.nb);
+  SK_LAUNCH_CHECK();
+  std::vector<double> h((size_t)out.nb);
+  SK_HIP(hipMemcpyAsync(h.data(), W, sizeof(double) * out.nb, hipMemcpyDeviceToHost, p->stream));
+  SK_HIP(hipStreamSynchronize(p->stream));
+  dev_free(W);
+  for (auto& v : h) v = v > 0.0 ? std::log(v) : -INFINITY;  // C library log
+  SK_HIP(hipMemcpyAsync(out.lw, h.data(), sizeof(double) * out.nb, hipMemcpyHostToDevice, p->stream));
+  SK_HIP(hipStreamSynchronize(p->stream));
+}
+
+void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, BlockSummary& s) {
+  hipLaunchKernelGGL(k_block_max, dim3((uint32_t)s.nb), dim3(64), 0, p->stream, pot, count, s.B, s.F);
+  SK_LAUNCH_CHECK();
+}
+
+// Row-major list of the tiles admitted between `rows` and `cols` summaries.
+// ptr [rows.nb + 1] is always written; idx only when the count fits cap.
+// Returns the count. counts_tmp must hold rows.nb + 1 int64.
+int64_t screen_tiles(sinkhorn_problem* p, const BlockSummary& rows, const BlockSummary& cols,
+                     double eps, double delta_rel, int64_t* ptr, int32_t* idx, int64_t cap,
+                     int64_t* counts_tmp) {
+  ScreenArgs A;
+  A.rlo = rows.lo;
+  A.rhi = rows.hi;
+  A.rF = rows.F;
+  A.rlw = rows.lw;
+  A.nr = rows.nb;
+  A.clo = cols.lo;
+  A.chi = cols.hi;
+  A.cF = cols.F;
+  A.clw = cols.lw;
+  A.nc = cols.nb;
+  A.scale = p->scale;
+  A.eps = eps;
+  A.log_delta = std::log(delta_rel);  // C library log
+  A.counts = counts_tmp;
+  A.ptr = ptr;
+  A.idx = idx;
+  auto screen = [&](bool fill) {
+    switch (p->d) {
+      case 1: launch_screen<1>(p->stream, A, fill); break;
+      case 2: launch_screen<2>(p->stream, A, fill); break;
+      case 3: launch_screen<3>(p->stream, A, fill); break;
+      default: fail(SINKHORN_ERR_UNSUPPORTED, "block screen needs d <= 3");
+    }
+  };
+  screen(false);
+  // ptr = exclusive scan of counts (counts_tmp[nb] = 0 makes ptr[nb] the total)
+  zero_i32((int32_t*)(counts_tmp + rows.nb), 2, p->stream);
+  size_t tb = 0;
+  SK_HIP(rocprim::exclusive_scan(nullptr, tb, counts_tmp, ptr, (int64_t)0, (size_t)(rows.nb + 1),
+                                 rocprim::plus<int64_t>(), p->stream));
+  void* temp = dev_alloc(tb);
+  const hipError_t e = rocprim::exclusive_scan(temp, tb, counts_tmp, ptr, (int64_t)0,
+                                               (size_t)(rows.nb + 1), rocprim::plus<int64_t>(),
+                                               p->stream);
+  int64_t nnz = 0;
+  if (e == hipSuccess) {
+    const hipError_t c = hipMemcpyAsync(&nnz, ptr + rows.nb, sizeof(int64_t), hipMemcpyDeviceToHost,
+                                        p->stream);
+    const hipError_t s = hipStreamSynchronize(p->stream);
+    dev_free(temp);
+    check_hip(c, "hipMemcpyAsync");
+    check_hip(s, "hipStreamSynchronize");
+  } else {
+    dev_free(temp);
+    check_hip(e, "rocprim::exclusive_scan");
+  }
+  if (idx && nnz <= cap) screen(true);
+  return nnz;
+}
+
+int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
+  uint32_t* d = (uint32_t*)dev_alloc(sizeof(uint32_t));
+  zero_i32((int32_t*)d, 1, p->stream);
+  hipLaunchKernelGGL(k_count_empty, dim3((uint32_t)((nr + 255) / 256)), dim3(256), 0, p->stream, ptr,
+                     nr, d);
+  SK_LAUNCH_CHECK();
+  uint32_t h = 0;
+  SK_HIP(hipMemcpyAsync(&h, d, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+  SK_HIP(hipStreamSynchronize(p->stream));
+  dev_free(d);
+  return (int64_t)h;
+}
+
+// ---------------------------------------------------------------- sparse half-step
+void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const int64_t* ptr,
+                     const int32_t* idx, double pairs) {
+  const Side& rows = *hs.rows;
+  const Side& cols = *hs.cols;
+  if (B % kSRows != 0) fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need B a multiple of 128");
+  const int64_t tiles = (rows.count + kSRows - 1) / kSRows;
+  if (tiles > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
+  SparseArgs A;
+  A.P = rows.soa;
+  A.pstride = rows.padded;
+  A.Q = cols.soa;
+  A.qstride = cols.padded;
+  A.H = hs.Hcols;
+  A.nkappa = (float)(-p->scale * kLog2e / hs.eps);
+  A.nchunks = (cols.count + kChunk - 1) / kChunk;
+  A.B = B;
+  A.ptr = ptr;
+  A.idx = idx;
+  A.F = make_rowfinal(p, hs);
+  prof_begin(p);
+  switch (p->d) {
+    case 1: hipLaunchKernelGGL((k_lse_sparse<1>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
+    case 2: hipLaunchKernelGGL((k_lse_sparse<2>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
+    case 3: hipLaunchKernelGGL((k_lse_sparse<3>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
+    default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
+  }
+  SK_LAUNCH_CHECK();
+  prof_end(p, pairs);
+  if (A.F.prev) launch_reduce(p, tiles);
+}
+
+void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_t* idx, int64_t nc) {
+  uint32_t* d = (uint32_t*)dev_alloc(sizeof(uint32_t));
+  zero_i32((int32_t*)d, 1, p->stream);
+  hipLaunchKernelGGL(k_check_csr, dim3((uint32_t)((nr + 255) / 256)), dim3(256), 0, p->stream, ptr,
+                     nr, idx, nc, d);
+  SK_LAUNCH_CHECK();
+  uint32_t h = 0;
+  SK_HIP(hipMemcpyAsync(&h, d, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+  SK_HIP(hipStreamSynchronize(p->stream));
+  dev_free(d);
+  if (h) fail(SINKHORN_ERR_INVALID_ARG, "tile list has out-of-range entries");
+}
+
+}  // namespace sk
+
+using namespace sk;
+
+namespace {
+
+template <class F>
+int guarded(F&& body) {
+  try {
+    return body();
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+void require(bool ok, const char* what) {
+  if (!ok) fail(SINKHORN_ERR_INVALID_ARG, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sinkhorn_block_screen(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                          int32_t B, double delta_rel, int32_t transpose, int64_t* ptr,
+                          int32_t* idx, int64_t cap, int64_t* nnz_out) {
+  return guarded([&] {
+    require(p && f && g && ptr && nnz_out, "null pointer");
+    require(std::isfinite(eps) && eps > 0.0, "eps must be finite and > 0");
+    require(B >= 1 && B <= 1024, "B must be in [1, 1024]");
+    require(delta_rel > 0.0 && std::isfinite(delta_rel), "delta_rel must be finite and > 0");
+    require(cap >= 0, "cap must be >= 0");
+    if (p->d > 3) fail(SINKHORN_ERR_UNSUPPORTED, "block screen needs d <= 3");
+    BlockSummary sx, sy;
+    try {
+      block_static(p, p->X, B, sx);
+      block_static(p, p->Y, B, sy);
+      block_potential_max(p, f, p->n, sx);
+      block_potential_max(p, g, p->m, sy);
+      const BlockSummary& R = transpose ? sy : sx;
+      const BlockSummary& C = transpose ? sx : sy;
+      int64_t* tmp = (int64_t*)dev_alloc(sizeof(int64_t) * (R.nb + 1));
+      int64_t nnz = 0;
+      try {
+        nnz = screen_tiles(p, R, C, eps, delta_rel, ptr, idx, cap, tmp);
+        SK_HIP(hipStreamSynchronize(p->stream));
+      } catch (...) {
+        dev_free(tmp);
+        throw;
+      }
+      dev_free(tmp);
+      *nnz_out = nnz;
+      sx.release();
+      sy.release();
+      if (!idx || nnz > cap) return nnz == 0 ? SINKHORN_OK : SINKHORN_ERR_CAPACITY;
+      return SINKHORN_OK;
+    } catch (...) {
+      sx.release();
+      sy.release();
+      throw;
+    }
+  });
+}
+
+int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, int32_t B,
+                               const int64_t* ptr, const int32_t* idx, float* f_out,
+                               const float* f_prev, double* row_l1) {
+  return guarded([&] {
+    require(p && g && ptr && f_out, "null pointer");
+    require(std::isfinite(eps) && eps > 0.0, "eps must be finite and > 0");
+    require(B >= 1 && B <= 1024, "B must be in [1, 1024]");
+    if (p->d > 3) fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
+    const int64_t nr = (p->n + B - 1) / B, nc = (p->m + B - 1) / B;
+    check_csr(p, ptr, nr, idx, nc);
+    prep_column_term(p, p->Y, g, eps, p->Y.H);
+    reset_nonfinite(p);
+    HalfStep hs{&p->X, &p->Y, p->Y.H, f_out, f_prev, nullptr, eps, eps, f_prev && row_l1};
+    sparse_halfstep(p, hs, B, ptr, idx, 0.0);
+    double v = 0.0;
+    int32_t bad = 0;
+    read_reduction(p, &v, &bad);
+    if (row_l1) *row_l1 = hs.residual ? v : NAN;
+    if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in sparse half-step");
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_sparse_halfstep_g(sinkhorn_problem* p, double eps, const float* f, int32_t B,
+                               const int64_t* ptr, const int32_t* idx, float* g_out,
+                               const float* g_prev, double* col_l1) {
+  return guarded([&] {
+    require(p && f && ptr && g_out, "null pointer");
+    require(std::isfinite(eps) && eps > 0.0, "eps must be finite and > 0");
+    require(B >= 1 && B <= 1024, "B must be in [1, 1024]");
+    if (p->d > 3) fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
+    const int64_t nr = (p->m + B - 1) / B, nc = (p->n + B - 1) / B;
+    check_csr(p, ptr, nr, idx, nc);
+    prep_column_term(p, p->X, f, eps, p->X.H);
+    reset_nonfinite(p);
+    HalfStep hs{&p->Y, &p->X, p->X.H, g_out, g_prev, nullptr, eps, eps, g_prev && col_l1};
+    sparse_halfstep(p, hs, B, ptr, idx, 0.0);
+    double v = 0.0;
+    int32_t bad = 0;
+    read_reduction(p, &v, &bad);
+    if (col_l1) *col_l1 = hs.residual ? v : NAN;
+    if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in sparse half-step");
+    return SINKHORN_OK;
+  });
+}
+
+}  // extern "C"

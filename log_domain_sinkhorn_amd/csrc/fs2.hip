@@ -1,0 +1,406 @@
+// Block-sparse multiscale solve (d <= 3).
+//
+// FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport:
+//   §3, §B.1   Morton order; blocks of B consecutive sorted points; cells are
+//              Morton-prefix groups, at most about twice as many as blocks
+//              (prefix of p = floor(log2(2 max(NB, MB))) bits by default);
+//   §3.1, §B.2 annealed dense Sinkhorn on cell records (mass-weighted
+//              centroid, mass), continued at the target eps until the coarse
+//              residual is small, stalls, or hits its cap;
+//   §1, §A.1   the coarse potentials are lifted to the points by one
+//              log-sum-exp against the other side's centroids;
+//   §3.2       every fine update rebuilds the mask at the current potentials
+//              and runs the sparse f- and g-steps on it (g on the transpose);
+//   §C.4       the stop certificate is the admitted-plan residual plus a bound
+//              on the omitted mass: max(R_A,row, R_A,col) + Omega <= tol with
+//              Omega = max(NB, MB) delta_rel, the a-priori total omitted mass
+//              of the threshold rule (§3.2).
+// The admitted-plan residual of the state (f, g) is the fused residual of the
+// sparse f-step built at (f, g); the column residual is a sparse g pass at
+// (f, g), run only when the row test already passes.
+#include <chrono>
+#include <cmath>
+#include <vector>
+
+#include <rocprim/device/device_scan.hpp>
+
+#include "internal.h"
+
+namespace sk {
+namespace {
+
+__global__ __launch_bounds__(256) void k_gather(const float* __restrict__ soa, int64_t istride,
+                                                const float* __restrict__ w,
+                                                const int32_t* __restrict__ perm, int64_t count,
+                                                int32_t d, float* __restrict__ out,
+                                                int64_t ostride, float* __restrict__ wout) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const int64_t s = perm[i];
+  for (int k = 0; k < d; ++k) out[k * ostride + i] = soa[k * istride + s];
+  wout[i] = w[s];
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const float* __restrict__ in,
+                                                 const int32_t* __restrict__ perm, int64_t count,
+                                                 float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) out[perm[i]] = in[i];
+}
+
+__global__ __launch_bounds__(256) void k_cell_flags(const uint64_t* __restrict__ codes,
+                                                    int64_t count, int32_t shift,
+                                                    int32_t* __restrict__ flags) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  flags[i] = (i == 0 || (codes[i] >> shift) != (codes[i - 1] >> shift)) ? 1 : 0;
+}
+
+// incl = inclusive scan of flags; a cell c starts where flags[i] = 1 and incl[i] = c + 1.
+__global__ __launch_bounds__(256) void k_cell_offsets(const int32_t* __restrict__ flags,
+                                                      const int32_t* __restrict__ incl,
+                                                      int64_t count, int64_t* __restrict__ off) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  if (flags[i]) off[incl[i] - 1] = i;
+  if (i == count - 1) off[incl[i]] = count;
+}
+
+// One thread per cell: mass and mass-weighted centroid, accumulated in fp64.
+__global__ __launch_bounds__(256) void k_cell_records(const float* __restrict__ soa,
+                                                      int64_t stride, const float* __restrict__ w,
+                                                      const int64_t* __restrict__ off,
+                                                      int64_t ncells, int32_t d,
+                                                      float* __restrict__ cent, int64_t cstride,
+                                                      float* __restrict__ mass) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncells) return;
+  const int64_t s = off[c], e = off[c + 1];
+  double m = 0.0, acc[3] = {0.0, 0.0, 0.0}, plain[3] = {0.0, 0.0, 0.0};
+  for (int64_t i = s; i < e; ++i) {
+    const double wi = (double)w[i];
+    m += wi;
+    for (int k = 0; k < d; ++k) {
+      const double v = (double)soa[k * stride + i];
+      acc[k] += wi * v;
+      plain[k] += v;
+    }
+  }
+  for (int k = 0; k < d; ++k)
+    cent[k * cstride + c] = (float)(m > 0.0 ? acc[k] / m : plain[k] / (double)(e - s));
+  mass[c] = (float)m;
+}
+
+void free_side(Side& s) {
+  dev_free(s.soa);
+  dev_free(s.w);
+  dev_free(s.H);
+  s = Side();
+}
+
+void alloc_side(Side& s, int64_t count, int32_t d, hipStream_t st) {
+  s.count = count;
+  s.padded = round_up(count, kPad);
+  s.soa = (float*)dev_alloc(sizeof(float) * d * s.padded);
+  s.w = (float*)dev_alloc(sizeof(float) * count);
+  s.H = (float*)dev_alloc(sizeof(float) * s.padded);
+  fill_f32(s.soa, d * s.padded, 0.0f, st);
+  fill_f32(s.H, s.padded, -INFINITY, st);
+}
+
+// Morton-prefix cells of a sorted side: centroids and masses as a new side.
+void build_cells(sinkhorn_problem* p, const Side& sorted, const uint64_t* codes, int32_t p_bits,
+                 Side& cells) {
+  hipStream_t st = p->stream;
+  const int64_t n = sorted.count;
+  const int32_t shift = 21 * p->d - p_bits;
+  int32_t* flags = (int32_t*)dev_alloc(sizeof(int32_t) * n);
+  int32_t* incl = (int32_t*)dev_alloc(sizeof(int32_t) * n);
+  int64_t* off = nullptr;
+  void* temp = nullptr;
+  try {
+    hipLaunchKernelGGL(k_cell_flags, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, codes, n,
+                       shift, flags);
+    SK_LAUNCH_CHECK();
+    size_t tb = 0;
+    SK_HIP(rocprim::inclusive_scan(nullptr, tb, flags, incl, (size_t)n, rocprim::plus<int32_t>(), st));
+    temp = dev_alloc(tb);
+    SK_HIP(rocprim::inclusive_scan(temp, tb, flags, incl, (size_t)n, rocprim::plus<int32_t>(), st));
+    int32_t ncell = 0;
+    SK_HIP(hipMemcpyAsync(&ncell, incl + n - 1, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    SK_HIP(hipStreamSynchronize(st));
+    off = (int64_t*)dev_alloc(sizeof(int64_t) * (ncell + 1));
+    hipLaunchKernelGGL(k_cell_offsets, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, flags,
+                       incl, n, off);
+    SK_LAUNCH_CHECK();
+    alloc_side(cells, ncell, p->d, st);
+    hipLaunchKernelGGL(k_cell_records, dim3((uint32_t)((ncell + 255) / 256)), dim3(256), 0, st,
+                       sorted.soa, sorted.padded, sorted.w, off, (int64_t)ncell, p->d, cells.soa,
+                       cells.padded, cells.w);
+    SK_LAUNCH_CHECK();
+    SK_HIP(hipStreamSynchronize(st));
+  } catch (...) {
+    dev_free(flags);
+    dev_free(incl);
+    dev_free(off);
+    dev_free(temp);
+    throw;
+  }
+  dev_free(flags);
+  dev_free(incl);
+  dev_free(off);
+  dev_free(temp);
+}
+
+// Grow the split partial buffers to hold `floats` entries each.
+void ensure_partials(sinkhorn_problem* p, int64_t floats) {
+  if (floats <= p->part_cap) return;
+  SK_HIP(hipStreamSynchronize(p->stream));
+  dev_free(p->Mpart);
+  dev_free(p->Spart);
+  p->Mpart = p->Spart = nullptr;
+  p->part_cap = 0;
+  p->Mpart = (float*)dev_alloc(sizeof(float) * floats);
+  p->Spart = (float*)dev_alloc(sizeof(float) * floats);
+  p->part_cap = floats;
+}
+
+double now_s() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+// Device buffers of one tile list that grows on demand.
+struct TileList {
+  int64_t* ptr = nullptr;
+  int64_t* tmp = nullptr;
+  int32_t* idx = nullptr;
+  int64_t cap = 0;
+  int64_t nnz = 0;
+  ~TileList() {
+    dev_free(ptr);
+    dev_free(tmp);
+    dev_free(idx);
+  }
+  void build(sinkhorn_problem* p, const BlockSummary& r, const BlockSummary& c, double eps,
+             double delta) {
+    if (!ptr) {
+      ptr = (int64_t*)dev_alloc(sizeof(int64_t) * (r.nb + 1));
+      tmp = (int64_t*)dev_alloc(sizeof(int64_t) * (r.nb + 1));
+    }
+    nnz = screen_tiles(p, r, c, eps, delta, ptr, idx, cap, tmp);
+    if (nnz > cap) {
+      dev_free(idx);
+      idx = nullptr;
+      cap = 0;
+      const int64_t want = nnz + nnz / 4 + 1024;
+      idx = (int32_t*)dev_alloc(sizeof(int32_t) * want);
+      cap = want;
+      nnz = screen_tiles(p, r, c, eps, delta, ptr, idx, cap, tmp);
+    }
+  }
+};
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
+                                         float* f, float* g, sinkhorn_multiscale_report* rep) {
+  Side Xs, Ys, Cx, Cy;
+  uint64_t* codes[2] = {nullptr, nullptr};
+  int32_t* perm[2] = {nullptr, nullptr};
+  float* pot[8] = {};
+  BlockSummary sx, sy;
+  auto cleanup = [&]() {
+    free_side(Xs);
+    free_side(Ys);
+    free_side(Cx);
+    free_side(Cy);
+    for (int k = 0; k < 2; ++k) {
+      dev_free(codes[k]);
+      dev_free(perm[k]);
+    }
+    for (auto& q : pot) dev_free(q);
+    sx.release();
+    sy.release();
+  };
+  try {
+    if (!p || !prm || !f || !g) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    const sinkhorn_multiscale_params P = *prm;
+    if (p->d > 3) fail(SINKHORN_ERR_UNSUPPORTED, "the multiscale solve needs d <= 3");
+    if (P.B < 128 || P.B % 128 != 0) fail(SINKHORN_ERR_UNSUPPORTED, "B must be a multiple of 128");
+    if (!(std::isfinite(P.eps) && P.eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(P.tol > 0.0) || !(P.delta_scale > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "tol and delta_scale must be > 0");
+    if (P.max_fine < 0 || P.coarse_max < 1) fail(SINKHORN_ERR_INVALID_ARG, "bad iteration caps");
+    hipStream_t st = p->stream;
+    const int32_t d = p->d;
+    const int64_t n = p->n, m = p->m;
+    const double t_start = now_s();
+    const int64_t NB = (n + P.B - 1) / P.B, MB = (m + P.B - 1) / P.B;
+    const double delta = P.delta_scale / (double)(NB > MB ? NB : MB);
+    const double omega = (double)(NB > MB ? NB : MB) * delta;
+    int32_t p_bits = P.p_bits;
+    if (p_bits <= 0) p_bits = (int32_t)std::floor(std::log2(2.0 * (double)(NB > MB ? NB : MB)));
+    if (p_bits > 21 * d) p_bits = 21 * d;
+    sinkhorn_multiscale_report R{};
+    R.omega = omega;
+
+    // ---- Morton order and sorted sides
+    for (int k = 0; k < 2; ++k) {
+      const int64_t c = k == 0 ? n : m;
+      codes[k] = (uint64_t*)dev_alloc(sizeof(uint64_t) * c);
+      perm[k] = (int32_t*)dev_alloc(sizeof(int32_t) * c);
+    }
+    morton_sort_soa(p->X.soa, p->X.padded, p->Y.soa, p->Y.padded, n, m, d, st, codes[0], perm[0],
+                    codes[1], perm[1]);
+    alloc_side(Xs, n, d, st);
+    alloc_side(Ys, m, d, st);
+    hipLaunchKernelGGL(k_gather, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p->X.soa,
+                       p->X.padded, p->X.w, perm[0], n, d, Xs.soa, Xs.padded, Xs.w);
+    SK_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_gather, dim3((uint32_t)((m + 255) / 256)), dim3(256), 0, st, p->Y.soa,
+                       p->Y.padded, p->Y.w, perm[1], m, d, Ys.soa, Ys.padded, Ys.w);
+    SK_LAUNCH_CHECK();
+    build_cells(p, Xs, codes[0], p_bits, Cx);
+    build_cells(p, Ys, codes[1], p_bits, Cy);
+    R.ncells_x = Cx.count;
+    R.ncells_y = Cy.count;
+    SK_HIP(hipStreamSynchronize(st));
+    const double t_sorted = now_s();
+    R.seconds_sort = t_sorted - t_start;
+
+    // ---- coarse annealed solve on the cells
+    auto need = [&](int64_t rows, int64_t cols) {
+      ensure_partials(p, partial_floats_needed(p, rows, round_up(rows, kPad), cols));
+    };
+    need(Cx.count, Cy.count);
+    need(Cy.count, Cx.count);
+    need(n, Cy.count);
+    need(m, Cx.count);
+    pot[0] = (float*)dev_alloc(sizeof(float) * Cx.count);  // F
+    pot[1] = (float*)dev_alloc(sizeof(float) * Cy.count);  // G
+    pot[2] = (float*)dev_alloc(sizeof(float) * Cx.count);
+    pot[3] = (float*)dev_alloc(sizeof(float) * Cx.count);
+    pot[4] = (float*)dev_alloc(sizeof(float) * Cy.count);
+    pot[5] = (float*)dev_alloc(sizeof(float) * Cy.count);
+    fill_f32(pot[0], Cx.count, 0.0f, st);
+    fill_f32(pot[1], Cy.count, 0.0f, st);
+    float* CF[2] = {pot[2], pot[3]};
+    float* CG[2] = {pot[4], pot[5]};
+    sinkhorn_schedule cs;
+    cs.eps_start = P.coarse_eps_start > P.eps ? P.coarse_eps_start : P.eps;
+    cs.eps_target = P.eps;
+    cs.eps_factor = P.coarse_factor;
+    cs.iters_per_stage = P.coarse_iters_per_stage;
+    cs.fixed_iters = 0;
+    cs.tol = P.coarse_tol;
+    cs.max_iters = P.coarse_max;
+    cs.check_every = 1;
+    const SolveOut co = dense_solve(p, Cx, Cy, pot[0], pot[1], CF, CG, cs, P.stall_window, P.stall_rel);
+    R.coarse_iters = co.iters;
+    R.pairs_evaluated += co.pairs;
+    const double t_coarse = now_s();
+    R.seconds_coarse = t_coarse - t_sorted;
+    for (int k = 2; k < 6; ++k) {
+      dev_free(pot[k]);
+      pot[k] = nullptr;
+    }
+
+    // ---- lift: f from the y cells, g from the x cells
+    float* fs[2] = {(float*)dev_alloc(sizeof(float) * n), (float*)dev_alloc(sizeof(float) * n)};
+    pot[2] = fs[0];
+    pot[3] = fs[1];
+    float* gs[2] = {(float*)dev_alloc(sizeof(float) * m), (float*)dev_alloc(sizeof(float) * m)};
+    pot[4] = gs[0];
+    pot[5] = gs[1];
+    const double eps = P.eps;
+    reset_nonfinite(p);
+    prep_column_term(p, Cy, pot[1], eps, Cy.H);
+    dense_halfstep(p, HalfStep{&Xs, &Cy, Cy.H, fs[0], nullptr, nullptr, eps, eps, false});
+    prep_column_term(p, Cx, pot[0], eps, Cx.H);
+    dense_halfstep(p, HalfStep{&Ys, &Cx, Cx.H, gs[0], nullptr, nullptr, eps, eps, false});
+    R.pairs_evaluated += (double)n * (double)Cy.count + (double)m * (double)Cx.count;
+    {
+      int32_t bad = 0;
+      read_reduction(p, nullptr, &bad);
+      if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite lifted potential");
+    }
+    const double t_lift = now_s();
+    R.seconds_lift = t_lift - t_coarse;
+
+    // ---- fine loop on the block-pair mask
+    block_static(p, Xs, P.B, sx);
+    block_static(p, Ys, P.B, sy);
+    TileList rowL, colL;
+    int cf = 0, cg = 0;
+    int status = SINKHORN_NOT_CONVERGED;
+    double Rrow = NAN, Rcol = NAN;
+    const double pair_block = (double)P.B * (double)P.B;
+    while (true) {
+      block_potential_max(p, fs[cf], n, sx);
+      block_potential_max(p, gs[cg], m, sy);
+      rowL.build(p, sx, sy, eps, delta);
+      colL.build(p, sy, sx, eps, delta);
+      R.last_tiles = rowL.nnz;
+      const double row_pairs = (double)rowL.nnz * pair_block +
+                               (double)count_empty_rows(p, rowL.ptr, sx.nb) * P.B * (double)m;
+      const double col_pairs = (double)colL.nnz * pair_block +
+                               (double)count_empty_rows(p, colL.ptr, sy.nb) * P.B * (double)n;
+      // sparse f-step at (f, g); its fused residual is R_A,row of (f, g)
+      reset_nonfinite(p);
+      prep_column_term(p, Ys, gs[cg], eps, Ys.H);
+      sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true},
+                      P.B, rowL.ptr, rowL.idx, row_pairs);
+      int32_t bad = 0;
+      read_reduction(p, &Rrow, &bad);
+      if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in the fine loop");
+      R.pairs_evaluated += row_pairs;
+      Rcol = NAN;
+      if (Rrow + omega <= P.tol) {
+        prep_column_term(p, Xs, fs[cf], eps, Xs.H);
+        sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true},
+                        P.B, colL.ptr, colL.idx, col_pairs);
+        read_reduction(p, &Rcol, nullptr);
+        R.pairs_evaluated += col_pairs;
+        if ((Rrow > Rcol ? Rrow : Rcol) + omega <= P.tol) {
+          status = SINKHORN_OK;
+          R.certified = 1;
+          break;
+        }
+      }
+      if (R.fine_updates >= P.max_fine) break;
+      cf = 1 - cf;  // accept the f-step
+      prep_column_term(p, Xs, fs[cf], eps, Xs.H);
+      sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false},
+                      P.B, colL.ptr, colL.idx, col_pairs);
+      R.pairs_evaluated += col_pairs;
+      cg = 1 - cg;
+      ++R.fine_updates;
+    }
+    R.R_A_row = Rrow;
+    R.R_A_col = Rcol;
+    // ---- back to the caller's order
+    hipLaunchKernelGGL(k_scatter, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, fs[cf],
+                       perm[0], n, f);
+    SK_LAUNCH_CHECK();
+    hipLaunchKernelGGL(k_scatter, dim3((uint32_t)((m + 255) / 256)), dim3(256), 0, st, gs[cg],
+                       perm[1], m, g);
+    SK_LAUNCH_CHECK();
+    SK_HIP(hipStreamSynchronize(st));
+    const double t_end = now_s();
+    R.seconds_fine = t_end - t_lift;
+    R.seconds_total = t_end - t_start;
+    if (rep) *rep = R;
+    cleanup();
+    return status;
+  } catch (const Failure& e) {
+    cleanup();
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    cleanup();
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -146,6 +147,46 @@ void setup_mfma(sinkhorn_problem* p, const float* x, const float* y);
 void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs);
 void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps);
 int64_t mfma_partial_floats(int64_t nrows, int64_t ncols);
+
+// blocks.hip: per-block summaries of a side in its stored order
+struct BlockSummary {
+  int64_t nb = 0;        // blocks
+  int32_t B = 0;         // points per block
+  double* lo = nullptr;  // [3][nb] per-axis minimum (fp32 values widened)
+  double* hi = nullptr;  // [3][nb] per-axis maximum
+  double* lw = nullptr;  // [nb] log(points * max weight), C library log on the host
+  double* F = nullptr;   // [nb] maximum potential, refreshed per screen
+  void release();
+};
+void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& out);
+void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, BlockSummary& s);
+int64_t screen_tiles(sinkhorn_problem* p, const BlockSummary& rows, const BlockSummary& cols,
+                     double eps, double delta_rel, int64_t* ptr, int32_t* idx, int64_t cap,
+                     int64_t* counts_tmp);
+int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr);
+void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const int64_t* ptr,
+                     const int32_t* idx, double pairs);
+void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_t* idx, int64_t nc);
+
+// api.hip: annealed dense solve between two sides (X rows, Y columns), f/g
+// in/out, F/G scratch pairs; stall_window > 0 adds the stall stop rule
+struct SolveOut {
+  int64_t halfsteps = 0, iters = 0, final_iters = 0;
+  double pairs = 0.0, row_l1 = NAN, col_l1 = NAN, seconds = 0.0;
+  int32_t stages = 0, converged = 0;
+  bool stalled = false;
+  int status = SINKHORN_OK;
+};
+SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, float* F[2],
+                     float* G[2], const sinkhorn_schedule& s, int32_t stall_window,
+                     double stall_rel);
+
+// morton.hip: sorted codes and the original index of each sorted point
+void morton_sort(const float* x, const float* y, int64_t n, int64_t m, int32_t d, hipStream_t st,
+                 uint64_t* codes_x, int32_t* perm_x, uint64_t* codes_y, int32_t* perm_y);
+void morton_sort_soa(const float* x, int64_t xpad, const float* y, int64_t ypad, int64_t n,
+                     int64_t m, int32_t d, hipStream_t st, uint64_t* codes_x, int32_t* perm_x,
+                     uint64_t* codes_y, int32_t* perm_y);
 
 double device_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
                             hipStream_t st);

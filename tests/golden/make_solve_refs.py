@@ -47,6 +47,39 @@ def run(name):
           f"converged {r.converged} in {time.time() - t:.1f}s -> {out}", flush=True)
 
 
+def main(names):
+    for name in names or list(CASES) + list(FS2_CASES):
+        if name in FS2_CASES:
+            run_fs2(name)
+        else:
+            run(name)
+
+
+# multiscale (block-sparse) solve cases: name -> (workload, n, FS2Params kwargs)
+FS2_CASES = {
+    "w5_n16384_fs2": (5, 16384, dict(B=128, eps=1e-4, tol=1e-2)),
+}
+
+
+def run_fs2(name):
+    from oracle.fs2 import FS2Params
+
+    w, n, kw = FS2_CASES[name]
+    c = synth.make(w, n=n, m=n)
+    prm = FS2Params(**kw)
+    t = time.time()
+    r = oracle.fs2_solve(c.x, c.y, c.a, c.b, prm)
+    out = os.path.join(HERE, f"fs2_{name}.npz")
+    np.savez_compressed(
+        out, f=r.f, g=r.g, coarse_iters=r.coarse_iters, fine_updates=r.fine_updates,
+        R_A_row=r.R_A_row, R_A_col=r.R_A_col, omega=r.omega, certified=r.certified,
+        ncells_x=r.ncells_x, ncells_y=r.ncells_y, tiles=np.asarray(r.tiles_history), workload=w, n=n,
+        **{k: v for k, v in prm.__dict__.items()},
+    )
+    print(f"{name}: coarse {r.coarse_iters} fine {r.fine_updates} certified {r.certified} "
+          f"R_A {r.R_A_row:.3e}/{r.R_A_col:.3e} cells {r.ncells_x}/{r.ncells_y} in {time.time() - t:.1f}s -> {out}",
+          flush=True)
+
+
 if __name__ == "__main__":
-    for name in sys.argv[1:] or list(CASES):
-        run(name)
+    main(sys.argv[1:])

@@ -1,0 +1,163 @@
+"""GPU parity of the block-sparse path against the fp64 oracle: Morton codes
+and order and the block-pair tile lists bit-exact on identical inputs; sparse
+half-steps within 1e-5 max(eps, |f|); the multiscale solve certified."""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def sk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import log_domain_sinkhorn_amd as sk
+
+    return sk
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _gpu_morton(sk, x, y):
+    cx, px, cy, py = sk.morton_order(_t(x), _t(y))
+    u = lambda c: c.cpu().numpy().view(np.uint64)
+    return u(cx), px.cpu().numpy(), u(cy), py.cpu().numpy()
+
+
+@pytest.mark.parametrize("w,n,m", [(5, None, None), (5, 5000, 3001), (4, 1000, 1000), (1, 999, 1001)])
+def test_morton_codes_and_order_bit_exact(sk, w, n, m):
+    c = synth.make(w, n=n, m=m)
+    x, y = c.x, c.y
+    if n == 5000:  # duplicates must keep their input order
+        x = x.copy()
+        x[100:200] = x[7]
+    _log(f"morton w={w} n={len(x)}")
+    got = _gpu_morton(sk, x, y)
+    ref = oracle.morton_order(x, y)
+    for g_, r_, what in zip(got, ref, ("codes_x", "perm_x", "codes_y", "perm_y")):
+        assert np.array_equal(g_, r_), what
+
+
+def _sorted_problem(w, n, seed_shift=0.0):
+    c = synth.make(w, n=n, m=n)
+    _, px, _, py = oracle.morton_order(c.x, c.y)
+    return c.x[px], c.y[py], c.a[px], c.b[py]
+
+
+def _near_plan_potentials(n, eps, rng):
+    """f = g ~ eps log(n)/2 (+ noise): near pairs carry mass ~ 1/n, so the mask
+    is neither empty nor full."""
+    base = eps * math.log(n) / 2
+    f = (base + rng.normal(0, 0.3 * eps, n)).astype(np.float32)
+    g = (base + rng.normal(0, 0.3 * eps, n)).astype(np.float32)
+    return f, g
+
+
+@pytest.mark.parametrize("n,B,eps", [(65536, 128, 1e-4), (16384, 256, 1e-3), (5000, 128, 1e-3)])
+def test_block_screen_bit_exact(sk, n, B, eps):
+    x, y, a, b = _sorted_problem(5, n)
+    rng = np.random.default_rng(1)
+    f, g = _near_plan_potentials(n, eps, rng)
+    NB = (n + B - 1) // B
+    delta = 1e-3 / NB
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr_r, col_r = oracle.screen(sx, sy, eps, 1.0, delta)
+    ptrT_r, rowT_r = oracle.screen_transpose(sx, sy, eps, 1.0, delta)
+    assert 0 < len(col_r) < NB * NB
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        ptr, idx = P.block_screen(eps, _t(f), _t(g), B, delta)
+        ptrT, idxT = P.block_screen(eps, _t(f), _t(g), B, delta, transpose=True)
+    assert np.array_equal(ptr.cpu().numpy(), ptr_r) and np.array_equal(idx.cpu().numpy(), col_r)
+    assert np.array_equal(ptrT.cpu().numpy(), ptrT_r) and np.array_equal(idxT.cpu().numpy(), rowT_r)
+
+
+def test_block_screen_full_size_sampled_row_blocks(sk):
+    """2^24 points, B = 128: every row block screened on the GPU against all
+    131072 column blocks; 24 sampled row blocks recomputed by the oracle."""
+    c = synth.make(5)
+    cx, px, cy, py = _gpu_morton(sk, c.x, c.y)
+    x, y, a, b = c.x[px], c.y[py], c.a[px], c.b[py]
+    eps = 1e-4
+    rng = np.random.default_rng(2)
+    f, g = _near_plan_potentials(c.n, eps, rng)
+    B = 128
+    NB = c.n // B
+    delta = 1e-3 / NB
+    _log("screen full size")
+    with sk.Problem(_t(x), _t(y), None, None, 1.0) as P:
+        ptr, idx = P.block_screen(eps, _t(f), _t(g), B, delta)
+    ptr = ptr.cpu().numpy()
+    idx = idx.cpu().numpy()
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    rows = np.sort(rng.choice(NB, 24, replace=False))
+    ptr_r, col_r = oracle.screen(sx, sy, eps, 1.0, delta, row_blocks=rows)
+    for k, I in enumerate(rows):
+        assert np.array_equal(idx[ptr[I]:ptr[I + 1]], col_r[ptr_r[k]:ptr_r[k + 1]]), I
+
+
+@pytest.mark.parametrize("n,B,eps", [(16384, 128, 1e-4), (16384, 256, 1e-3), (5000, 128, 1e-3)])
+def test_sparse_halfsteps_match_oracle(sk, n, B, eps):
+    x, y, a, b = _sorted_problem(5, n)
+    rng = np.random.default_rng(3)
+    f, g = _near_plan_potentials(n, eps, rng)
+    NB = (n + B - 1) // B
+    delta = 1e-3 / NB
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    ptrT, rowT = oracle.screen_transpose(sx, sy, eps, 1.0, delta)
+    # force one empty row block so the dense fallback is exercised
+    ptr = ptr.copy()
+    col = np.delete(col, np.s_[ptr[1]:ptr[2]])
+    ptr[2:] -= ptr[2] - ptr[1]
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        fo, r = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)), f_prev=_t(f))
+        go, rc = P.sparse_halfstep_g(eps, _t(f), B, _t(ptrT), _t(rowT.astype(np.int32)), g_prev=_t(g))
+    f_ref = oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B)
+    g_ref = oracle.sparse_halfstep_g(x, y, a, f, eps, 1.0, ptrT, rowT, B)
+    for got, ref, what in ((fo, f_ref, "f"), (go, g_ref, "g")):
+        got = got.cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref) / np.maximum(eps, np.abs(ref))
+        assert err.max() <= 1e-5, (what, err.max())
+    Rr, Rc = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
+    assert r == pytest.approx(Rr, rel=1e-3) and rc == pytest.approx(Rc, rel=1e-3)
+
+
+def test_multiscale_solve_is_certified_like_the_oracle(sk):
+    path = os.path.join(GOLDEN, "fs2_w5_n16384_fs2.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_solve_refs.py w5_n16384_fs2")
+    ref = dict(np.load(path))
+    n = int(ref["n"])
+    c = synth.make(5, n=n, m=n)
+    eps = float(ref["eps"])
+    prm = sk.MultiscaleParams(B=int(ref["B"]), eps=eps, tol=float(ref["tol"]))
+    _log("multiscale solve n=16384")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+    assert rep["status"] == sk.OK and rep["certified"] == 1
+    assert rep["ncells_x"] == int(ref["ncells_x"]) and rep["ncells_y"] == int(ref["ncells_y"])
+    assert abs(rep["coarse_iters"] - int(ref["coarse_iters"])) <= 2, (rep["coarse_iters"], int(ref["coarse_iters"]))
+    assert abs(rep["fine_updates"] - int(ref["fine_updates"])) <= 1, (rep["fine_updates"], int(ref["fine_updates"]))
+    # the certificate holds: the oracle's exact residual of the returned potentials
+    Fr, Fc = oracle.marginal_residuals(c.x, c.y, c.a, c.b, f.cpu().numpy(), g.cpu().numpy(), eps, 1.0)
+    assert max(Fr, Fc) <= max(rep["R_A_row"], rep["R_A_col"]) + rep["omega"] + 1e-6
+    assert max(Fr, Fc) <= prm.tol
