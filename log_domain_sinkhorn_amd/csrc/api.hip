@@ -79,7 +79,7 @@ void problem_free(sinkhorn_problem* p) {
   dev_free(p->Mpart);
   dev_free(p->Spart);
   dev_free(p->red_part);
-  dev_free(p->cnt);
+  dev_free(p->tile_flag);
   dev_free(p->ctl);
   host_free(p->host_ctl);
   host_free(p->host_tmp);
@@ -104,6 +104,7 @@ void halfstep(sinkhorn_problem* p, bool fside, double eps, const float* other, f
   prep_column_term(p, cols, other, eps, cols.H);
   reset_nonfinite(p);
   HalfStep hs{&rows, &cols, cols.H, out, prev, nullptr, eps, eps, prev != nullptr && l1 != nullptr};
+  hs.shift_pot = prev;  // the previous potential estimates the row shifts
   dense_halfstep(p, hs);
   if (l1) {
     double v = 0.0;
@@ -144,12 +145,14 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
   // one full iteration from state `cur`; eps_next is the eps of the f-step that follows
   auto iterate = [&](double eps, double eps_next, bool residual) {
     HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], X.H, eps, eps, residual};
+    fs.shift_pot = F[cur];
     dense_halfstep(p, fs);
     if (residual) {
       copy_ctl(p);
       SK_HIP(hipEventRecord(p->ev, st));
     }
     HalfStep gs{&Y, &X, X.H, G[1 - cur], G[cur], Y.H, eps, eps_next, false};
+    gs.shift_pot = G[cur];
     dense_halfstep(p, gs);
     o.halfsteps += 2;
     cur = 1 - cur;
@@ -321,8 +324,8 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->red_cap = std::max(row_groups(n), row_groups(m)) + 16;
       p->red_part = (double*)dev_alloc(sizeof(double) * p->red_cap);
-      p->cnt = (uint32_t*)dev_alloc(sizeof(uint32_t) * (p->red_cap + 1));
-      zero_i32((int32_t*)p->cnt, (int32_t)(p->red_cap + 1), p->stream);
+      p->tile_flag = (int32_t*)dev_alloc(sizeof(int32_t) * p->red_cap);
+      zero_i32(p->tile_flag, (int32_t)p->red_cap, p->stream);
       reset_nonfinite(p);
       for (int k = 0; k < 2; ++k) {
         p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);

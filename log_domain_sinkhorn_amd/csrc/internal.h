@@ -79,6 +79,9 @@ struct HalfStep {
   double eps;              // eps of this half-step
   double eps_next;         // eps used for H_next
   bool residual;
+  // previous potential of the row side: enables the shifted pair loop (its
+  // fixed per-row shift is estimated from it); null runs the exact loop
+  const float* shift_pot = nullptr;
 };
 
 }  // namespace sk
@@ -97,7 +100,7 @@ struct sinkhorn_problem {
   // residual block partials, arrival counters and the reduced values
   double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
-  uint32_t* cnt = nullptr;      // [red_cap + 1] arrival counters, zero between launches
+  int32_t* tile_flag = nullptr; // [red_cap] tiles marked for the exact recompute, zero between launches
   sk::Ctl* ctl = nullptr;       // device control block
   sk::Ctl* host_ctl = nullptr;  // pinned mirror
   double* host_tmp = nullptr;   // [8] pinned scratch

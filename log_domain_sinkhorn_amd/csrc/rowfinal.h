@@ -30,9 +30,9 @@ struct RowFinal {
 
 // potential_i = -eps ln2 (mx + log2 sum) [+ s ||p_i||^2]; returns the residual
 // term w_i |exp((prev_i - potential_i)/eps) - 1| (0 without prev).
-__device__ __forceinline__ double finalize_row(const RowFinal& F, int64_t i, float mx, double sum,
+__device__ __forceinline__ double finalize_row(const RowFinal& F, int64_t i, double mx, double sum,
                                                int* bad) {
-  double v = F.neg_eps_ln2 * ((double)mx + log2(sum));  // sum == 0 -> +inf
+  double v = F.neg_eps_ln2 * (mx + log2(sum));  // sum == 0 -> +inf
   if (F.norm2) v += F.row_scale * (double)F.norm2[i];
   const float v32 = (float)v;
   F.out[i] = v32;
