@@ -160,7 +160,7 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     certified = False
     R_row = R_col = math.nan
     updates = 0
-    while updates < prm.max_fine:
+    while True:
         f32 = f.astype(np.float32)
         g32 = g.astype(np.float32)
         sx = block_summaries(X, A, f32, B)
@@ -171,6 +171,8 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
         R_row, R_col = sparse_residuals(X, Y, A, Bw, f, g, prm.eps, prm.scale, ptr, col, ptrT, rowT, B)
         if max(R_row, R_col) + omega <= prm.tol:
             certified = True
+            break
+        if updates >= prm.max_fine:  # R_row, R_col belong to the returned state
             break
         f = sparse_halfstep_f(X, Y, Bw, g, prm.eps, prm.scale, ptr, col, B)
         g = sparse_halfstep_g(X, Y, A, f, prm.eps, prm.scale, ptrT, rowT, B)

@@ -56,8 +56,12 @@ def main(names):
 
 
 # multiscale (block-sparse) solve cases: name -> (workload, n, FS2Params kwargs)
+# "fixed": the coarse stage runs all its iterations (no tolerance, no stall)
+# and the fine loop runs exactly max_fine updates (tol is unreachable), so
+# both sides take the same number of steps.
 FS2_CASES = {
-    "w5_n16384_fs2": (5, 16384, dict(B=128, eps=1e-4, tol=1e-2)),
+    "w5_n16384_fixed": (5, 16384, dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0, coarse_max=40,
+                                       stall_window=1 << 30, max_fine=4)),
 }
 
 
