@@ -15,7 +15,9 @@ Prints ONE JSON line:
   value      = point pairs evaluated by all half-steps / wall time (pair-evals/s)
   roofline   = the pair-loop kernel against the VALU issue rate of the chip,
                timed with HIP events around each launch on the library's stream
-  cpu_baseline = the fp64 oracle's half-step on a bounded row sample
+               in a second run of the same K solves (the events cost a few
+               microseconds per launch, so the first, headline run has none)
+  cpu_baseline = the fp64 oracle's half-step on the host cores (bounded sample)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -49,13 +51,37 @@ WORKLOADS = {
 
 
 def ops_per_pair(d: int) -> int:
-    """Algorithmic vector-ALU operations per pair of the difference-form
-    half-step: d subs, 1 mul + (d-1) fma for the squared distance, 1 fma for
-    the exponent, 1 max, 1 sub, 1 exp2, 1 add."""
-    return 2 * d + 5
+    """Vector-ALU instructions per pair that the difference-form half-step
+    needs with a fixed per-row shift: d subs and d fmas for the shifted squared
+    distance (the shift folded into the first fma), 1 fma for the exponent and
+    1 add into the sum. The exp2 of each pair issues on the transcendental unit
+    alongside and is not counted against the VALU issue rate."""
+    return 2 * d + 2
+
+
+def pmc_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "k_lse_valu_w2_n20000_d3_pmc.md")
+    src = os.path.join(ROOT, "log_domain_sinkhorn_amd", "csrc", "dense.hip")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+dense_hip_sha256:\s*([0-9a-f]+)\s+kernel:\s*(\S+)", text)
+    if not m or m.group(2) != digest or m.group(3) != kernel:
+        return None
+    return float(m.group(1))
 
 
 def cpu_baseline(c, eps, budget_s=12.0):
+    """The fp64 oracle's f-half-step, timed on the host cores: whole half-steps
+    repeated until the budget is spent, or a leading row block of one when a
+    whole half-step would take longer."""
     import numpy as np
 
     threads = min(16, os.cpu_count() or 1)
@@ -68,18 +94,38 @@ def cpu_baseline(c, eps, budget_s=12.0):
     oracle.halfstep_f(c.x, c.y, c.b, g, eps, 1.0, rows=rows)
     dt = max(time.perf_counter() - t, 1e-3)
     k = int(min(c.n, max(64, len(rows) * budget_s / dt)))
-    rows = np.arange(k)
+    rows = None if k == c.n else np.arange(k)
+    reps = 0
     t = time.perf_counter()
-    oracle.halfstep_f(c.x, c.y, c.b, g, eps, 1.0, rows=rows)
-    dt = time.perf_counter() - t
+    while True:
+        oracle.halfstep_f(c.x, c.y, c.b, g, eps, 1.0, rows=rows)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= budget_s or rows is not None:
+            break
+    what = f"{reps} whole" if rows is None else f"the first {k} of {c.n} rows of one"
     return {
-        "value": k * c.m / dt,
+        "value": reps * k * c.m / dt,
         "unit": "pair-evals/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"one fp64 f-half-step over the first {k} of {c.n} rows x all {c.m} columns "
-                  f"({dt:.1f} s), explicit cost matrix in row chunks",
+        "sample": f"{what} fp64 f-half-step(s), {c.n} x {c.m} pairs each, explicit cost matrix "
+                  f"in row chunks over {threads} threads ({dt:.1f} s)",
     }
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain device copy of `mib` MiB (reads and writes that many bytes per
+    launch) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": reps}), flush=True)
 
 
 def main():
@@ -89,10 +135,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="no HIP events around the pair-kernel launches (no roofline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              "(sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -116,8 +169,8 @@ def main():
         P.solve(sched, f, g)
     torch.cuda.synchronize()
 
+    # timed region: K solves, nothing else on the stream
     reps = []
-    P.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -127,14 +180,27 @@ def main():
         reps.append(rep)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms, launches, kpairs = P.profile_read()
-    P.profile_enable(False)
     elapsed = t1 - t0
+
+    # second timed region for the roofline: the same K solves with a HIP event
+    # pair around every pair-kernel launch on the library's stream (the events
+    # add a few microseconds per launch, so they stay out of the first region)
+    kernel_ms, launches, kpairs = 0.0, 0, 0.0
+    if not args.no_kernel_timing:
+        P.profile_enable(True)
+        for _ in range(args.steps):
+            f.zero_()
+            g.zero_()
+            P.solve(sched, f, g)
+        kernel_ms, launches, kpairs = P.profile_read()
+        P.profile_enable(False)
+    timed = launches > 0 and kernel_ms > 0
 
     pairs = sum(r["pairs_evaluated"] for r in reps)
     value = pairs / elapsed
     ops = ops_per_pair(c.d)
-    achieved = kpairs * ops / (kernel_ms * 1e-3)
+    achieved = kpairs * ops / (kernel_ms * 1e-3) if timed else None
+    kname = f"k_lse_valu<{c.d},true>"
     out = {
         "metric": "pair-evals/s per Sinkhorn half-step (n*m/t) + wall-time to L1 residual 1e-3",
         "value": value,
@@ -160,23 +226,25 @@ def main():
         "iters_per_solve": reps[-1]["iters"],
         "final_row_l1": reps[-1]["row_l1"],
         "final_col_l1": reps[-1]["col_l1"],
-        "pair_kernel": {
+    }
+    if timed:
+        out["pair_kernel"] = {
             "launches": launches,
-            "avg_ms": kernel_ms / max(1, launches),
-            "pairs_per_launch": kpairs / max(1, launches),
+            "avg_ms": kernel_ms / launches,
+            "pairs_per_launch": kpairs / launches,
             "pair_evals_per_s": kpairs / (kernel_ms * 1e-3),
-        },
-        "roofline": {
+        }
+        out["roofline"] = {
             "bound": "alu",
             "achieved": achieved / 1e12,
             "peak": VALU_PEAK_OPS / 1e12,
             "unit": "Tops/s",
             "frac": achieved / VALU_PEAK_OPS,
-            "traffic": None,
+            "traffic": pmc_traffic(kname) if args.workload == 2 else None,
             "ops_per_pair": ops,
-            "kernel": f"k_lse_valu<{c.d},2>",
-        },
-    }
+            "pair_peak": VALU_PEAK_OPS / ops,
+            "kernel": kname,
+        }
     P.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, float(W["sched"]["eps_target"]))

@@ -79,7 +79,6 @@ void problem_free(sinkhorn_problem* p) {
   dev_free(p->Mpart);
   dev_free(p->Spart);
   dev_free(p->red_part);
-  dev_free(p->tile_flag);
   dev_free(p->ctl);
   host_free(p->host_ctl);
   host_free(p->host_tmp);
@@ -147,10 +146,7 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
     HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], X.H, eps, eps, residual};
     fs.shift_pot = F[cur];
     dense_halfstep(p, fs);
-    if (residual) {
-      copy_ctl(p);
-      SK_HIP(hipEventRecord(p->ev, st));
-    }
+    if (residual) SK_HIP(hipEventRecord(p->ev, st));  // the reduction wrote host_ctl
     HalfStep gs{&Y, &X, X.H, G[1 - cur], G[cur], Y.H, eps, eps_next, false};
     gs.shift_pot = G[cur];
     dense_halfstep(p, gs);
@@ -309,7 +305,14 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       p->scale = cost_scale;
       p->stream = (hipStream_t)stream;
       p->ctl = (Ctl*)dev_alloc(sizeof(Ctl));
-      p->host_ctl = (Ctl*)host_alloc(sizeof(Ctl));
+      p->host_ctl = (Ctl*)host_alloc_coherent(sizeof(Ctl));
+      SK_HIP(hipHostGetDevicePointer((void**)&p->host_ctl_dev, p->host_ctl, 0));
+      {
+        int dev = 0;
+        SK_HIP(hipGetDevice(&dev));
+        SK_HIP(hipDeviceGetAttribute(&p->num_cu, hipDeviceAttributeMultiprocessorCount, dev));
+        if (p->num_cu < 1) p->num_cu = 1;
+      }
       p->host_tmp = (double*)host_alloc(sizeof(double) * 8);
       side_init(p, p->X, x, a, n);
       side_init(p, p->Y, y, b, m);
@@ -324,8 +327,6 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->red_cap = std::max(row_groups(n), row_groups(m)) + 16;
       p->red_part = (double*)dev_alloc(sizeof(double) * p->red_cap);
-      p->tile_flag = (int32_t*)dev_alloc(sizeof(int32_t) * p->red_cap);
-      zero_i32(p->tile_flag, (int32_t)p->red_cap, p->stream);
       reset_nonfinite(p);
       for (int k = 0; k < 2; ++k) {
         p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);

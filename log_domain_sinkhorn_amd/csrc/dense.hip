@@ -7,12 +7,14 @@
 //   * a lane owns R = 2 rows (row side SoA, coalesced loads); the column tile
 //     (coordinates and column term of kChunk points) is wave-uniform and
 //     arrives through scalar loads, so the pair loop has no vector loads;
-//   * a workgroup holds W = 8 waves on the SAME 128-row tile, each wave a
-//     contiguous slice of the workgroup's columns; the W partials are merged
+//   * a workgroup holds W = 8 waves on the SAME 128-row tile, the waves taking
+//     the chunks of its column range in turn; their partials are merged
 //     through LDS in wave order;
-//   * when the rows alone give too few workgroups, G workgroups per tile split
-//     the columns further and a merge kernel (one workgroup per tile) combines
-//     their partials in split order; otherwise the workgroup finalizes in place.
+//   * G workgroups per tile split the columns (G a multiple of 8 when the
+//     columns outgrow an XCD's L2: workgroups are dealt to the 8 XCDs in turn,
+//     so each XCD then streams only its own splits), and a merge kernel (one
+//     workgroup per tile) combines their partials in split order and
+//     finalizes.
 //
 // Two pair loops, the same sum:
 //   exact   z = h_j - kappa q_ij; per 16-column chunk the running max M is
@@ -58,18 +60,18 @@ struct LseArgs {
   int64_t qstride;
   const float* H;       // column term of the column side, log2 units, -inf padding
   float nkappa;         // -s log2(e) / eps
-  int32_t G;            // workgroups per tile (global column splits)
   int64_t nchunks;      // column chunks of kChunk points
-  int64_t cps;          // chunks per global split
-  double* Mp;           // [G][np] partial shift / max (G > 1)
-  float* Sp;            // [G][np] partial sum (G > 1)
+  int64_t tiles;        // row tiles of kRowsPerTile rows
+  int32_t G;            // column splits: workgroup w works on tile w / G, split w % G
+  int64_t cps;          // chunks per split
+  double* Mp;           // [G][np] partial shift / max
+  float* Sp;            // [G][np] partial sum
   const float* shift_pot;  // shifted mode: previous potential of the row side
   float lam;               // log2(e) / eps
   float inv_kappa;         // 1 / kappa
-  int32_t* tile_flag;      // [tiles] tiles to recompute exactly
-  int32_t fallback;        // 1: exact recompute of the flagged tiles only (G = 1)
   RowFinal F;
 };
+
 
 // Keeps a wave-uniform value in a VGPR (a lane shuffle is divergent to the
 // compiler), so that a VOP3 with an SGPR operand (the scalar-loaded column
@@ -77,51 +79,27 @@ struct LseArgs {
 // scalar loads of the column tile provably unclobbered.
 __device__ __forceinline__ float in_vgpr(float s) { return __shfl(s, (int)(threadIdx.x & 63), 64); }
 
+// One wave's pass over column chunks c0, c0 + step, ... < c1 for the lane's
+// kR rows x.
+// Exact mode starts from an empty sum and returns the running max in Md;
+// shifted mode starts from the shifts (u, Md) the caller set and may raise
+// them chunk by chunk.
 template <int D, bool SHIFT>
-__global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
-  const bool fb = A.fallback != 0;
-  const int32_t G = fb ? 1 : A.G;
-  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)G);
-  const int64_t tile = blockIdx.x / (uint32_t)G;
-  if (fb && A.tile_flag[tile] == 0) return;  // uniform
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int lane = threadIdx.x & 63;
-  const int64_t row0 = tile * kRowsPerTile + lane;
+__device__ __forceinline__ void pair_pass(const LseArgs& A, const float* __restrict__ Q,
+                                          const float* __restrict__ H, const float (&x)[kR][D],
+                                          int64_t c0, int64_t c1, int64_t step, float (&u)[kR],
+                                          double (&Md)[kR], float (&S)[kR]) {
   const float nk = A.nkappa;
   const float nkv = in_vgpr(nk);
   const double kd = -(double)nk;
-
-  float x[kR][D];
-  float S[kR];
-  float Mf[kR];   // exact mode: running max
-  float u[kR];    // shifted mode: shift / kappa
-  double Md[kR];  // shifted mode: shift = kappa * u
+  float Mf[kR];
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-#pragma unroll
-    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
     S[r] = 0.0f;
     Mf[r] = -FLT_MAX;
-    if (SHIFT) {
-      const int64_t i = row0 + 64 * r;
-      const float p = i < A.F.np ? A.shift_pot[i] : 0.0f;
-      const float c = -p * A.lam - kHeadroom;
-      u[r] = c * A.inv_kappa;
-      Md[r] = kd * (double)u[r];
-    }
   }
-  const float* __restrict__ Q = A.Q;
-  const float* __restrict__ H = A.H;
   const int64_t qs = A.qstride;
-
-  // this wave's slice of this workgroup's column range
-  const int64_t cps = fb ? A.nchunks : A.cps;
-  const int64_t g0 = (int64_t)gs * cps;
-  const int64_t g1 = g0 + cps < A.nchunks ? g0 + cps : A.nchunks;
-  const int64_t per = (g1 - g0 + kW - 1) / kW;
-  const int64_t c0 = g0 + wave * per;
-  const int64_t c1 = c0 + per < g1 ? c0 + per : g1;
-  for (int64_t c = c0; c < c1; ++c) {
+  for (int64_t c = c0; c < c1; c += step) {
     const int64_t j0 = c * kChunk;
     float yv[D][kChunk];
     float hv[kChunk];
@@ -199,101 +177,164 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A) {
 #pragma unroll
     for (int r = 0; r < kR; ++r) Md[r] = (double)Mf[r];
   }
+}
 
-  // ---- merge the W waves through LDS (wave order)
-  __shared__ double sM[kW][kRowsPerTile];
-  __shared__ float sS[kW][kRowsPerTile];
-  __shared__ double sRed[kThreads];
+struct TileLds {
+  double M[kW][kRowsPerTile];
+  float S[kW][kRowsPerTile];
+  double red[kThreads];
+};
+
+// Merge of the W waves' (max, sum) through LDS in wave order; thread t < 128
+// gets row t of the tile.
+__device__ __forceinline__ void merge_waves(TileLds& L, int wave, int lane, const double (&Md)[kR],
+                                            const float (&S)[kR], double& mx, double& sum) {
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-    sM[wave][lane + 64 * r] = Md[r];
-    sS[wave][lane + 64 * r] = S[r];
+    L.M[wave][lane + 64 * r] = Md[r];
+    L.S[wave][lane + 64 * r] = S[r];
+  }
+  __syncthreads();
+  mx = -DBL_MAX;
+  sum = 0.0;
+  const int t = threadIdx.x;
+  if (t < kRowsPerTile) {
+#pragma unroll
+    for (int v = 0; v < kW; ++v) mx = fmax(mx, L.M[v][t]);
+#pragma unroll
+    for (int v = 0; v < kW; ++v) sum += (double)L.S[v][t] * (double)ex2((float)(L.M[v][t] - mx));
+  }
+}
+
+// Exact recompute of a whole tile (all columns) by the kW waves of the
+// workgroup: the fallback of shifted mode when a row's shift was too high.
+template <int D>
+__device__ void exact_tile(const LseArgs& A, TileLds& L, int64_t tile, double& mx,
+                           double& sum) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = tile * kRowsPerTile + lane;
+  float x[kR][D];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
+  float u[kR], S[kR];
+  double Md[kR];
+  pair_pass<D, false>(A, A.Q, A.H, x, wave, A.nchunks, kW, u, Md, S);
+  __syncthreads();  // LDS reuse
+  merge_waves(L, wave, lane, Md, S, mx, sum);
+}
+
+// Writes the potentials of a tile's rows (threads t < 128) and its residual
+// partial (fixed-order tree over the workgroup).
+__device__ __forceinline__ void finish_tile(const LseArgs& A, TileLds& L, int64_t tile, double mx,
+                                            double sum) {
+  const int t = threadIdx.x;
+  const int64_t i = tile * kRowsPerTile + t;
+  const bool own = t < kRowsPerTile && i < A.F.np;
+  double term = 0.0;
+  int bad = 0;
+  if (own) term = finalize_row(A.F, i, mx, sum, &bad);
+  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
+  if (A.F.prev) {
+    L.red[t] = term;
+    __syncthreads();
+#pragma unroll
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+      if (t < w) L.red[t] += L.red[t + w];
+      __syncthreads();
+    }
+    if (t == 0) A.F.red_part[tile] = L.red[0];
+  }
+}
+
+// True (workgroup-uniform) when some row of the tile has a sum below kTiny:
+// its shift was too high and terms may have underflowed.
+__device__ __forceinline__ bool needs_exact(const LseArgs& A, int64_t tile, double sum) {
+  const int64_t i = tile * kRowsPerTile + threadIdx.x;
+  const bool own = threadIdx.x < kRowsPerTile && i < A.F.np;
+  return __syncthreads_or(own && !(sum >= kTiny));
+}
+
+// Q, H, Mp and Sp come as separate no-alias arguments, so the column data
+// provably stays unclobbered by the partial stores and arrives through scalar
+// loads.
+template <int D, bool SHIFT>
+__global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A, const float* __restrict__ Q,
+                                                      const float* __restrict__ H,
+                                                      double* __restrict__ Mp,
+                                                      float* __restrict__ Sp) {
+  __shared__ TileLds L;
+  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)A.G);
+  const int64_t tile = blockIdx.x / (uint32_t)A.G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = tile * kRowsPerTile + lane;
+  float x[kR][D];
+  float u[kR], S[kR];
+  double Md[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
+    if (SHIFT) {
+      const int64_t i = row0 + 64 * r;
+      const float p = i < A.F.np ? A.shift_pot[i] : 0.0f;
+      const float c = -p * A.lam - kHeadroom;
+      u[r] = c * A.inv_kappa;
+      Md[r] = -(double)A.nkappa * (double)u[r];
+    }
+  }
+  const int64_t g0 = (int64_t)gs * A.cps;
+  const int64_t g1 = g0 + A.cps < A.nchunks ? g0 + A.cps : A.nchunks;
+  pair_pass<D, SHIFT>(A, Q, H, x, g0 + wave, g1, kW, u, Md, S);
+  double mx, sum;
+  merge_waves(L, wave, lane, Md, S, mx, sum);
+  const int64_t i = tile * kRowsPerTile + threadIdx.x;
+  if (threadIdx.x < kRowsPerTile && i < A.F.np) {
+    Mp[(int64_t)gs * A.F.np + i] = mx;
+    Sp[(int64_t)gs * A.F.np + i] = (float)sum;
+  }
+}
+
+// Merge of the G splits of each row of a 128-row tile, then finalize: wave w
+// combines splits w, w + 8, ... of the lane's rows (fp64), and the 8 wave
+// results are combined through LDS in wave order. In shifted mode a tile with
+// a too-small row sum is recomputed exactly by the whole workgroup first.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_merge(LseArgs A, int32_t shifted) {
+  __shared__ TileLds L;
+  __shared__ double sS[kW][kRowsPerTile];
+  const int64_t tile = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t np = A.F.np;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int64_t i = tile * kRowsPerTile + lane + 64 * r;
+    double m = -DBL_MAX, acc = 0.0;
+    if (i < np) {
+      for (int32_t t = wave; t < A.G; t += kW) m = fmax(m, A.Mp[(int64_t)t * np + i]);
+      for (int32_t t = wave; t < A.G; t += kW) {
+        const int64_t o = (int64_t)t * np + i;
+        acc += (double)A.Sp[o] * (double)ex2((float)(A.Mp[o] - m));
+      }
+    }
+    L.M[wave][lane + 64 * r] = m;
+    sS[wave][lane + 64 * r] = acc;
   }
   __syncthreads();
   double mx = -DBL_MAX, sum = 0.0;
   const int t = threadIdx.x;
-  const int64_t i = tile * kRowsPerTile + t;
-  const bool own = t < kRowsPerTile && i < A.F.np;
   if (t < kRowsPerTile) {
 #pragma unroll
-    for (int v = 0; v < kW; ++v) mx = fmax(mx, sM[v][t]);
+    for (int v = 0; v < kW; ++v) mx = fmax(mx, L.M[v][t]);
 #pragma unroll
-    for (int v = 0; v < kW; ++v) sum += (double)sS[v][t] * (double)ex2((float)(sM[v][t] - mx));
+    for (int v = 0; v < kW; ++v) sum += sS[v][t] * (double)ex2((float)(L.M[v][t] - mx));
   }
-  if (A.G > 1 && !fb) {
-    if (own) {
-      A.Mp[(int64_t)gs * A.F.np + i] = mx;
-      A.Sp[(int64_t)gs * A.F.np + i] = (float)sum;
-    }
-    return;
-  }
-  if (SHIFT) {
-    const bool redo = __syncthreads_or(own && !(sum >= kTiny));
-    if (redo) {
-      if (threadIdx.x == 0) {
-        A.tile_flag[tile] = 1;
-        if (A.F.prev) A.F.red_part[tile] = 0.0;
-      }
-      return;
-    }
-  }
-  double term = 0.0;
-  int bad = 0;
-  if (own) term = finalize_row(A.F, i, mx, sum, &bad);
-  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
-  if (fb && threadIdx.x == 0) A.tile_flag[tile] = 0;
-  if (A.F.prev) {
-    sRed[threadIdx.x] = term;
-    __syncthreads();
-#pragma unroll
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) A.F.red_part[tile] = sRed[0];
-  }
-}
-
-// Merge of the G global splits of each row of a 128-row tile (split order),
-// then finalize; in shifted mode a tile with a too-small row sum is flagged
-// for the exact recompute instead.
-__global__ __launch_bounds__(kRowsPerTile) void k_merge(LseArgs A, int32_t shifted) {
-  __shared__ double sRed[kRowsPerTile];
-  const int64_t tile = blockIdx.x;
-  const int64_t i = tile * kRowsPerTile + threadIdx.x;
-  const bool own = i < A.F.np;
-  double mx = -DBL_MAX, sum = 0.0;
-  if (own) {
-    for (int32_t t = 0; t < A.G; ++t) mx = fmax(mx, A.Mp[(int64_t)t * A.F.np + i]);
-    for (int32_t t = 0; t < A.G; ++t) {
-      const int64_t o = (int64_t)t * A.F.np + i;
-      sum += (double)A.Sp[o] * (double)ex2((float)(A.Mp[o] - mx));
-    }
-  }
-  if (shifted) {
-    const bool redo = __syncthreads_or(own && !(sum >= kTiny));
-    if (redo) {
-      if (threadIdx.x == 0) {
-        A.tile_flag[tile] = 1;
-        if (A.F.prev) A.F.red_part[tile] = 0.0;
-      }
-      return;
-    }
-  }
-  double term = 0.0;
-  int bad = 0;
-  if (own) term = finalize_row(A.F, i, mx, sum, &bad);
-  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
-  if (A.F.prev) {
-    sRed[threadIdx.x] = term;
-    __syncthreads();
-#pragma unroll
-    for (int w = kRowsPerTile / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) A.F.red_part[tile] = sRed[0];
-  }
+  if (shifted && needs_exact(A, tile, sum)) exact_tile<D>(A, L, tile, mx, sum);
+  finish_tile(A, L, tile, mx, sum);
 }
 
 // Merge of G split partials for the shared merge entry point (fp32 maxima).
@@ -327,8 +368,10 @@ __global__ __launch_bounds__(256) void k_merge_f32(RowFinal F, int32_t G, const 
 }
 
 // Sum of count doubles in a fixed order into ctl->residual (one block).
+// The result and the non-finite count also go to the host-mapped mirror, so
+// the host reads them after an event without a copy.
 __global__ __launch_bounds__(256) void k_reduce(const double* __restrict__ part, int64_t count,
-                                                Ctl* ctl) {
+                                                Ctl* ctl, Ctl* host) {
   __shared__ double sh[256];
   double acc = 0.0;
   for (int64_t k = threadIdx.x; k < count; k += 256) acc += part[k];
@@ -339,7 +382,11 @@ __global__ __launch_bounds__(256) void k_reduce(const double* __restrict__ part,
     if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) ctl->residual = sh[0];
+  if (threadIdx.x == 0) {
+    ctl->residual = sh[0];
+    __hip_atomic_store(&host->residual, sh[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&host->nonfinite, ctl->nonfinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 // Column term H_j = log2 w_j + pot_j * log2(e) / eps, rounded once to fp32.
@@ -358,54 +405,82 @@ __global__ void k_reset_ctl(Ctl* ctl) {
   }
 }
 
-struct SplitPlan {
-  int32_t G;
-  int64_t cps;
-  int64_t nchunks;
-  int64_t tiles;
-};
+// Workgroups of the pair kernel resident on the whole chip at once.
+template <int D>
+int64_t resident_slots(sinkhorn_problem* p) {
+  static int per_cu[kMaxValuD + 1] = {};
+  if (per_cu[D] == 0) {
+    int nb = 0;
+    SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_valu<D, true>, kThreads, 0));
+    per_cu[D] = nb > 0 ? nb : 1;
+  }
+  return (int64_t)per_cu[D] * p->num_cu;
+}
 
-SplitPlan plan_split(int64_t nrows, int64_t ncols) {
-  SplitPlan sp;
-  sp.nchunks = (ncols + kChunk - 1) / kChunk;
-  sp.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
-  // aim at >= 2048 workgroups (8 per CU, so the last round is short) with at
-  // least 4 chunks per wave
-  int64_t want = (2048 + sp.tiles - 1) / sp.tiles;
-  const int64_t maxsplit = sp.nchunks / (4 * kW) > 1 ? sp.nchunks / (4 * kW) : 1;
-  if (want > 64) want = 64;
-  if (want > maxsplit) want = maxsplit;
-  if (want < 1) want = 1;
-  sp.cps = (sp.nchunks + want - 1) / want;
-  sp.G = (int32_t)((sp.nchunks + sp.cps - 1) / sp.cps);
-  return sp;
+constexpr int64_t kXcds = 8;
+constexpr int64_t kL2Slice = 2 << 20;  // column bytes an XCD's L2 keeps comfortably
+
+// Column splits G per row tile: at least 4 chunks per wave, at most 64. The
+// workgroups run in rounds of `slots` and finish unevenly, so aim at three
+// rounds or more for the load to even out. Workgroups are dealt to the XCDs
+// in turn, so a G that is a multiple of 8 gives each XCD its own column
+// splits: used whenever the column data would not fit an XCD's L2 whole, and
+// preferred whenever G reaches 8 anyway.
+int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int d) {
+  A.nchunks = (ncols + kChunk - 1) / kChunk;
+  A.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
+  int64_t maxsplit = A.nchunks / (4 * kW);
+  if (maxsplit > 64) maxsplit = 64;
+  if (maxsplit < 1) maxsplit = 1;
+  const int64_t want = (3 * slots + A.tiles - 1) / A.tiles;
+  const bool big = A.nchunks * kChunk * (int64_t)(d + 1) * 4 > kL2Slice;
+  int64_t G;
+  if (big || want >= kXcds) {
+    G = (want + kXcds - 1) / kXcds * kXcds;
+    if (G > maxsplit) G = maxsplit / kXcds * kXcds;
+    if (G < kXcds) G = maxsplit < kXcds ? maxsplit : kXcds;
+  } else {
+    G = want < maxsplit ? want : maxsplit;
+  }
+  if (G < 1) G = 1;
+  A.cps = (A.nchunks + G - 1) / G;
+  A.G = (int32_t)((A.nchunks + A.cps - 1) / A.cps);
+  return A.tiles * A.G;
 }
 
 template <int D>
-void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shifted, double pairs,
-                bool timed) {
-  if (timed) prof_begin(p);
+void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shifted, double pairs) {
+  prof_begin(p);
   if (shifted)
-    hipLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream, A);
+    hipLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream, A,
+                       A.Q, A.H, A.Mp, A.Sp);
   else
-    hipLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream, A);
+    hipLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
+                       A, A.Q, A.H, A.Mp, A.Sp);
   SK_LAUNCH_CHECK();
-  if (timed) prof_end(p, pairs);
+  prof_end(p, pairs);
 }
 
 template <int D>
-void run_halfstep(sinkhorn_problem* p, LseArgs& A, const SplitPlan& sp, bool shifted, double pairs) {
-  launch_lse<D>(p, A, sp.tiles * sp.G, shifted, pairs, true);
-  if (sp.G > 1) {
-    hipLaunchKernelGGL(k_merge, dim3((uint32_t)sp.tiles), dim3(kRowsPerTile), 0, p->stream, A,
-                       (int32_t)shifted);
-    SK_LAUNCH_CHECK();
-  }
-  if (shifted) {  // exact recompute of flagged tiles (most workgroups exit at once)
-    LseArgs B = A;
-    B.fallback = 1;
-    launch_lse<D>(p, B, sp.tiles, false, 0.0, false);
-  }
+void run_halfstep(sinkhorn_problem* p, const HalfStep& hs, LseArgs& A, bool shifted, double pairs) {
+  const int64_t blocks = plan_split(A, hs.rows->count, hs.cols->count, resident_slots<D>(p), D);
+  if (blocks >= (int64_t)UINT32_MAX) fail(SINKHORN_ERR_UNSUPPORTED, "too many row tiles");
+  // fp64 maxima: two float slots per partial
+  if (2 * (int64_t)A.G * hs.rows->count > p->part_cap)
+    fail(SINKHORN_ERR_HIP, "partial buffer too small");
+  if (row_groups(hs.rows->count) > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
+  launch_lse<D>(p, A, blocks, shifted, pairs);
+  hipLaunchKernelGGL(k_merge<D>, dim3((uint32_t)A.tiles), dim3(kThreads), 0, p->stream, A,
+                     (int32_t)shifted);
+  SK_LAUNCH_CHECK();
+  if (A.F.prev) launch_reduce(p, A.tiles);
+}
+
+template <int D>
+int64_t split_floats(sinkhorn_problem* p, int64_t nrows, int64_t ncols) {
+  LseArgs A;
+  plan_split(A, nrows, ncols, resident_slots<D>(p), D);
+  return 2 * (int64_t)A.G * nrows;  // fp64 maxima take two slots
 }
 
 }  // namespace
@@ -439,7 +514,8 @@ void launch_merge(sinkhorn_problem* p, const RowFinal& F, int32_t G, const float
 }
 
 void launch_reduce(sinkhorn_problem* p, int64_t count) {
-  hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, count, p->ctl);
+  hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, count, p->ctl,
+                     p->host_ctl_dev);
   SK_LAUNCH_CHECK();
 }
 
@@ -449,12 +525,20 @@ int64_t row_groups(int64_t rows) {
   return tiles > merge_blocks ? tiles : merge_blocks;
 }
 
-int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
+int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols) {
   (void)rows_padded;
-  if (p->d > kMaxValuD) return mfma_partial_floats(nrows, ncols);
-  const SplitPlan sp = plan_split(nrows, ncols);
-  return sp.G > 1 ? 2 * (int64_t)sp.G * nrows : 1;  // fp64 maxima take two slots
+  switch (p->d) {
+    case 1: return split_floats<1>(p, nrows, ncols);
+    case 2: return split_floats<2>(p, nrows, ncols);
+    case 3: return split_floats<3>(p, nrows, ncols);
+    case 4: return split_floats<4>(p, nrows, ncols);
+    case 5: return split_floats<5>(p, nrows, ncols);
+    case 6: return split_floats<6>(p, nrows, ncols);
+    case 7: return split_floats<7>(p, nrows, ncols);
+    case 8: return split_floats<8>(p, nrows, ncols);
+    default: return mfma_partial_floats(nrows, ncols);
+  }
 }
 
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
@@ -476,11 +560,6 @@ void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
   }
   const Side& rows = *hs.rows;
   const Side& cols = *hs.cols;
-  const SplitPlan sp = plan_split(rows.count, cols.count);
-  // fp64 maxima: two float slots per partial
-  if (sp.G > 1 && 2 * (int64_t)sp.G * rows.count > p->part_cap)
-    fail(SINKHORN_ERR_HIP, "partial buffer too small");
-  if (row_groups(rows.count) > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
   const bool shifted = hs.shift_pot != nullptr;
   LseArgs A;
   A.P = rows.soa;
@@ -490,30 +569,24 @@ void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
   A.H = hs.Hcols;
   const double kappa = p->scale * kLog2e / hs.eps;
   A.nkappa = (float)(-kappa);
-  A.G = sp.G;
-  A.nchunks = sp.nchunks;
-  A.cps = sp.cps;
   A.Mp = reinterpret_cast<double*>(p->Mpart);
   A.Sp = p->Spart;
   A.shift_pot = hs.shift_pot;
   A.lam = (float)(kLog2e / hs.eps);
   A.inv_kappa = (float)(1.0 / kappa);
-  A.tile_flag = p->tile_flag;
-  A.fallback = 0;
   A.F = make_rowfinal(p, hs);
   const double pairs = (double)rows.count * (double)cols.count;
   switch (p->d) {
-    case 1: run_halfstep<1>(p, A, sp, shifted, pairs); break;
-    case 2: run_halfstep<2>(p, A, sp, shifted, pairs); break;
-    case 3: run_halfstep<3>(p, A, sp, shifted, pairs); break;
-    case 4: run_halfstep<4>(p, A, sp, shifted, pairs); break;
-    case 5: run_halfstep<5>(p, A, sp, shifted, pairs); break;
-    case 6: run_halfstep<6>(p, A, sp, shifted, pairs); break;
-    case 7: run_halfstep<7>(p, A, sp, shifted, pairs); break;
-    case 8: run_halfstep<8>(p, A, sp, shifted, pairs); break;
+    case 1: run_halfstep<1>(p, hs, A, shifted, pairs); break;
+    case 2: run_halfstep<2>(p, hs, A, shifted, pairs); break;
+    case 3: run_halfstep<3>(p, hs, A, shifted, pairs); break;
+    case 4: run_halfstep<4>(p, hs, A, shifted, pairs); break;
+    case 5: run_halfstep<5>(p, hs, A, shifted, pairs); break;
+    case 6: run_halfstep<6>(p, hs, A, shifted, pairs); break;
+    case 7: run_halfstep<7>(p, hs, A, shifted, pairs); break;
+    case 8: run_halfstep<8>(p, hs, A, shifted, pairs); break;
     default: fail(SINKHORN_ERR_UNSUPPORTED, "VALU half-step supports d <= 8");
   }
-  if (A.F.prev) launch_reduce(p, sp.tiles);
 }
 
 void reset_nonfinite(sinkhorn_problem* p) {

@@ -47,6 +47,7 @@ inline int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
 void* dev_alloc(size_t bytes);
 void dev_free(void* p);
 void* host_alloc(size_t bytes);  // pinned
+void* host_alloc_coherent(size_t bytes);  // pinned, mapped, coherent with device writes
 void host_free(void* p);
 
 // One cloud as stored by a handle.
@@ -100,9 +101,10 @@ struct sinkhorn_problem {
   // residual block partials, arrival counters and the reduced values
   double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
-  int32_t* tile_flag = nullptr; // [red_cap] tiles marked for the exact recompute, zero between launches
   sk::Ctl* ctl = nullptr;       // device control block
-  sk::Ctl* host_ctl = nullptr;  // pinned mirror
+  sk::Ctl* host_ctl = nullptr;  // pinned, host-coherent mirror (the residual kernel writes it)
+  sk::Ctl* host_ctl_dev = nullptr;  // device address of host_ctl
+  int32_t num_cu = 0;           // compute units of the device
   double* host_tmp = nullptr;   // [8] pinned scratch
   // solve scratch: double-buffered potentials
   float* fbuf[2] = {nullptr, nullptr};
@@ -127,7 +129,7 @@ void prof_begin(sinkhorn_problem* p);
 void prof_end(sinkhorn_problem* p, double pairs);
 
 // dense.hip
-int64_t partial_floats_needed(const sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
+int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols);
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
                       float* H);

@@ -170,6 +170,16 @@ void* host_alloc(size_t bytes) {
   return p;
 }
 
+void* host_alloc_coherent(size_t bytes) {
+  void* p = nullptr;
+  const hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    fail(SINKHORN_ERR_OOM, "hipHostMalloc failed");
+  }
+  return p;
+}
+
 void host_free(void* p) {
   if (p) (void)hipHostFree(p);
 }
