@@ -35,6 +35,8 @@ CUS = 256
 CLOCK_HZ = 2.4e9
 VALU_LANES_PER_CU = 64
 VALU_PEAK_OPS = CUS * VALU_LANES_PER_CU * CLOCK_HZ  # 3.93e13 lane-ops/s (no packed fp32)
+MFMA_F32_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
+HBM_PEAK = 8.0e12  # bytes/s
 
 WORKLOADS = {
     1: dict(n=None, m=None, sched=dict(eps_start=0.01, eps_target=0.01, fixed_iters=200),
@@ -43,6 +45,11 @@ WORKLOADS = {
                                        tol=1e-3, max_iters=20000),
             desc="w2: n=m=20000 d=3, 8-component GMM clouds (sigma 0.05), Dirichlet weights, "
                  "eps 1->1e-3 halving x10/stage, then to L1 residual 1e-3"),
+    3: dict(n=None, m=None, sched=dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=20000),
+            scale="mean", materialize=1024,
+            desc="w3: n=50000 m=60000 d=50, 20-cluster anisotropic GMM (PCA-embedding-like), uniform weights, "
+                 "cost / mean cost, eps=0.05 to L1 residual 1e-3, then every plan row materialized in batches "
+                 "of 1024 and min_i max_j T_ij"),
     4: dict(n=None, m=None, sched=dict(eps_start=1.0, eps_target=1e-4, eps_factor=0.5, iters_per_stage=10,
                                        tol=1e-3, max_iters=20000),
             desc="w4: n=m=1e6 d=3, x~U[0,1]^3, y=jittered 100^3 grid, uniform weights, "
@@ -78,7 +85,7 @@ def pmc_traffic(kernel: str):
     return float(m.group(1))
 
 
-def cpu_baseline(c, eps, budget_s=12.0):
+def cpu_baseline(c, eps, scale=1.0, budget_s=12.0):
     """The fp64 oracle's f-half-step, timed on the host cores: whole half-steps
     repeated until the budget is spent, or a leading row block of one when a
     whole half-step would take longer."""
@@ -91,14 +98,14 @@ def cpu_baseline(c, eps, budget_s=12.0):
     g = np.zeros(c.m)
     rows = np.arange(min(c.n, 64))
     t = time.perf_counter()
-    oracle.halfstep_f(c.x, c.y, c.b, g, eps, 1.0, rows=rows)
+    oracle.halfstep_f(c.x, c.y, c.b, g, eps, scale, rows=rows)
     dt = max(time.perf_counter() - t, 1e-3)
     k = int(min(c.n, max(64, len(rows) * budget_s / dt)))
     rows = None if k == c.n else np.arange(k)
     reps = 0
     t = time.perf_counter()
     while True:
-        oracle.halfstep_f(c.x, c.y, c.b, g, eps, 1.0, rows=rows)
+        oracle.halfstep_f(c.x, c.y, c.b, g, eps, scale, rows=rows)
         reps += 1
         dt = time.perf_counter() - t
         if dt >= budget_s or rows is not None:
@@ -158,49 +165,75 @@ def main():
     dev = torch.device("cuda:0")
     x, y = torch.from_numpy(c.x).to(dev), torch.from_numpy(c.y).to(dev)
     a, b = torch.from_numpy(c.a).to(dev), torch.from_numpy(c.b).to(dev)
+    # the cost scale is resolved once, as a number, before anything is timed
+    scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
     sched = sk.Schedule(**W["sched"])
-    P = sk.Problem(x, y, a, b, 1.0)
+    eps = float(W["sched"]["eps_target"])
+    P = sk.Problem(x, y, a, b, scale)
     f = torch.zeros(c.n, dtype=torch.float32, device=dev)
     g = torch.zeros(c.m, dtype=torch.float32, device=dev)
+    batch = W.get("materialize", 0)
+    if batch:
+        T = torch.empty((batch, c.m), dtype=torch.float32, device=dev)
+        rmax = torch.empty(batch, dtype=torch.float32, device=dev)
+        row_ids = torch.arange(c.n, dtype=torch.int64, device=dev)
 
-    for _ in range(args.warmup):
+    def step(timing=False):
         f.zero_()
         g.zero_()
-        P.solve(sched, f, g)
+        P.profile_enable(timing)
+        _, _, rep = P.solve(sched, f, g)
+        kt = P.profile_read() if timing else None
+        P.profile_enable(False)
+        mat = None
+        if batch:
+            # every plan row, batch by batch; min over rows of the row maxima
+            P.profile_enable(timing)
+            lo = torch.full((), float("inf"), device=dev)
+            for r0 in range(0, c.n, batch):
+                k = min(batch, c.n - r0)
+                P.materialize_rows(eps, f, g, row_ids[r0:r0 + k], T=T[:k], row_max=rmax[:k])
+                lo = torch.minimum(lo, rmax[:k].min())
+            mat = (lo, P.profile_read() if timing else None)
+            P.profile_enable(False)
+        return rep, kt, mat
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
 
-    # timed region: K solves, nothing else on the stream
+    # timed region: K steps, nothing else on the stream
     reps = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        f.zero_()
-        g.zero_()
-        _, _, rep = P.solve(sched, f, g)
-        reps.append(rep)
+        reps.append(step())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    # second timed region for the roofline: the same K solves with a HIP event
-    # pair around every pair-kernel launch on the library's stream (the events
-    # add a few microseconds per launch, so they stay out of the first region)
+    # second timed region for the roofline: the same K steps with a HIP event
+    # pair around every pair-kernel (and materializer) launch on the library's
+    # stream; the events add a few microseconds per launch, so they stay out of
+    # the first region
     kernel_ms, launches, kpairs = 0.0, 0, 0.0
+    mat_ms, mat_launches, mat_pairs = 0.0, 0, 0.0
     if not args.no_kernel_timing:
-        P.profile_enable(True)
         for _ in range(args.steps):
-            f.zero_()
-            g.zero_()
-            P.solve(sched, f, g)
-        kernel_ms, launches, kpairs = P.profile_read()
-        P.profile_enable(False)
+            _, kt, mat = step(timing=True)
+            kernel_ms += kt[0]
+            launches += kt[1]
+            kpairs += kt[2]
+            if mat:
+                mat_ms += mat[1][0]
+                mat_launches += mat[1][1]
+                mat_pairs += mat[1][2]
     timed = launches > 0 and kernel_ms > 0
 
-    pairs = sum(r["pairs_evaluated"] for r in reps)
-    value = pairs / elapsed
-    ops = ops_per_pair(c.d)
-    achieved = kpairs * ops / (kernel_ms * 1e-3) if timed else None
-    kname = f"k_lse_valu<{c.d},true>"
+    solve_pairs = sum(r[0]["pairs_evaluated"] for r in reps)
+    mat_entries = (c.n * c.m if batch else 0) * args.steps
+    value = (solve_pairs + mat_entries) / elapsed
+    last = reps[-1][0]
     out = {
         "metric": "pair-evals/s per Sinkhorn half-step (n*m/t) + wall-time to L1 residual 1e-3",
         "value": value,
@@ -219,14 +252,19 @@ def main():
             "n": c.n,
             "m": c.m,
             "d": c.d,
-            "step": "one annealed solve from zero potentials to the stop test",
+            "cost_scale": scale,
+            "step": "one solve from zero potentials to the stop test"
+                    + (", then all plan rows materialized" if batch else ""),
         },
-        "wall_time_to_residual_s": sum(r["seconds"] for r in reps) / len(reps),
-        "halfsteps_per_solve": reps[-1]["halfsteps"],
-        "iters_per_solve": reps[-1]["iters"],
-        "final_row_l1": reps[-1]["row_l1"],
-        "final_col_l1": reps[-1]["col_l1"],
+        "wall_time_to_residual_s": sum(r[0]["seconds"] for r in reps) / len(reps),
+        "halfsteps_per_solve": last["halfsteps"],
+        "iters_per_solve": last["iters"],
+        "final_row_l1": last["row_l1"],
+        "final_col_l1": last["col_l1"],
     }
+    if batch:
+        out["min_row_max"] = float(reps[-1][2][0])
+    mfma = c.d > 8
     if timed:
         out["pair_kernel"] = {
             "launches": launches,
@@ -234,20 +272,47 @@ def main():
             "pairs_per_launch": kpairs / launches,
             "pair_evals_per_s": kpairs / (kernel_ms * 1e-3),
         }
-        out["roofline"] = {
-            "bound": "alu",
-            "achieved": achieved / 1e12,
-            "peak": VALU_PEAK_OPS / 1e12,
-            "unit": "Tops/s",
-            "frac": achieved / VALU_PEAK_OPS,
-            "traffic": pmc_traffic(kname) if args.workload == 2 else None,
-            "ops_per_pair": ops,
-            "pair_peak": VALU_PEAK_OPS / ops,
-            "kernel": kname,
-        }
+        if mfma:
+            kp = (c.d + 1 + 3) // 4 * 4
+            flops = 2.0 * c.d  # the cross term x . y, algorithmic
+            achieved = kpairs * flops / (kernel_ms * 1e-3)
+            out["roofline"] = {
+                "bound": "mfma",
+                "achieved": achieved / 1e12,
+                "peak": MFMA_F32_PEAK / 1e12,
+                "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F32_PEAK,
+                "traffic": None,
+                "flops_per_pair": flops,
+                "kernel": f"k_lse_mfma<{kp}>",
+            }
+        else:
+            kname = f"k_lse_valu<{c.d},true>"
+            ops = ops_per_pair(c.d)
+            achieved = kpairs * ops / (kernel_ms * 1e-3)
+            out["roofline"] = {
+                "bound": "alu",
+                "achieved": achieved / 1e12,
+                "peak": VALU_PEAK_OPS / 1e12,
+                "unit": "Tops/s",
+                "frac": achieved / VALU_PEAK_OPS,
+                "traffic": pmc_traffic(kname) if args.workload == 2 else None,
+                "ops_per_pair": ops,
+                "pair_peak": VALU_PEAK_OPS / ops,
+                "kernel": kname,
+            }
+        if mat_launches:
+            wbytes = mat_pairs * 4.0
+            out["materializer"] = {
+                "launches": mat_launches,
+                "avg_ms": mat_ms / mat_launches,
+                "entries_per_launch": mat_pairs / mat_launches,
+                "write_GBps": wbytes / (mat_ms * 1e-3) / 1e9,
+                "hbm_frac": wbytes / (mat_ms * 1e-3) / HBM_PEAK,
+            }
     P.close()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(c, float(W["sched"]["eps_target"]))
+        out["cpu_baseline"] = cpu_baseline(c, eps, scale)
     print(json.dumps(out), flush=True)
 
 

@@ -32,6 +32,11 @@
  * success with a note, negative = error. No exception or abort crosses the
  * ABI. sinkhorn_last_error() gives a detail string for the calling thread.
  * Index arithmetic is 64-bit throughout (n * m may exceed 2^31).
+ *
+ * Progress: with the environment variable SINKHORN_LOG set (to anything but
+ * "" or "0"), sinkhorn_solve prints a line per annealing stage and at its end,
+ * and sinkhorn_solve_multiscale a line per stage and per fine update, on
+ * stderr.
  */
 #ifndef SINKHORN_H
 #define SINKHORN_H

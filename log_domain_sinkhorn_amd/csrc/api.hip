@@ -2,6 +2,9 @@
 // exact residual and the annealed dense solve driver.
 #include <chrono>
 #include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -17,6 +20,21 @@ thread_local std::string g_last_error;
 void set_last_error(const std::string& msg) { g_last_error = msg; }
 
 void fail(int code, const std::string& msg) { throw Failure{code, msg}; }
+
+void progress(const char* fmt, ...) {
+  static const bool on = [] {
+    const char* e = std::getenv("SINKHORN_LOG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  if (!on) return;
+  va_list ap;
+  va_start(ap, fmt);
+  std::fputs("[sinkhorn] ", stderr);
+  std::vfprintf(stderr, fmt, ap);
+  std::fputc('\n', stderr);
+  std::fflush(stderr);
+  va_end(ap);
+}
 
 void check_hip(hipError_t e, const char* what) {
   if (e != hipSuccess) {
@@ -170,6 +188,8 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
       }
     }
     ++o.stages;
+    progress("solve: stage %d at eps %.4g done (%d iterations, %.3f s)", (int)o.stages, eps,
+             (int)o.iters, seconds_since(t0));
     eps = nxt;
   }
   eps = s.eps_target;
@@ -247,6 +267,8 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
     ++o.halfsteps;
   }
   if (o.seconds == 0.0) o.seconds = seconds_since(t0);
+  progress("solve: %d iterations at eps %.4g, row residual %.4g, column residual %.4g (%.3f s)",
+           (int)o.iters, eps, o.row_l1, o.col_l1, o.seconds);
   copy_f32(F[ret], X.count, f, st);
   copy_f32(G[ret], Y.count, g, st);
   SK_HIP(hipStreamSynchronize(st));

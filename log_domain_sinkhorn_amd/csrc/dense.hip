@@ -420,16 +420,19 @@ int64_t resident_slots(sinkhorn_problem* p) {
 constexpr int64_t kXcds = 8;
 constexpr int64_t kL2Slice = 2 << 20;  // column bytes an XCD's L2 keeps comfortably
 
-// Column splits G per row tile: at least 4 chunks per wave, at most 64. The
-// workgroups run in rounds of `slots` and finish unevenly, so aim at three
-// rounds or more for the load to even out. Workgroups are dealt to the XCDs
-// in turn, so a G that is a multiple of 8 gives each XCD its own column
-// splits: used whenever the column data would not fit an XCD's L2 whole, and
-// preferred whenever G reaches 8 anyway.
+// Column splits G per row tile: at least 4 chunks per wave (1 when the tiles
+// are too few to fill the chip), at most 64. The workgroups run in rounds of
+// `slots` and finish unevenly, so aim at three rounds or more for the load to
+// even out. Workgroups are dealt to the XCDs in turn, so a G that is a
+// multiple of 8 gives each XCD its own column splits: used whenever the
+// column data would not fit an XCD's L2 whole, and preferred whenever G
+// reaches 8 anyway.
 int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int d) {
   A.nchunks = (ncols + kChunk - 1) / kChunk;
   A.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
   int64_t maxsplit = A.nchunks / (4 * kW);
+  // too few tiles to fill the chip even so: down to one chunk per wave
+  if (A.tiles * (maxsplit > 1 ? maxsplit : 1) < slots) maxsplit = A.nchunks / kW;
   if (maxsplit > 64) maxsplit = 64;
   if (maxsplit < 1) maxsplit = 1;
   const int64_t want = (3 * slots + A.tiles - 1) / A.tiles;

@@ -269,6 +269,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     SK_HIP(hipStreamSynchronize(st));
     const double t_sorted = now_s();
     R.seconds_sort = t_sorted - t_start;
+    progress("multiscale: Morton order and cells done: %d x %d cells (%.3f s)", (int)R.ncells_x,
+             (int)R.ncells_y, R.seconds_sort);
 
     // ---- coarse annealed solve on the cells
     auto need = [&](int64_t rows, int64_t cols) {
@@ -302,6 +304,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     R.pairs_evaluated += co.pairs;
     const double t_coarse = now_s();
     R.seconds_coarse = t_coarse - t_sorted;
+    progress("multiscale: coarse solve done: %d iterations (%.3f s)", (int)R.coarse_iters,
+             R.seconds_coarse);
     for (int k = 2; k < 6; ++k) {
       dev_free(pot[k]);
       pot[k] = nullptr;
@@ -328,6 +332,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     }
     const double t_lift = now_s();
     R.seconds_lift = t_lift - t_coarse;
+    progress("multiscale: lift done (%.3f s)", R.seconds_lift);
 
     // ---- fine loop on the block-pair mask
     block_static(p, Xs, P.B, sx);
@@ -369,6 +374,9 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
           break;
         }
       }
+      progress("multiscale: fine update %d: %lld row / %lld column tiles, R_A row %.4g column %.4g "
+               "(%.3f s)", (int)R.fine_updates, (long long)rowL.nnz, (long long)colL.nnz, Rrow, Rcol,
+               now_s() - t_lift);
       if (R.fine_updates >= P.max_fine) break;
       cf = 1 - cf;  // accept the f-step
       prep_column_term(p, Xs, fs[cf], eps, Xs.H);

@@ -21,6 +21,9 @@ struct Failure {
 [[noreturn]] void fail(int code, const std::string& msg);
 void check_hip(hipError_t e, const char* what);
 void set_last_error(const std::string& msg);
+// Progress line on stderr (flushed) when the environment variable
+// SINKHORN_LOG is set to a non-empty value other than "0"; printf format.
+void progress(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
 #define SK_HIP(call) ::sk::check_hip((call), #call)
 #define SK_LAUNCH_CHECK() ::sk::check_hip(hipGetLastError(), "kernel launch")
