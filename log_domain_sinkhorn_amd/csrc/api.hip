@@ -405,8 +405,11 @@ int sinkhorn_marginal_residual(sinkhorn_problem* p, double eps, const float* f, 
   return guard([&] {
     require(p && f && g, "null pointer");
     double r = NAN, c = NAN;
+    const auto t0 = std::chrono::steady_clock::now();
     halfstep(p, true, eps, g, p->fbuf[0], f, &r);
+    progress("marginal residual: row %.6g (%.3f s)", r, seconds_since(t0));
     halfstep(p, false, eps, f, p->gbuf[0], g, &c);
+    progress("marginal residual: column %.6g (%.3f s)", c, seconds_since(t0));
     if (row_l1) *row_l1 = r;
     if (col_l1) *col_l1 = c;
     return SINKHORN_OK;

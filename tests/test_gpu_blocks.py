@@ -197,3 +197,57 @@ def test_multiscale_solve_certificate_holds(sk):
     # fp32 potentials carry 1e-5 max(eps, |f|) / eps relative error into each row's mass
     fl = 1e-5 * max(1.0, float(np.abs(f.cpu().numpy()).max()) / eps)
     assert max(Fr, Fc) <= max(rep["R_A_row"], rep["R_A_col"]) + rep["omega"] + fl, (Fr, Fc, rep)
+
+
+def _dense_check(sk, P, rep, eps, f, g, tol):
+    """The certificate against the exact dense residuals of the returned
+    potentials (every pair, fp64 sums on the GPU; parity-tested against the
+    oracle in test_gpu_dense)."""
+    assert rep["status"] == sk.OK and rep["certified"] == 1
+    R_A = max(rep["R_A_row"], rep["R_A_col"])
+    assert R_A + rep["omega"] <= tol
+    Rr, Rc = P.marginal_residual(eps, f, g)
+    _log(f"  certificate {R_A:.6g} + {rep['omega']:.3g}; dense residuals {Rr:.6g} / {Rc:.6g}")
+    # fp32 potentials: each row's mass carries ~1e-5 max(eps, |f|)/eps relative error
+    fl = 1e-5 * max(1.0, float(f.abs().max()) / eps)
+    assert max(Rr, Rc) <= R_A + rep["omega"] + fl
+
+
+@pytest.mark.parametrize("eps", [1e-3, 1e-4])
+def test_multiscale_certificate_holds_at_2e18(sk, eps):
+    """n = m = 2^18 of the clustered workload: the stop certificate bounds the
+    exact dense residual of the returned potentials."""
+    n = 1 << 18
+    c = synth.make(5, n=n, m=n)
+    prm = sk.MultiscaleParams(B=128, eps=eps, tol=1e-2)
+    _log(f"multiscale n={n} eps={eps}")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+        _log(f"  coarse {rep['coarse_iters']} fine {rep['fine_updates']} in {rep['seconds_total']:.2f} s")
+        _dense_check(sk, P, rep, eps, f, g, prm.tol)
+
+
+@pytest.mark.skipif(os.environ.get("SINKHORN_FULL", "") in ("", "0"),
+                    reason="full-size run (about 5 minutes): set SINKHORN_FULL=1")
+def test_multiscale_full_size_certified_and_rows_match_oracle(sk):
+    """n = m = 2^24, B = 128, eps = 1e-4, tol = 1e-2: certified; the exact
+    dense residuals (2 x 2.8e14 pairs on the GPU) sit under the certificate;
+    8 sampled plan rows (2^24 entries each) match the oracle's fp64 rows."""
+    c = synth.make(5)
+    eps = 1e-4
+    prm = sk.MultiscaleParams(B=128, eps=eps, tol=1e-2)
+    _log("multiscale full size")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+        _log(f"  coarse {rep['coarse_iters']} fine {rep['fine_updates']} in {rep['seconds_total']:.1f} s")
+        _dense_check(sk, P, rep, eps, f, g, prm.tol)
+        rng = np.random.default_rng(7)
+        rows = np.sort(rng.choice(c.n, 8, replace=False))
+        T, _ = P.materialize_rows(eps, f, g, _t(rows))
+        T = T.cpu().numpy().astype(np.float64)
+    ref = oracle.materialize_rows(c.x, c.y, c.a, c.b, f.cpu().numpy(), g.cpu().numpy(), eps, 1.0, rows)
+    # entries within 1e-5 relative; below the smallest normal fp32 number,
+    # absolutely at that level (fp32 cannot hold them)
+    err = np.abs(T - ref)
+    assert not np.any(err > 1e-5 * ref + 2.0 ** -126), int(np.sum(err > 1e-5 * ref + 2.0 ** -126))
+    np.testing.assert_allclose(T.sum(axis=1), ref.sum(axis=1), rtol=1e-5)
