@@ -97,6 +97,7 @@ void problem_free(sinkhorn_problem* p) {
   dev_free(p->Mpart);
   dev_free(p->Spart);
   dev_free(p->red_part);
+  dev_free(p->tile_flag);
   dev_free(p->ctl);
   host_free(p->host_ctl);
   host_free(p->host_tmp);
@@ -233,6 +234,9 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
         if (p->host_ctl->nonfinite) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
         const double v = p->host_ctl->residual;
         hist.push_back(v);
+        if (hist.size() % 100 == 0)
+          progress("solve: %d iterations at eps %.4g, row residual %.4g (%.3f s)", (int)o.iters, eps,
+                   v, seconds_since(t0));
         const bool stalled = stall_window > 0 && (int64_t)hist.size() > stall_window &&
                              v > (1.0 - stall_rel) * hist[hist.size() - 1 - stall_window];
         if (v <= s.tol || stalled) {
@@ -349,6 +353,8 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->red_cap = std::max(row_groups(n), row_groups(m)) + 16;
       p->red_part = (double*)dev_alloc(sizeof(double) * p->red_cap);
+      p->tile_flag = (int32_t*)dev_alloc(sizeof(int32_t) * p->red_cap);
+      zero_i32(p->tile_flag, (int32_t)p->red_cap, p->stream);
       reset_nonfinite(p);
       for (int k = 0; k < 2; ++k) {
         p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);

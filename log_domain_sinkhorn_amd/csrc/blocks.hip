@@ -25,12 +25,10 @@
 
 #include <rocprim/device/device_scan.hpp>
 
-#include "rowfinal.h"
+#include "pairloop.h"
 
 namespace sk {
 namespace {
-
-__device__ __forceinline__ float ex2(float v) { return __builtin_amdgcn_exp2f(v); }
 
 // One wave per block: min / max of each axis and the max weight.
 __global__ __launch_bounds__(64) void k_block_static(const float* __restrict__ soa, int64_t stride,
@@ -145,10 +143,6 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   if (!FILL && live) A.counts[I] = cnt;
 }
 
-constexpr int kSW = 8;   // waves per workgroup of the sparse half-step
-constexpr int kSR = 2;   // rows per lane
-constexpr int kSRows = 64 * kSR;
-
 struct SparseArgs {
   const float* P;      // row side SoA [D][pstride]
   int64_t pstride;
@@ -157,124 +151,65 @@ struct SparseArgs {
   const float* H;      // column term of the column side
   float nkappa;
   int64_t nchunks;     // column chunks of kChunk points (all columns)
-  int32_t B;           // block size (multiple of kSRows)
+  int32_t B;           // block size (multiple of kRowsPerTile)
   const int64_t* ptr;  // [row blocks + 1]
   const int32_t* idx;  // admitted column blocks
+  const float* shift_pot;  // shifted mode: previous potential of the row side
+  float lam;               // log2(e) / eps
+  float inv_kappa;         // 1 / kappa
+  int32_t* tile_flag;      // [tiles] tiles left for the exact recompute
+  int32_t fallback;        // 1: exact recompute of the flagged tiles only
   RowFinal F;
 };
 
 // Workgroup = one 128-row tile of row block I = tile * 128 / B; its waves
 // share out the admitted column blocks (or, for an empty list, all column
-// chunks) and merge through LDS in wave order.
-template <int D>
-__global__ __launch_bounds__(64 * kSW) void k_lse_sparse(SparseArgs A) {
+// chunks) and merge through LDS in wave order. In shifted mode a tile with a
+// too-small row sum is flagged (its residual partial zeroed) and left to the
+// fallback launch, which recomputes exactly the flagged tiles only.
+template <int D, bool SHIFT>
+__global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const float* __restrict__ Q,
+                                                        const float* __restrict__ H) {
+  __shared__ TileLds L;
   const int64_t tile = blockIdx.x;
-  const int64_t I = tile * kSRows / A.B;
+  if (!SHIFT && A.fallback && A.tile_flag[tile] == 0) return;  // uniform
+  const int64_t I = tile * kRowsPerTile / A.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = tile * kSRows + lane;
-  float x[kSR][D];
-  float M[kSR], S[kSR];
-#pragma unroll
-  for (int r = 0; r < kSR; ++r) {
-#pragma unroll
-    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
-    M[r] = -FLT_MAX;
-    S[r] = 0.0f;
+  float x[kR][D];
+  load_rows<D>(A.P, A.pstride, tile, lane, x);
+  RowAcc<SHIFT> R;
+  if (SHIFT) {
+    float pot[kR];
+    load_shift_pot(A.shift_pot, A.F.np, tile, lane, pot);
+    R.init_shift(pot, A.lam, A.inv_kappa, A.nkappa);
+  } else {
+    R.init_exact();
   }
-  const float nk = A.nkappa;
-  const float* __restrict__ Q = A.Q;
-  const float* __restrict__ H = A.H;
-  const int64_t qs = A.qstride;
   const int64_t p0 = A.ptr[I];
   const int64_t p1 = A.ptr[I + 1];
   const int64_t cpb = A.B / kChunk;  // chunks per column block
-
-  auto run = [&](int64_t c0, int64_t c1) {
-    for (int64_t c = c0; c < c1; ++c) {
-      const int64_t j0 = c * kChunk;
-      float yv[D][kChunk];
-      float hv[kChunk];
-#pragma unroll
-      for (int k = 0; k < D; ++k)
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qs + j0 + jj];
-#pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) hv[jj] = H[j0 + jj];
-#pragma unroll
-      for (int r = 0; r < kSR; ++r) {
-        float z[kChunk];
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) {
-          float dd = x[r][0] - yv[0][jj];
-          float q = dd * dd;
-#pragma unroll
-          for (int k = 1; k < D; ++k) {
-            dd = x[r][k] - yv[k][jj];
-            q = __builtin_fmaf(dd, dd, q);
-          }
-          z[jj] = __builtin_fmaf(nk, q, hv[jj]);
-        }
-        float cm = z[0];
-#pragma unroll
-        for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
-        const float Mn = fmaxf(M[r], cm);
-        float acc = 0.0f;
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) acc += ex2(z[jj] - Mn);
-        S[r] = __builtin_fmaf(S[r], ex2(M[r] - Mn), acc);
-        M[r] = Mn;
-      }
-    }
-  };
-
   if (p1 > p0) {
-    for (int64_t q = p0 + wave; q < p1; q += kSW) {
+    for (int64_t q = p0 + wave; q < p1; q += kW) {
       const int64_t J = A.idx[q];
       const int64_t c0 = J * cpb;
       const int64_t c1 = c0 + cpb < A.nchunks ? c0 + cpb : A.nchunks;
-      run(c0, c1);
+      pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, c0, c1, 1);
     }
   } else {
-    const int64_t per = (A.nchunks + kSW - 1) / kSW;
-    const int64_t c0 = wave * per;
-    const int64_t c1 = c0 + per < A.nchunks ? c0 + per : A.nchunks;
-    run(c0, c1);
+    pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, wave, A.nchunks, kW);
   }
-
-  __shared__ float sM[kSW][kSRows];
-  __shared__ float sS[kSW][kSRows];
-  __shared__ double sRed[64 * kSW];
-#pragma unroll
-  for (int r = 0; r < kSR; ++r) {
-    sM[wave][lane + 64 * r] = M[r];
-    sS[wave][lane + 64 * r] = S[r];
-  }
-  __syncthreads();
-  double term = 0.0;
-  int bad = 0;
-  if (threadIdx.x < kSRows) {
-    const int t = threadIdx.x;
-    float mx = -FLT_MAX;
-#pragma unroll
-    for (int v = 0; v < kSW; ++v) mx = fmaxf(mx, sM[v][t]);
-    float sum = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kSW; ++v) sum = __builtin_fmaf(sS[v][t], ex2(sM[v][t] - mx), sum);
-    const int64_t i = tile * kSRows + t;
-    if (i < A.F.np) term = finalize_row(A.F, i, mx, (double)sum, &bad);
-  }
-  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
-  if (A.F.prev) {
-    sRed[threadIdx.x] = term;
-    __syncthreads();
-#pragma unroll
-    for (int w = 64 * kSW / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
-      __syncthreads();
+  double mx, sum;
+  merge_waves(L, wave, lane, R, mx, sum);
+  if (SHIFT && needs_exact(A.F.np, tile, sum)) {
+    if (threadIdx.x == 0) {
+      A.tile_flag[tile] = 1;
+      if (A.F.prev) A.F.red_part[tile] = 0.0;
     }
-    if (threadIdx.x == 0) A.F.red_part[tile] = sRed[0];
+    return;
   }
+  if (!SHIFT && A.fallback && threadIdx.x == 0) A.tile_flag[tile] = 0;
+  finish_tile(A.F, L, tile, mx, sum);
 }
 
 // Counts entries of idx outside [0, nc) and rows whose ptr decreases.
@@ -418,34 +353,59 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
 }
 
 // ---------------------------------------------------------------- sparse half-step
+template <int D>
+void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted) {
+  if (shifted)
+    hipLaunchKernelGGL((k_lse_sparse<D, true>), dim3((uint32_t)tiles), dim3(kThreads), 0, p->stream,
+                       A, A.Q, A.H);
+  else
+    hipLaunchKernelGGL((k_lse_sparse<D, false>), dim3((uint32_t)tiles), dim3(kThreads), 0,
+                       p->stream, A, A.Q, A.H);
+  SK_LAUNCH_CHECK();
+}
+
 void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const int64_t* ptr,
                      const int32_t* idx, double pairs) {
   const Side& rows = *hs.rows;
   const Side& cols = *hs.cols;
-  if (B % kSRows != 0) fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need B a multiple of 128");
-  const int64_t tiles = (rows.count + kSRows - 1) / kSRows;
+  if (B % kRowsPerTile != 0) fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need B a multiple of 128");
+  const int64_t tiles = (rows.count + kRowsPerTile - 1) / kRowsPerTile;
   if (tiles > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
+  const bool shifted = hs.shift_pot != nullptr;
   SparseArgs A;
   A.P = rows.soa;
   A.pstride = rows.padded;
   A.Q = cols.soa;
   A.qstride = cols.padded;
   A.H = hs.Hcols;
-  A.nkappa = (float)(-p->scale * kLog2e / hs.eps);
+  const double kappa = p->scale * kLog2e / hs.eps;
+  A.nkappa = (float)(-kappa);
   A.nchunks = (cols.count + kChunk - 1) / kChunk;
   A.B = B;
   A.ptr = ptr;
   A.idx = idx;
+  A.shift_pot = hs.shift_pot;
+  A.lam = (float)(kLog2e / hs.eps);
+  A.inv_kappa = (float)(1.0 / kappa);
+  A.tile_flag = p->tile_flag;
+  A.fallback = 0;
   A.F = make_rowfinal(p, hs);
+  auto launch = [&](const SparseArgs& a, bool sh) {
+    switch (p->d) {
+      case 1: launch_sparse<1>(p, a, tiles, sh); break;
+      case 2: launch_sparse<2>(p, a, tiles, sh); break;
+      case 3: launch_sparse<3>(p, a, tiles, sh); break;
+      default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
+    }
+  };
   prof_begin(p);
-  switch (p->d) {
-    case 1: hipLaunchKernelGGL((k_lse_sparse<1>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
-    case 2: hipLaunchKernelGGL((k_lse_sparse<2>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
-    case 3: hipLaunchKernelGGL((k_lse_sparse<3>), dim3((uint32_t)tiles), dim3(64 * kSW), 0, p->stream, A); break;
-    default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
-  }
-  SK_LAUNCH_CHECK();
+  launch(A, shifted);
   prof_end(p, pairs);
+  if (shifted) {  // exact recompute of flagged tiles (the other workgroups exit at once)
+    SparseArgs E = A;
+    E.fallback = 1;
+    launch(E, false);
+  }
   if (A.F.prev) launch_reduce(p, tiles);
 }
 
@@ -543,6 +503,7 @@ int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, 
     prep_column_term(p, p->Y, g, eps, p->Y.H);
     reset_nonfinite(p);
     HalfStep hs{&p->X, &p->Y, p->Y.H, f_out, f_prev, nullptr, eps, eps, f_prev && row_l1};
+    hs.shift_pot = f_prev;  // the previous potential estimates the row shifts
     sparse_halfstep(p, hs, B, ptr, idx, 0.0);
     double v = 0.0;
     int32_t bad = 0;
@@ -566,6 +527,7 @@ int sinkhorn_sparse_halfstep_g(sinkhorn_problem* p, double eps, const float* f, 
     prep_column_term(p, p->X, f, eps, p->X.H);
     reset_nonfinite(p);
     HalfStep hs{&p->Y, &p->X, p->X.H, g_out, g_prev, nullptr, eps, eps, g_prev && col_l1};
+    hs.shift_pot = g_prev;
     sparse_halfstep(p, hs, B, ptr, idx, 0.0);
     double v = 0.0;
     int32_t bad = 0;

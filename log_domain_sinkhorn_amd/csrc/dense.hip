@@ -16,20 +16,7 @@
 //     workgroup per tile) combines their partials in split order and
 //     finalizes.
 //
-// Two pair loops, the same sum:
-//   exact   z = h_j - kappa q_ij; per 16-column chunk the running max M is
-//           raised to the chunk max and S rescaled: per pair d sub, 1 mul +
-//           (d-1) fma, 1 fma, 1/2 max3, 1 sub, 1 add on the VALU + 1 exp2;
-//   shifted every row carries a fixed shift c = kappa u (log2 units) chosen
-//           from its previous potential (c ~ LSE - 16), folded into the first
-//           squared term: q' = (x - y)^2 + u, z' = h_j - kappa q' = z - c, and
-//           S += exp2(z'): per pair d sub, d fma, 1 fma, 1 add + 1 exp2. A
-//           chunk whose sum exceeds 2^64 (or overflows) is redone exactly for
-//           the lanes concerned (the shift moves up to the chunk max); a row
-//           whose final sum is below 2^-40 (shift too high: terms may have
-//           underflowed) marks its tile, and the whole tile is recomputed in
-//           exact mode by a second launch. The shift is kept in fp64 as the
-//           exact product kappa * u of the two fp32 values the loop uses.
+// The pair loop itself (exact and shifted) is in pairloop.h.
 // Finalizing writes the potential, optionally the next column term of the row
 // side and the residual terms, summed per tile and then, on request, in tile
 // order by a one-block kernel. Results are bit-reproducible.
@@ -37,21 +24,10 @@
 #include <cmath>
 #include <cstring>
 
-#include "rowfinal.h"
+#include "pairloop.h"
 
 namespace sk {
 namespace {
-
-// Base-2 exponential of the hardware (v_exp_f32): about 1 ulp; -inf gives +0.
-__device__ __forceinline__ float ex2(float v) { return __builtin_amdgcn_exp2f(v); }
-
-constexpr int kR = 2;                // rows per lane
-constexpr int kW = 8;                // waves per workgroup
-constexpr int kRowsPerTile = 64 * kR;
-constexpr int kThreads = 64 * kW;
-constexpr float kBig = 0x1p64f;      // shifted mode: redo a chunk whose sum exceeds this
-constexpr double kTiny = 0x1p-40;    // shifted mode: a row sum below this is redone exactly
-constexpr float kHeadroom = 16.0f;   // shift = estimated LSE - headroom (log2 units)
 
 struct LseArgs {
   const float* P;       // row side SoA [D][pstride]
@@ -73,188 +49,19 @@ struct LseArgs {
 };
 
 
-// Keeps a wave-uniform value in a VGPR (a lane shuffle is divergent to the
-// compiler), so that a VOP3 with an SGPR operand (the scalar-loaded column
-// term) can use it without a copy per pair. Unlike inline asm it leaves the
-// scalar loads of the column tile provably unclobbered.
-__device__ __forceinline__ float in_vgpr(float s) { return __shfl(s, (int)(threadIdx.x & 63), 64); }
-
-// One wave's pass over column chunks c0, c0 + step, ... < c1 for the lane's
-// kR rows x.
-// Exact mode starts from an empty sum and returns the running max in Md;
-// shifted mode starts from the shifts (u, Md) the caller set and may raise
-// them chunk by chunk.
-template <int D, bool SHIFT>
-__device__ __forceinline__ void pair_pass(const LseArgs& A, const float* __restrict__ Q,
-                                          const float* __restrict__ H, const float (&x)[kR][D],
-                                          int64_t c0, int64_t c1, int64_t step, float (&u)[kR],
-                                          double (&Md)[kR], float (&S)[kR]) {
-  const float nk = A.nkappa;
-  const float nkv = in_vgpr(nk);
-  const double kd = -(double)nk;
-  float Mf[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    S[r] = 0.0f;
-    Mf[r] = -FLT_MAX;
-  }
-  const int64_t qs = A.qstride;
-  for (int64_t c = c0; c < c1; c += step) {
-    const int64_t j0 = c * kChunk;
-    float yv[D][kChunk];
-    float hv[kChunk];
-#pragma unroll
-    for (int k = 0; k < D; ++k)
-#pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qs + j0 + jj];
-#pragma unroll
-    for (int jj = 0; jj < kChunk; ++jj) hv[jj] = H[j0 + jj];
-
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      float z[kChunk];
-      if (SHIFT) {
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) {
-          float dd = x[r][0] - yv[0][jj];
-          float q = __builtin_fmaf(dd, dd, u[r]);
-#pragma unroll
-          for (int k = 1; k < D; ++k) {
-            dd = x[r][k] - yv[k][jj];
-            q = __builtin_fmaf(dd, dd, q);
-          }
-          z[jj] = __builtin_fmaf(q, nkv, hv[jj]);
-        }
-        float acc = ex2(z[0]);
-#pragma unroll
-        for (int jj = 1; jj < kChunk; ++jj) acc += ex2(z[jj]);
-        const bool big = !(acc <= kBig);
-        if (__builtin_amdgcn_ballot_w64(big) != 0) {
-          // exact redo of this chunk for the lanes whose sum ran away
-          float cm = z[0];
-#pragma unroll
-          for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
-          float delta = 0.0f;
-          if (big) {
-            const float un = (float)((Md[r] + (double)cm) / kd);
-            const double Mn = kd * (double)un;
-            delta = (float)(Mn - Md[r]);
-            u[r] = un;
-            Md[r] = Mn;
-          }
-          float acc2 = 0.0f;
-#pragma unroll
-          for (int jj = 0; jj < kChunk; ++jj) acc2 += ex2(z[jj] - delta);
-          S[r] = big ? __builtin_fmaf(S[r], ex2(-delta), acc2) : S[r] + acc;
-        } else {
-          S[r] += acc;
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) {
-          float dd = x[r][0] - yv[0][jj];
-          float q = dd * dd;
-#pragma unroll
-          for (int k = 1; k < D; ++k) {
-            dd = x[r][k] - yv[k][jj];
-            q = __builtin_fmaf(dd, dd, q);
-          }
-          z[jj] = __builtin_fmaf(q, nkv, hv[jj]);
-        }
-        float cm = z[0];
-#pragma unroll
-        for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
-        const float Mn = fmaxf(Mf[r], cm);
-        float acc = 0.0f;
-#pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) acc += ex2(z[jj] - Mn);
-        S[r] = __builtin_fmaf(S[r], ex2(Mf[r] - Mn), acc);
-        Mf[r] = Mn;
-      }
-    }
-  }
-  if (!SHIFT) {
-#pragma unroll
-    for (int r = 0; r < kR; ++r) Md[r] = (double)Mf[r];
-  }
-}
-
-struct TileLds {
-  double M[kW][kRowsPerTile];
-  float S[kW][kRowsPerTile];
-  double red[kThreads];
-};
-
-// Merge of the W waves' (max, sum) through LDS in wave order; thread t < 128
-// gets row t of the tile.
-__device__ __forceinline__ void merge_waves(TileLds& L, int wave, int lane, const double (&Md)[kR],
-                                            const float (&S)[kR], double& mx, double& sum) {
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    L.M[wave][lane + 64 * r] = Md[r];
-    L.S[wave][lane + 64 * r] = S[r];
-  }
-  __syncthreads();
-  mx = -DBL_MAX;
-  sum = 0.0;
-  const int t = threadIdx.x;
-  if (t < kRowsPerTile) {
-#pragma unroll
-    for (int v = 0; v < kW; ++v) mx = fmax(mx, L.M[v][t]);
-#pragma unroll
-    for (int v = 0; v < kW; ++v) sum += (double)L.S[v][t] * (double)ex2((float)(L.M[v][t] - mx));
-  }
-}
-
 // Exact recompute of a whole tile (all columns) by the kW waves of the
 // workgroup: the fallback of shifted mode when a row's shift was too high.
 template <int D>
-__device__ void exact_tile(const LseArgs& A, TileLds& L, int64_t tile, double& mx,
-                           double& sum) {
+__device__ void exact_tile(const LseArgs& A, TileLds& L, int64_t tile, double& mx, double& sum) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = tile * kRowsPerTile + lane;
   float x[kR][D];
-#pragma unroll
-  for (int r = 0; r < kR; ++r)
-#pragma unroll
-    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
-  float u[kR], S[kR];
-  double Md[kR];
-  pair_pass<D, false>(A, A.Q, A.H, x, wave, A.nchunks, kW, u, Md, S);
+  load_rows<D>(A.P, A.pstride, tile, lane, x);
+  RowAcc<false> R;
+  R.init_exact();
+  pair_pass<D, false>(R, A.Q, A.H, A.qstride, A.nkappa, x, wave, A.nchunks, kW);
   __syncthreads();  // LDS reuse
-  merge_waves(L, wave, lane, Md, S, mx, sum);
-}
-
-// Writes the potentials of a tile's rows (threads t < 128) and its residual
-// partial (fixed-order tree over the workgroup).
-__device__ __forceinline__ void finish_tile(const LseArgs& A, TileLds& L, int64_t tile, double mx,
-                                            double sum) {
-  const int t = threadIdx.x;
-  const int64_t i = tile * kRowsPerTile + t;
-  const bool own = t < kRowsPerTile && i < A.F.np;
-  double term = 0.0;
-  int bad = 0;
-  if (own) term = finalize_row(A.F, i, mx, sum, &bad);
-  if (bad) atomicAdd(&A.F.ctl->nonfinite, bad);
-  if (A.F.prev) {
-    L.red[t] = term;
-    __syncthreads();
-#pragma unroll
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (t < w) L.red[t] += L.red[t + w];
-      __syncthreads();
-    }
-    if (t == 0) A.F.red_part[tile] = L.red[0];
-  }
-}
-
-// True (workgroup-uniform) when some row of the tile has a sum below kTiny:
-// its shift was too high and terms may have underflowed.
-__device__ __forceinline__ bool needs_exact(const LseArgs& A, int64_t tile, double sum) {
-  const int64_t i = tile * kRowsPerTile + threadIdx.x;
-  const bool own = threadIdx.x < kRowsPerTile && i < A.F.np;
-  return __syncthreads_or(own && !(sum >= kTiny));
+  merge_waves(L, wave, lane, R, mx, sum);
 }
 
 // Q, H, Mp and Sp come as separate no-alias arguments, so the column data
@@ -270,27 +77,21 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A, const float* _
   const int64_t tile = blockIdx.x / (uint32_t)A.G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
-  const int64_t row0 = tile * kRowsPerTile + lane;
   float x[kR][D];
-  float u[kR], S[kR];
-  double Md[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-#pragma unroll
-    for (int k = 0; k < D; ++k) x[r][k] = A.P[k * A.pstride + row0 + 64 * r];
-    if (SHIFT) {
-      const int64_t i = row0 + 64 * r;
-      const float p = i < A.F.np ? A.shift_pot[i] : 0.0f;
-      const float c = -p * A.lam - kHeadroom;
-      u[r] = c * A.inv_kappa;
-      Md[r] = -(double)A.nkappa * (double)u[r];
-    }
+  load_rows<D>(A.P, A.pstride, tile, lane, x);
+  RowAcc<SHIFT> R;
+  if (SHIFT) {
+    float pot[kR];
+    load_shift_pot(A.shift_pot, A.F.np, tile, lane, pot);
+    R.init_shift(pot, A.lam, A.inv_kappa, A.nkappa);
+  } else {
+    R.init_exact();
   }
   const int64_t g0 = (int64_t)gs * A.cps;
   const int64_t g1 = g0 + A.cps < A.nchunks ? g0 + A.cps : A.nchunks;
-  pair_pass<D, SHIFT>(A, Q, H, x, g0 + wave, g1, kW, u, Md, S);
+  pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, g0 + wave, g1, kW);
   double mx, sum;
-  merge_waves(L, wave, lane, Md, S, mx, sum);
+  merge_waves(L, wave, lane, R, mx, sum);
   const int64_t i = tile * kRowsPerTile + threadIdx.x;
   if (threadIdx.x < kRowsPerTile && i < A.F.np) {
     Mp[(int64_t)gs * A.F.np + i] = mx;
@@ -333,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void k_merge(LseArgs A, int32_t shifted) 
 #pragma unroll
     for (int v = 0; v < kW; ++v) sum += sS[v][t] * (double)ex2((float)(L.M[v][t] - mx));
   }
-  if (shifted && needs_exact(A, tile, sum)) exact_tile<D>(A, L, tile, mx, sum);
-  finish_tile(A, L, tile, mx, sum);
+  if (shifted && needs_exact(A.F.np, tile, sum)) exact_tile<D>(A, L, tile, mx, sum);
+  finish_tile(A.F, L, tile, mx, sum);
 }
 
 // Merge of G split partials for the shared merge entry point (fp32 maxima).

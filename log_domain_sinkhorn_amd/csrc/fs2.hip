@@ -355,7 +355,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       // sparse f-step at (f, g); its fused residual is R_A,row of (f, g)
       reset_nonfinite(p);
       prep_column_term(p, Ys, gs[cg], eps, Ys.H);
-      sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true},
+      sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true, fs[cf]},
                       P.B, rowL.ptr, rowL.idx, row_pairs);
       int32_t bad = 0;
       read_reduction(p, &Rrow, &bad);
@@ -364,7 +364,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       Rcol = NAN;
       if (Rrow + omega <= P.tol) {
         prep_column_term(p, Xs, fs[cf], eps, Xs.H);
-        sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true},
+        sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true, gs[cg]},
                         P.B, colL.ptr, colL.idx, col_pairs);
         read_reduction(p, &Rcol, nullptr);
         R.pairs_evaluated += col_pairs;
@@ -380,7 +380,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       if (R.fine_updates >= P.max_fine) break;
       cf = 1 - cf;  // accept the f-step
       prep_column_term(p, Xs, fs[cf], eps, Xs.H);
-      sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false},
+      sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false, gs[cg]},
                       P.B, colL.ptr, colL.idx, col_pairs);
       R.pairs_evaluated += col_pairs;
       cg = 1 - cg;

@@ -104,6 +104,7 @@ struct sinkhorn_problem {
   // residual block partials, arrival counters and the reduced values
   double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
+  int32_t* tile_flag = nullptr; // [red_cap] tiles marked for the exact recompute, zero between launches
   sk::Ctl* ctl = nullptr;       // device control block
   sk::Ctl* host_ctl = nullptr;  // pinned, host-coherent mirror (the residual kernel writes it)
   sk::Ctl* host_ctl_dev = nullptr;  // device address of host_ctl

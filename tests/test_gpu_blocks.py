@@ -113,8 +113,11 @@ def test_block_screen_full_size_sampled_row_blocks(sk):
         assert np.array_equal(idx[ptr[I]:ptr[I + 1]], col_r[ptr_r[k]:ptr_r[k + 1]]), I
 
 
+@pytest.mark.parametrize("prev", [True, False], ids=["shifted", "exact"])
 @pytest.mark.parametrize("n,B,eps", [(16384, 128, 1e-4), (16384, 256, 1e-3), (5000, 128, 1e-3)])
-def test_sparse_halfsteps_match_oracle(sk, n, B, eps):
+def test_sparse_halfsteps_match_oracle(sk, n, B, eps, prev):
+    """With the previous potentials the kernel runs the shifted loop (and
+    reports the residual); without, the exact loop."""
     x, y, a, b = _sorted_problem(5, n)
     rng = np.random.default_rng(3)
     f, g = _near_plan_potentials(n, eps, rng)
@@ -129,16 +132,21 @@ def test_sparse_halfsteps_match_oracle(sk, n, B, eps):
     col = np.delete(col, np.s_[ptr[1]:ptr[2]])
     ptr[2:] -= ptr[2] - ptr[1]
     with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
-        fo, r = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)), f_prev=_t(f))
-        go, rc = P.sparse_halfstep_g(eps, _t(f), B, _t(ptrT), _t(rowT.astype(np.int32)), g_prev=_t(g))
+        fo, r = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)),
+                                    f_prev=_t(f) if prev else None)
+        go, rc = P.sparse_halfstep_g(eps, _t(f), B, _t(ptrT), _t(rowT.astype(np.int32)),
+                                     g_prev=_t(g) if prev else None)
     f_ref = oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B)
     g_ref = oracle.sparse_halfstep_g(x, y, a, f, eps, 1.0, ptrT, rowT, B)
     for got, ref, what in ((fo, f_ref, "f"), (go, g_ref, "g")):
         got = got.cpu().numpy().astype(np.float64)
         err = np.abs(got - ref) / np.maximum(eps, np.abs(ref))
         assert err.max() <= 1e-5, (what, err.max())
-    Rr, Rc = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
-    assert r == pytest.approx(Rr, rel=1e-3) and rc == pytest.approx(Rc, rel=1e-3)
+    if prev:
+        Rr, Rc = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
+        assert r == pytest.approx(Rr, rel=1e-3) and rc == pytest.approx(Rc, rel=1e-3)
+    else:
+        assert r is None and rc is None
 
 
 def _gauge_close(f, g, fr, gr, tol):
