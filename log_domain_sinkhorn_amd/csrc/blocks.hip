@@ -78,6 +78,44 @@ __global__ __launch_bounds__(64) void k_block_max(const float* __restrict__ pot,
   if (threadIdx.x == 0) F[I] = (double)v;
 }
 
+// Groups of kGrp consecutive blocks: union box, maximum potential and
+// maximum log W (min / max only, so exact).
+__global__ __launch_bounds__(256) void k_group_static(const double* __restrict__ lo,
+                                                      const double* __restrict__ hi,
+                                                      const double* __restrict__ lw, int64_t nb,
+                                                      int32_t d, int64_t ng,
+                                                      double* __restrict__ glo,
+                                                      double* __restrict__ ghi,
+                                                      double* __restrict__ glw) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ng) return;
+  const int64_t s = g * kGrp;
+  const int64_t e = s + kGrp < nb ? s + kGrp : nb;
+  for (int k = 0; k < d; ++k) {
+    double a = INFINITY, b = -INFINITY;
+    for (int64_t J = s; J < e; ++J) {
+      a = fmin(a, lo[k * nb + J]);
+      b = fmax(b, hi[k * nb + J]);
+    }
+    glo[k * ng + g] = a;
+    ghi[k * ng + g] = b;
+  }
+  double w = -INFINITY;
+  for (int64_t J = s; J < e; ++J) w = fmax(w, lw[J]);
+  glw[g] = w;
+}
+
+__global__ __launch_bounds__(256) void k_group_max(const double* __restrict__ F, int64_t nb,
+                                                   int64_t ng, double* __restrict__ gF) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ng) return;
+  const int64_t s = g * kGrp;
+  const int64_t e = s + kGrp < nb ? s + kGrp : nb;
+  double v = -INFINITY;
+  for (int64_t J = s; J < e; ++J) v = fmax(v, F[J]);
+  gF[g] = v;
+}
+
 struct ScreenArgs {
   const double* rlo;  // row side summaries [d][nr]
   const double* rhi;
@@ -89,6 +127,11 @@ struct ScreenArgs {
   const double* cF;
   const double* clw;
   int64_t nc;
+  const double* glo;  // column groups [d][ng]
+  const double* ghi;
+  const double* gF;
+  const double* glw;
+  int64_t ng;
   double scale;
   double eps;
   double log_delta;
@@ -97,50 +140,78 @@ struct ScreenArgs {
   int32_t* idx;
 };
 
-// Thread = row block I; the column blocks stream through as wave-uniform
-// scalar loads. FILL = false counts admitted tiles, FILL = true writes them.
+// Wave = row block I (its summary comes in through scalar loads). The 64
+// lanes first test 64 column groups at a time; then, for each group that may
+// hold an admitted tile, lane l takes member block l of the group. Admitted
+// tiles are counted (FILL = false) or written in increasing block order
+// (FILL = true) from wave ballots.
+//
+// The group test only skips work: with the union box, the largest potential
+// and the largest log W of a group, (F_I + G_K) - D_IK bounds every member's
+// left side from above and the right side from below (in exact arithmetic),
+// so when the group's left side stays below its right side by a margin far
+// above the fp64 rounding of either evaluation (1e-12 relative to the terms),
+// every member is omitted by the exact test too. Members of the other groups
+// take the exact per-tile test, so the lists do not depend on the grouping.
 template <int D, bool FILL>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
-  const int64_t I = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool live = I < A.nr;
-  const int64_t Ir = live ? I : 0;
+  static_assert(kGrp == 64, "one member block per lane");
+  const int64_t I = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (I >= A.nr) return;  // wave-uniform; no barriers below
+  const int lane = threadIdx.x & 63;
   double lo[D], hi[D];
 #pragma unroll
   for (int k = 0; k < D; ++k) {
-    lo[k] = A.rlo[k * A.nr + Ir];
-    hi[k] = A.rhi[k * A.nr + Ir];
+    lo[k] = A.rlo[k * A.nr + I];
+    hi[k] = A.rhi[k * A.nr + I];
   }
-  const double FI = A.rF[Ir];
-  const double lwI = A.rlw[Ir];
-  int64_t cnt = 0;
-  int64_t out = (FILL && live) ? A.ptr[I] : 0;
-  const double* __restrict__ clo = A.clo;
-  const double* __restrict__ chi = A.chi;
-  const double* __restrict__ cF = A.cF;
-  const double* __restrict__ clw = A.clw;
-  for (int64_t J = 0; J < A.nc; ++J) {
-    double acc = 0.0;
+  const double FI = A.rF[I];
+  const double lwI = A.rlw[I];
+  int64_t out = FILL ? A.ptr[I] : 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
+  for (int64_t K0 = 0; K0 < A.ng; K0 += 64) {
+    const int64_t K = K0 + lane;
+    bool cand = false;
+    if (K < A.ng) {
+      double gacc = 0.0;
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-      const double a = __dsub_rn(clo[k * A.nc + J], hi[k]);
-      const double b = __dsub_rn(lo[k], chi[k * A.nc + J]);
-      const double gap = fmax(fmax(a, b), 0.0);
-      const double sq = __dmul_rn(gap, gap);
-      acc = k == 0 ? sq : __dadd_rn(acc, sq);
-    }
-    const double Dst = __dmul_rn(A.scale, acc);
-    const double lhs = __dsub_rn(__dadd_rn(FI, cF[J]), Dst);
-    const double rhs = __dmul_rn(A.eps, __dsub_rn(A.log_delta, fmax(lwI, clw[J])));
-    if (lhs > rhs) {
-      if (FILL) {
-        if (live) A.idx[out] = (int32_t)J;
-        ++out;
-      } else {
-        ++cnt;
+      for (int k = 0; k < D; ++k) {
+        const double gap = fmax(fmax(A.glo[k * A.ng + K] - hi[k], lo[k] - A.ghi[k * A.ng + K]), 0.0);
+        gacc += gap * gap;
       }
+      const double Dg = A.scale * gacc;
+      const double glhs = (FI + A.gF[K]) - Dg;
+      const double grhs = A.eps * (A.log_delta - fmax(lwI, A.glw[K]));
+      const double margin = 1e-12 * (fabs(FI) + fabs(A.gF[K]) + Dg + fabs(grhs));
+      cand = !(glhs + margin <= grhs);
+    }
+    uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+    while (m) {
+      const int b = __builtin_ctzll(m);
+      m &= m - 1;
+      const int64_t J = (K0 + b) * kGrp + lane;
+      bool adm = false;
+      if (J < A.nc) {
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+          const double a = __dsub_rn(A.clo[k * A.nc + J], hi[k]);
+          const double c = __dsub_rn(lo[k], A.chi[k * A.nc + J]);
+          const double gap = fmax(fmax(a, c), 0.0);
+          const double sq = __dmul_rn(gap, gap);
+          acc = k == 0 ? sq : __dadd_rn(acc, sq);
+        }
+        const double Dst = __dmul_rn(A.scale, acc);
+        const double lhs = __dsub_rn(__dadd_rn(FI, A.cF[J]), Dst);
+        const double rhs = __dmul_rn(A.eps, __dsub_rn(A.log_delta, fmax(lwI, A.clw[J])));
+        adm = lhs > rhs;
+      }
+      const uint64_t am = __builtin_amdgcn_ballot_w64(adm);
+      if (FILL && adm) A.idx[out + __builtin_popcountll(am & below)] = (int32_t)J;
+      out += __builtin_popcountll(am);
     }
   }
-  if (!FILL && live) A.counts[I] = cnt;
+  if (!FILL && lane == 0) A.counts[I] = out;
 }
 
 struct SparseArgs {
@@ -236,7 +307,7 @@ __global__ __launch_bounds__(256) void k_count_empty(const int64_t* __restrict__
 
 template <int D>
 void launch_screen(hipStream_t st, const ScreenArgs& A, bool fill) {
-  const dim3 grid((uint32_t)((A.nr + 255) / 256));
+  const dim3 grid((uint32_t)((A.nr + 3) / 4));  // a wave per row block
   if (fill)
     hipLaunchKernelGGL((k_screen<D, true>), grid, dim3(256), 0, st, A);
   else
@@ -252,8 +323,12 @@ void BlockSummary::release() {
   dev_free(hi);
   dev_free(lw);
   dev_free(F);
-  lo = hi = lw = F = nullptr;
-  nb = 0;
+  dev_free(glo);
+  dev_free(ghi);
+  dev_free(glw);
+  dev_free(gF);
+  lo = hi = lw = F = glo = ghi = glw = gF = nullptr;
+  nb = ng = 0;
 }
 
 void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& out) {
@@ -274,11 +349,23 @@ void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& o
   dev_free(W);
   for (auto& v : h) v = v > 0.0 ? std::log(v) : -INFINITY;  // C library log
   SK_HIP(hipMemcpyAsync(out.lw, h.data(), sizeof(double) * out.nb, hipMemcpyHostToDevice, p->stream));
+  out.ng = (out.nb + kGrp - 1) / kGrp;
+  out.glo = (double*)dev_alloc(sizeof(double) * 3 * out.ng);
+  out.ghi = (double*)dev_alloc(sizeof(double) * 3 * out.ng);
+  out.glw = (double*)dev_alloc(sizeof(double) * out.ng);
+  out.gF = (double*)dev_alloc(sizeof(double) * out.ng);
+  hipLaunchKernelGGL(k_group_static, dim3((uint32_t)((out.ng + 255) / 256)), dim3(256), 0,
+                     p->stream, out.lo, out.hi, out.lw, out.nb, p->d, out.ng, out.glo, out.ghi,
+                     out.glw);
+  SK_LAUNCH_CHECK();
   SK_HIP(hipStreamSynchronize(p->stream));
 }
 
 void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, BlockSummary& s) {
   hipLaunchKernelGGL(k_block_max, dim3((uint32_t)s.nb), dim3(64), 0, p->stream, pot, count, s.B, s.F);
+  SK_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_group_max, dim3((uint32_t)((s.ng + 255) / 256)), dim3(256), 0, p->stream, s.F,
+                     s.nb, s.ng, s.gF);
   SK_LAUNCH_CHECK();
 }
 
@@ -299,6 +386,11 @@ int64_t screen_tiles(sinkhorn_problem* p, const BlockSummary& rows, const BlockS
   A.cF = cols.F;
   A.clw = cols.lw;
   A.nc = cols.nb;
+  A.glo = cols.glo;
+  A.ghi = cols.ghi;
+  A.gF = cols.gF;
+  A.glw = cols.glw;
+  A.ng = cols.ng;
   A.scale = p->scale;
   A.eps = eps;
   A.log_delta = std::log(delta_rel);  // C library log

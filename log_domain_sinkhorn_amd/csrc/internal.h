@@ -158,6 +158,8 @@ void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, d
 int64_t mfma_partial_floats(int64_t nrows, int64_t ncols);
 
 // blocks.hip: per-block summaries of a side in its stored order
+constexpr int64_t kGrp = 64;  // blocks per screen group
+
 struct BlockSummary {
   int64_t nb = 0;        // blocks
   int32_t B = 0;         // points per block
@@ -165,6 +167,12 @@ struct BlockSummary {
   double* hi = nullptr;  // [3][nb] per-axis maximum
   double* lw = nullptr;  // [nb] log(points * max weight), C library log on the host
   double* F = nullptr;   // [nb] maximum potential, refreshed per screen
+  // groups of kGrp consecutive blocks for the screen's skip test
+  int64_t ng = 0;
+  double* glo = nullptr;  // [3][ng] union box
+  double* ghi = nullptr;
+  double* glw = nullptr;  // [ng] maximum log W
+  double* gF = nullptr;   // [ng] maximum potential, refreshed with F
   void release();
 };
 void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& out);
