@@ -38,22 +38,30 @@ VALU_PEAK_OPS = CUS * VALU_LANES_PER_CU * CLOCK_HZ  # 3.93e13 lane-ops/s (no pac
 MFMA_F32_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
 HBM_PEAK = 8.0e12  # bytes/s
 
+# steps / warmup: defaults per workload (a full solve of 4 or 5 takes minutes).
+# roofline: how the second, event-timed region runs (None: the same steps).
 WORKLOADS = {
-    1: dict(n=None, m=None, sched=dict(eps_start=0.01, eps_target=0.01, fixed_iters=200),
+    1: dict(sched=dict(eps_start=0.01, eps_target=0.01, fixed_iters=200), steps=5, warmup=1,
             desc="w1: n=m=1000 d=2, x~U[0,1]^2, y~N(0.5,0.1^2), uniform weights, eps=0.01, 200 iterations"),
-    2: dict(n=None, m=None, sched=dict(eps_start=1.0, eps_target=1e-3, eps_factor=0.5, iters_per_stage=10,
-                                       tol=1e-3, max_iters=20000),
+    2: dict(sched=dict(eps_start=1.0, eps_target=1e-3, eps_factor=0.5, iters_per_stage=10,
+                       tol=1e-3, max_iters=20000), steps=5, warmup=1,
             desc="w2: n=m=20000 d=3, 8-component GMM clouds (sigma 0.05), Dirichlet weights, "
                  "eps 1->1e-3 halving x10/stage, then to L1 residual 1e-3"),
-    3: dict(n=None, m=None, sched=dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=20000),
+    3: dict(sched=dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=20000), steps=2, warmup=1,
             scale="mean", materialize=1024,
             desc="w3: n=50000 m=60000 d=50, 20-cluster anisotropic GMM (PCA-embedding-like), uniform weights, "
                  "cost / mean cost, eps=0.05 to L1 residual 1e-3, then every plan row materialized in batches "
                  "of 1024 and min_i max_j T_ij"),
-    4: dict(n=None, m=None, sched=dict(eps_start=1.0, eps_target=1e-4, eps_factor=0.5, iters_per_stage=10,
-                                       tol=1e-3, max_iters=20000),
+    4: dict(sched=dict(eps_start=1.0, eps_target=1e-4, eps_factor=0.5, iters_per_stage=10,
+                       tol=1e-3, max_iters=20000), steps=1, warmup=0,
+            roofline=dict(eps_start=1e-4, eps_target=1e-4, fixed_iters=5),
             desc="w4: n=m=1e6 d=3, x~U[0,1]^3, y=jittered 100^3 grid, uniform weights, "
                  "eps 1->1e-4 halving x10/stage, then to L1 residual 1e-3"),
+    5: dict(multiscale=dict(B=128, eps=1e-4, tol=1e-2), steps=1, warmup=0, roofline=dict(max_fine=3),
+            desc="w5: n=m=2^24 d=3, 64-component GMM in [0,1]^3 (sigma U[0.01,0.05]), y = shifted means, "
+                 "uniform weights; Morton order, B=128 blocks, cells <= 2x blocks, coarse annealed centroid "
+                 "solve + lift, fine loop on block pairs screened with block potential maxima "
+                 "(delta_rel = 1e-3/NB), eps=1e-4, to certified L1 residual 1e-2"),
 }
 
 
@@ -138,14 +146,16 @@ def copy_calibration(mib: int, reps: int = 5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="no HIP events around the pair-kernel launches (no roofline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--max-fine", type=int, default=None,
+                    help="workload 5: cap on fine updates (profiling runs; the default runs to the certificate)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -161,14 +171,27 @@ def main():
     import synth
 
     W = WORKLOADS[args.workload]
-    c = synth.make(args.workload, n=W["n"], m=W["m"])
+    if args.steps is None:
+        args.steps = W["steps"]
+    if args.warmup is None:
+        args.warmup = W["warmup"]
+    c = synth.make(args.workload)
     dev = torch.device("cuda:0")
     x, y = torch.from_numpy(c.x).to(dev), torch.from_numpy(c.y).to(dev)
     a, b = torch.from_numpy(c.a).to(dev), torch.from_numpy(c.b).to(dev)
     # the cost scale is resolved once, as a number, before anything is timed
     scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
-    sched = sk.Schedule(**W["sched"])
-    eps = float(W["sched"]["eps_target"])
+    multiscale = "multiscale" in W
+    if multiscale:
+        prm = sk.MultiscaleParams(**W["multiscale"])
+        if args.max_fine is not None:
+            prm.max_fine = args.max_fine
+        eps = prm.eps
+        kind = sk.PROF_SPARSE
+    else:
+        sched = sk.Schedule(**W["sched"])
+        eps = float(W["sched"]["eps_target"])
+        kind = sk.PROF_DENSE
     P = sk.Problem(x, y, a, b, scale)
     f = torch.zeros(c.n, dtype=torch.float32, device=dev)
     g = torch.zeros(c.m, dtype=torch.float32, device=dev)
@@ -178,24 +201,34 @@ def main():
         rmax = torch.empty(batch, dtype=torch.float32, device=dev)
         row_ids = torch.arange(c.n, dtype=torch.int64, device=dev)
 
-    def step(timing=False):
+    def step(timing=False, bounded=False):
         f.zero_()
         g.zero_()
-        P.profile_enable(timing)
-        _, _, rep = P.solve(sched, f, g)
+        P.profile_enable(kind if timing else 0)
+        if multiscale:
+            q = prm
+            if bounded and "roofline" in W:
+                q = sk.MultiscaleParams(**{**prm.__dict__, **W["roofline"]})
+            f_, g_, rep = P.solve_multiscale(q, f, g)
+            f.copy_(f_)
+            g.copy_(g_)
+            rep = dict(rep, pairs_evaluated=rep["pairs_evaluated"], seconds=rep["seconds_total"])
+        else:
+            sc = sk.Schedule(**W["roofline"]) if bounded and "roofline" in W else sched
+            _, _, rep = P.solve(sc, f, g)
         kt = P.profile_read() if timing else None
-        P.profile_enable(False)
+        P.profile_enable(0)
         mat = None
         if batch:
             # every plan row, batch by batch; min over rows of the row maxima
-            P.profile_enable(timing)
+            P.profile_enable(sk.PROF_MATERIALIZE if timing else 0)
             lo = torch.full((), float("inf"), device=dev)
             for r0 in range(0, c.n, batch):
                 k = min(batch, c.n - r0)
                 P.materialize_rows(eps, f, g, row_ids[r0:r0 + k], T=T[:k], row_max=rmax[:k])
                 lo = torch.minimum(lo, rmax[:k].min())
             mat = (lo, P.profile_read() if timing else None)
-            P.profile_enable(False)
+            P.profile_enable(0)
         return rep, kt, mat
 
     for _ in range(args.warmup):
@@ -212,15 +245,16 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    # second timed region for the roofline: the same K steps with a HIP event
-    # pair around every pair-kernel (and materializer) launch on the library's
-    # stream; the events add a few microseconds per launch, so they stay out of
-    # the first region
+    # second timed region for the roofline: the same steps (workloads 4 and 5:
+    # a bounded run of the same kernels) with a HIP event pair around every
+    # pair-kernel (and materializer) launch on the library's stream; the
+    # events add a few microseconds per launch, so they stay out of the first
+    # region
     kernel_ms, launches, kpairs = 0.0, 0, 0.0
     mat_ms, mat_launches, mat_pairs = 0.0, 0, 0.0
     if not args.no_kernel_timing:
         for _ in range(args.steps):
-            _, kt, mat = step(timing=True)
+            _, kt, mat = step(timing=True, bounded=True)
             kernel_ms += kt[0]
             launches += kt[1]
             kpairs += kt[2]
@@ -253,15 +287,21 @@ def main():
             "m": c.m,
             "d": c.d,
             "cost_scale": scale,
-            "step": "one solve from zero potentials to the stop test"
+            "step": ("one multiscale solve (Morton order, cells, coarse solve, lift, fine loop) to the "
+                     "certified stop" if multiscale else "one solve from zero potentials to the stop test")
                     + (", then all plan rows materialized" if batch else ""),
         },
         "wall_time_to_residual_s": sum(r[0]["seconds"] for r in reps) / len(reps),
-        "halfsteps_per_solve": last["halfsteps"],
-        "iters_per_solve": last["iters"],
-        "final_row_l1": last["row_l1"],
-        "final_col_l1": last["col_l1"],
     }
+    if multiscale:
+        for k in ("certified", "coarse_iters", "fine_updates", "ncells_x", "ncells_y", "last_tiles", "R_A_row",
+                  "R_A_col", "omega", "seconds_sort", "seconds_coarse", "seconds_lift", "seconds_fine"):
+            out[k] = last[k]
+    else:
+        out.update(halfsteps_per_solve=last["halfsteps"], iters_per_solve=last["iters"],
+                   final_row_l1=last["row_l1"], final_col_l1=last["col_l1"])
+    if "roofline" in W and timed:
+        out["roofline_region"] = ("bounded run of the same kernels: " + json.dumps(W["roofline"]))
     if batch:
         out["min_row_max"] = float(reps[-1][2][0])
     mfma = c.d > 8
@@ -287,7 +327,7 @@ def main():
                 "kernel": f"k_lse_mfma<{kp}>",
             }
         else:
-            kname = f"k_lse_valu<{c.d},true>"
+            kname = f"k_lse_sparse<{c.d},true>" if multiscale else f"k_lse_valu<{c.d},true>"
             ops = ops_per_pair(c.d)
             achieved = kpairs * ops / (kernel_ms * 1e-3)
             out["roofline"] = {

@@ -252,13 +252,20 @@ typedef struct {
 int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
                               float* f, float* g, sinkhorn_multiscale_report* rep);
 
-/* Measurement hook. With enable = 1, every later launch of a pair-loop kernel
- * (the dense, MFMA or sparse reduction over point pairs) is bracketed by two
- * HIP events recorded on the handle's stream; enable = 0 stops recording.
+/* Measurement hook. `kinds` is a bit set of the kernels to time: every later
+ * launch of a selected kernel is bracketed by two HIP events recorded on the
+ * handle's stream; 0 stops recording.
+ *   SINKHORN_PROF_DENSE        dense pair-loop reductions (VALU and MFMA)
+ *   SINKHORN_PROF_SPARSE       sparse (block-masked) pair-loop reductions
+ *   SINKHORN_PROF_MATERIALIZE  plan-row materializer
  * sinkhorn_profile_read synchronizes the stream and returns (host pointers,
  * any may be NULL) the summed event time of the recorded launches in ms, their
- * number, and the point pairs they evaluated; it then clears the record. */
-int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t enable);
+ * number, and the point pairs (materializer: entries) they evaluated; it then
+ * clears the record. */
+#define SINKHORN_PROF_DENSE 1
+#define SINKHORN_PROF_SPARSE 2
+#define SINKHORN_PROF_MATERIALIZE 4
+int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t kinds);
 int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launches,
                           double* pairs);
 

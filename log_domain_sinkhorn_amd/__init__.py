@@ -44,6 +44,11 @@ ERR_NONFINITE = -5
 ERR_MASS = -6
 ERR_UNSUPPORTED = -7
 
+# kernel kinds for Problem.profile_enable (SINKHORN_PROF_* in sinkhorn.h)
+PROF_DENSE = 1
+PROF_SPARSE = 2
+PROF_MATERIALIZE = 4
+
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -417,9 +422,10 @@ class Problem:
                "sparse_halfstep_g")
         return out, (res.value if res is not None else None)
 
-    def profile_enable(self, enable: bool = True):
-        """Bracket every later pair-loop kernel launch with HIP events."""
-        _check(lib().sinkhorn_profile_enable(self._h, int(bool(enable))), "profile_enable")
+    def profile_enable(self, kinds: int = PROF_DENSE):
+        """Bracket every later launch of the selected kernel kinds (PROF_*
+        bits; 0 stops) with HIP events on the library's stream."""
+        _check(lib().sinkhorn_profile_enable(self._h, int(kinds)), "profile_enable")
 
     def profile_read(self):
         """(kernel_ms, launches, pairs) recorded since the last read (syncs)."""

@@ -43,8 +43,8 @@ void check_hip(hipError_t e, const char* what) {
   }
 }
 
-void prof_begin(sinkhorn_problem* p) {
-  if (!p->prof) return;
+void prof_begin(sinkhorn_problem* p, int32_t kind) {
+  if (!(p->prof & kind)) return;
   if (p->prof_ev.size() < 2 * (p->prof_used + 1)) {
     for (int k = 0; k < 2; ++k) {
       hipEvent_t e;
@@ -55,8 +55,8 @@ void prof_begin(sinkhorn_problem* p) {
   SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used], p->stream));
 }
 
-void prof_end(sinkhorn_problem* p, double pairs) {
-  if (!p->prof) return;
+void prof_end(sinkhorn_problem* p, int32_t kind, double pairs) {
+  if (!(p->prof & kind)) return;
   SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used + 1], p->stream));
   ++p->prof_used;
   p->prof_pairs += pairs;
@@ -448,10 +448,10 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
 
 extern "C" {
 
-int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t enable) {
+int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t kinds) {
   return guard([&] {
     require(p != nullptr, "null handle");
-    p->prof = enable != 0;
+    p->prof = kinds;
     return SINKHORN_OK;
   });
 }

@@ -490,9 +490,9 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
       default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
     }
   };
-  prof_begin(p);
+  prof_begin(p, SINKHORN_PROF_SPARSE);
   launch(A, shifted);
-  prof_end(p, pairs);
+  prof_end(p, SINKHORN_PROF_SPARSE, pairs);
   if (shifted) {  // exact recompute of flagged tiles (the other workgroups exit at once)
     SparseArgs E = A;
     E.fallback = 1;

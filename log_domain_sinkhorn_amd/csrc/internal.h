@@ -115,7 +115,7 @@ struct sinkhorn_problem {
   float* gbuf[2] = {nullptr, nullptr};
   hipEvent_t ev = nullptr;
   // measurement hook: event pairs around pair-loop kernel launches
-  bool prof = false;
+  int32_t prof = 0;                 // SINKHORN_PROF_* kinds being timed
   std::vector<hipEvent_t> prof_ev;  // 2 per launch, reused across reads
   size_t prof_used = 0;             // launches recorded since the last read
   double prof_pairs = 0.0;
@@ -129,8 +129,8 @@ void fill_f32(float* v, int64_t count, float value, hipStream_t st);
 void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st);
 
 // measurement hook (api.hip): call around a pair-loop kernel launch
-void prof_begin(sinkhorn_problem* p);
-void prof_end(sinkhorn_problem* p, double pairs);
+void prof_begin(sinkhorn_problem* p, int32_t kind);
+void prof_end(sinkhorn_problem* p, int32_t kind, double pairs);
 
 // dense.hip
 int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,

@@ -296,7 +296,7 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
   hipLaunchKernelGGL(k_row_terms, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream, rows,
                      row0, k, p->X.w, f, mf ? p->X.norm2 : nullptr, lam, kappa, P, live, keys);
   SK_LAUNCH_CHECK();
-  prof_begin(p);
+  prof_begin(p, SINKHORN_PROF_MATERIALIZE);
   if (mf) {
     switch (p->kpad) {
 #define SK_KP(v) case v: launch_mfma<v>(p, rows, row0, k, P, 2.0 * kappa, T, keys); break;
@@ -318,7 +318,7 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
       default: fail(SINKHORN_ERR_UNSUPPORTED, "materializer: unsupported d");
     }
   }
-  prof_end(p, (double)k * (double)p->m);
+  prof_end(p, SINKHORN_PROF_MATERIALIZE, (double)k * (double)p->m);
 }
 
 // Column terms for this eps and g: the MFMA path writes H'_j into slot d of y,

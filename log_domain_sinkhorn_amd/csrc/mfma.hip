@@ -245,10 +245,10 @@ MPlan mplan(int64_t nrows, int64_t ncols) {
 
 template <int KP>
 void launch_kp(sinkhorn_problem* p, const MfmaArgs& A, int64_t blocks, double pairs) {
-  prof_begin(p);
+  prof_begin(p, SINKHORN_PROF_DENSE);
   hipLaunchKernelGGL((k_lse_mfma<KP>), dim3((uint32_t)blocks), dim3(256), 0, p->stream, A);
   SK_LAUNCH_CHECK();
-  prof_end(p, pairs);
+  prof_end(p, SINKHORN_PROF_DENSE, pairs);
 }
 
 }  // namespace
