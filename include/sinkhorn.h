@@ -252,6 +252,27 @@ typedef struct {
 int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
                               float* f, float* g, sinkhorn_multiscale_report* rep);
 
+/* Barycentric projection of plan rows and the source-coordinate gradient
+ * (FlashSinkhorn 2, §A.2): with the target side and g held fixed,
+ *   T_i    = sum_j pi_ij y_j / sum_j pi_ij
+ *          = sum_j w_ij y_j / sum_j w_ij,   w_ij = b_j exp((g_j - C_ij)/eps)
+ *   grad_i = 2 s a_i (x_i - T_i)            (the derivative in x_i, C = s||x - y||^2)
+ * The row factor of the plan cancels, so only g enters; f_hint (device [n],
+ * nullable) is used only to choose each row's shift in the streaming sum (the
+ * f-step potential of g is best; NULL runs the running-max loop). T and grad
+ * (device, [n][d] row-major fp32, caller order) may each be NULL, not both.
+ * d <= 8; ERR_UNSUPPORTED otherwise. Synchronizes the stream. */
+int sinkhorn_barycentric(sinkhorn_problem* p, double eps, const float* g, const float* f_hint,
+                         float* T, float* grad);
+
+/* The same on the block mask (FlashSinkhorn 2, §A.4, masked gradient): row
+ * block I of B stored points averages over the columns of its admitted tiles
+ * (ptr/idx as from sinkhorn_block_screen; all columns for a block with none).
+ * B a multiple of 128 (at most 1024), d <= 3. */
+int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
+                                const float* f_hint, int32_t B, const int64_t* ptr,
+                                const int32_t* idx, float* T, float* grad);
+
 /* Measurement hook. `kinds` is a bit set of the kernels to time: every later
  * launch of a selected kernel is bracketed by two HIP events recorded on the
  * handle's stream; 0 stops recording.

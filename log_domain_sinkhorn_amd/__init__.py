@@ -138,6 +138,8 @@ _SIGS = {
     "sinkhorn_block_screen": ([_p, _f64, _p, _p, _i32, _f64, _i32, _p, _p, _i64, _p], _i32),
     "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_g": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
+    "sinkhorn_barycentric": ([_p, _f64, _p, _p, _p, _p], _i32),
+    "sinkhorn_sparse_barycentric": ([_p, _f64, _p, _p, _i32, _p, _p, _p, _p], _i32),
     "sinkhorn_solve_multiscale": ([_p, _p, _p, _p, _p], _i32),
     "sinkhorn_profile_enable": ([_p, _i32], _i32),
     "sinkhorn_profile_read": ([_p, _p, _p, _p], _i32),
@@ -421,6 +423,41 @@ class Problem:
                                                 ctypes.byref(res) if res is not None else None),
                "sparse_halfstep_g")
         return out, (res.value if res is not None else None)
+
+    def barycentric(self, eps, g, f_hint=None, T=None, grad=None, want_T=True, want_grad=True):
+        """(T, grad): barycentric projection of the plan rows and the source
+        gradient 2 s a_i (x_i - T_i), [n, d] fp32 each (None when not wanted).
+        f_hint, the f-step potential of g, only speeds up the loop."""
+        self._pot(g, self.m, "g")
+        if f_hint is not None:
+            self._pot(f_hint, self.n, "f_hint")
+        T, grad = self._bary_out(T, grad, want_T, want_grad)
+        _check(lib().sinkhorn_barycentric(self._h, float(eps), _ptr(g), _ptr(f_hint), _ptr(T), _ptr(grad)),
+               "barycentric")
+        return T, grad
+
+    def sparse_barycentric(self, eps, g, B, ptr, idx, f_hint=None, T=None, grad=None, want_T=True,
+                           want_grad=True):
+        """The projection and gradient restricted to the admitted tiles."""
+        self._pot(g, self.m, "g")
+        if f_hint is not None:
+            self._pot(f_hint, self.n, "f_hint")
+        T, grad = self._bary_out(T, grad, want_T, want_grad)
+        _check(lib().sinkhorn_sparse_barycentric(self._h, float(eps), _ptr(g), _ptr(f_hint), int(B), _ptr(ptr),
+                                                 _ptr(idx), _ptr(T), _ptr(grad)), "sparse_barycentric")
+        return T, grad
+
+    def _bary_out(self, T, grad, want_T, want_grad):
+        shape = (self.n, self.d)
+        if T is None and want_T:
+            T = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif T is not None:
+            _dev(T, torch.float32, "T", shape)
+        if grad is None and want_grad:
+            grad = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif grad is not None:
+            _dev(grad, torch.float32, "grad", shape)
+        return T, grad
 
     def profile_enable(self, kinds: int = PROF_DENSE):
         """Bracket every later launch of the selected kernel kinds (PROF_*

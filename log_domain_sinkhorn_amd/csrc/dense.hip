@@ -323,6 +323,22 @@ void launch_reduce(sinkhorn_problem* p, int64_t count) {
   SK_LAUNCH_CHECK();
 }
 
+SplitInfo dense_split(sinkhorn_problem* p, int64_t nrows, int64_t ncols) {
+  LseArgs A;
+  switch (p->d) {
+    case 1: plan_split(A, nrows, ncols, resident_slots<1>(p), 1); break;
+    case 2: plan_split(A, nrows, ncols, resident_slots<2>(p), 2); break;
+    case 3: plan_split(A, nrows, ncols, resident_slots<3>(p), 3); break;
+    case 4: plan_split(A, nrows, ncols, resident_slots<4>(p), 4); break;
+    case 5: plan_split(A, nrows, ncols, resident_slots<5>(p), 5); break;
+    case 6: plan_split(A, nrows, ncols, resident_slots<6>(p), 6); break;
+    case 7: plan_split(A, nrows, ncols, resident_slots<7>(p), 7); break;
+    case 8: plan_split(A, nrows, ncols, resident_slots<8>(p), 8); break;
+    default: fail(SINKHORN_ERR_UNSUPPORTED, "VALU kernels support d <= 8");
+  }
+  return SplitInfo{A.G, A.cps, A.nchunks, A.tiles};
+}
+
 int64_t row_groups(int64_t rows) {
   const int64_t tiles = (rows + kRowsPerTile - 1) / kRowsPerTile;
   const int64_t merge_blocks = (rows + 255) / 256;

@@ -133,6 +133,13 @@ void prof_begin(sinkhorn_problem* p, int32_t kind);
 void prof_end(sinkhorn_problem* p, int32_t kind, double pairs);
 
 // dense.hip
+// Column split of the dense VALU pair kernels for nrows x ncols: G splits of
+// cps chunks over nchunks chunks of kChunk columns, tiles of 128 rows.
+struct SplitInfo {
+  int32_t G;
+  int64_t cps, nchunks, tiles;
+};
+SplitInfo dense_split(sinkhorn_problem* p, int64_t nrows, int64_t ncols);
 int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_padded,
                               int64_t ncols);
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,

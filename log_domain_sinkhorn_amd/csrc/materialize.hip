@@ -110,8 +110,10 @@ __global__ __launch_bounds__(256) void k_materialize_valu(
 
 // MFMA path (9 <= d <= 63): A = selected x rows (slot d := 1), B = column tile
 // of y from LDS (slot d = H'_j), D[i][j] = x_i . y_j + H'_j, E = 2 kappa D + P_i.
-// A wave owns 2 tiles of 32 rows; lane (l32, kh) holds rows 8(r/4) + 4kh + r%4
-// of each tile at column l32, so the T stores are 128-byte row segments.
+// A wave owns one tile of 32 rows (so the A fragment, accumulators, row terms
+// and row maxima of a lane stay small enough for several waves per SIMD);
+// lane (l32, kh) holds rows 8(r/4) + 4kh + r%4 at column l32, so the T stores
+// are 128-byte row segments.
 template <int KP>
 __global__ __launch_bounds__(256) void k_materialize_mfma(
     const float* __restrict__ X, const float* __restrict__ Y, int32_t d, int64_t m,
@@ -123,35 +125,31 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
   constexpr int NV4 = 32 * KP / 4;
   constexpr int PER = (NV4 + 255) / 256;
   __shared__ float sY[2][32 * LW];
+  __shared__ double sP[4][32];  // row terms of each wave's 32 rows
   const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)G);
   const int64_t rt = blockIdx.x / (uint32_t)G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int kh = lane >> 5;
-  const int64_t rbase = rt * 256 + wave * 64;  // first selected row of this wave
+  const int64_t rbase = rt * 128 + wave * 32;  // first selected row of this wave
+  if (kh == 0) sP[wave][l32] = rbase + l32 < k ? P[rbase + l32] : -INFINITY;
 
-  float ax[2][KH];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t rr = rbase + it * 32 + l32;
+  float ax[KH];
+  {
+    const int64_t rr = rbase + l32;
     const int64_t i = rr < k ? (rows ? rows[rr] : row0 + rr) : -1;
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int c = 2 * kk + kh;
-      ax[it][kk] = i < 0 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
+      ax[kk] = i < 0 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
     }
   }
-  double prow[2][16];
-  float emax[2][16];
+  float emax[16];
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
-      prow[it][r] = rr < k ? P[rr] : -INFINITY;
-      emax[it][r] = -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) emax[r] = -INFINITY;
+  const int nrows = rbase + 32 <= k ? 32 : (int)(k - rbase);  // rows of this wave that exist
+  float* Tw = (T && nrows > 0) ? T + (rbase + 4 * kh) * m : nullptr;
 
   const int64_t t0 = (int64_t)gs * tps;
   const int64_t t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
@@ -187,43 +185,34 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
   for (int64_t t = t0; t < t1; ++t) {
     const bool more = t + 1 < t1;
     if (more) gload(t + 1);
-    v16f acc[2];
-    acc[0] = (v16f){};
-    acc[1] = (v16f){};
+    v16f acc = (v16f){};
     const float* ys = &sY[buf][l32 * LW + kh];
 #pragma unroll
-    for (int kk = 0; kk < KH; ++kk) {
-      const float bv = ys[2 * kk];
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[0][kk], bv, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[1][kk], bv, acc[1], 0, 0, 0);
-    }
+    for (int kk = 0; kk < KH; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[kk], ys[2 * kk], acc, 0, 0, 0);
     const int64_t j = t * 32 + l32;
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
-        const float e32 = (float)__builtin_fma(twokappa, (double)acc[it][r], prow[it][r]);
-        if (j < m && rr < k) {
-          if (T) T[rr * m + j] = ex2(e32);
-          emax[it][r] = fmaxf(emax[it][r], e32);
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int lr = 8 * (r / 4) + 4 * kh + (r % 4);  // row within the wave's tile
+      const float e32 = (float)__builtin_fma(twokappa, (double)acc[r], sP[wave][lr]);
+      if (j < m && lr < nrows) {
+        if (Tw) Tw[(int64_t)(8 * (r / 4) + (r % 4)) * m + j] = ex2(e32);
+        emax[r] = fmaxf(emax[r], e32);
       }
+    }
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
   // max over the 32 columns held by the lanes of each half
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
+  for (int r = 0; r < 16; ++r) {
+    float v = emax[r];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = emax[it][r];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-      const int64_t rr = rbase + it * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
-      if (l32 == 0 && rr < k && v > -INFINITY) atomicMax(&keys[rr], okey(v));
-    }
+    for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int64_t rr = rbase + 8 * (r / 4) + 4 * kh + (r % 4);
+    if (l32 == 0 && rr < k && v > -INFINITY) atomicMax(&keys[rr], okey(v));
+  }
 }
 
 // row_max[r] = exp2(E max) from the keys (0 key: no column -> 0).
@@ -273,9 +262,9 @@ void launch_valu(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t
 template <int KP>
 void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t k,
                  const double* P, double twokappa, float* T, uint32_t* keys) {
-  const int64_t rtiles = (k + 255) / 256;
+  const int64_t rtiles = (k + 127) / 128;
   const int64_t ntiles = (p->m + 31) / 32;
-  int64_t want = (1024 + rtiles - 1) / rtiles;
+  int64_t want = (2048 + rtiles - 1) / rtiles;
   const int64_t maxsplit = ntiles / 4 > 1 ? ntiles / 4 : 1;
   if (want > maxsplit) want = maxsplit;
   if (want < 1) want = 1;

@@ -52,13 +52,16 @@ constexpr float kHeadroom = 16.0f;   // shift = estimated LSE - headroom (log2 u
 // scalar loads of the column tile provably unclobbered.
 __device__ __forceinline__ float in_vgpr(float s) { return __shfl(s, (int)(threadIdx.x & 63), 64); }
 
-// Per-lane running sums of kR rows.
-template <bool SHIFT>
+// Per-lane running sums of kR rows; with NA > 0 also the weighted sums
+// sum_j exp2(z_ij - shift) y_jk of the first NA coordinates of the columns
+// (barycentric projection), on the same scale as S.
+template <bool SHIFT, int NA = 0>
 struct RowAcc {
   float S[kR];    // sum, relative to the max (exact) or to the shift (shifted)
   float M[kR];    // exact: running max (log2 units)
   float u[kR];    // shifted: shift / kappa
   double Md[kR];  // shifted: shift = kappa u, exact in fp64
+  float A[kR][NA > 0 ? NA : 1];
 
   // Exact mode: empty sums.
   __device__ __forceinline__ void init_exact() {
@@ -66,6 +69,8 @@ struct RowAcc {
     for (int r = 0; r < kR; ++r) {
       S[r] = 0.0f;
       M[r] = -FLT_MAX;
+#pragma unroll
+      for (int k = 0; k < NA; ++k) A[r][k] = 0.0f;
     }
   }
   // Shifted mode: shift c = -pot * lam - kHeadroom from the previous potential.
@@ -74,6 +79,8 @@ struct RowAcc {
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       S[r] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NA; ++k) A[r][k] = 0.0f;
       const float c = -pot[r] * lam - kHeadroom;
       u[r] = c * inv_kappa;
       Md[r] = -(double)nkappa * (double)u[r];
@@ -88,23 +95,27 @@ struct RowAcc {
 // One wave's pass over column chunks c0, c0 + step, ... < c1 for the lane's
 // kR rows x, accumulated into R. Q is the column side's SoA [D][qs], H its
 // column term; both must stay unwritten during the kernel (scalar loads).
-template <int D, bool SHIFT>
-__device__ __forceinline__ void pair_pass(RowAcc<SHIFT>& R, const float* __restrict__ Q,
+template <int D, bool SHIFT, int NA = 0>
+__device__ __forceinline__ void pair_pass(RowAcc<SHIFT, NA>& R, const float* __restrict__ Q,
                                           const float* __restrict__ H, int64_t qs, float nk,
                                           const float (&x)[kR][D], int64_t c0, int64_t c1,
                                           int64_t step) {
   const float nkv = in_vgpr(nk);
   const double kd = -(double)nk;
-  for (int64_t c = c0; c < c1; c += step) {
-    const int64_t j0 = c * kChunk;
+  // chunk pointers advanced by a uniform stride: the addresses stay scalar
+  const int32_t niter = c1 > c0 ? (int32_t)((c1 - c0 + step - 1) / step) : 0;
+  const float* qc = Q + c0 * kChunk;
+  const float* hc = H + c0 * kChunk;
+  const int64_t adv = step * kChunk;
+  for (int32_t it = 0; it < niter; ++it, qc += adv, hc += adv) {
     float yv[D][kChunk];
     float hv[kChunk];
 #pragma unroll
     for (int k = 0; k < D; ++k)
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = Q[k * qs + j0 + jj];
+      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = qc[k * qs + jj];
 #pragma unroll
-    for (int jj = 0; jj < kChunk; ++jj) hv[jj] = H[j0 + jj];
+    for (int jj = 0; jj < kChunk; ++jj) hv[jj] = hc[jj];
 
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
@@ -121,29 +132,68 @@ __device__ __forceinline__ void pair_pass(RowAcc<SHIFT>& R, const float* __restr
           }
           z[jj] = __builtin_fmaf(q, nkv, hv[jj]);
         }
-        float acc = ex2(z[0]);
+        if constexpr (NA == 0) {
+          float acc = ex2(z[0]);
 #pragma unroll
-        for (int jj = 1; jj < kChunk; ++jj) acc += ex2(z[jj]);
-        const bool big = !(acc <= kBig);
-        if (__builtin_amdgcn_ballot_w64(big) != 0) {
-          // exact redo of this chunk for the lanes whose sum ran away
-          float cm = z[0];
+          for (int jj = 1; jj < kChunk; ++jj) acc += ex2(z[jj]);
+          const bool big = !(acc <= kBig);
+          if (__builtin_amdgcn_ballot_w64(big) != 0) {
+            // exact redo of this chunk for the lanes whose sum ran away
+            float cm = z[0];
 #pragma unroll
-          for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
-          float delta = 0.0f;
-          if (big) {
-            const float un = (float)((R.Md[r] + (double)cm) / kd);
-            const double Mn = kd * (double)un;
-            delta = (float)(Mn - R.Md[r]);
-            R.u[r] = un;
-            R.Md[r] = Mn;
+            for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
+            float delta = 0.0f;
+            if (big) {
+              const float un = (float)((R.Md[r] + (double)cm) / kd);
+              const double Mn = kd * (double)un;
+              delta = (float)(Mn - R.Md[r]);
+              R.u[r] = un;
+              R.Md[r] = Mn;
+            }
+            float acc2 = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < kChunk; ++jj) acc2 += ex2(z[jj] - delta);
+            R.S[r] = big ? __builtin_fmaf(R.S[r], ex2(-delta), acc2) : R.S[r] + acc;
+          } else {
+            R.S[r] += acc;
           }
-          float acc2 = 0.0f;
-#pragma unroll
-          for (int jj = 0; jj < kChunk; ++jj) acc2 += ex2(z[jj] - delta);
-          R.S[r] = big ? __builtin_fmaf(R.S[r], ex2(-delta), acc2) : R.S[r] + acc;
         } else {
+          // the same, keeping every term for the weighted coordinate sums
+          float e[kChunk];
+#pragma unroll
+          for (int jj = 0; jj < kChunk; ++jj) e[jj] = ex2(z[jj]);
+          float acc = e[0];
+#pragma unroll
+          for (int jj = 1; jj < kChunk; ++jj) acc += e[jj];
+          const bool big = !(acc <= kBig);
+          if (__builtin_amdgcn_ballot_w64(big) != 0) {
+            float cm = z[0];
+#pragma unroll
+            for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
+            float delta = 0.0f;
+            if (big) {
+              const float un = (float)((R.Md[r] + (double)cm) / kd);
+              const double Mn = kd * (double)un;
+              delta = (float)(Mn - R.Md[r]);
+              R.u[r] = un;
+              R.Md[r] = Mn;
+              acc = 0.0f;
+#pragma unroll
+              for (int jj = 0; jj < kChunk; ++jj) {
+                e[jj] = ex2(z[jj] - delta);
+                acc += e[jj];
+              }
+              const float sc = ex2(-delta);
+              R.S[r] *= sc;
+#pragma unroll
+              for (int k = 0; k < NA; ++k) R.A[r][k] *= sc;
+            }
+          }
           R.S[r] += acc;
+#pragma unroll
+          for (int k = 0; k < NA; ++k)
+#pragma unroll
+            for (int jj = 0; jj < kChunk; ++jj) R.A[r][k] = __builtin_fmaf(e[jj], yv[k][jj], R.A[r][k]);
         }
       } else {
 #pragma unroll
@@ -161,10 +211,28 @@ __device__ __forceinline__ void pair_pass(RowAcc<SHIFT>& R, const float* __restr
 #pragma unroll
         for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
         const float Mn = fmaxf(R.M[r], cm);
-        float acc = 0.0f;
+        if constexpr (NA == 0) {
+          float acc = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) acc += ex2(z[jj] - Mn);
-        R.S[r] = __builtin_fmaf(R.S[r], ex2(R.M[r] - Mn), acc);
+          for (int jj = 0; jj < kChunk; ++jj) acc += ex2(z[jj] - Mn);
+          R.S[r] = __builtin_fmaf(R.S[r], ex2(R.M[r] - Mn), acc);
+        } else {
+          const float sc = ex2(R.M[r] - Mn);
+          float acc = 0.0f;
+          float t[NA];
+#pragma unroll
+          for (int k = 0; k < NA; ++k) t[k] = R.A[r][k] * sc;
+#pragma unroll
+          for (int jj = 0; jj < kChunk; ++jj) {
+            const float e = ex2(z[jj] - Mn);
+            acc += e;
+#pragma unroll
+            for (int k = 0; k < NA; ++k) t[k] = __builtin_fmaf(e, yv[k][jj], t[k]);
+          }
+          R.S[r] = __builtin_fmaf(R.S[r], sc, acc);
+#pragma unroll
+          for (int k = 0; k < NA; ++k) R.A[r][k] = t[k];
+        }
         R.M[r] = Mn;
       }
     }
@@ -200,8 +268,8 @@ struct TileLds {
 
 // Merge of the kW waves' (max, sum) through LDS in wave order; thread t < 128
 // gets row t of the tile (fp64 max and sum).
-template <bool SHIFT>
-__device__ __forceinline__ void merge_waves(TileLds& L, int wave, int lane, const RowAcc<SHIFT>& R,
+template <bool SHIFT, int NA>
+__device__ __forceinline__ void merge_waves(TileLds& L, int wave, int lane, const RowAcc<SHIFT, NA>& R,
                                             double& mx, double& sum) {
 #pragma unroll
   for (int r = 0; r < kR; ++r) {

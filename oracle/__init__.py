@@ -20,6 +20,8 @@ Sources (cited by page title and section in each module):
     the resolved cost scale and the ``min_row`` threshold.
   * POT pull request #868 (N-D convolutional barycenters): the all -inf
     row convention of a log-sum-exp.
+  * FlashSinkhorn 2, §A.2 and §A.4: the barycentric projection of plan rows
+    and the source-coordinate gradient (``bary``).
 
 Pinning status: every public function is pinned by a CPU test in
 ``tests/test_oracle_*.py`` (closed forms, brute force on tiny inputs,
@@ -51,3 +53,4 @@ from .blocks import (  # noqa: F401
     sparse_residuals,
 )
 from .fs2 import FS2Params, cells, fs2_solve, lift  # noqa: F401
+from .bary import barycentric_rows, coordinate_gradient, sparse_barycentric_rows  # noqa: F401
