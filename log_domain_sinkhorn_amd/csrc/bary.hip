@@ -33,7 +33,8 @@ struct BaryArgs {
   float nkappa;     // -s log2(e) / eps
   int64_t nchunks;  // column chunks
   int64_t tiles;    // row tiles
-  int32_t G;        // dense: column splits
+  int32_t G;        // dense: column splits (a power of two)
+  int32_t glog;     // dense: log2 G
   int64_t cps;      // dense: chunks per split
   double* Mp;       // dense: [G][np] partial max / shift
   float* Sp;        // dense: [G][np] partial sum
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void k_bary_valu(BaryArgs A, const float*
                                                        float* __restrict__ Sp,
                                                        float* __restrict__ Ap) {
   __shared__ BaryLds<D> L;
-  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)A.G);
-  const int64_t tile = blockIdx.x / (uint32_t)A.G;
+  const int32_t gs = (int32_t)(blockIdx.x & (uint32_t)(A.G - 1));
+  const int64_t tile = blockIdx.x >> A.glog;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   float x[kR][D];
@@ -279,6 +280,7 @@ template <int D>
 void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
   const SplitInfo sp = dense_split(p, p->n, p->m);
   A.G = sp.G;
+  A.glog = sp.glog;
   A.cps = sp.cps;
   A.nchunks = sp.nchunks;
   A.tiles = sp.tiles;

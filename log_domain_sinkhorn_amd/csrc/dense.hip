@@ -38,7 +38,8 @@ struct LseArgs {
   float nkappa;         // -s log2(e) / eps
   int64_t nchunks;      // column chunks of kChunk points
   int64_t tiles;        // row tiles of kRowsPerTile rows
-  int32_t G;            // column splits: workgroup w works on tile w / G, split w % G
+  int32_t G;            // column splits (a power of two): workgroup w works on tile w / G, split w % G
+  int32_t glog;         // log2 G
   int64_t cps;          // chunks per split
   double* Mp;           // [G][np] partial shift / max
   float* Sp;            // [G][np] partial sum
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(LseArgs A, const float* _
                                                       double* __restrict__ Mp,
                                                       float* __restrict__ Sp) {
   __shared__ TileLds L;
-  const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)A.G);
-  const int64_t tile = blockIdx.x / (uint32_t)A.G;
+  const int32_t gs = (int32_t)(blockIdx.x & (uint32_t)(A.G - 1));
+  const int64_t tile = blockIdx.x >> A.glog;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   float x[kR][D];
@@ -221,13 +222,14 @@ int64_t resident_slots(sinkhorn_problem* p) {
 constexpr int64_t kXcds = 8;
 constexpr int64_t kL2Slice = 2 << 20;  // column bytes an XCD's L2 keeps comfortably
 
-// Column splits G per row tile: at least 4 chunks per wave (1 when the tiles
-// are too few to fill the chip), at most 64. The workgroups run in rounds of
-// `slots` and finish unevenly, so aim at three rounds or more for the load to
-// even out. Workgroups are dealt to the XCDs in turn, so a G that is a
-// multiple of 8 gives each XCD its own column splits: used whenever the
-// column data would not fit an XCD's L2 whole, and preferred whenever G
-// reaches 8 anyway.
+// Column splits G per row tile, a power of two (the kernels split the block
+// index with a mask and a shift): at least 4 chunks per wave (1 when the
+// tiles are too few to fill the chip), at most 64. The workgroups run in
+// rounds of `slots` and finish unevenly, so aim at three rounds or more for
+// the load to even out. Workgroups are dealt to the XCDs in turn, so with G
+// a multiple of 8 each XCD streams its own column splits: preferred whenever
+// the column data would not fit an XCD's L2 whole, or G reaches 8 anyway.
+// Trailing splits may be empty; they leave an empty partial.
 int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int d) {
   A.nchunks = (ncols + kChunk - 1) / kChunk;
   A.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
@@ -238,17 +240,14 @@ int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int 
   if (maxsplit < 1) maxsplit = 1;
   const int64_t want = (3 * slots + A.tiles - 1) / A.tiles;
   const bool big = A.nchunks * kChunk * (int64_t)(d + 1) * 4 > kL2Slice;
-  int64_t G;
-  if (big || want >= kXcds) {
-    G = (want + kXcds - 1) / kXcds * kXcds;
-    if (G > maxsplit) G = maxsplit / kXcds * kXcds;
-    if (G < kXcds) G = maxsplit < kXcds ? maxsplit : kXcds;
-  } else {
-    G = want < maxsplit ? want : maxsplit;
-  }
-  if (G < 1) G = 1;
+  int64_t G = 1;
+  while (2 * G <= maxsplit && G < want) G *= 2;  // smallest power of two >= want, capped
+  if (big && G < kXcds && kXcds <= maxsplit) G = kXcds;
+  int32_t lg = 0;
+  while ((int64_t(1) << lg) < G) ++lg;
+  A.G = (int32_t)G;
+  A.glog = lg;
   A.cps = (A.nchunks + G - 1) / G;
-  A.G = (int32_t)((A.nchunks + A.cps - 1) / A.cps);
   return A.tiles * A.G;
 }
 
@@ -336,7 +335,7 @@ SplitInfo dense_split(sinkhorn_problem* p, int64_t nrows, int64_t ncols) {
     case 8: plan_split(A, nrows, ncols, resident_slots<8>(p), 8); break;
     default: fail(SINKHORN_ERR_UNSUPPORTED, "VALU kernels support d <= 8");
   }
-  return SplitInfo{A.G, A.cps, A.nchunks, A.tiles};
+  return SplitInfo{A.G, A.glog, A.cps, A.nchunks, A.tiles};
 }
 
 int64_t row_groups(int64_t rows) {

@@ -134,9 +134,11 @@ void prof_end(sinkhorn_problem* p, int32_t kind, double pairs);
 
 // dense.hip
 // Column split of the dense VALU pair kernels for nrows x ncols: G splits of
-// cps chunks over nchunks chunks of kChunk columns, tiles of 128 rows.
+// cps chunks over nchunks chunks of kChunk columns (trailing splits may be
+// empty), tiles of 128 rows.
 struct SplitInfo {
-  int32_t G;
+  int32_t G;     // a power of two
+  int32_t glog;  // log2 G
   int64_t cps, nchunks, tiles;
 };
 SplitInfo dense_split(sinkhorn_problem* p, int64_t nrows, int64_t ncols);
