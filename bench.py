@@ -74,20 +74,32 @@ def ops_per_pair(d: int) -> int:
     return 2 * d + 2
 
 
+KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the sources the dense pair kernel is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "log_domain_sinkhorn_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def pmc_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed PMC summary, or None
     when there is none or the kernel source changed since it was taken."""
-    import hashlib
     import re
 
     path = os.path.join(ROOT, "profiles", "k_lse_valu_w2_n20000_d3_pmc.md")
-    src = os.path.join(ROOT, "log_domain_sinkhorn_amd", "csrc", "dense.hip")
     try:
         text = open(path).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_source_digest()
     except OSError:
         return None
-    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+dense_hip_sha256:\s*([0-9a-f]+)\s+kernel:\s*(\S+)", text)
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+kernel_sources_sha256:\s*([0-9a-f]+)\s+kernel:\s*(\S+)", text)
     if not m or m.group(2) != digest or m.group(3) != kernel:
         return None
     return float(m.group(1))
@@ -350,6 +362,26 @@ def main():
                 "write_GBps": wbytes / (mat_ms * 1e-3) / 1e9,
                 "hbm_frac": wbytes / (mat_ms * 1e-3) / HBM_PEAK,
             }
+    if not multiscale and c.d <= 8 and not args.no_kernel_timing:
+        # barycentric projection + source gradient at the solved potentials
+        # (the f-step's loop with d weighted sums: 2d+2 + d VALU per pair)
+        reps_b = 3 if c.n * c.m <= 1e10 else 1
+        P.barycentric(eps, g, f_hint=f)  # first call: module load, buffers
+        torch.cuda.synchronize()
+        P.profile_enable(sk.PROF_BARY)
+        for _ in range(reps_b):
+            P.barycentric(eps, g, f_hint=f)
+        bms, bl, bp = P.profile_read()
+        P.profile_enable(0)
+        bops = ops_per_pair(c.d) + c.d
+        out["barycentric"] = {
+            "launches": bl,
+            "avg_ms": bms / bl,
+            "pair_evals_per_s": bp / (bms * 1e-3),
+            "ops_per_pair": bops,
+            "valu_frac": bp * bops / (bms * 1e-3) / VALU_PEAK_OPS,
+            "kernel": f"k_bary_valu<{c.d},true>",
+        }
     P.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, eps, scale)

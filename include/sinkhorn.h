@@ -261,14 +261,15 @@ int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_par
  * nullable) is used only to choose each row's shift in the streaming sum (the
  * f-step potential of g is best; NULL runs the running-max loop). T and grad
  * (device, [n][d] row-major fp32, caller order) may each be NULL, not both.
- * d <= 8; ERR_UNSUPPORTED otherwise. Synchronizes the stream. */
+ * d <= 8; ERR_UNSUPPORTED otherwise. Asynchronous on the handle's stream. */
 int sinkhorn_barycentric(sinkhorn_problem* p, double eps, const float* g, const float* f_hint,
                          float* T, float* grad);
 
 /* The same on the block mask (FlashSinkhorn 2, §A.4, masked gradient): row
  * block I of B stored points averages over the columns of its admitted tiles
  * (ptr/idx as from sinkhorn_block_screen; all columns for a block with none).
- * B a multiple of 128 (at most 1024), d <= 3. */
+ * B a multiple of 128 (at most 1024), d <= 3. Asynchronous on the handle's
+ * stream (the tile-list check synchronizes it first). */
 int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
                                 const float* f_hint, int32_t B, const int64_t* ptr,
                                 const int32_t* idx, float* T, float* grad);
@@ -279,6 +280,7 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
  *   SINKHORN_PROF_DENSE        dense pair-loop reductions (VALU and MFMA)
  *   SINKHORN_PROF_SPARSE       sparse (block-masked) pair-loop reductions
  *   SINKHORN_PROF_MATERIALIZE  plan-row materializer
+ *   SINKHORN_PROF_BARY         dense barycentric pair kernel
  * sinkhorn_profile_read synchronizes the stream and returns (host pointers,
  * any may be NULL) the summed event time of the recorded launches in ms, their
  * number, and the point pairs (materializer: entries) they evaluated; it then
@@ -286,6 +288,7 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
 #define SINKHORN_PROF_DENSE 1
 #define SINKHORN_PROF_SPARSE 2
 #define SINKHORN_PROF_MATERIALIZE 4
+#define SINKHORN_PROF_BARY 8
 int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t kinds);
 int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launches,
                           double* pairs);

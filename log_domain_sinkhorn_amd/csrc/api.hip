@@ -96,6 +96,7 @@ void problem_free(sinkhorn_problem* p) {
   side_free(p->Y);
   dev_free(p->Mpart);
   dev_free(p->Spart);
+  dev_free(p->bary_part);
   dev_free(p->red_part);
   dev_free(p->tile_flag);
   dev_free(p->ctl);

@@ -285,12 +285,25 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
   A.nchunks = sp.nchunks;
   A.tiles = sp.tiles;
   const int64_t np = p->n;
-  A.Mp = (double*)dev_alloc(sizeof(double) * (size_t)(A.G * np));
-  A.Sp = (float*)dev_alloc(sizeof(float) * (size_t)(A.G * np));
-  A.Ap = (float*)dev_alloc(sizeof(float) * (size_t)(A.G * D * np));
+  // the split partials of the half-step (same plan, so they fit) and a
+  // grown-on-demand buffer for the weighted sums: no allocation per call
+  if (2 * (int64_t)A.G * np > p->part_cap) fail(SINKHORN_ERR_HIP, "partial buffer too small");
+  A.Mp = reinterpret_cast<double*>(p->Mpart);
+  A.Sp = p->Spart;
+  const int64_t need = (int64_t)A.G * D * np;
+  if (need > p->bary_cap) {
+    SK_HIP(hipStreamSynchronize(p->stream));
+    dev_free(p->bary_part);
+    p->bary_part = nullptr;
+    p->bary_cap = 0;
+    p->bary_part = (float*)dev_alloc(sizeof(float) * (size_t)need);
+    p->bary_cap = need;
+  }
+  A.Ap = p->bary_part;
   const bool shifted = A.shift_pot != nullptr;
-  try {
+  {
     const dim3 grid((uint32_t)(A.tiles * A.G));
+    prof_begin(p, SINKHORN_PROF_BARY);
     if (shifted)
       hipLaunchKernelGGL((k_bary_valu<D, true>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H,
                          A.Mp, A.Sp, A.Ap);
@@ -298,20 +311,11 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
       hipLaunchKernelGGL((k_bary_valu<D, false>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H,
                          A.Mp, A.Sp, A.Ap);
     SK_LAUNCH_CHECK();
+    prof_end(p, SINKHORN_PROF_BARY, (double)p->n * (double)p->m);
     hipLaunchKernelGGL(k_bary_merge<D>, dim3((uint32_t)A.tiles), dim3(kThreads), 0, p->stream, A,
                        (int32_t)shifted);
     SK_LAUNCH_CHECK();
-    SK_HIP(hipStreamSynchronize(p->stream));
-  } catch (...) {
-    (void)hipStreamSynchronize(p->stream);
-    dev_free(A.Mp);
-    dev_free(A.Sp);
-    dev_free(A.Ap);
-    throw;
   }
-  dev_free(A.Mp);
-  dev_free(A.Sp);
-  dev_free(A.Ap);
 }
 
 template <int D>
@@ -327,7 +331,6 @@ void sparse_bary(sinkhorn_problem* p, BaryArgs& A) {
     hipLaunchKernelGGL((k_bary_sparse<D, false>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H);
   }
   SK_LAUNCH_CHECK();
-  SK_HIP(hipStreamSynchronize(p->stream));
 }
 
 void check_args(sinkhorn_problem* p, double eps, const float* g, float* T, float* grad) {

@@ -101,6 +101,8 @@ struct sinkhorn_problem {
   float* Mpart = nullptr;
   float* Spart = nullptr;
   int64_t part_cap = 0;  // floats per partial array
+  float* bary_part = nullptr;  // barycentric weighted-sum partials, grown on demand
+  int64_t bary_cap = 0;        // floats in bary_part
   // residual block partials, arrival counters and the reduced values
   double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
