@@ -252,6 +252,22 @@ typedef struct {
 int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
                               float* f, float* g, sinkhorn_multiscale_report* rep);
 
+/* Sparsified plan (moscot pull request #846: thresholding on the device and
+ * moving only the surviving values and indices): every entry T_ij >= threshold,
+ * as CSR in the caller's row order. row_ptr [n + 1] (device int64) is always
+ * written; col [cap] (device int32 column indices, increasing within a row)
+ * and val [cap] (device fp32 T_ij) when both are given and cap >= nnz. Entries
+ * are computed exactly as sinkhorn_materialize_rows computes them, `batch`
+ * rows at a time (<= 0: 1024; at most 2^28 entries per batch), so only
+ * surviving entries are stored. threshold must be finite and > 0, so rows
+ * without mass keep no entry; with the value sinkhorn_min_row returns, every
+ * row with mass keeps at least its largest entry. nnz_out (host) receives
+ * the count. Returns SINKHORN_ERR_CAPACITY when col/val are given but cap <
+ * nnz (row_ptr and nnz_out are still valid). Synchronizes the stream. */
+int sinkhorn_sparsify(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                      float threshold, int64_t batch, int64_t* row_ptr, int32_t* col, float* val,
+                      int64_t cap, int64_t* nnz_out);
+
 /* Barycentric projection of plan rows and the source-coordinate gradient
  * (FlashSinkhorn 2, §A.2): with the target side and g held fixed,
  *   T_i    = sum_j pi_ij y_j / sum_j pi_ij

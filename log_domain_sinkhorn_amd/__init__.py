@@ -140,6 +140,7 @@ _SIGS = {
     "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_g": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_barycentric": ([_p, _f64, _p, _p, _p, _p], _i32),
+    "sinkhorn_sparsify": ([_p, _f64, _p, _p, ctypes.c_float, _i64, _p, _p, _p, _i64, _p], _i32),
     "sinkhorn_sparse_barycentric": ([_p, _f64, _p, _p, _i32, _p, _p, _p, _p], _i32),
     "sinkhorn_solve_multiscale": ([_p, _p, _p, _p, _p], _i32),
     "sinkhorn_profile_enable": ([_p, _i32], _i32),
@@ -424,6 +425,27 @@ class Problem:
                                                 ctypes.byref(res) if res is not None else None),
                "sparse_halfstep_g")
         return out, (res.value if res is not None else None)
+
+    def sparsify(self, eps, f, g, threshold: float, batch: int = 1024, cap=None):
+        """(row_ptr, col, val): the plan entries >= threshold as CSR (int64,
+        int32, fp32 device tensors). With cap=None the count is taken first
+        (row_ptr only), then the entries are written into buffers of that size."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        row_ptr = torch.empty(self.n + 1, dtype=torch.int64, device=self.device)
+        nnz = _i64()
+        if cap is None:
+            _check(lib().sinkhorn_sparsify(self._h, float(eps), _ptr(f), _ptr(g), float(threshold), int(batch),
+                                           _ptr(row_ptr), None, None, 0, ctypes.byref(nnz)), "sparsify")
+            cap = nnz.value
+        col = torch.empty(max(1, cap), dtype=torch.int32, device=self.device)
+        val = torch.empty(max(1, cap), dtype=torch.float32, device=self.device)
+        st = lib().sinkhorn_sparsify(self._h, float(eps), _ptr(f), _ptr(g), float(threshold), int(batch),
+                                     _ptr(row_ptr), _ptr(col), _ptr(val), int(cap), ctypes.byref(nnz))
+        if st != OK:
+            raise SinkhornError(st, "sparsify")
+        k = nnz.value
+        return row_ptr, col[:k], val[:k]
 
     def barycentric(self, eps, g, f_hint=None, T=None, grad=None, want_T=True, want_grad=True):
         """(T, grad): barycentric projection of the plan rows and the source

@@ -15,6 +15,8 @@
 #include <cmath>
 #include <cstring>
 
+#include <rocprim/device/device_scan.hpp>
+
 #include "internal.h"
 
 namespace sk {
@@ -322,6 +324,58 @@ void column_terms(sinkhorn_problem* p, double eps, const float* g, double* Hd) {
   }
 }
 
+// Sparsify: entries of row r of the batch buffer T [k][m] with T >= thr.
+// One workgroup (256 threads) per row.
+__global__ __launch_bounds__(256) void k_row_count(const float* __restrict__ T, int64_t m, float thr,
+                                                   int64_t* __restrict__ counts) {
+  __shared__ int64_t sc[4];
+  const int64_t r = blockIdx.x;
+  const float* row = T + r * m;
+  int64_t c = 0;
+  for (int64_t j = threadIdx.x; j < m; j += 256) c += row[j] >= thr ? 1 : 0;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[r] = sc[0] + sc[1] + sc[2] + sc[3];
+}
+
+// Writes the surviving entries of row r in increasing column order at
+// ptr[r]: column index and value. Wave ballots give each entry its rank
+// within a 256-column step; LDS carries the wave totals.
+__global__ __launch_bounds__(256) void k_row_fill(const float* __restrict__ T, int64_t m, float thr,
+                                                  const int64_t* __restrict__ ptr,
+                                                  int32_t* __restrict__ col,
+                                                  float* __restrict__ val) {
+  __shared__ int32_t sw[4];
+  const int64_t r = blockIdx.x;
+  const float* row = T + r * m;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int64_t out = ptr[r];
+  for (int64_t j0 = 0; j0 < m; j0 += 256) {
+    const int64_t j = j0 + threadIdx.x;
+    const float v = j < m ? row[j] : 0.0f;
+    const bool keep = j < m && v >= thr;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    if (lane == 0) sw[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int64_t base = out;
+    for (int w = 0; w < wave; ++w) base += sw[w];
+    if (keep) {
+      const int64_t o = base + __builtin_popcountll(bal & below);
+      col[o] = (int32_t)j;
+      val[o] = v;
+    }
+    out += sw[0] + sw[1] + sw[2] + sw[3];
+    __syncthreads();  // sw reuse
+  }
+}
+
+__global__ void k_set_i64(int64_t* p, int64_t v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
 struct Scratch {
   double* P = nullptr;
   double* Hd = nullptr;
@@ -403,18 +457,102 @@ int sinkhorn_min_row(sinkhorn_problem* p, double eps, const float* f, const floa
                          s.keys, s.live, k, best);
       SK_LAUNCH_CHECK();
     }
+    // the value through the device exp2 the plan entries use, so that
+    // "T_ij >= min_row" keeps the largest entry of every row with mass
+    float* v = reinterpret_cast<float*>(s.live);
+    hipLaunchKernelGGL(k_keys_to_max, dim3(1), dim3(256), 0, p->stream, best, (int64_t)1, v);
+    SK_LAUNCH_CHECK();
     uint32_t key = 0;
-    SK_HIP(hipMemcpyAsync(p->host_tmp, best, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+    float val = 0.0f;
+    SK_HIP(hipMemcpyAsync(&p->host_tmp[0], best, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+    SK_HIP(hipMemcpyAsync(&p->host_tmp[1], v, sizeof(float), hipMemcpyDeviceToHost, p->stream));
     SK_HIP(hipStreamSynchronize(p->stream));
-    memcpy(&key, p->host_tmp, sizeof(uint32_t));
-    if (key == 0xffffffffu) {
-      *out = NAN;  // no row carries mass
-    } else {
-      const float e = (key & 0x80000000u) ? __builtin_bit_cast(float, key & 0x7fffffffu)
-                                          : __builtin_bit_cast(float, ~key);
-      *out = key == 0u ? 0.0f : std::exp2(e);
-    }
+    memcpy(&key, &p->host_tmp[0], sizeof(uint32_t));
+    memcpy(&val, &p->host_tmp[1], sizeof(float));
+    *out = key == 0xffffffffu ? NAN : val;  // NaN: no row carries mass
     return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+int sinkhorn_sparsify(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                      float threshold, int64_t batch, int64_t* row_ptr, int32_t* col, float* val,
+                      int64_t cap, int64_t* nnz_out) {
+  try {
+    if (!p || !f || !g || !row_ptr || !nnz_out) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(std::isfinite(threshold) && threshold > 0.0f))
+      fail(SINKHORN_ERR_INVALID_ARG, "threshold must be finite and > 0");
+    if ((col == nullptr) != (val == nullptr)) fail(SINKHORN_ERR_INVALID_ARG, "col and val go together");
+    if (p->m >= ((int64_t)1 << 31)) fail(SINKHORN_ERR_UNSUPPORTED, "column index needs m < 2^31");
+    const int64_t n = p->n, m = p->m;
+    if (batch <= 0) batch = 1024;
+    const int64_t maxb = ((int64_t)1 << 28) / m > 1 ? ((int64_t)1 << 28) / m : 1;  // <= 1 GiB buffer
+    if (batch > maxb) batch = maxb;
+    if (batch > n) batch = n;
+    Scratch s;
+    s.P = (double*)dev_alloc(sizeof(double) * batch);
+    s.keys = (uint32_t*)dev_alloc(sizeof(uint32_t) * batch);
+    if (p->d <= kMaxValuD) s.Hd = (double*)dev_alloc(sizeof(double) * m);
+    float* T = (float*)dev_alloc(sizeof(float) * batch * m);
+    int64_t* counts = nullptr;
+    void* temp = nullptr;
+    auto cleanup = [&] {
+      dev_free(T);
+      dev_free(counts);
+      dev_free(temp);
+    };
+    try {
+      counts = (int64_t*)dev_alloc(sizeof(int64_t) * batch);
+      size_t tb = 0;
+      SK_HIP(rocprim::exclusive_scan(nullptr, tb, counts, row_ptr, (int64_t)0, (size_t)batch,
+                                     rocprim::plus<int64_t>(), p->stream));
+      temp = dev_alloc(tb > 0 ? tb : 1);
+      column_terms(p, eps, g, s.Hd);
+      const bool fill = col != nullptr;
+      int64_t total = 0;
+      for (int64_t r0 = 0; r0 < n; r0 += batch) {
+        const int64_t k = n - r0 < batch ? n - r0 : batch;
+        rows_pass(p, eps, f, nullptr, r0, k, s.P, nullptr, s.keys, s.Hd, T);
+        hipLaunchKernelGGL(k_row_count, dim3((uint32_t)k), dim3(256), 0, p->stream, T, m, threshold,
+                           counts);
+        SK_LAUNCH_CHECK();
+        // row_ptr[r0 .. r0 + k) = total + exclusive prefix of the batch counts
+        SK_HIP(rocprim::exclusive_scan(temp, tb, counts, row_ptr + r0, total, (size_t)k,
+                                       rocprim::plus<int64_t>(), p->stream));
+        int64_t last = 0, cnt = 0;
+        SK_HIP(hipMemcpyAsync(&p->host_tmp[0], row_ptr + r0 + k - 1, sizeof(int64_t),
+                              hipMemcpyDeviceToHost, p->stream));
+        SK_HIP(hipMemcpyAsync(&p->host_tmp[1], counts + k - 1, sizeof(int64_t), hipMemcpyDeviceToHost,
+                              p->stream));
+        SK_HIP(hipStreamSynchronize(p->stream));
+        memcpy(&last, &p->host_tmp[0], sizeof(int64_t));
+        memcpy(&cnt, &p->host_tmp[1], sizeof(int64_t));
+        const int64_t after = last + cnt;
+        if (fill && after <= cap) {
+          hipLaunchKernelGGL(k_row_fill, dim3((uint32_t)k), dim3(256), 0, p->stream, T, m, threshold,
+                             row_ptr + r0, col, val);
+          SK_LAUNCH_CHECK();
+        }
+        total = after;
+      }
+      hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(64), 0, p->stream, row_ptr + n, total);
+      SK_LAUNCH_CHECK();
+      SK_HIP(hipStreamSynchronize(p->stream));
+      *nnz_out = total;
+      cleanup();
+      if (!fill) return SINKHORN_OK;
+      return total <= cap ? SINKHORN_OK : SINKHORN_ERR_CAPACITY;
+    } catch (...) {
+      (void)hipStreamSynchronize(p->stream);
+      cleanup();
+      throw;
+    }
   } catch (const Failure& e) {
     set_last_error(e.msg);
     return e.code;

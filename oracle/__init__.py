@@ -42,6 +42,7 @@ from .dense import (  # noqa: F401
     plan_rows,
     row_residual_identity,
     solve,
+    sparsify,
 )
 from .morton import interleave, morton_codes, morton_order, quantize  # noqa: F401
 from .blocks import (  # noqa: F401

@@ -280,3 +280,25 @@ def min_row(x, y, a, b, f, g, eps: float, scale: float) -> float:
         return plan_rows(x, y, a, b, f, g, eps, scale, live[lo:hi]).max(axis=1)
 
     return float(np.concatenate(_map_chunks(run, live.size, len(y))).min())
+
+
+def sparsify(x, y, a, b, f, g, eps: float, scale: float, threshold: float):
+    """The plan entries >= threshold as CSR (row_ptr int64, col int64, val
+    float64), rows in order and columns increasing within a row.
+
+    moscot pull request #846: rows are thresholded from the materialized plan
+    rows, so only the surviving values and indices are kept; a threshold > 0
+    leaves rows without mass empty.
+    """
+    ptr = [0]
+    cols, vals = [], []
+    for lo, hi in _chunks(len(x), len(y)):
+        T = plan_rows(x, y, a, b, f, g, eps, scale, rows=np.arange(lo, hi))
+        for r in range(T.shape[0]):
+            keep = np.nonzero(T[r] >= threshold)[0]
+            cols.append(keep)
+            vals.append(T[r, keep])
+            ptr.append(ptr[-1] + len(keep))
+    col = np.concatenate(cols) if cols else np.zeros(0, np.int64)
+    val = np.concatenate(vals) if vals else np.zeros(0)
+    return np.asarray(ptr, np.int64), col.astype(np.int64), val

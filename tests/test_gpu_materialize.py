@@ -114,3 +114,41 @@ def test_bad_row_index_is_rejected(sk):
         with pytest.raises(sk.SinkhornError) as ei:
             P.materialize_rows(0.1, z, zg, _t(np.array([3, 100], np.int64)))
         assert ei.value.code == sk.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("w,n,m,d,eps,rule", CASES)
+def test_sparsify_at_min_row_matches_rows_and_oracle(sk, w, n, m, d, eps, rule):
+    """moscot #846 thresholding on the device: the CSR holds exactly the
+    entries of the GPU's own materialized rows that reach min_row (same
+    arithmetic, so bit-exact), every row with mass keeps its largest entry,
+    and against the fp64 oracle the kept set agrees wherever an entry is not
+    within rounding (2e-5 relative) of the threshold."""
+    c = synth.make(w, n=n, m=m, d=d)
+    a = c.a.copy()
+    a[::7] = 0.0
+    a = (a / a.astype(np.float64).sum() * c.b.astype(np.float64).sum()).astype(np.float32)
+    scale = 1.0 if rule == "one" else 1.0 / oracle.mean_sqeuclid(c.x, c.y)
+    rng = np.random.default_rng(8)
+    g = (rng.normal(0, 1, c.m) * eps).astype(np.float32)
+    f = oracle.halfstep_f(c.x, c.y, c.b, g, eps, scale).astype(np.float32)
+    with sk.Problem(_t(c.x), _t(c.y), _t(a), _t(c.b), scale) as P:
+        thr = P.min_row(eps, _t(f), _t(g))
+        ptr, col, val = P.sparsify(eps, _t(f), _t(g), thr, batch=64)
+        T, _ = P.materialize_rows(eps, _t(f), _t(g), _t(np.arange(c.n, dtype=np.int64)))
+        T = T.cpu().numpy()
+        # a too-small capacity: the count and row pointers still come back
+        with pytest.raises(sk.SinkhornError) as ei:
+            P.sparsify(eps, _t(f), _t(g), thr, cap=int(ptr[-1].item()) - 1)
+        assert ei.value.code == sk.ERR_CAPACITY
+    ptr, col, val = ptr.cpu().numpy(), col.cpu().numpy(), val.cpu().numpy()
+    per_row = np.diff(ptr)
+    assert np.all(per_row[a == 0] == 0) and np.all(per_row[a > 0] >= 1)
+    for i in range(c.n):  # bit-exact against the GPU's own rows
+        keep = np.nonzero(T[i] >= thr)[0]
+        assert np.array_equal(col[ptr[i]:ptr[i + 1]], keep), i
+        assert np.array_equal(val[ptr[i]:ptr[i + 1]], T[i, keep]), i
+    ref = oracle.materialize_rows(c.x, c.y, a, c.b, f, g, eps, scale, np.arange(c.n))
+    sure = np.abs(ref - thr) > 2e-5 * thr
+    assert np.array_equal((T >= thr)[sure], (ref >= thr)[sure])
+    kept = T >= thr
+    np.testing.assert_allclose(T[kept], ref[kept], rtol=1e-5)

@@ -186,3 +186,43 @@ def test_solve_fixed_iterations_counts(rng):
     assert res.iters == 7 and res.final_iters == 7
     res = oracle.solve(x, y, a, b, 1.0, Schedule(0.4, 0.1, iters_per_stage=3, fixed_iters=2))
     assert res.iters == 2 * 3 + 2
+
+
+def test_sparsify_matches_a_scipy_csr_of_the_thresholded_plan(rng):
+    """moscot #846: the kept entries are exactly the plan entries >= the
+    threshold; scipy's CSR of the thresholded dense plan is the reference."""
+    from scipy.sparse import csr_matrix
+
+    x, y, a, b = _clouds(rng, 23, 31, 2)
+    f = rng.normal(0, 0.01, 23)
+    g = rng.normal(0, 0.01, 31)
+    eps = 0.02
+    P = oracle.plan_rows(x, y, a, b, f, g, eps, 1.0)
+    thr = float(np.quantile(P, 0.8))
+    ptr, col, val = oracle.sparsify(x, y, a, b, f, g, eps, 1.0, thr)
+    ref = csr_matrix(np.where(P >= thr, P, 0.0))
+    ref.sort_indices()
+    np.testing.assert_array_equal(ptr, ref.indptr)
+    np.testing.assert_array_equal(col, ref.indices)
+    np.testing.assert_allclose(val, ref.data, rtol=0, atol=0)
+
+
+def test_sparsify_at_min_row_keeps_every_row_with_mass(rng):
+    x, y, a, b = _clouds(rng, 30, 26, 3)
+    a = a.astype(np.float64)
+    a[[3, 17]] = 0.0  # rows without mass: no entry, no part in the threshold
+    f = rng.normal(0, 0.02, 30)
+    g = rng.normal(0, 0.02, 26)
+    eps = 0.01
+    thr = oracle.min_row(x, y, a, b, f, g, eps, 1.0)
+    ptr, col, val = oracle.sparsify(x, y, a, b, f, g, eps, 1.0, thr)
+    per_row = np.diff(ptr)
+    assert per_row[3] == 0 and per_row[17] == 0
+    assert np.all(per_row[a > 0] >= 1)
+    # the row that sets the threshold keeps exactly its largest entry
+    P = oracle.plan_rows(x, y, a, b, f, g, eps, 1.0)
+    i = int(np.argmin(np.where(a > 0, P.max(axis=1), np.inf)))
+    assert per_row[i] >= 1 and val[ptr[i]:ptr[i + 1]].max() == P[i].max()
+    # above the largest entry nothing survives
+    ptr, col, val = oracle.sparsify(x, y, a, b, f, g, eps, 1.0, float(P.max()) * 1.5)
+    assert ptr[-1] == 0 and len(col) == 0
