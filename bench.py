@@ -362,6 +362,20 @@ def main():
                 "write_GBps": wbytes / (mat_ms * 1e-3) / 1e9,
                 "hbm_frac": wbytes / (mat_ms * 1e-3) / HBM_PEAK,
             }
+    if batch and not args.no_kernel_timing:
+        # the consumer of the row materializer: sparsify at min_row on the device
+        thr = P.min_row(eps, f, g)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ptr, col, val = P.sparsify(eps, f, g, thr, batch=batch)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        out["sparsify"] = {
+            "threshold": thr,
+            "nnz": int(ptr[-1].item()),
+            "seconds": dt,
+            "note": "count pass, then the entries (two materializations per batch), min_row threshold",
+        }
     if not multiscale and c.d <= 8 and not args.no_kernel_timing:
         # barycentric projection + source gradient at the solved potentials
         # (the f-step's loop with d weighted sums: 2d+2 + d VALU per pair)
