@@ -259,3 +259,34 @@ def test_multiscale_full_size_certified_and_rows_match_oracle(sk):
     err = np.abs(T - ref)
     assert not np.any(err > 1e-5 * ref + 2.0 ** -126), int(np.sum(err > 1e-5 * ref + 2.0 ** -126))
     np.testing.assert_allclose(T.sum(axis=1), ref.sum(axis=1), rtol=1e-5)
+
+
+@pytest.mark.parametrize("d", [1, 2])
+def test_sparse_halfsteps_low_dimensions(sk, d):
+    """The sparse kernels at d = 1 and 2 (clustered points projected to the
+    first d axes, Morton order of that cloud), shifted loop with residual."""
+    n, B, eps = 6000, 128, 1e-3
+    c = synth.make(5, n=n, m=n)
+    x = np.ascontiguousarray(c.x[:, :d])
+    y = np.ascontiguousarray(c.y[:, :d])
+    _, px, _, py = oracle.morton_order(x, y)
+    x, y, a, b = x[px], y[py], c.a[px], c.b[py]
+    rng = np.random.default_rng(11)
+    f, g = _near_plan_potentials(n, eps, rng)
+    NB = (n + B - 1) // B
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, 1e-3 / NB)
+    ptrT, rowT = oracle.screen_transpose(sx, sy, eps, 1.0, 1e-3 / NB)
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        got_ptr, got_col = P.block_screen(eps, _t(f), _t(g), B, 1e-3 / NB)
+        assert np.array_equal(got_ptr.cpu().numpy(), ptr) and np.array_equal(got_col.cpu().numpy(), col)
+        fo, r = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)), f_prev=_t(f))
+        go, _ = P.sparse_halfstep_g(eps, _t(f), B, _t(ptrT), _t(rowT.astype(np.int32)))
+    for got, ref, what in ((fo, oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B), "f"),
+                           (go, oracle.sparse_halfstep_g(x, y, a, f, eps, 1.0, ptrT, rowT, B), "g")):
+        got = got.cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref) / np.maximum(eps, np.abs(ref))
+        assert err.max() <= 1e-5, (what, d, err.max())
+    Rr, _ = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
+    assert r == pytest.approx(Rr, rel=1e-3)

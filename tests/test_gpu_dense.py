@@ -326,3 +326,27 @@ def test_shifted_full_size_workload4_sampled_rows(sk):
         rows = rng.choice(c.n, 128, replace=False)
         f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, 1.0, rows=rows)
         _assert_halfstep(f1.cpu().numpy()[rows], f_ref, eps, "shifted f-step sampled rows")
+
+
+@pytest.mark.parametrize("d", [1, 4, 5, 8])
+@pytest.mark.parametrize("shifted", [False, True], ids=["exact", "shifted"])
+def test_halfsteps_in_other_dimensions(sk, d, shifted):
+    """The VALU kernels for every d <= 8 (the PCA-like generator in d
+    dimensions, cost divided by its mean, ragged sizes)."""
+    c = synth.make(3, n=1100, m=1337, d=d)
+    scale = 1.0 / oracle.mean_sqeuclid(c.x, c.y)
+    eps = 0.02
+    rng = np.random.default_rng(40 + d)
+    g0 = (rng.normal(0, 1, c.m) * eps).astype(np.float32)
+    f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, scale)
+    prev = (f_ref + rng.normal(0, 3 * eps, c.n)).astype(np.float32)  # a rough shift estimate
+    _log(f"halfstep d={d} shifted={shifted}")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), scale) as P:
+        f, r = P.halfstep_f(eps, _t(g0), f_prev=_t(prev) if shifted else None)
+        _assert_halfstep(f.cpu().numpy(), f_ref, eps, f"f-step d={d}")
+        f32 = f_ref.astype(np.float32)
+        g, _ = P.halfstep_g(eps, _t(f32))
+        _assert_halfstep(g.cpu().numpy(), oracle.halfstep_g(c.x, c.y, c.a, f32, eps, scale), eps, f"g-step d={d}")
+        if shifted:  # the fused residual of (prev, g0)
+            ref = oracle.row_residual_identity(c.a, prev, f_ref, eps)
+            assert r == pytest.approx(ref, rel=1e-3)
