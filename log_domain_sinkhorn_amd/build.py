@@ -38,6 +38,10 @@ COMMON = [
     "-ffp-contract=off",
     # no packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the log-sum-exp reads them with
+    # VALU instructions directly (no accvgpr copies) and the unified register
+    # file then holds one more wave per SIMD
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
     "-Wall",

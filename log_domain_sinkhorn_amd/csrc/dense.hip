@@ -356,7 +356,7 @@ int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_p
     case 6: return split_floats<6>(p, nrows, ncols);
     case 7: return split_floats<7>(p, nrows, ncols);
     case 8: return split_floats<8>(p, nrows, ncols);
-    default: return mfma_partial_floats(nrows, ncols);
+    default: return mfma_partial_floats(p, nrows, ncols);
   }
 }
 

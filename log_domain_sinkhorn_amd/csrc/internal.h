@@ -166,7 +166,7 @@ void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double*
 void setup_mfma(sinkhorn_problem* p, const float* x, const float* y);
 void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs);
 void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps);
-int64_t mfma_partial_floats(int64_t nrows, int64_t ncols);
+int64_t mfma_partial_floats(sinkhorn_problem* p, int64_t nrows, int64_t ncols);
 
 // blocks.hip: per-block summaries of a side in its stored order
 constexpr int64_t kGrp = 64;  // blocks per screen group

@@ -229,11 +229,50 @@ struct MPlan {
   int64_t tiles;
 };
 
-MPlan mplan(int64_t nrows, int64_t ncols) {
+// Workgroups of k_lse_mfma<KP> resident on the whole chip at once.
+template <int KP>
+int64_t slots_kp(sinkhorn_problem* p) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_mfma<KP>, 256, 0));
+    per_cu = nb > 0 ? nb : 1;
+  }
+  return (int64_t)per_cu * p->num_cu;
+}
+
+int64_t mfma_slots(sinkhorn_problem* p) {
+  switch (p->kpad) {
+    case 12: return slots_kp<12>(p);
+    case 16: return slots_kp<16>(p);
+    case 20: return slots_kp<20>(p);
+    case 24: return slots_kp<24>(p);
+    case 28: return slots_kp<28>(p);
+    case 32: return slots_kp<32>(p);
+    case 36: return slots_kp<36>(p);
+    case 40: return slots_kp<40>(p);
+    case 44: return slots_kp<44>(p);
+    case 48: return slots_kp<48>(p);
+    case 52: return slots_kp<52>(p);
+    case 56: return slots_kp<56>(p);
+    case 60: return slots_kp<60>(p);
+    case 64: return slots_kp<64>(p);
+    default: fail(SINKHORN_ERR_UNSUPPORTED, "MFMA half-step: unsupported K");
+  }
+}
+
+// Column splits G per 256-row block: enough workgroups for six rounds of the
+// resident slots (every workgroup carries the same number of column tiles,
+// so the last, partly filled round costs at most a sixth), a multiple of 8
+// once it reaches 8 (workgroups are dealt to the 8 XCDs in turn, so each XCD
+// then streams its own column splits), at most 64 and at least 8 column
+// tiles per split.
+MPlan mplan(int64_t nrows, int64_t ncols, int64_t slots) {
   MPlan mp;
   mp.ntiles = (ncols + 31) / 32;
   mp.tiles = (nrows + kRowsPerWG - 1) / kRowsPerWG;
-  int64_t want = (1024 + mp.tiles - 1) / mp.tiles;  // ~4 workgroups per CU
+  int64_t want = (6 * slots + mp.tiles - 1) / mp.tiles;
+  if (want >= 8) want = (want + 7) / 8 * 8;
   const int64_t maxsplit = mp.ntiles / 8 > 1 ? mp.ntiles / 8 : 1;
   if (want > 64) want = 64;
   if (want > maxsplit) want = maxsplit;
@@ -253,8 +292,8 @@ void launch_kp(sinkhorn_problem* p, const MfmaArgs& A, int64_t blocks, double pa
 
 }  // namespace
 
-int64_t mfma_partial_floats(int64_t nrows, int64_t ncols) {
-  const MPlan mp = mplan(nrows, ncols);
+int64_t mfma_partial_floats(sinkhorn_problem* p, int64_t nrows, int64_t ncols) {
+  const MPlan mp = mplan(nrows, ncols, mfma_slots(p));
   return mp.G > 1 ? (int64_t)mp.G * nrows : 1;
 }
 
@@ -293,7 +332,7 @@ void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, d
 void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
   const Side& rows = *hs.rows;
   const Side& cols = *hs.cols;
-  const MPlan mp = mplan(rows.count, cols.count);
+  const MPlan mp = mplan(rows.count, cols.count, mfma_slots(p));
   if (mp.G > 1 && (int64_t)mp.G * rows.count > p->part_cap) fail(SINKHORN_ERR_HIP, "partial buffer too small");
   if (mp.tiles > p->red_cap || (rows.count + 255) / 256 > p->red_cap)
     fail(SINKHORN_ERR_HIP, "reduction buffer too small");
