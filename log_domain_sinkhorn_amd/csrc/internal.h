@@ -58,7 +58,7 @@ struct Side {
   int64_t count = 0;   // points
   int64_t padded = 0;  // round_up(count, kPad)
   float* soa = nullptr;    // [d][padded] coordinates (VALU path), zero padding
-  float* rowmaj = nullptr; // [padded][kpad] centred coordinates (MFMA path), zero padding
+  float* rowmaj = nullptr; // [padded][kpad] centred coordinates, column term, 1 (MFMA path)
   float* norm2 = nullptr;  // [padded] ||centred point||^2 (MFMA path)
   float* w = nullptr;      // [count] weights
   float* H = nullptr;      // [padded] column term of this side, -inf padding
@@ -93,7 +93,7 @@ struct HalfStep {
 struct sinkhorn_problem {
   int64_t n = 0, m = 0;
   int32_t d = 0;
-  int32_t kpad = 0;  // MFMA K (d rounded up to a multiple of 4), 0 on the VALU path
+  int32_t kpad = 0;  // MFMA K (d + 2 rounded up to a multiple of 4), 0 on the VALU path
   double scale = 1.0;
   hipStream_t stream = nullptr;
   sk::Side X, Y;

@@ -110,8 +110,9 @@ __global__ __launch_bounds__(256) void k_materialize_valu(
   }
 }
 
-// MFMA path (9 <= d <= 63): A = selected x rows (slot d := 1), B = column tile
-// of y from LDS (slot d = H'_j), D[i][j] = x_i . y_j + H'_j, E = 2 kappa D + P_i.
+// MFMA path (9 <= d <= 63): A = selected x rows (slot d := 1, slot KP - 1 :=
+// 0), B = column tile of y from LDS (slot d = H'_j), D[i][j] = x_i . y_j +
+// H'_j, E = 2 kappa D + P_i.
 // A wave owns one tile of 32 rows (so the A fragment, accumulators, row terms
 // and row maxima of a lane stay small enough for several waves per SIMD);
 // lane (l32, kh) holds rows 8(r/4) + 4kh + r%4 at column l32, so the T stores
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int c = 2 * kk + kh;
-      ax[kk] = i < 0 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
+      ax[kk] = i < 0 || c == KP - 1 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
     }
   }
   float emax[16];
@@ -292,7 +293,7 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
     switch (p->kpad) {
 #define SK_KP(v) case v: launch_mfma<v>(p, rows, row0, k, P, 2.0 * kappa, T, keys); break;
       SK_KP(12) SK_KP(16) SK_KP(20) SK_KP(24) SK_KP(28) SK_KP(32) SK_KP(36)
-      SK_KP(40) SK_KP(44) SK_KP(48) SK_KP(52) SK_KP(56) SK_KP(60) SK_KP(64)
+      SK_KP(40) SK_KP(44) SK_KP(48) SK_KP(52) SK_KP(56) SK_KP(60) SK_KP(64) SK_KP(68)
 #undef SK_KP
       default: fail(SINKHORN_ERR_UNSUPPORTED, "materializer: unsupported K");
     }

@@ -11,13 +11,22 @@
 //   kappa = s log2(e) / eps,
 // so f_i = s ||x_i||^2 - eps ln2 LSE2_j(2 kappa D_ij) with
 //   D_ij = sum_k y_jk x_ik + H'_j.
-// Each side is stored row-major [padded][KP] with KP = round_up(d + 1, 4):
+// Each side is stored row-major [padded][KP] with KP = round_up(d + 2, 4):
 // slots 0..d-1 hold the centred coordinates, slot d holds H' of that side
-// (written whenever the side is the column side, -inf on padding rows), the
-// rest zeros. The row side substitutes 1 for slot d in registers, so one
-// v_mfma_f32_32x32x2f32 chain over KP produces D directly; every column j of
-// a 32-point tile lands in one of 16 accumulator registers of a lane whose
-// lane % 32 selects the row i, and the log-sum-exp runs over those registers.
+// (written whenever the side is the column side, -inf on padding rows), slot
+// KP - 1 holds 1, the rest zeros. In registers the row side takes 2 kappa x
+// for the coordinates, 2 kappa for slot d and -c_i for slot KP - 1, where c_i
+// is the row's running shift, so one v_mfma_f32_32x32x2f32 chain over KP
+// produces 2 kappa D_ij - c_i directly; every column j of a 32-point tile
+// lands in one of 16 accumulator registers of a lane whose lane % 32 selects
+// the row i, and the log-sum-exp runs over those registers.
+//
+// The shift c_i is an integer no smaller than some exponent already seen in
+// the row, so the row sum S_i = sum 2^(z - c_i) stays >= 1/2 and nothing
+// underflows that matters; it is raised (and S_i rescaled) only when a tile
+// holds an exponent more than 64 above it, or at the row's first finite
+// tile. Every other tile costs one exp2 and one add per pair on the VALU,
+// which runs serially with the matrix pipe on this SIMD.
 //
 // Mapping: a workgroup = 4 waves x 2 row tiles of 32 (256 rows); all waves of
 // a workgroup stream the same column tiles, staged in LDS (double-buffered,
@@ -53,18 +62,6 @@ struct MfmaArgs {
   RowFinal F;
 };
 
-__device__ __forceinline__ void lse_update(float& M, float& S, const v16f& acc, float tk) {
-  float cm = acc[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) cm = fmaxf(cm, acc[r]);
-  const float Mn = fmaxf(M, cm * tk);
-  float s = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s += ex2(__builtin_fmaf(acc[r], tk, -Mn));
-  S = __builtin_fmaf(S, ex2(M - Mn), s);
-  M = Mn;
-}
-
 template <int KP>
 __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
   constexpr int KH = KP / 2;
@@ -82,7 +79,9 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
   const int kh = lane >> 5;
   const int64_t ibase = tile * kRowsPerWG + wave * (kIT * 32);
 
-  // B operands: row i = ibase + it*32 + l32, k = 2 kk + kh
+  // B operands: row i = ibase + it*32 + l32, k = 2 kk + kh; slot KP - 1
+  // (lanes with kh = 1, kk = KH - 1) carries -c_i, starting at 0
+  const float tk = A.twokappa;
   float bx[kIT][KH];
 #pragma unroll
   for (int it = 0; it < kIT; ++it)
@@ -90,16 +89,18 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
     for (int kk = 0; kk < KH; ++kk) {
       const int k = 2 * kk + kh;
       const float v = A.P[(ibase + it * 32 + l32) * KP + k];
-      bx[it][kk] = k == A.d ? 1.0f : v;
+      bx[it][kk] = k == A.d ? tk : (k == KP - 1 ? 0.0f : tk * v);
     }
 
   const int64_t t0 = (int64_t)gs * A.tps;
   const int64_t t1 = t0 + A.tps < A.ntiles ? t0 + A.tps : A.ntiles;
-  float M[kIT], S[kIT];
+  float c[kIT], S[kIT];
+  bool have[kIT];  // the row has seen a finite exponent (same on both lanes of a row)
 #pragma unroll
   for (int it = 0; it < kIT; ++it) {
-    M[it] = -FLT_MAX;
+    c[it] = 0.0f;
     S[it] = 0.0f;
+    have[it] = false;
   }
   float4 pre[PER];
   auto gload = [&](int64_t t) {
@@ -130,7 +131,6 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
   }
   __syncthreads();
   int buf = 0;
-  const float tk = A.twokappa;
   for (int64_t t = t0; t < t1; ++t) {
     const bool more = t + 1 < t1;
     if (more) gload(t + 1);
@@ -145,8 +145,43 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
       for (int it = 0; it < kIT; ++it)
         acc[it] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bx[it][kk], acc[it], 0, 0, 0);
     }
+    // acc = z - c: one exp2 and one add per pair unless a shift must move
+    float s[kIT];
+    bool need = false;
 #pragma unroll
-    for (int it = 0; it < kIT; ++it) lse_update(M[it], S[it], acc[it], tk);
+    for (int it = 0; it < kIT; ++it) {
+      float v = ex2(acc[it][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) v += ex2(acc[it][r]);
+      s[it] = v;
+      need = need || !have[it] || !(v <= 0x1p64f);
+    }
+    if (__ballot(need) == 0) {
+#pragma unroll
+      for (int it = 0; it < kIT; ++it) S[it] += s[it];
+    } else {
+      // all lanes: raise each row's shift to the ceiling of the tile's
+      // largest exponent when that is above it (or set it at the row's first
+      // finite tile), then add the tile relative to the new shift
+#pragma unroll
+      for (int it = 0; it < kIT; ++it) {
+        float cm = acc[it][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) cm = fmaxf(cm, acc[it][r]);
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        if (cm > -INFINITY) {
+          float k = ceilf(cm);
+          if (have[it]) k = fmaxf(k, 0.0f);
+          float v = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v += ex2(acc[it][r] - k);
+          S[it] = __builtin_fmaf(S[it], ex2(-k), v);
+          c[it] += k;
+          have[it] = true;
+          if (kh) bx[it][KH - 1] = -c[it];
+        }
+      }
+    }
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -157,10 +192,11 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
   int bad = 0;
 #pragma unroll
   for (int it = 0; it < kIT; ++it) {
-    const float Mo = __shfl_xor(M[it], 32, 64);
+    const float M = have[it] ? c[it] : -FLT_MAX;
+    const float Mo = __shfl_xor(M, 32, 64);
     const float So = __shfl_xor(S[it], 32, 64);
-    const float mx = fmaxf(M[it], Mo);
-    const float s = __builtin_fmaf(S[it], ex2(M[it] - mx), So * ex2(Mo - mx));
+    const float mx = fmaxf(M, Mo);
+    const float s = __builtin_fmaf(S[it], ex2(M - mx), So * ex2(Mo - mx));
     const int64_t i = ibase + it * 32 + l32;
     if (kh == 0 && i < A.F.np) {
       if (A.G > 1) {
@@ -187,7 +223,7 @@ __global__ __launch_bounds__(256) void k_lse_mfma(MfmaArgs A) {
 }
 
 // Centred row-major layout: slot d = 0 for real rows, -inf for padding rows,
-// norm2 = ||centred fp32 point||^2 (fp64 sum, rounded once).
+// slot kp - 1 = 1, norm2 = ||centred fp32 point||^2 (fp64 sum, rounded once).
 __global__ __launch_bounds__(256) void k_centre(const float* __restrict__ pts, int64_t count,
                                                 int32_t d, int32_t kp, int64_t padded,
                                                 const double* __restrict__ c,
@@ -203,6 +239,8 @@ __global__ __launch_bounds__(256) void k_centre(const float* __restrict__ pts, i
       n2 += (double)v * (double)v;
     } else if (k == d && i >= count) {
       v = -INFINITY;
+    } else if (k == kp - 1) {
+      v = 1.0f;
     }
     out[i * kp + k] = v;
   }
@@ -257,6 +295,7 @@ int64_t mfma_slots(sinkhorn_problem* p) {
     case 56: return slots_kp<56>(p);
     case 60: return slots_kp<60>(p);
     case 64: return slots_kp<64>(p);
+    case 68: return slots_kp<68>(p);
     default: fail(SINKHORN_ERR_UNSUPPORTED, "MFMA half-step: unsupported K");
   }
 }
@@ -300,7 +339,7 @@ int64_t mfma_partial_floats(sinkhorn_problem* p, int64_t nrows, int64_t ncols) {
 void setup_mfma(sinkhorn_problem* p, const float* x, const float* y) {
   const int32_t d = p->d;
   if (d > kMaxMfmaD) fail(SINKHORN_ERR_UNSUPPORTED, "d must be <= 63");
-  p->kpad = (int32_t)round_up(d + 1, 4);
+  p->kpad = (int32_t)round_up(d + 2, 4);
   std::vector<double> mx(2 * d), my(2 * d), c(d);
   moments(x, p->n, d, p->stream, mx.data());
   moments(y, p->m, d, p->stream, my.data());
@@ -374,6 +413,7 @@ void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
     case 56: launch_kp<56>(p, A, blocks, pairs); break;
     case 60: launch_kp<60>(p, A, blocks, pairs); break;
     case 64: launch_kp<64>(p, A, blocks, pairs); break;
+    case 68: launch_kp<68>(p, A, blocks, pairs); break;
     default: fail(SINKHORN_ERR_UNSUPPORTED, "MFMA half-step: unsupported K");
   }
   if (mp.G > 1)
