@@ -139,36 +139,6 @@ __global__ __launch_bounds__(kThreads) void k_merge(LseArgs A, int32_t shifted) 
   finish_tile(A.F, L, tile, mx, sum);
 }
 
-// Merge of G split partials for the shared merge entry point (fp32 maxima).
-__global__ __launch_bounds__(256) void k_merge_f32(RowFinal F, int32_t G, const float* __restrict__ Mp,
-                                                   const float* __restrict__ Sp) {
-  __shared__ double sRed[256];
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  double term = 0.0;
-  int bad = 0;
-  if (i < F.np) {
-    float mx = -FLT_MAX;
-    for (int32_t t = 0; t < G; ++t) mx = fmaxf(mx, Mp[(int64_t)t * F.np + i]);
-    double sum = 0.0;
-    for (int32_t t = 0; t < G; ++t) {
-      const int64_t o = (int64_t)t * F.np + i;
-      sum += (double)Sp[o] * (double)ex2(Mp[o] - mx);
-    }
-    term = finalize_row(F, i, (double)mx, sum, &bad);
-  }
-  if (bad) atomicAdd(&F.ctl->nonfinite, bad);
-  if (F.prev) {
-    sRed[threadIdx.x] = term;
-    __syncthreads();
-#pragma unroll
-    for (int w = 128; w > 0; w >>= 1) {
-      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) F.red_part[blockIdx.x] = sRed[0];
-  }
-}
-
 // Sum of count doubles in a fixed order into ctl->residual (one block).
 // The result and the non-finite count also go to the host-mapped mirror, so
 // the host reads them after an event without a copy.
@@ -308,13 +278,6 @@ RowFinal make_rowfinal(sinkhorn_problem* p, const HalfStep& hs) {
   return F;
 }
 
-void launch_merge(sinkhorn_problem* p, const RowFinal& F, int32_t G, const float* Mp,
-                  const float* Sp) {
-  const int64_t nblocks = (F.np + 255) / 256;
-  hipLaunchKernelGGL(k_merge_f32, dim3((uint32_t)nblocks), dim3(256), 0, p->stream, F, G, Mp, Sp);
-  SK_LAUNCH_CHECK();
-  if (F.prev) launch_reduce(p, nblocks);
-}
 
 void launch_reduce(sinkhorn_problem* p, int64_t count) {
   hipLaunchKernelGGL(k_reduce, dim3(1), dim3(256), 0, p->stream, p->red_part, count, p->ctl,

@@ -260,6 +260,73 @@ __global__ __launch_bounds__(256) void k_column_term_mfma(const float* __restric
                            0.5 * (double)norm2[j]);
 }
 
+// Merge of the G split partials [G][np] (fp32 shift or max, fp32 sum) of
+// each row, then finalize; with F.prev the residual terms are summed per
+// 256-row block. A workgroup holds 256 rows and 4 groups of 4 waves: group q
+// folds splits q, q + 4, ... of its rows (coalesced across the rows) with a
+// running maximum, and the first group combines the four in group order, so
+// the result does not depend on timing.
+constexpr int kMergeGroups = 4;
+
+__global__ __launch_bounds__(256 * kMergeGroups) void k_merge_splits(RowFinal F, int32_t G,
+                                                                     const float* __restrict__ Mp,
+                                                                     const float* __restrict__ Sp) {
+  __shared__ float sM[kMergeGroups][256];
+  __shared__ double sS[kMergeGroups][256];
+  __shared__ double sRed[256];
+  const int r = threadIdx.x & 255;
+  const int q = threadIdx.x >> 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + r;
+  float mx = -FLT_MAX;
+  double sum = 0.0;
+  if (i < F.np) {
+    for (int32_t t = q; t < G; t += kMergeGroups) {
+      const int64_t o = (int64_t)t * F.np + i;
+      const float m = Mp[o];
+      const double s = (double)Sp[o];
+      if (m > mx) {
+        sum = __builtin_fma(sum, (double)ex2(mx - m), s);
+        mx = m;
+      } else {
+        sum = __builtin_fma(s, (double)ex2(m - mx), sum);
+      }
+    }
+  }
+  sM[q][r] = mx;
+  sS[q][r] = sum;
+  __syncthreads();
+  double term = 0.0;
+  int bad = 0;
+  if (q == 0 && i < F.np) {
+    float m = sM[0][r];
+#pragma unroll
+    for (int k = 1; k < kMergeGroups; ++k) m = fmaxf(m, sM[k][r]);
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) s = __builtin_fma(sS[k][r], (double)ex2(sM[k][r] - m), s);
+    term = finalize_row(F, i, (double)m, s, &bad);
+  }
+  if (bad) atomicAdd(&F.ctl->nonfinite, bad);
+  if (F.prev) {
+    if (q == 0) sRed[r] = term;
+    __syncthreads();
+#pragma unroll
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) sRed[threadIdx.x] += sRed[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) F.red_part[blockIdx.x] = sRed[0];
+  }
+}
+
+void merge_splits(sinkhorn_problem* p, const RowFinal& F, int32_t G) {
+  const int64_t nblocks = (F.np + 255) / 256;
+  hipLaunchKernelGGL(k_merge_splits, dim3((uint32_t)nblocks), dim3(256 * kMergeGroups), 0,
+                     p->stream, F, G, p->Mpart, p->Spart);
+  SK_LAUNCH_CHECK();
+  if (F.prev) launch_reduce(p, nblocks);
+}
+
 struct MPlan {
   int32_t G;
   int64_t tps;
@@ -417,7 +484,7 @@ void mfma_halfstep(sinkhorn_problem* p, const HalfStep& hs) {
     default: fail(SINKHORN_ERR_UNSUPPORTED, "MFMA half-step: unsupported K");
   }
   if (mp.G > 1)
-    launch_merge(p, A.F, mp.G, p->Mpart, p->Spart);
+    merge_splits(p, A.F, mp.G);
   else if (A.F.prev)
     launch_reduce(p, mp.tiles);
 }

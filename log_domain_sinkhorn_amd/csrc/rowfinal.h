@@ -47,10 +47,6 @@ __device__ __forceinline__ double finalize_row(const RowFinal& F, int64_t i, dou
   return 0.0;
 }
 
-// dense.hip: merge G split partials [G][np] per row (split order) and
-// finalize; then, if F.prev, reduce the residual into ctl->residual.
-void launch_merge(sinkhorn_problem* p, const RowFinal& F, int32_t G, const float* Mp,
-                  const float* Sp);
 // fixed-order sum of red_part[0, count) into ctl->residual
 void launch_reduce(sinkhorn_problem* p, int64_t count);
 // finalize description of a half-step (VALU conventions; the MFMA path adjusts it)
