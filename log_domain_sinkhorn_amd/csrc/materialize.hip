@@ -110,9 +110,13 @@ __global__ __launch_bounds__(256) void k_materialize_valu(
   }
 }
 
-// MFMA path (9 <= d <= 63): A = selected x rows (slot d := 1, slot KP - 1 :=
-// 0), B = column tile of y from LDS (slot d = H'_j), D[i][j] = x_i . y_j +
-// H'_j, E = 2 kappa D + P_i.
+// MFMA path (9 <= d <= 63): A = selected x rows scaled by 2 kappa (slot d :=
+// 2 kappa, slot KP - 1 := the fp32 part P_hi of the row term), B = column
+// tile of y from LDS (slot d = H'_j, slot KP - 1 = 1), so the chain yields
+// 2 kappa (x_i . y_j + H'_j) + P_hi and E = that + P_lo (P_lo = P_i - P_hi in
+// fp32): one add, one exp2 and one max per entry besides the store. The
+// row maximum is taken before the add (rounding is monotone, so it equals
+// the maximum of the stored exponents).
 // A wave owns one tile of 32 rows (so the A fragment, accumulators, row terms
 // and row maxima of a lane stay small enough for several waves per SIMD);
 // lane (l32, kh) holds rows 8(r/4) + 4kh + r%4 at column l32, so the T stores
@@ -128,7 +132,6 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
   constexpr int NV4 = 32 * KP / 4;
   constexpr int PER = (NV4 + 255) / 256;
   __shared__ float sY[2][32 * LW];
-  __shared__ double sP[4][32];  // row terms of each wave's 32 rows
   const int32_t gs = (int32_t)(blockIdx.x % (uint32_t)G);
   const int64_t rt = blockIdx.x / (uint32_t)G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -136,21 +139,27 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
   const int l32 = lane & 31;
   const int kh = lane >> 5;
   const int64_t rbase = rt * 128 + wave * 32;  // first selected row of this wave
-  if (kh == 0) sP[wave][l32] = rbase + l32 < k ? P[rbase + l32] : -INFINITY;
+  const float tk = (float)twokappa;
 
   float ax[KH];
   {
     const int64_t rr = rbase + l32;
     const int64_t i = rr < k ? (rows ? rows[rr] : row0 + rr) : -1;
+    const float phi = i < 0 ? 0.0f : (float)P[rr];
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       const int c = 2 * kk + kh;
-      ax[kk] = i < 0 || c == KP - 1 ? 0.0f : (c == d ? 1.0f : X[i * KP + c]);
+      ax[kk] = i < 0 ? 0.0f : (c == KP - 1 ? phi : (c == d ? tk : tk * X[i * KP + c]));
     }
   }
-  float emax[16];
+  float plo[16], emax[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) emax[r] = -INFINITY;
+  for (int r = 0; r < 16; ++r) {
+    const int64_t rr = rbase + 8 * (r / 4) + 4 * kh + (r % 4);
+    const double pr = rr < k ? P[rr] : 0.0;
+    plo[r] = (float)(pr - (double)(float)pr);
+    emax[r] = -INFINITY;
+  }
   const int nrows = rbase + 32 <= k ? 32 : (int)(k - rbase);  // rows of this wave that exist
   float* Tw = (T && nrows > 0) ? T + (rbase + 4 * kh) * m : nullptr;
 
@@ -194,15 +203,22 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
     for (int kk = 0; kk < KH; ++kk)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[kk], ys[2 * kk], acc, 0, 0, 0);
     const int64_t j = t * 32 + l32;
+    if (Tw) {
+      float* Tj = Tw + j;
+      if ((t + 1) * 32 <= m && nrows == 32) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = 8 * (r / 4) + 4 * kh + (r % 4);  // row within the wave's tile
-      const float e32 = (float)__builtin_fma(twokappa, (double)acc[r], sP[wave][lr]);
-      if (j < m && lr < nrows) {
-        if (Tw) Tw[(int64_t)(8 * (r / 4) + (r % 4)) * m + j] = ex2(e32);
-        emax[r] = fmaxf(emax[r], e32);
+        for (int r = 0; r < 16; ++r) Tj[(int64_t)(8 * (r / 4) + (r % 4)) * m] = ex2(acc[r] + plo[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = 8 * (r / 4) + 4 * kh + (r % 4);  // row within the wave's tile
+          if (j < m && lr < nrows) Tj[(int64_t)(8 * (r / 4) + (r % 4)) * m] = ex2(acc[r] + plo[r]);
+        }
       }
     }
+    // padding columns give -inf (their column term), absent rows are not read
+#pragma unroll
+    for (int r = 0; r < 16; ++r) emax[r] = fmaxf(emax[r], acc[r]);
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     const int64_t rr = rbase + 8 * (r / 4) + 4 * kh + (r % 4);
-    if (l32 == 0 && rr < k && v > -INFINITY) atomicMax(&keys[rr], okey(v));
+    if (l32 == 0 && rr < k && v > -INFINITY) atomicMax(&keys[rr], okey(v + plo[r]));
   }
 }
 
@@ -267,7 +283,10 @@ void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t
                  const double* P, double twokappa, float* T, uint32_t* keys) {
   const int64_t rtiles = (k + 127) / 128;
   const int64_t ntiles = (p->m + 31) / 32;
-  int64_t want = (2048 + rtiles - 1) / rtiles;
+  // about two workgroups per CU, each streaming a long column range: shorter
+  // ranges (more workgroups) measured slower, the per-workgroup set-up and
+  // the row-maximum epilogue then weigh more
+  int64_t want = (2 * (int64_t)p->num_cu + rtiles - 1) / rtiles;
   const int64_t maxsplit = ntiles / 4 > 1 ? ntiles / 4 : 1;
   if (want > maxsplit) want = maxsplit;
   if (want < 1) want = 1;
