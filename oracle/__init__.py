@@ -47,11 +47,14 @@ from .dense import (  # noqa: F401
 from .morton import interleave, morton_codes, morton_order, quantize  # noqa: F401
 from .blocks import (  # noqa: F401
     block_summaries,
+    compact_tiles,
     screen,
     screen_transpose,
     sparse_halfstep_f,
     sparse_halfstep_g,
     sparse_residuals,
+    tile_shares,
+    verify_tiles,
 )
 from .fs2 import FS2Params, cells, fs2_solve, lift  # noqa: F401
 from .bary import barycentric_rows, coordinate_gradient, sparse_barycentric_rows  # noqa: F401

@@ -24,6 +24,19 @@ is omitted iff u_IJ * max(W_I, W_J) <= delta_rel, evaluated in float64 as
 
 with D_IJ accumulated axis by axis without fused multiply-adds and each
 log taken by the C library's ``log`` (``math.log``) on the host.
+
+Tile verification (§3.2: the screened candidates are checked with their exact
+mass over the B^2 point pairs; §C.5 measures it). Read here as the exact form
+of the same per-tile guarantee: with the row share of tile (I, J) for i in I
+    s_i = sum_{j in J} b_j exp((f_i + g_j - C_ij)/eps)   (= sum_j pi_ij / a_i)
+and the column share for j in J
+    t_j = sum_{i in I} a_i exp((f_i + g_j - C_ij)/eps)   (= sum_i pi_ij / b_j),
+a candidate is omitted iff every s_i <= delta_rel and every t_j <= delta_rel,
+so each omitted tile still takes at most delta_rel * a_i from row i and
+delta_rel * b_j from column j and the a-priori bound on the omitted mass is
+unchanged. A block that would lose every candidate keeps them all (rows
+first, then columns), so verification never turns a sparse block into a
+dense one; keeping tiles never weakens the bound.
 """
 from __future__ import annotations
 
@@ -161,3 +174,65 @@ def sparse_residuals(P, Q, wp, wq, f, g, eps, scale, ptr, col, ptrT, rowsT, B):
         return R
 
     return side(P, Q, wp, wq, f, g, ptr, col), side(Q, P, wq, wp, g, f, ptrT, rowsT)
+
+
+def tile_shares(P, Q, wp, wq, f, g, eps: float, scale: float, I: int, J: int, B: int):
+    """(s [rows of I], t [columns of J]): the row and column shares of tile
+    (I, J) defined in the module docstring, in float64."""
+    P = np.asarray(P)
+    Q = np.asarray(Q)
+    rs, re_ = I * B, min(len(P), (I + 1) * B)
+    cs, ce = J * B, min(len(Q), (J + 1) * B)
+    C = cost_rows(P[rs:re_], Q[cs:ce], scale)
+    E = np.exp((np.asarray(f, np.float64)[rs:re_, None] + np.asarray(g, np.float64)[None, cs:ce] - C)
+               / float(eps))
+    s = E @ np.asarray(wq, np.float64)[cs:ce]
+    t = np.asarray(wp, np.float64)[rs:re_] @ E
+    return s, t
+
+
+def verify_tiles(P, Q, wp, wq, f, g, eps: float, scale: float, ptr, col, B: int,
+                 delta_rel: float):
+    """Keep flags (bool per candidate, in CSR order) of the candidates (ptr,
+    col) at potentials (f, g): a candidate stays unless every row share and
+    every column share is <= delta_rel; then a row block that kept none of
+    its candidates keeps them all, and after that a column block that kept
+    none of its candidates keeps them all."""
+    ptr = np.asarray(ptr, np.int64)
+    col = np.asarray(col, np.int64)
+    keep = np.zeros(len(col), dtype=bool)
+    for I in range(len(ptr) - 1):
+        for e in range(int(ptr[I]), int(ptr[I + 1])):
+            s, t = tile_shares(P, Q, wp, wq, f, g, eps, scale, I, int(col[e]), B)
+            keep[e] = bool((s > delta_rel).any() or (t > delta_rel).any())
+    for I in range(len(ptr) - 1):
+        lo, hi = int(ptr[I]), int(ptr[I + 1])
+        if hi > lo and not keep[lo:hi].any():
+            keep[lo:hi] = True
+    for J in np.unique(col):
+        sel = col == J
+        if not keep[sel].any():
+            keep[sel] = True
+    return keep
+
+
+def compact_tiles(ptr, col, keep, ncol_blocks: int):
+    """The kept candidates as a row-major CSR (ptr, col) and the same tiles
+    column-major (ptrT, rowsT: for each J the row blocks in increasing order)."""
+    ptr = np.asarray(ptr, np.int64)
+    col = np.asarray(col, np.int32)
+    keep = np.asarray(keep, bool)
+    nrow = len(ptr) - 1
+    rows = np.repeat(np.arange(nrow, dtype=np.int32), np.diff(ptr))
+    counts = np.array([int(keep[int(ptr[I]):int(ptr[I + 1])].sum()) for I in range(nrow)], np.int64)
+    ptrV = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    colV = col[keep].astype(np.int32)
+    rk = rows[keep]
+    ptrT = [0]
+    rowsT = []
+    for J in range(ncol_blocks):
+        r = rk[colV == J]
+        rowsT.append(r)
+        ptrT.append(ptrT[-1] + len(r))
+    rowsT = np.concatenate(rowsT).astype(np.int32) if rowsT else np.zeros(0, np.int32)
+    return ptrV, colV, np.asarray(ptrT, np.int64), rowsT

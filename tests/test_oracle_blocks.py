@@ -170,3 +170,155 @@ def test_row_block_without_admitted_tiles_takes_the_dense_update(problem):
     fs = oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B)
     dense = oracle.halfstep_f(x[:B], y, b, g, eps, 1.0)
     np.testing.assert_allclose(fs[:B], dense, rtol=1e-13)
+
+
+# ---- tile verification (FlashSinkhorn 2, §3.2: exact B^2-pair mass of each candidate)
+
+def _plan(x, y, a, b, f, g, eps):
+    """The explicit plan pi from scipy's distance routine (not cost_rows)."""
+    C = cdist(x.astype(np.float64), y.astype(np.float64), "sqeuclidean")
+    return (a.astype(np.float64)[:, None] * b.astype(np.float64)[None, :]
+            * np.exp((f.astype(np.float64)[:, None] + g.astype(np.float64)[None, :] - C) / eps))
+
+
+def _verified(problem, B):
+    x, y, a, b, f, g, eps = problem
+    NB, MB = math.ceil(len(x) / B), math.ceil(len(y) / B)
+    delta = 1e-3 / max(NB, MB)
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    keep = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr, col, B, delta)
+    return ptr, col, keep, delta, NB, MB
+
+
+def test_tile_shares_match_the_explicit_plan(problem):
+    x, y, a, b, f, g, eps = problem
+    B = 32
+    P = _plan(x, y, a, b, f, g, eps)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    for I, J in [(0, 0), (3, 5), (19, 17), (7, 2)]:
+        s, t = oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, I, J, B)
+        T = P[I * B:(I + 1) * B, J * B:(J + 1) * B]
+        np.testing.assert_allclose(s, T.sum(axis=1) / a64[I * B:(I + 1) * B], rtol=1e-10, atol=1e-300)
+        np.testing.assert_allclose(t, T.sum(axis=0) / b64[J * B:(J + 1) * B], rtol=1e-10, atol=1e-300)
+
+
+def test_verification_keeps_exactly_the_tiles_with_a_large_share(problem):
+    """Against brute force on the explicit plan: every candidate with some
+    row share above delta a_i or column share above delta b_j is kept, every
+    other candidate is dropped unless a fallback restores it."""
+    x, y, a, b, f, g, eps = problem
+    B = 32
+    ptr, col, keep, delta, NB, MB = _verified(problem, B)
+    P = _plan(x, y, a, b, f, g, eps)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    big = np.zeros(len(col), bool)
+    for I in range(NB):
+        for e in range(ptr[I], ptr[I + 1]):
+            J = int(col[e])
+            T = P[I * B:(I + 1) * B, J * B:(J + 1) * B]
+            big[e] = ((T.sum(axis=1) > delta * a64[I * B:(I + 1) * B]).any()
+                      or (T.sum(axis=0) > delta * b64[J * B:(J + 1) * B]).any())
+    assert (keep | ~big).all() and (keep >= big).all()
+    restored = keep & ~big
+    for e in np.nonzero(restored)[0]:
+        I = int(np.searchsorted(ptr, e, side="right") - 1)
+        J = int(col[e])
+        row_none = not big[ptr[I]:ptr[I + 1]].any()
+        col_none = not big[col == J].any()
+        assert row_none or col_none, (I, J)
+    assert 0 < keep.sum() < len(col)  # the workload drops some candidates and keeps some
+
+
+def test_verification_keeps_the_omitted_mass_bound(problem):
+    x, y, a, b, f, g, eps = problem
+    B = 32
+    ptr, col, keep, delta, NB, MB = _verified(problem, B)
+    ptrV, colV, ptrT, rowsT = oracle.compact_tiles(ptr, col, keep, MB)
+    M = _dense_mask(ptrV, colV, NB, MB)
+    P = _plan(x, y, a, b, f, g, eps)
+    mask = np.kron(M, np.ones((B, B), bool))[:len(x), :len(y)]
+    omitted = np.where(mask, 0.0, P)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    per_row_tiles = (~M).sum(axis=1)
+    per_col_tiles = (~M).sum(axis=0)
+    rows = np.repeat(np.arange(NB), B)[:len(x)]
+    cols = np.repeat(np.arange(MB), B)[:len(y)]
+    assert (omitted.sum(axis=1) <= delta * a64 * per_row_tiles[rows] * (1 + 1e-12)).all()
+    assert (omitted.sum(axis=0) <= delta * b64 * per_col_tiles[cols] * (1 + 1e-12)).all()
+    assert omitted.sum() <= max(NB, MB) * delta * (1 + 1e-12)
+
+
+def test_single_point_blocks_verify_to_the_screen(rng):
+    """With B = 1 the screen's bound is the plan entry itself, so the exact
+    check agrees with it and drops no candidate (away from exact ties)."""
+    x = rng.uniform(0, 1, (40, 2)).astype(np.float32)
+    y = rng.uniform(0, 1, (35, 2)).astype(np.float32)
+    a = np.full(40, 1 / 40, np.float32)
+    b = np.full(35, 1 / 35, np.float32)
+    eps = 0.01
+    f, g = _potentials(x, y, a, b, eps, iters=20)
+    delta = 1e-2 / 40
+    sx = oracle.block_summaries(x, a, f, 1)
+    sy = oracle.block_summaries(y, b, g, 1)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    keep = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr, col, 1, delta)
+    assert 0 < len(col) < 40 * 35 and keep.all()
+
+
+def test_fallbacks_keep_blocks_that_would_lose_every_candidate(problem):
+    x, y, a, b, f, g, eps = problem
+    B = 32
+    NB, MB = math.ceil(len(x) / B), math.ceil(len(y) / B)
+    # every tile a candidate, threshold far above any share: all would go
+    ptr = np.arange(NB + 1, dtype=np.int64) * MB
+    col = np.tile(np.arange(MB, dtype=np.int32), NB)
+    keep = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr, col, B, 10.0)
+    assert keep.all()
+    # row block 0 alone has candidates and all of them fail: kept by the
+    # row fallback
+    ptr1 = np.zeros(NB + 1, np.int64)
+    ptr1[1:] = 3
+    col1 = np.array([1, 4, MB - 1], np.int32)
+    keep1 = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr1, col1, B, 10.0)
+    assert keep1.all()
+    # row block 0 has its heaviest tile J0 and a near-empty tile Jc; no other
+    # row block has Jc. Verification drops (0, Jc), the row keeps J0, and the
+    # column fallback restores (0, Jc) since column block Jc would lose all
+    delta = 1e-3 / max(NB, MB)
+    share = np.array([max(oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, 0, J, B)[0].max(),
+                          oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, 0, J, B)[1].max())
+                      for J in range(MB)])
+    J0, Jc = int(np.argmax(share)), int(np.argmin(share))
+    assert share[J0] > delta >= share[Jc]
+    col2 = np.array(sorted([J0, Jc]), np.int32)
+    ptr2 = np.zeros(NB + 1, np.int64)
+    ptr2[1:] = 2
+    keep2 = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr2, col2, B, delta)
+    assert keep2.all()
+    # with Jc also a (heavy) candidate of another row block, it is dropped
+    # from row block 0
+    Ih = int(np.argmax([oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, I, Jc, B)[0].max()
+                        for I in range(NB)]))
+    assert Ih != 0
+    assert oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, Ih, Jc, B)[0].max() > delta
+    ptr3 = np.zeros(NB + 1, np.int64)
+    ptr3[1:Ih + 1] = 2
+    ptr3[Ih + 1:] = 3
+    col3 = np.concatenate([col2, np.array([Jc], np.int32)])
+    keep3 = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr3, col3, B, delta)
+    assert list(keep3) == [J0 < Jc, J0 > Jc, True]
+
+
+def test_compacted_lists_are_transposes(problem):
+    B = 32
+    ptr, col, keep, delta, NB, MB = _verified(problem, B)
+    ptrV, colV, ptrT, rowsT = oracle.compact_tiles(ptr, col, keep, MB)
+    M = _dense_mask(ptrV, colV, NB, MB)
+    MT = _dense_mask(ptrT, rowsT, MB, NB)
+    assert (M == MT.T).all()
+    assert ptrV[-1] == keep.sum() == ptrT[-1]
+    for J in range(MB):
+        r = rowsT[ptrT[J]:ptrT[J + 1]]
+        assert (np.diff(r) > 0).all()
