@@ -200,6 +200,27 @@ int sinkhorn_block_screen(sinkhorn_problem* p, double eps, const float* f, const
                           int32_t B, double delta_rel, int32_t transpose, int64_t* ptr,
                           int32_t* idx, int64_t cap, int64_t* nnz_out);
 
+/* Tile verification (FlashSinkhorn 2, §3.2: screened tiles are checked with
+ * their exact mass over the B^2 point pairs; §C.5). Input: a row-major
+ * candidate list ptr [NB+1] (ptr[0] = 0) / idx [nnz] as written by
+ * sinkhorn_block_screen (transpose = 0), B = 128, d <= 3. A candidate (I, J)
+ * is dropped iff at (f, g), for every i in I,
+ *   sum_{j in J} b_j exp((f_i + g_j - C_ij)/eps) <= delta_rel
+ * and for every j in J,
+ *   sum_{i in I} a_i exp((f_i + g_j - C_ij)/eps) <= delta_rel
+ * (each dropped tile then takes at most delta_rel a_i from row i and
+ * delta_rel b_j from column j, the screen's own guarantee; sums in fp32, a NaN
+ * keeps the tile). A row block that would lose every candidate keeps them all,
+ * then likewise a column block. Outputs (device, caller-owned): vptr [NB+1] /
+ * vidx the kept tiles row-major in candidate order, tptr [MB+1] / tidx the
+ * same tiles column-major (source blocks increasing per target block); vidx
+ * and tidx need room for nnz entries. *kept_out (host) = kept count.
+ * Synchronizes the handle's stream. */
+int sinkhorn_verify_tiles(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                          int32_t B, double delta_rel, const int64_t* ptr, const int32_t* idx,
+                          int64_t* vptr, int32_t* vidx, int64_t* tptr, int32_t* tidx,
+                          int64_t* kept_out);
+
 /* Sparse f-step on a row-major tile list (FlashSinkhorn 2, §3.2: log-sum-exp
  * over admitted tiles only; a block with no admitted tile takes a dense
  * update). Same outputs as sinkhorn_halfstep_f, with the residual (when
@@ -228,6 +249,8 @@ typedef struct {
   int32_t stall_window;     /* ... or R > (1 - stall_rel) * R of stall_window iterations before */
   double stall_rel;
   int32_t max_fine;         /* cap on fine updates */
+  int32_t verify;           /* nonzero: verify the screened tiles (sinkhorn_verify_tiles rule,
+                               B = 128) before each fine update's half-steps */
 } sinkhorn_multiscale_params;
 
 typedef struct {
@@ -240,6 +263,7 @@ typedef struct {
   double omega;             /* a-priori omitted-mass bound */
   double seconds_total, seconds_sort, seconds_coarse, seconds_lift, seconds_fine;
   int32_t certified;
+  int64_t last_candidates;  /* screened tiles of the last mask (= last_tiles without verify) */
 } sinkhorn_multiscale_report;
 
 /* Block-sparse multiscale solve for d <= 3 (FlashSinkhorn 2): Morton sort,

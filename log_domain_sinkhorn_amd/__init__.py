@@ -98,6 +98,7 @@ class _MultiscaleParamsC(ctypes.Structure):
         ("stall_window", _i32),
         ("stall_rel", _f64),
         ("max_fine", _i32),
+        ("verify", _i32),
     ]
 
 
@@ -118,6 +119,7 @@ class _MultiscaleReportC(ctypes.Structure):
         ("seconds_lift", _f64),
         ("seconds_fine", _f64),
         ("certified", _i32),
+        ("last_candidates", _i64),
     ]
 
 
@@ -137,6 +139,7 @@ _SIGS = {
     "sinkhorn_min_row": ([_p, _f64, _p, _p, _p], _i32),
     "sinkhorn_morton_order": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_block_screen": ([_p, _f64, _p, _p, _i32, _f64, _i32, _p, _p, _i64, _p], _i32),
+    "sinkhorn_verify_tiles": ([_p, _f64, _p, _p, _i32, _f64, _p, _p, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_g": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_barycentric": ([_p, _f64, _p, _p, _p, _p], _i32),
@@ -239,12 +242,14 @@ class MultiscaleParams:
     stall_window: int = 10
     stall_rel: float = 0.01
     max_fine: int = 8192
+    verify: bool = False
 
     def _c(self) -> _MultiscaleParamsC:
         return _MultiscaleParamsC(self.B, self.p_bits, self.eps, self.tol, self.delta_scale,
                                   self.coarse_eps_start, self.coarse_factor,
                                   self.coarse_iters_per_stage, self.coarse_tol, self.coarse_max,
-                                  self.stall_window, self.stall_rel, self.max_fine)
+                                  self.stall_window, self.stall_rel, self.max_fine,
+                                  int(bool(self.verify)))
 
 
 def _struct_dict(s) -> dict:
@@ -405,6 +410,29 @@ class Problem:
                                            int(transpose), _ptr(ptr), _ptr(idx), cap,
                                            ctypes.byref(nnz)), "block_screen")
         return ptr, idx[: nnz.value]
+
+    def verify_tiles(self, eps, f, g, B, delta_rel, ptr, idx):
+        """Verified tiles of a row-major candidate list: (vptr, vidx, tptr,
+        tidx) device tensors, the kept tiles row-major and column-major."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        nb = (self.n + B - 1) // B
+        mb = (self.m + B - 1) // B
+        _dev(ptr, torch.int64, "ptr", (nb + 1,))
+        nnz = int(idx.shape[0])
+        if nnz:
+            _dev(idx, torch.int32, "idx")
+        vptr = torch.empty(nb + 1, dtype=torch.int64, device=self.device)
+        tptr = torch.empty(mb + 1, dtype=torch.int64, device=self.device)
+        vidx = torch.empty(max(1, nnz), dtype=torch.int32, device=self.device)
+        tidx = torch.empty(max(1, nnz), dtype=torch.int32, device=self.device)
+        kept = _i64()
+        _check(lib().sinkhorn_verify_tiles(self._h, float(eps), _ptr(f), _ptr(g), int(B),
+                                           float(delta_rel), _ptr(ptr), _ptr(idx) if nnz else None,
+                                           _ptr(vptr), _ptr(vidx), _ptr(tptr), _ptr(tidx),
+                                           ctypes.byref(kept)), "verify_tiles")
+        k = kept.value
+        return vptr, vidx[:k], tptr, tidx[:k]
 
     def sparse_halfstep_f(self, eps, g, B, ptr, idx, out=None, f_prev=None):
         self._pot(g, self.m, "g")

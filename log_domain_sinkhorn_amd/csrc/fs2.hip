@@ -25,6 +25,7 @@
 #include <rocprim/device/device_scan.hpp>
 
 #include "internal.h"
+#include "verify.h"
 
 namespace sk {
 namespace {
@@ -200,6 +201,30 @@ struct TileList {
   }
 };
 
+// Device buffers of one verified tile list (row- or column-major).
+struct VerifiedList {
+  int64_t* ptr = nullptr;
+  int32_t* idx = nullptr;
+  int64_t cap = 0;
+  int64_t nnz = 0;
+  ~VerifiedList() {
+    dev_free(ptr);
+    dev_free(idx);
+  }
+  void reserve(sinkhorn_problem* p, int64_t nb, int64_t want) {
+    if (!ptr) ptr = (int64_t*)dev_alloc(sizeof(int64_t) * (nb + 1));
+    if (want > cap) {
+      SK_HIP(hipStreamSynchronize(p->stream));
+      dev_free(idx);
+      idx = nullptr;
+      cap = 0;
+      const int64_t c = want + want / 4 + 1024;
+      idx = (int32_t*)dev_alloc(sizeof(int32_t) * c);
+      cap = c;
+    }
+  }
+};
+
 }  // namespace
 }  // namespace sk
 
@@ -233,6 +258,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     if (!(std::isfinite(P.eps) && P.eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (!(P.tol > 0.0) || !(P.delta_scale > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "tol and delta_scale must be > 0");
     if (P.max_fine < 0 || P.coarse_max < 1) fail(SINKHORN_ERR_INVALID_ARG, "bad iteration caps");
+    if (P.verify && P.B != kVerifyB) fail(SINKHORN_ERR_UNSUPPORTED, "tile verification needs B = 128");
     hipStream_t st = p->stream;
     const int32_t d = p->d;
     const int64_t n = p->n, m = p->m;
@@ -338,6 +364,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     block_static(p, Xs, P.B, sx);
     block_static(p, Ys, P.B, sy);
     TileList rowL, colL;
+    VerifiedList rowV, colV;
+    VerifyScratch vscr;
     int cf = 0, cg = 0;
     int status = SINKHORN_NOT_CONVERGED;
     double Rrow = NAN, Rcol = NAN;
@@ -346,17 +374,40 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       block_potential_max(p, fs[cf], n, sx);
       block_potential_max(p, gs[cg], m, sy);
       rowL.build(p, sx, sy, eps, delta);
-      colL.build(p, sy, sx, eps, delta);
-      R.last_tiles = rowL.nnz;
-      const double row_pairs = (double)rowL.nnz * pair_block +
-                               (double)count_empty_rows(p, rowL.ptr, sx.nb) * P.B * (double)m;
-      const double col_pairs = (double)colL.nnz * pair_block +
-                               (double)count_empty_rows(p, colL.ptr, sy.nb) * P.B * (double)n;
+      const int64_t *rptr = rowL.ptr, *cptr = nullptr;
+      const int32_t *ridx = rowL.idx, *cidx = nullptr;
+      int64_t rnnz = rowL.nnz, cnnz = 0;
+      if (P.verify) {
+        // the exact share check at (f, g) on the screened tiles; both lists
+        // come from the survivors
+        rowV.reserve(p, sx.nb, rowL.nnz);
+        colV.reserve(p, sy.nb, rowL.nnz);
+        const int64_t kept = verify_tiles(p, Xs, Ys, fs[cf], gs[cg], eps, delta, rowL.ptr, rowL.idx,
+                                          rowL.nnz, sx.nb, sy.nb, rowV.ptr, rowV.idx, colV.ptr,
+                                          colV.idx, vscr);
+        rowV.nnz = colV.nnz = kept;
+        rptr = rowV.ptr;
+        ridx = rowV.idx;
+        cptr = colV.ptr;
+        cidx = colV.idx;
+        rnnz = cnnz = kept;
+      } else {
+        colL.build(p, sy, sx, eps, delta);
+        cptr = colL.ptr;
+        cidx = colL.idx;
+        cnnz = colL.nnz;
+      }
+      R.last_candidates = rowL.nnz;
+      R.last_tiles = rnnz;
+      const double row_pairs = (double)rnnz * pair_block +
+                               (double)count_empty_rows(p, rptr, sx.nb) * P.B * (double)m;
+      const double col_pairs = (double)cnnz * pair_block +
+                               (double)count_empty_rows(p, cptr, sy.nb) * P.B * (double)n;
       // sparse f-step at (f, g); its fused residual is R_A,row of (f, g)
       reset_nonfinite(p);
       prep_column_term(p, Ys, gs[cg], eps, Ys.H);
       sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true, fs[cf]},
-                      P.B, rowL.ptr, rowL.idx, row_pairs);
+                      P.B, rptr, ridx, row_pairs);
       int32_t bad = 0;
       read_reduction(p, &Rrow, &bad);
       if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in the fine loop");
@@ -365,7 +416,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       if (Rrow + omega <= P.tol) {
         prep_column_term(p, Xs, fs[cf], eps, Xs.H);
         sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true, gs[cg]},
-                        P.B, colL.ptr, colL.idx, col_pairs);
+                        P.B, cptr, cidx, col_pairs);
         read_reduction(p, &Rcol, nullptr);
         R.pairs_evaluated += col_pairs;
         if ((Rrow > Rcol ? Rrow : Rcol) + omega <= P.tol) {
@@ -374,14 +425,14 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
           break;
         }
       }
-      progress("multiscale: fine update %d: %lld row / %lld column tiles, R_A row %.4g column %.4g "
-               "(%.3f s)", (int)R.fine_updates, (long long)rowL.nnz, (long long)colL.nnz, Rrow, Rcol,
-               now_s() - t_lift);
+      progress("multiscale: fine update %d: %lld row / %lld column tiles (%lld screened), R_A row "
+               "%.4g column %.4g (%.3f s)", (int)R.fine_updates, (long long)rnnz, (long long)cnnz,
+               (long long)rowL.nnz, Rrow, Rcol, now_s() - t_lift);
       if (R.fine_updates >= P.max_fine) break;
       cf = 1 - cf;  // accept the f-step
       prep_column_term(p, Xs, fs[cf], eps, Xs.H);
       sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false, gs[cg]},
-                      P.B, colL.ptr, colL.idx, col_pairs);
+                      P.B, cptr, cidx, col_pairs);
       R.pairs_evaluated += col_pairs;
       cg = 1 - cg;
       ++R.fine_updates;

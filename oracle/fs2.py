@@ -14,6 +14,9 @@ FlashSinkhorn 2:
     per side in one cell give lifted residual cosh(2h^2/eps) - 1).
   * §3.2: every fine update rebuilds the mask at the current potentials and
     runs both sparse half-steps on it.
+  * §3.2 (with §C.5): optionally, the screened tiles are verified with their
+    exact row and column shares before the half-steps (``verify_tiles``), and
+    both supports come from the survivors.
   * §C.4: the stop certificate is the admitted-plan residual plus a bound on
     the omitted mass. Read here as R_A + Omega <= tol with
     Omega = max(NB, MB) * delta_rel, the a-priori total omitted-mass bound
@@ -28,11 +31,13 @@ import numpy as np
 
 from .blocks import (
     block_summaries,
+    compact_tiles,
     screen,
     screen_transpose,
     sparse_halfstep_f,
     sparse_halfstep_g,
     sparse_residuals,
+    verify_tiles,
 )
 from .dense import Schedule, annealing_stages, halfstep_f, halfstep_g, marginal_residuals
 from .morton import BITS, morton_order
@@ -86,6 +91,7 @@ class FS2Params:
     max_fine: int = 8192
     p_bits: int = -1  # -1: floor(log2(2 * max(NB, MB)))
     scale: float = 1.0
+    verify: bool = False  # exact share check of the screened tiles
 
 
 @dataclass
@@ -101,6 +107,7 @@ class FS2Result:
     ncells_x: int
     ncells_y: int
     tiles_history: list = field(default_factory=list)
+    candidates_history: list = field(default_factory=list)
 
 
 def prefix_bits(NB: int, MB: int, d: int) -> int:
@@ -157,6 +164,7 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     g = lift(Y, centx, massx, F, prm.eps, prm.scale)
 
     tiles = []
+    cands = []
     certified = False
     R_row = R_col = math.nan
     updates = 0
@@ -166,7 +174,12 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
         sx = block_summaries(X, A, f32, B)
         sy = block_summaries(Y, Bw, g32, B)
         ptr, col = screen(sx, sy, prm.eps, prm.scale, delta)
-        ptrT, rowT = screen_transpose(sx, sy, prm.eps, prm.scale, delta)
+        cands.append(int(ptr[-1]))
+        if prm.verify:
+            keep = verify_tiles(X, Y, A, Bw, f32, g32, prm.eps, prm.scale, ptr, col, B, delta)
+            ptr, col, ptrT, rowT = compact_tiles(ptr, col, keep, len(sy[2]))
+        else:
+            ptrT, rowT = screen_transpose(sx, sy, prm.eps, prm.scale, delta)
         tiles.append(int(ptr[-1]))
         R_row, R_col = sparse_residuals(X, Y, A, Bw, f, g, prm.eps, prm.scale, ptr, col, ptrT, rowT, B)
         if max(R_row, R_col) + omega <= prm.tol:
@@ -183,4 +196,4 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     fu[px] = f
     gu[py] = g
     return FS2Result(fu, gu, coarse_iters, updates, R_row, R_col, omega, certified,
-                     len(centx), len(centy), tiles)
+                     len(centx), len(centy), tiles, cands)

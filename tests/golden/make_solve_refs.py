@@ -62,6 +62,9 @@ def main(names):
 FS2_CASES = {
     "w5_n16384_fixed": (5, 16384, dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0, coarse_max=40,
                                        stall_window=1 << 30, max_fine=4)),
+    "w5_n16384_fixed_verify": (5, 16384, dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0,
+                                              coarse_max=40, stall_window=1 << 30, max_fine=4,
+                                              verify=True)),
 }
 
 
@@ -77,7 +80,8 @@ def run_fs2(name):
     np.savez_compressed(
         out, f=r.f, g=r.g, coarse_iters=r.coarse_iters, fine_updates=r.fine_updates,
         R_A_row=r.R_A_row, R_A_col=r.R_A_col, omega=r.omega, certified=r.certified,
-        ncells_x=r.ncells_x, ncells_y=r.ncells_y, tiles=np.asarray(r.tiles_history), workload=w, n=n,
+        ncells_x=r.ncells_x, ncells_y=r.ncells_y, tiles=np.asarray(r.tiles_history),
+        candidates=np.asarray(r.candidates_history), workload=w, n=n,
         **{k: v for k, v in prm.__dict__.items()},
     )
     print(f"{name}: coarse {r.coarse_iters} fine {r.fine_updates} certified {r.certified} "

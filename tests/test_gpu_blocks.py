@@ -189,13 +189,14 @@ def test_multiscale_fixed_budget_matches_the_oracle(sk):
     assert rep["R_A_row"] == pytest.approx(float(ref["R_A_row"]), rel=1e-2)
 
 
-def test_multiscale_solve_certificate_holds(sk):
+@pytest.mark.parametrize("verify", [False, True], ids=["screened", "verified"])
+def test_multiscale_solve_certificate_holds(sk, verify):
     """Run to the stop rule; the oracle's exact dense residuals of the returned
     potentials must sit under the certificate R_A + Omega <= tol."""
     n, eps = 16384, 1e-3
     c = synth.make(5, n=n, m=n)
-    prm = sk.MultiscaleParams(B=128, eps=eps, tol=1e-2)
-    _log(f"multiscale certified n={n}")
+    prm = sk.MultiscaleParams(B=128, eps=eps, tol=1e-2, verify=verify)
+    _log(f"multiscale certified n={n} verify={verify}")
     with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
         f, g, rep = P.solve_multiscale(prm)
     _log(f"  coarse {rep['coarse_iters']} fine {rep['fine_updates']} R_A {rep['R_A_row']:.3e}/{rep['R_A_col']:.3e}")
@@ -290,3 +291,106 @@ def test_sparse_halfsteps_low_dimensions(sk, d):
         assert err.max() <= 1e-5, (what, d, err.max())
     Rr, _ = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
     assert r == pytest.approx(Rr, rel=1e-3)
+
+
+# ---- tile verification (FlashSinkhorn 2, §3.2: exact B^2-pair mass of each screened tile)
+
+def _kept_flags(ptr, idx, vptr, vidx):
+    """Keep flag per candidate from the verified row-major list."""
+    keep = np.zeros(len(idx), bool)
+    for I in range(len(ptr) - 1):
+        kept = set(vidx[vptr[I]:vptr[I + 1]].tolist())
+        keep[ptr[I]:ptr[I + 1]] = [int(J) in kept for J in idx[ptr[I]:ptr[I + 1]]]
+    return keep
+
+
+@pytest.mark.parametrize("n,eps", [(16384, 1e-3), (5000, 1e-3), (65536, 1e-4)])
+def test_verify_tiles_match_oracle(sk, n, eps):
+    """Keep decisions agree with the fp64 oracle except for tiles whose largest
+    share is within 1e-3 of the threshold (fp32 sums decide); the two lists are
+    exactly the oracle's compaction of the GPU's decisions."""
+    x, y, a, b = _sorted_problem(5, n)
+    rng = np.random.default_rng(1)
+    f, g = _near_plan_potentials(n, eps, rng)
+    B = 128
+    NB = MB = (n + B - 1) // B
+    delta = 1e-3 / NB
+    _log(f"verify n={n} eps={eps}")
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        ptr, idx = P.block_screen(eps, _t(f), _t(g), B, delta)
+        vptr, vidx, tptr, tidx = P.verify_tiles(eps, _t(f), _t(g), B, delta, ptr, idx)
+    ptr, idx = ptr.cpu().numpy(), idx.cpu().numpy()
+    vptr, vidx = vptr.cpu().numpy(), vidx.cpu().numpy()
+    tptr, tidx = tptr.cpu().numpy(), tidx.cpu().numpy()
+    keep = _kept_flags(ptr, idx, vptr, vidx)
+    assert 0 < keep.sum() < len(idx)
+    ref = oracle.verify_tiles(x, y, a, b, f, g, eps, 1.0, ptr, idx, B, delta)
+    for e in np.nonzero(keep != ref)[0]:
+        I = int(np.searchsorted(ptr, e, side="right") - 1)
+        s, t = oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, I, int(idx[e]), B)
+        top = max(s.max(), t.max())
+        assert abs(top / delta - 1.0) < 1e-3, (I, int(idx[e]), top / delta, keep[e], ref[e])
+    ptrV, colV, ptrT, rowsT = oracle.compact_tiles(ptr, idx, keep, MB)
+    assert np.array_equal(vptr, ptrV) and np.array_equal(vidx, colV)
+    assert np.array_equal(tptr, ptrT) and np.array_equal(tidx, rowsT)
+
+
+def test_verify_tiles_edge_cases(sk):
+    n, eps, B = 1000, 1e-3, 128
+    x, y, a, b = _sorted_problem(5, n)
+    f, g = _near_plan_potentials(n, eps, np.random.default_rng(3))
+    NB = (n + B - 1) // B
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        # no candidates: empty lists
+        ptr0 = torch.zeros(NB + 1, dtype=torch.int64, device=DEV)
+        idx0 = torch.zeros(0, dtype=torch.int32, device=DEV)
+        vptr, vidx, tptr, tidx = P.verify_tiles(eps, _t(f), _t(g), B, 1e-3, ptr0, idx0)
+        assert vidx.numel() == 0 and tidx.numel() == 0
+        assert int(vptr.abs().sum()) == 0 and int(tptr.abs().sum()) == 0
+        # every tile a candidate and a threshold no share reaches: all kept by
+        # the fallbacks
+        ptr = torch.arange(NB + 1, dtype=torch.int64, device=DEV) * NB
+        idx = torch.arange(NB, dtype=torch.int32, device=DEV).repeat(NB)
+        vptr, vidx, tptr, tidx = P.verify_tiles(eps, _t(f), _t(g), B, 1e30, ptr, idx)
+        assert torch.equal(vptr, ptr) and torch.equal(vidx, idx)
+        # B other than 128, a list that does not start at 0, an index out of range
+        with pytest.raises(sk.SinkhornError, match="B = 128") as e:
+            P.verify_tiles(eps, _t(f), _t(g), 256, 1e-3, ptr[: (n + 255) // 256 + 1], idx)
+        assert e.value.code == sk.ERR_UNSUPPORTED
+        with pytest.raises(sk.SinkhornError, match="start at 0") as e:
+            P.verify_tiles(eps, _t(f), _t(g), B, 1e-3, ptr + 1, idx)
+        assert e.value.code == sk.ERR_INVALID_ARG
+        bad = idx.clone()
+        bad[3] = NB
+        with pytest.raises(sk.SinkhornError, match="out-of-range") as e:
+            P.verify_tiles(eps, _t(f), _t(g), B, 1e-3, ptr, bad)
+        assert e.value.code == sk.ERR_INVALID_ARG
+
+
+def test_multiscale_verified_fixed_budget_matches_the_oracle(sk):
+    """The fixed-budget solve with tile verification: same cell and iteration
+    counts, kept-tile count within fp32 borderline flips, potentials within
+    1e-3 eps of the oracle's verified run."""
+    path = os.path.join(GOLDEN, "fs2_w5_n16384_fixed_verify.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_solve_refs.py w5_n16384_fixed_verify")
+    ref = dict(np.load(path))
+    n = int(ref["n"])
+    c = synth.make(5, n=n, m=n)
+    eps = float(ref["eps"])
+    prm = sk.MultiscaleParams(B=int(ref["B"]), eps=eps, tol=float(ref["tol"]), coarse_tol=float(ref["coarse_tol"]),
+                              coarse_max=int(ref["coarse_max"]), stall_window=int(ref["stall_window"]),
+                              max_fine=int(ref["max_fine"]), verify=True)
+    _log(f"multiscale verified fixed budget n={n}")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+    assert rep["status"] == sk.NOT_CONVERGED and rep["certified"] == 0
+    assert rep["ncells_x"] == int(ref["ncells_x"]) and rep["ncells_y"] == int(ref["ncells_y"])
+    assert rep["coarse_iters"] == int(ref["coarse_iters"])
+    assert rep["fine_updates"] == int(ref["fine_updates"]) == prm.max_fine
+    cands, tiles = int(ref["candidates"][-1]), int(ref["tiles"][-1])
+    assert abs(rep["last_candidates"] - cands) <= max(2, cands // 1000), (rep["last_candidates"], cands)
+    assert abs(rep["last_tiles"] - tiles) <= max(2, tiles // 200), (rep["last_tiles"], tiles)
+    assert rep["last_tiles"] < rep["last_candidates"]
+    _gauge_close(f, g, ref["f"], ref["g"], 1e-3 * eps)
+    assert rep["R_A_row"] == pytest.approx(float(ref["R_A_row"]), rel=1e-2)

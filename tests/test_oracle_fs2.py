@@ -69,16 +69,19 @@ def test_cells_partition_and_centroids(rng):
         np.testing.assert_allclose(cent[c], (ws[s:e, None] * xs[s:e]).sum(0) / ws[s:e].sum(), rtol=1e-12)
 
 
-def test_pipeline_is_certified_and_the_certificate_holds(rng):
+@pytest.mark.parametrize("verify", [False, True], ids=["screened", "verified"])
+def test_pipeline_is_certified_and_the_certificate_holds(rng, verify):
     cx = rng.uniform(0.2, 0.8, size=(4, 3))
     n = 2048
     lab = rng.integers(0, 4, n)
     x = (cx[lab] + rng.normal(0, 0.03, size=(n, 3))).astype(np.float32)
     y = (cx[lab] + rng.normal(0, 0.03, size=(n, 3)) + 0.01).astype(np.float32)
     w = np.full(n, 1 / n, np.float32)
-    prm = FS2Params(B=64, eps=2e-3, tol=2e-2, max_fine=60)
+    prm = FS2Params(B=64, eps=2e-3, tol=2e-2, max_fine=60, verify=verify)
     res = oracle.fs2_solve(x, y, w, w, prm)
     assert res.certified
+    if verify:  # verification drops some screened tiles
+        assert res.tiles_history[-1] < res.candidates_history[-1]
     Fr, Fc = oracle.marginal_residuals(x, y, w, w, res.f, res.g, prm.eps, 1.0)
     assert max(Fr, Fc) <= prm.tol
     assert max(Fr, Fc) <= max(res.R_A_row, res.R_A_col) + res.omega + 1e-12
