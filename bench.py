@@ -166,6 +166,8 @@ def main():
                     help="no HIP events around the pair-kernel launches (no roofline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--verify", action="store_true",
+                    help="workload 5: verify the screened tiles (exact shares) before each fine update")
     ap.add_argument("--max-fine", type=int, default=None,
                     help="workload 5: cap on fine updates (profiling runs; the default runs to the certificate)")
     args = ap.parse_args()
@@ -194,10 +196,14 @@ def main():
     # the cost scale is resolved once, as a number, before anything is timed
     scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
     multiscale = "multiscale" in W
+    if args.verify and not multiscale:
+        print("bench.py: --verify applies to the multiscale workload (5) only", file=sys.stderr)
+        sys.exit(2)
     if multiscale:
         prm = sk.MultiscaleParams(**W["multiscale"])
         if args.max_fine is not None:
             prm.max_fine = args.max_fine
+        prm.verify = bool(args.verify)
         eps = prm.eps
         kind = sk.PROF_SPARSE
     else:
@@ -306,9 +312,11 @@ def main():
         "wall_time_to_residual_s": sum(r[0]["seconds"] for r in reps) / len(reps),
     }
     if multiscale:
-        for k in ("certified", "coarse_iters", "fine_updates", "ncells_x", "ncells_y", "last_tiles", "R_A_row",
-                  "R_A_col", "omega", "seconds_sort", "seconds_coarse", "seconds_lift", "seconds_fine"):
+        for k in ("certified", "coarse_iters", "fine_updates", "ncells_x", "ncells_y", "last_tiles",
+                  "last_candidates", "R_A_row", "R_A_col", "omega", "seconds_sort", "seconds_coarse",
+                  "seconds_lift", "seconds_fine"):
             out[k] = last[k]
+        out["verify"] = bool(prm.verify)
     else:
         out.update(halfsteps_per_solve=last["halfsteps"], iters_per_solve=last["iters"],
                    final_row_l1=last["row_l1"], final_col_l1=last["col_l1"])

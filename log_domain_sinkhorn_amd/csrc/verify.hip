@@ -59,10 +59,7 @@ struct VerifyArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void k_verify(VerifyArgs A) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t e = (int64_t)blockIdx.x * 4 + wave;
-  if (e >= A.nnz) return;
+__device__ __forceinline__ void verify_tile(const VerifyArgs& A, int64_t e) {
   // row block of candidate e: the last I with ptr[I] <= e
   int64_t lo = 0, hi = A.nb;
   while (hi - lo > 1) {
@@ -82,21 +79,36 @@ __global__ __launch_bounds__(256) void k_verify(VerifyArgs A) {
   for (int q = 0; q < 16; ++q) {
     const int64_t i = I * kVerifyB + r8 + 8 * q;
     const bool ok = i < A.n;
+    const int64_t ic = ok ? i : A.n - 1;  // clamped: the loads need no branch
 #pragma unroll
-    for (int k = 0; k < D; ++k) x[q][k] = ok ? A.xs[k * A.xstride + i] : 0.0f;
-    u[q] = ok ? -A.f[i] * A.inv_s : INFINITY;
-    aw[q] = ok ? A.a[i] : 0.0f;
+    for (int k = 0; k < D; ++k) x[q][k] = A.xs[k * A.xstride + ic];
+    const float fv = A.f[ic], av = A.a[ic];
+    u[q] = ok ? -fv * A.inv_s : INFINITY;
+    aw[q] = ok ? av : 0.0f;
     R[q] = 0.0f;
   }
   bool big = false;
-  for (int bb = 0; bb < 16; ++bb) {
+  // column data of step bb + 1 is loaded while step bb computes
+  float yn[D], gn, bn;
+  auto load_col = [&](int bb) {
     const int64_t j = J * kVerifyB + c8 + 8 * bb;
     const bool ok = j < A.m;
+    const int64_t jc = ok ? j : A.m - 1;
+#pragma unroll
+    for (int k = 0; k < D; ++k) yn[k] = A.ys[k * A.ystride + jc];
+    const float gv = A.g[jc], bv = A.b[jc];
+    gn = ok ? gv : -INFINITY;
+    bn = ok ? bv : 0.0f;
+  };
+  load_col(0);
+#pragma unroll 1
+  for (int bb = 0; bb < 16; ++bb) {
     float y[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) y[k] = ok ? A.ys[k * A.ystride + j] : 0.0f;
-    const float lg = ok ? A.lam * A.g[j] : -INFINITY;
-    const float bj = ok ? A.b[j] : 0.0f;
+    for (int k = 0; k < D; ++k) y[k] = yn[k];
+    const float lg = A.lam * gn;
+    const float bj = bn;
+    if (bb + 1 < 16) load_col(bb + 1);
     float c = 0.0f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -130,6 +142,15 @@ __global__ __launch_bounds__(256) void k_verify(VerifyArgs A) {
   if (lane == 0) A.keep[e] = any != 0 ? 1 : 0;
 }
 
+// Tiles are taken in a wave-stride loop: a grid of one wave per tile would
+// exceed the 2^32 work-items of one dispatch at 2^24 points.
+template <int D>
+__global__ __launch_bounds__(256) void k_verify(VerifyArgs A) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * 4;
+  for (int64_t e = (int64_t)blockIdx.x * 4 + wave; e < A.nnz; e += step)
+    verify_tile<D>(A, e);
+}
 // One wave per row block: a block whose candidates all failed keeps them all.
 __global__ __launch_bounds__(64) void k_row_fallback(const int64_t* __restrict__ ptr, int64_t nb,
                                                      uint8_t* __restrict__ keep) {
@@ -217,7 +238,10 @@ __global__ __launch_bounds__(256) void k_col_bounds(const int32_t* __restrict__ 
 
 template <int D>
 void launch_verify(hipStream_t st, const VerifyArgs& A) {
-  hipLaunchKernelGGL((k_verify<D>), dim3((uint32_t)((A.nnz + 3) / 4)), dim3(256), 0, st, A);
+  constexpr int64_t kMaxGroups = 1 << 20;  // 2^28 work-items
+  const int64_t want = (A.nnz + 3) / 4;
+  hipLaunchKernelGGL((k_verify<D>), dim3((uint32_t)(want < kMaxGroups ? want : kMaxGroups)), dim3(256),
+                     0, st, A);
   SK_LAUNCH_CHECK();
 }
 

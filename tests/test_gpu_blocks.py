@@ -394,3 +394,48 @@ def test_multiscale_verified_fixed_budget_matches_the_oracle(sk):
     assert rep["last_tiles"] < rep["last_candidates"]
     _gauge_close(f, g, ref["f"], ref["g"], 1e-3 * eps)
     assert rep["R_A_row"] == pytest.approx(float(ref["R_A_row"]), rel=1e-2)
+
+
+def test_verify_tiles_full_size_sampled(sk):
+    """2^24 points, B = 128, every screened tile verified in one launch (more
+    tiles than one wave per tile could address); sampled candidates checked
+    against the oracle's exact shares: a tile clearly above the threshold is
+    kept, a tile clearly below is dropped unless its row or column block
+    fallback keeps all of that block's candidates."""
+    c = synth.make(5)
+    cx, px, cy, py = _gpu_morton(sk, c.x, c.y)
+    x, y, a, b = c.x[px], c.y[py], c.a[px], c.b[py]
+    eps = 1e-4
+    rng = np.random.default_rng(4)
+    f, g = _near_plan_potentials(c.n, eps, rng)
+    B = 128
+    NB = c.n // B
+    delta = 1e-3 / NB
+    _log("verify full size")
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        ptr, idx = P.block_screen(eps, _t(f), _t(g), B, delta)
+        vptr, vidx, tptr, tidx = P.verify_tiles(eps, _t(f), _t(g), B, delta, ptr, idx)
+    nnz = int(idx.shape[0])
+    _log(f"  {nnz} candidates, {int(vidx.shape[0])} kept")
+    assert nnz > (1 << 22)  # more tiles than one pass of the kernel's grid: the stride loop runs
+    ptr, idx = ptr.cpu().numpy(), idx.cpu().numpy()
+    vptr, vidx = vptr.cpu().numpy(), vidx.cpu().numpy()
+    assert np.array_equal(np.diff(tptr.cpu().numpy()).sum(), len(vidx))
+    checked = 0
+    for e in np.sort(rng.choice(nnz, 64, replace=False)):
+        I = int(np.searchsorted(ptr, e, side="right") - 1)
+        J = int(idx[e])
+        kept_row = vidx[vptr[I]:vptr[I + 1]]
+        kept = bool(np.any(kept_row == J))
+        s, t = oracle.tile_shares(x, y, a, b, f, g, eps, 1.0, I, J, B)
+        top = max(s.max(), t.max()) / delta
+        if abs(top - 1.0) < 1e-3:
+            continue
+        checked += 1
+        if top > 1.0:
+            assert kept, (I, J, top)
+        elif kept:
+            row_all = len(kept_row) == ptr[I + 1] - ptr[I]
+            col_all = np.count_nonzero(vidx == J) == np.count_nonzero(idx == J)
+            assert row_all or col_all, (I, J, top)
+    assert checked >= 48
