@@ -17,6 +17,14 @@ FlashSinkhorn 2:
   * §3.2 (with §C.5): optionally, the screened tiles are verified with their
     exact row and column shares before the half-steps (``verify_tiles``), and
     both supports come from the survivors.
+  * §3.1 and §B.2 (optional adaptive switch): the coarse stage runs in batches
+    of centroid updates; after each, the lifted potentials are accepted when
+    sampled row and column residual estimates plus three standard errors are
+    below tol (1024 sampled indices per side, expanded to 8192 when that
+    interval straddles tol, the same samples at every check); otherwise more
+    centroid updates follow until they stall or reach their cap, and the fine
+    loop takes over. Sample indices: the raw outputs of Philox4x64-10 keyed
+    (seed, side) (numpy's ``Philox``), each reduced modulo the side's size.
   * §C.4: the stop certificate is the admitted-plan residual plus a bound on
     the omitted mass. Read here as R_A + Omega <= tol with
     Omega = max(NB, MB) * delta_rel, the a-priori total omitted-mass bound
@@ -39,7 +47,7 @@ from .blocks import (
     sparse_residuals,
     verify_tiles,
 )
-from .dense import Schedule, annealing_stages, halfstep_f, halfstep_g, marginal_residuals
+from .dense import Schedule, annealing_stages, halfstep_f, halfstep_g, marginal_residuals, plan_rows
 from .morton import BITS, morton_order
 
 
@@ -92,6 +100,11 @@ class FS2Params:
     p_bits: int = -1  # -1: floor(log2(2 * max(NB, MB)))
     scale: float = 1.0
     verify: bool = False  # exact share check of the screened tiles
+    adaptive: bool = False  # sampled lift checks between batches of coarse updates
+    check_every: int = 128  # coarse updates per batch
+    check_samples: int = 1024
+    check_samples_max: int = 8192
+    sample_seed: int = 0
 
 
 @dataclass
@@ -108,6 +121,9 @@ class FS2Result:
     ncells_y: int
     tiles_history: list = field(default_factory=list)
     candidates_history: list = field(default_factory=list)
+    accepted_by_sample: bool = False
+    checks: int = 0
+    check_history: list = field(default_factory=list)  # (R_row, SE_row, R_col, SE_col, samples)
 
 
 def prefix_bits(NB: int, MB: int, d: int) -> int:
@@ -141,6 +157,73 @@ def coarse_solve(cx, cy, mx, my, prm: FS2Params):
     return F, G, iters
 
 
+def sample_indices(count: int, k: int, seed: int, stream: int) -> np.ndarray:
+    """k indices in [0, count), uniform with replacement: the first k raw
+    outputs of Philox4x64-10 keyed (seed, stream), each modulo count."""
+    raw = np.random.Philox(key=np.array([seed, stream], dtype=np.uint64)).random_raw(k)
+    return (raw % np.uint64(count)).astype(np.int64)
+
+
+def sampled_residual(P, Q, wp, wq, fp, gq, eps: float, scale: float, idx):
+    """(estimate, standard error) of R = sum_i |sum_j pi_ij - a_i| from the
+    rows idx drawn uniformly with replacement: count * mean(t) and
+    count * std(t, ddof=1) / sqrt(k), t = |sum_j pi_ij - a_i| of each drawn row
+    (FlashSinkhorn 2, §3.1: sampled row sums cost O(md))."""
+    rows = np.asarray(idx, np.int64)
+    T = plan_rows(P, Q, wp, wq, fp, gq, eps, scale, rows=rows)
+    t = np.abs(T.sum(axis=1) - np.asarray(wp, np.float64)[rows])
+    k = len(rows)
+    est = len(P) * float(t.mean())
+    se = len(P) * float(t.std(ddof=1)) / math.sqrt(k) if k > 1 else math.inf
+    return est, se
+
+
+def lift_accepted(X, Y, A, Bw, f, g, prm):
+    """The sampled check of lifted potentials: (accepted, (R_row, SE_row,
+    R_col, SE_col, samples))."""
+    k = prm.check_samples
+    while True:
+        er, sr = sampled_residual(X, Y, A, Bw, f, g, prm.eps, prm.scale,
+                                  sample_indices(len(X), k, prm.sample_seed, 0))
+        ec, sc = sampled_residual(Y, X, Bw, A, g, f, prm.eps, prm.scale,
+                                  sample_indices(len(Y), k, prm.sample_seed, 1))
+        info = (er, sr, ec, sc, k)
+        hi = max(er + 3.0 * sr, ec + 3.0 * sc)
+        lo = max(er - 3.0 * sr, ec - 3.0 * sc)
+        if hi < prm.tol:
+            return True, info
+        if lo >= prm.tol or k >= prm.check_samples_max:
+            return False, info
+        k = prm.check_samples_max
+
+
+def coarse_batch(cx, cy, mx, my, F, G, prm, count: int, anneal: bool):
+    """Optionally the annealing stages, then up to ``count`` updates at the
+    target eps, stopping early when R <= coarse_tol or the residual stalls
+    (stall window counted within the batch). Returns F, G, the annealing
+    updates, the updates at the target eps, and done (converged or stalled)."""
+    iters = 0
+    annealed = 0
+    if anneal:
+        sched = Schedule(prm.coarse_eps_start, prm.eps, prm.coarse_factor, prm.coarse_iters_per_stage)
+        for eps in annealing_stages(sched):
+            for _ in range(prm.coarse_iters_per_stage):
+                F = halfstep_f(cx, cy, my, G, eps, prm.scale)
+                G = halfstep_g(cx, cy, mx, F, eps, prm.scale)
+                annealed += 1
+    hist = []
+    for _ in range(count):
+        F = halfstep_f(cx, cy, my, G, prm.eps, prm.scale)
+        G = halfstep_g(cx, cy, mx, F, prm.eps, prm.scale)
+        iters += 1
+        R = max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale))
+        hist.append(R)
+        w = prm.stall_window
+        if R <= prm.coarse_tol or (len(hist) > w and hist[-1] > (1.0 - prm.stall_rel) * hist[-1 - w]):
+            return F, G, annealed, iters, True
+    return F, G, annealed, iters, False
+
+
 def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     x = np.asarray(x, np.float32)
     y = np.asarray(y, np.float32)
@@ -159,9 +242,36 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     offx, centx, massx = cells(cxs, X, A, p_bits)
     offy, centy, massy = cells(cys, Y, Bw, p_bits)
 
-    F, G, coarse_iters = coarse_solve(centx, centy, massx, massy, prm)
-    f = lift(X, centy, massy, G, prm.eps, prm.scale)
-    g = lift(Y, centx, massx, F, prm.eps, prm.scale)
+    accepted = False
+    checks = []
+    if prm.adaptive:
+        F = np.zeros(len(centx))
+        G = np.zeros(len(centy))
+        coarse_iters = 0
+        at_eps = 0
+        while True:
+            count = min(prm.check_every, prm.coarse_max - at_eps)
+            F, G, ann, it, done = coarse_batch(centx, centy, massx, massy, F, G, prm, count,
+                                               coarse_iters == 0)
+            at_eps += it
+            coarse_iters += ann + it
+            f = lift(X, centy, massy, G, prm.eps, prm.scale)
+            g = lift(Y, centx, massx, F, prm.eps, prm.scale)
+            accepted, info = lift_accepted(X, Y, A, Bw, f.astype(np.float32), g.astype(np.float32), prm)
+            checks.append(info)
+            if accepted or done or at_eps >= prm.coarse_max:
+                break
+    else:
+        F, G, coarse_iters = coarse_solve(centx, centy, massx, massy, prm)
+        f = lift(X, centy, massy, G, prm.eps, prm.scale)
+        g = lift(Y, centx, massx, F, prm.eps, prm.scale)
+    if accepted:
+        fu = np.empty(n)
+        gu = np.empty(m)
+        fu[px] = f
+        gu[py] = g
+        return FS2Result(fu, gu, coarse_iters, 0, math.nan, math.nan, omega, False,
+                         len(centx), len(centy), [], [], True, len(checks), checks)
 
     tiles = []
     cands = []
@@ -196,4 +306,4 @@ def fs2_solve(x, y, a, b, prm: FS2Params) -> FS2Result:
     fu[px] = f
     gu[py] = g
     return FS2Result(fu, gu, coarse_iters, updates, R_row, R_col, omega, certified,
-                     len(centx), len(centy), tiles, cands)
+                     len(centx), len(centy), tiles, cands, False, len(checks), checks)

@@ -85,3 +85,94 @@ def test_pipeline_is_certified_and_the_certificate_holds(rng, verify):
     Fr, Fc = oracle.marginal_residuals(x, y, w, w, res.f, res.g, prm.eps, 1.0)
     assert max(Fr, Fc) <= prm.tol
     assert max(Fr, Fc) <= max(res.R_A_row, res.R_A_col) + res.omega + 1e-12
+
+
+# ---- sampled lift checks and the adaptive coarse-to-fine switch (FlashSinkhorn 2, §3.1, §B.2)
+
+from oracle.fs2 import lift_accepted, sample_indices, sampled_residual  # noqa: E402
+
+
+def test_sample_indices_range_reuse_and_uniformity():
+    a = sample_indices(1000, 8192, 7, 0)
+    assert a.dtype == np.int64 and a.min() >= 0 and a.max() < 1000
+    assert np.array_equal(sample_indices(1000, 1024, 7, 0), a[:1024])  # the first draws are reused
+    assert not np.array_equal(sample_indices(1000, 1024, 7, 1), a[:1024])  # other side, other stream
+    counts = np.bincount(sample_indices(10, 200000, 3, 0), minlength=10)
+    chi2 = float(((counts - 20000.0) ** 2 / 20000.0).sum())
+    assert chi2 < 40.0  # 9 degrees of freedom: p ~ 1e-5
+
+
+def _small_problem(rng, n=600, eps=0.02, iters=5):
+    x = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    y = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    a = rng.uniform(0.5, 1.5, n)
+    a = (a / a.sum()).astype(np.float32)
+    b = np.full(n, 1.0 / n, np.float32)
+    res = oracle.solve(x, y, a, b, 1.0, oracle.Schedule(eps, eps, fixed_iters=iters))
+    return x, y, a, b, res.f, res.g, eps
+
+
+def test_sampled_residual_with_every_row_once_is_the_residual(rng):
+    x, y, a, b, f, g, eps = _small_problem(rng)
+    R_row, R_col = oracle.marginal_residuals(x, y, a, b, f, g, eps, 1.0)
+    est, se = sampled_residual(x, y, a, b, f, g, eps, 1.0, np.arange(len(x)))
+    assert est == pytest.approx(R_row, rel=1e-12)
+    est_c, _ = sampled_residual(y, x, b, a, g, f, eps, 1.0, np.arange(len(y)))
+    assert est_c == pytest.approx(R_col, rel=1e-12, abs=1e-15)
+
+
+def test_sampled_residual_is_unbiased_and_its_error_is_the_sample_spread(rng):
+    x, y, a, b, f, g, eps = _small_problem(rng)
+    R_row, _ = oracle.marginal_residuals(x, y, a, b, f, g, eps, 1.0)
+    ests, ses = [], []
+    for seed in range(40):
+        e, s = sampled_residual(x, y, a, b, f, g, eps, 1.0, sample_indices(len(x), 64, seed, 0))
+        ests.append(e)
+        ses.append(s)
+    # the mean of 40 independent estimates sits within 4 of its standard errors
+    assert abs(np.mean(ests) - R_row) < 4.0 * np.mean(ses) / math.sqrt(40)
+    # and the reported standard error matches the spread of the estimates
+    assert 0.5 < np.std(ests, ddof=1) / np.mean(ses) < 1.6
+    # a residual that is the same on every row has no spread
+    f0 = f.copy()
+    est, se = sampled_residual(x, y, a, b, f0, g, eps, 1.0, np.zeros(16, np.int64))
+    assert se == 0.0
+
+
+def test_adaptive_switch_accepts_an_exact_lift(rng):
+    """Singleton cells make the lift an ordinary half-step, so after enough
+    centroid updates the lifted potentials pass the sampled check and are
+    returned without fine updates; their exact residual is under tol."""
+    n = 512
+    x = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    y = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    w = np.full(n, 1.0 / n, np.float32)
+    prm = FS2Params(B=16, eps=0.005, tol=1e-2, p_bits=42, coarse_tol=0.0, stall_window=1 << 30,
+                    coarse_iters_per_stage=2, adaptive=True, check_every=3, check_samples=128,
+                    check_samples_max=512)
+    res = oracle.fs2_solve(x, y, w, w, prm)
+    assert res.accepted_by_sample and res.fine_updates == 0 and not res.certified
+    assert res.ncells_x == n and res.ncells_y == n
+    R = max(oracle.marginal_residuals(x, y, w, w, res.f, res.g, prm.eps, 1.0))
+    assert R < prm.tol
+    er, sr, ec, sc, k = res.check_history[-1]
+    assert max(er + 3 * sr, ec + 3 * sc) < prm.tol
+    assert res.checks > 1  # earlier lifts failed the check
+    er, sr, ec, sc, k = res.check_history[-2]
+    assert max(er + 3 * sr, ec + 3 * sc) >= prm.tol
+    # a check whose interval straddled tol was repeated with the larger sample
+    assert any(h[4] == prm.check_samples_max for h in res.check_history)
+
+
+def test_adaptive_switch_falls_back_to_certified_fine_updates(rng):
+    cx = rng.uniform(0.2, 0.8, size=(4, 3))
+    n = 2048
+    lab = rng.integers(0, 4, n)
+    x = (cx[lab] + rng.normal(0, 0.03, size=(n, 3))).astype(np.float32)
+    y = (cx[lab] + rng.normal(0, 0.03, size=(n, 3)) + 0.01).astype(np.float32)
+    w = np.full(n, 1 / n, np.float32)
+    prm = FS2Params(B=64, eps=2e-3, tol=2e-2, max_fine=60, adaptive=True, check_every=32)
+    res = oracle.fs2_solve(x, y, w, w, prm)
+    assert not res.accepted_by_sample and res.checks >= 1 and res.certified and res.fine_updates > 0
+    Fr, Fc = oracle.marginal_residuals(x, y, w, w, res.f, res.g, prm.eps, 1.0)
+    assert max(Fr, Fc) <= max(res.R_A_row, res.R_A_col) + res.omega + 1e-12
