@@ -168,6 +168,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--verify", action="store_true",
                     help="workload 5: verify the screened tiles (exact shares) before each fine update")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="workload 5: sampled lift checks between batches of coarse updates")
     ap.add_argument("--max-fine", type=int, default=None,
                     help="workload 5: cap on fine updates (profiling runs; the default runs to the certificate)")
     args = ap.parse_args()
@@ -196,14 +198,15 @@ def main():
     # the cost scale is resolved once, as a number, before anything is timed
     scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
     multiscale = "multiscale" in W
-    if args.verify and not multiscale:
-        print("bench.py: --verify applies to the multiscale workload (5) only", file=sys.stderr)
+    if (args.verify or args.adaptive) and not multiscale:
+        print("bench.py: --verify and --adaptive apply to the multiscale workload (5) only", file=sys.stderr)
         sys.exit(2)
     if multiscale:
         prm = sk.MultiscaleParams(**W["multiscale"])
         if args.max_fine is not None:
             prm.max_fine = args.max_fine
         prm.verify = bool(args.verify)
+        prm.adaptive = bool(args.adaptive)
         eps = prm.eps
         kind = sk.PROF_SPARSE
     else:
@@ -317,6 +320,11 @@ def main():
                   "seconds_lift", "seconds_fine"):
             out[k] = last[k]
         out["verify"] = bool(prm.verify)
+        out["adaptive"] = bool(prm.adaptive)
+        if prm.adaptive:
+            out.update(accepted_by_sample=bool(last["accepted_by_sample"]), checks=last["checks"],
+                       last_check=dict(zip(("row", "row_se", "col", "col_se"), last["last_check"]),
+                                       samples=last["last_check_samples"]))
     else:
         out.update(halfsteps_per_solve=last["halfsteps"], iters_per_solve=last["iters"],
                    final_row_l1=last["row_l1"], final_col_l1=last["col_l1"])

@@ -251,6 +251,21 @@ typedef struct {
   int32_t max_fine;         /* cap on fine updates */
   int32_t verify;           /* nonzero: verify the screened tiles (sinkhorn_verify_tiles rule,
                                B = 128) before each fine update's half-steps */
+  /* Adaptive coarse-to-fine switch (FlashSinkhorn 2, §3.1, §B.2), when nonzero: the coarse
+   * stage runs in batches of check_every centroid updates (the first after the annealing
+   * stages), each ending early on coarse_tol or a stall; after each batch the potentials are
+   * lifted and accepted, with no fine update, when the sampled row and column residual
+   * estimates plus three standard errors are below tol (check_samples indices per side,
+   * check_samples_max when that interval straddles tol; the same indices at every check).
+   * Otherwise batches continue until the coarse stage converges, stalls or reaches
+   * coarse_max, and the certified fine loop follows. Sample k of a side of size c is
+   * word k % 4 of Philox4x64-10 at counter (k / 4 + 1, 0, 0, 0) with key
+   * (sample_seed, side), side 0 for x and 1 for y, modulo c. */
+  int32_t adaptive;
+  int32_t check_every;
+  int32_t check_samples;
+  int32_t check_samples_max;
+  uint64_t sample_seed;
 } sinkhorn_multiscale_params;
 
 typedef struct {
@@ -264,6 +279,11 @@ typedef struct {
   double seconds_total, seconds_sort, seconds_coarse, seconds_lift, seconds_fine;
   int32_t certified;
   int64_t last_candidates;  /* screened tiles of the last mask (= last_tiles without verify) */
+  int32_t accepted_by_sample;  /* adaptive: a lift passed the sampled check (no fine update) */
+  int64_t checks;              /* adaptive: sampled checks run */
+  int64_t last_check_samples;  /* samples per side of the last check */
+  double last_check[4];        /* its row estimate, row standard error, column estimate, column
+                                  standard error */
 } sinkhorn_multiscale_report;
 
 /* Block-sparse multiscale solve for d <= 3 (FlashSinkhorn 2): Morton sort,
@@ -275,6 +295,25 @@ typedef struct {
  * rep (host) may be NULL. Returns SINKHORN_NOT_CONVERGED at the fine cap. */
 int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
                               float* f, float* g, sinkhorn_multiscale_report* rep);
+
+/* Sample indices of the sampled residual checks (FlashSinkhorn 2, §B.2: 1024
+ * indices per side, up to 8192): out[k] (device int32) = word k % 4 of
+ * Philox4x64-10 (Salmon et al., SC 2011) at counter (k / 4 + 1, 0, 0, 0) with
+ * key (seed, stream_id), modulo count; uniform with replacement, and a longer
+ * draw repeats a shorter one. 1 <= count < 2^31. Synchronizes `stream`. */
+int sinkhorn_sample_indices(int64_t count, int32_t k, uint64_t seed, uint64_t stream_id, void* stream,
+                            int32_t* out);
+
+/* Sampled marginal residual (FlashSinkhorn 2, §3.1: sampled row sums cost
+ * O(md)): draws k indices of one side of the handle's clouds in their stored
+ * order (side 0: rows of x, stream 0; side 1: rows of y, stream 1; indices as
+ * sinkhorn_sample_indices with this seed), evaluates each drawn row's
+ * |sum_j pi_ij - w_i| at (f, g) with one dense half-step of those rows, and
+ * returns (host) the estimate count * mean and its standard error
+ * count * std (k - 1 in the variance) / sqrt(k) of the L1 residual of that
+ * side. 2 <= k <= 2^24, d <= 8. Synchronizes the handle's stream. */
+int sinkhorn_sampled_residual(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                              int32_t side, int32_t k, uint64_t seed, double* est, double* se);
 
 /* Sparsified plan (moscot pull request #846: thresholding on the device and
  * moving only the surviving values and indices): every entry T_ij >= threshold,

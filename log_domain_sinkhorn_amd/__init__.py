@@ -99,6 +99,11 @@ class _MultiscaleParamsC(ctypes.Structure):
         ("stall_rel", _f64),
         ("max_fine", _i32),
         ("verify", _i32),
+        ("adaptive", _i32),
+        ("check_every", _i32),
+        ("check_samples", _i32),
+        ("check_samples_max", _i32),
+        ("sample_seed", ctypes.c_uint64),
     ]
 
 
@@ -120,6 +125,10 @@ class _MultiscaleReportC(ctypes.Structure):
         ("seconds_fine", _f64),
         ("certified", _i32),
         ("last_candidates", _i64),
+        ("accepted_by_sample", _i32),
+        ("checks", _i64),
+        ("last_check_samples", _i64),
+        ("last_check", _f64 * 4),
     ]
 
 
@@ -146,6 +155,8 @@ _SIGS = {
     "sinkhorn_sparsify": ([_p, _f64, _p, _p, ctypes.c_float, _i64, _p, _p, _p, _i64, _p], _i32),
     "sinkhorn_sparse_barycentric": ([_p, _f64, _p, _p, _i32, _p, _p, _p, _p], _i32),
     "sinkhorn_solve_multiscale": ([_p, _p, _p, _p, _p], _i32),
+    "sinkhorn_sample_indices": ([_i64, _i32, ctypes.c_uint64, ctypes.c_uint64, _p, _p], _i32),
+    "sinkhorn_sampled_residual": ([_p, _f64, _p, _p, _i32, _i32, ctypes.c_uint64, _p, _p], _i32),
     "sinkhorn_profile_enable": ([_p, _i32], _i32),
     "sinkhorn_profile_read": ([_p, _p, _p, _p], _i32),
 }
@@ -243,17 +254,35 @@ class MultiscaleParams:
     stall_rel: float = 0.01
     max_fine: int = 8192
     verify: bool = False
+    adaptive: bool = False
+    check_every: int = 128
+    check_samples: int = 1024
+    check_samples_max: int = 8192
+    sample_seed: int = 0
 
     def _c(self) -> _MultiscaleParamsC:
         return _MultiscaleParamsC(self.B, self.p_bits, self.eps, self.tol, self.delta_scale,
                                   self.coarse_eps_start, self.coarse_factor,
                                   self.coarse_iters_per_stage, self.coarse_tol, self.coarse_max,
                                   self.stall_window, self.stall_rel, self.max_fine,
-                                  int(bool(self.verify)))
+                                  int(bool(self.verify)), int(bool(self.adaptive)), self.check_every,
+                                  self.check_samples, self.check_samples_max, self.sample_seed)
 
 
 def _struct_dict(s) -> dict:
-    return {name: getattr(s, name) for name, _ in s._fields_}
+    out = {}
+    for name, _ in s._fields_:
+        v = getattr(s, name)
+        out[name] = list(v) if isinstance(v, ctypes.Array) else v
+    return out
+
+
+def sample_indices(count: int, k: int, seed: int, stream_id: int, device="cuda:0") -> torch.Tensor:
+    """The sampled checks' indices as an int32 device tensor."""
+    out = torch.empty(max(1, k), dtype=torch.int32, device=device)
+    _check(lib().sinkhorn_sample_indices(int(count), int(k), int(seed), int(stream_id),
+                                         _stream(torch.device(device)), _ptr(out)), "sample_indices")
+    return out[:k]
 
 
 def mean_sqeuclid(x: torch.Tensor, y: torch.Tensor) -> float:
@@ -521,6 +550,17 @@ class Problem:
         _check(lib().sinkhorn_profile_read(self._h, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(pairs)),
                "profile_read")
         return ms.value, n.value, pairs.value
+
+    def sampled_residual(self, eps, f, g, side=0, k=1024, seed=0):
+        """(estimate, standard error) of one side's L1 marginal residual from k
+        drawn rows (side 0: x, side 1: y)."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        est, se = _f64(), _f64()
+        _check(lib().sinkhorn_sampled_residual(self._h, float(eps), _ptr(f), _ptr(g), int(side), int(k),
+                                               int(seed), ctypes.byref(est), ctypes.byref(se)),
+               "sampled_residual")
+        return est.value, se.value
 
     def solve_multiscale(self, prm: MultiscaleParams, f=None, g=None):
         f = self._new(self.n) if f is None else self._pot(f, self.n, "f")

@@ -201,6 +201,91 @@ struct TileList {
   }
 };
 
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 64 x 64 -> 128-bit products
+// with the key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kM0, c[0]), lo0 = kM0 * c[0];
+    const uint64_t hi1 = __umul64hi(kM1, c[2]), lo1 = kM1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += kW0;
+    k1 += kW1;
+  }
+}
+
+// Sample k of a side of size count: word k % 4 of the block at counter
+// (k / 4 + 1, 0, 0, 0), key (seed, stream), modulo count.
+__global__ __launch_bounds__(256) void k_sample_idx(uint64_t seed, uint64_t stream, int64_t count,
+                                                    int32_t K, int32_t* __restrict__ out) {
+  const int32_t k = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (k >= K) return;
+  uint64_t c[4] = {(uint64_t)(k / 4) + 1ull, 0ull, 0ull, 0ull};
+  philox4x64_10(c, seed, stream);
+  out[k] = (int32_t)(c[k & 3] % (uint64_t)count);
+}
+
+// Drawn points of a side (coordinates, weight, potential) into a small side.
+__global__ __launch_bounds__(256) void k_gather_samples(const float* __restrict__ soa, int64_t stride,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ pot,
+                                                        const int32_t* __restrict__ idx, int32_t K,
+                                                        int32_t d, float* __restrict__ dsoa,
+                                                        int64_t dstride, float* __restrict__ dw,
+                                                        float* __restrict__ dpot) {
+  const int32_t k = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (k >= K) return;
+  const int64_t i = idx[k];
+  for (int32_t a = 0; a < d; ++a) dsoa[a * dstride + k] = soa[a * stride + i];
+  dw[k] = w[i];
+  dpot[k] = pot[i];
+}
+
+// One block: t_k = w_k |exp((f_k - ft_k)/eps) - 1| (the drawn row's |row sum
+// - w_k| from the half-step identity), out[0] = mean t, out[1] = sum (t -
+// mean)^2, in a fixed order.
+__global__ __launch_bounds__(256) void k_sample_terms(const float* __restrict__ w,
+                                                      const float* __restrict__ f,
+                                                      const float* __restrict__ ft, int32_t K,
+                                                      double inv_eps, double* __restrict__ out) {
+  __shared__ double sh[256];
+  auto term = [&](int32_t k) {
+    return (double)w[k] * fabs(expm1(((double)f[k] - (double)ft[k]) * inv_eps));
+  };
+  double s = 0.0;
+  for (int32_t k = threadIdx.x; k < K; k += 256) s += term(k);
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const double mean = sh[0] / (double)K;
+  __syncthreads();
+  double v = 0.0;
+  for (int32_t k = threadIdx.x; k < K; k += 256) {
+    const double e = term(k) - mean;
+    v += e * e;
+  }
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = mean;
+    out[1] = sh[0];
+  }
+}
+
 // Device buffers of one verified tile list (row- or column-major).
 struct VerifiedList {
   int64_t* ptr = nullptr;
@@ -225,6 +310,66 @@ struct VerifiedList {
   }
 };
 
+// Drawn points of one side for the sampled residual check.
+struct SampleSide {
+  Side S;
+  int32_t* idx = nullptr;
+  float* pot = nullptr;   // potential at the drawn points
+  float* ft = nullptr;    // half-step at the drawn points
+  double* sums = nullptr; // [2] mean term, sum of squared deviations
+  int32_t K = 0;
+  void release() {
+    free_side(S);
+    dev_free(idx);
+    dev_free(pot);
+    dev_free(ft);
+    dev_free(sums);
+    idx = nullptr;
+    pot = ft = nullptr;
+    sums = nullptr;
+    K = 0;
+  }
+  ~SampleSide() { release(); }
+};
+
+// (estimate, standard error) of sum_i |sum_j pi_ij - w_i| over the rows of
+// `rows` from K rows drawn with replacement (FlashSinkhorn 2, §3.1: sampled
+// row sums cost O(md)); `cols.H` must hold the column term of the other
+// side's potential at eps.
+void sampled_residual(sinkhorn_problem* p, const Side& rows, const Side& cols, const float* pot,
+                      double eps, uint64_t seed, uint64_t stream, int32_t K, SampleSide& S,
+                      double* est, double* se) {
+  hipStream_t st = p->stream;
+  if (S.K != K) {
+    SK_HIP(hipStreamSynchronize(st));
+    S.release();
+    alloc_side(S.S, K, p->d, st);
+    S.idx = (int32_t*)dev_alloc(sizeof(int32_t) * K);
+    S.pot = (float*)dev_alloc(sizeof(float) * K);
+    S.ft = (float*)dev_alloc(sizeof(float) * K);
+    S.sums = (double*)dev_alloc(sizeof(double) * 2);
+    S.K = K;
+  }
+  const uint32_t blocks = (uint32_t)((K + 255) / 256);
+  hipLaunchKernelGGL(k_sample_idx, dim3(blocks), dim3(256), 0, st, seed, stream, rows.count, K, S.idx);
+  SK_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_gather_samples, dim3(blocks), dim3(256), 0, st, rows.soa, rows.padded, rows.w,
+                     pot, S.idx, K, p->d, S.S.soa, S.S.padded, S.S.w, S.pot);
+  SK_LAUNCH_CHECK();
+  HalfStep hs{&S.S, &cols, cols.H, S.ft, nullptr, nullptr, eps, eps, false};
+  hs.shift_pot = S.pot;
+  dense_halfstep(p, hs);
+  hipLaunchKernelGGL(k_sample_terms, dim3(1), dim3(256), 0, st, S.S.w, S.pot, S.ft, K, 1.0 / eps,
+                     S.sums);
+  SK_LAUNCH_CHECK();
+  double h[2] = {0.0, 0.0};
+  SK_HIP(hipMemcpyAsync(h, S.sums, sizeof(h), hipMemcpyDeviceToHost, st));
+  SK_HIP(hipStreamSynchronize(st));
+  const double c = (double)rows.count;
+  *est = c * h[0];
+  *se = K > 1 ? c * std::sqrt(h[1] / (double)(K - 1)) / std::sqrt((double)K) : INFINITY;
+}
+
 }  // namespace
 }  // namespace sk
 
@@ -235,7 +380,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
   Side Xs, Ys, Cx, Cy;
   uint64_t* codes[2] = {nullptr, nullptr};
   int32_t* perm[2] = {nullptr, nullptr};
-  float* pot[8] = {};
+  float* pot[10] = {};
   BlockSummary sx, sy;
   auto cleanup = [&]() {
     free_side(Xs);
@@ -259,6 +404,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     if (!(P.tol > 0.0) || !(P.delta_scale > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "tol and delta_scale must be > 0");
     if (P.max_fine < 0 || P.coarse_max < 1) fail(SINKHORN_ERR_INVALID_ARG, "bad iteration caps");
     if (P.verify && P.B != kVerifyB) fail(SINKHORN_ERR_UNSUPPORTED, "tile verification needs B = 128");
+    if (P.adaptive && (P.check_every < 1 || P.check_samples < 2 || P.check_samples_max < P.check_samples ||
+                       P.check_samples_max > (1 << 24)))
+      fail(SINKHORN_ERR_INVALID_ARG, "adaptive switch: need check_every >= 1 and "
+                                     "2 <= check_samples <= check_samples_max <= 2^24");
     hipStream_t st = p->stream;
     const int32_t d = p->d;
     const int64_t n = p->n, m = p->m;
@@ -325,40 +474,99 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     cs.tol = P.coarse_tol;
     cs.max_iters = P.coarse_max;
     cs.check_every = 1;
-    const SolveOut co = dense_solve(p, Cx, Cy, pot[0], pot[1], CF, CG, cs, P.stall_window, P.stall_rel);
-    R.coarse_iters = co.iters;
-    R.pairs_evaluated += co.pairs;
-    const double t_coarse = now_s();
-    R.seconds_coarse = t_coarse - t_sorted;
-    progress("multiscale: coarse solve done: %d iterations (%.3f s)", (int)R.coarse_iters,
-             R.seconds_coarse);
+    float* fs[2] = {(float*)dev_alloc(sizeof(float) * n), (float*)dev_alloc(sizeof(float) * n)};
+    pot[6] = fs[0];
+    pot[7] = fs[1];
+    float* gs[2] = {(float*)dev_alloc(sizeof(float) * m), (float*)dev_alloc(sizeof(float) * m)};
+    pot[8] = gs[0];
+    pot[9] = gs[1];
+    const double eps = P.eps;
+    // lift: f from the y cells, g from the x cells
+    auto lift = [&]() {
+      reset_nonfinite(p);
+      prep_column_term(p, Cy, pot[1], eps, Cy.H);
+      dense_halfstep(p, HalfStep{&Xs, &Cy, Cy.H, fs[0], nullptr, nullptr, eps, eps, false});
+      prep_column_term(p, Cx, pot[0], eps, Cx.H);
+      dense_halfstep(p, HalfStep{&Ys, &Cx, Cx.H, gs[0], nullptr, nullptr, eps, eps, false});
+      R.pairs_evaluated += (double)n * (double)Cy.count + (double)m * (double)Cx.count;
+      int32_t bad = 0;
+      read_reduction(p, nullptr, &bad);
+      if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite lifted potential");
+    };
+    bool accepted = false;
+    double t_coarse, t_lift;
+    if (!P.adaptive) {
+      const SolveOut co = dense_solve(p, Cx, Cy, pot[0], pot[1], CF, CG, cs, P.stall_window, P.stall_rel);
+      R.coarse_iters = co.iters;
+      R.pairs_evaluated += co.pairs;
+      t_coarse = now_s();
+      R.seconds_coarse = t_coarse - t_sorted;
+      progress("multiscale: coarse solve done: %d iterations (%.3f s)", (int)R.coarse_iters,
+               R.seconds_coarse);
+      lift();
+      t_lift = now_s();
+      R.seconds_lift = t_lift - t_coarse;
+    } else {
+      // batches of centroid updates, each followed by a lift and the sampled check
+      need(P.check_samples_max, m);
+      need(P.check_samples_max, n);
+      SampleSide smp[2][2];  // [side][small, large sample]
+      int64_t at_eps = 0;
+      double lift_s = 0.0;
+      for (bool first = true;; first = false) {
+        sinkhorn_schedule bs = cs;
+        if (!first) bs.eps_start = P.eps;
+        const int64_t left = (int64_t)P.coarse_max - at_eps;
+        bs.max_iters = (int32_t)(left < P.check_every ? (left > 0 ? left : 1) : P.check_every);
+        const SolveOut co = dense_solve(p, Cx, Cy, pot[0], pot[1], CF, CG, bs, P.stall_window, P.stall_rel);
+        R.coarse_iters += co.iters;
+        R.pairs_evaluated += co.pairs;
+        at_eps += co.final_iters;
+        const bool done = co.converged || co.stalled;
+        const double tl = now_s();
+        lift();
+        lift_s += now_s() - tl;
+        int32_t K = P.check_samples;
+        double er = 0.0, sr = 0.0, ec = 0.0, sc = 0.0;
+        while (true) {
+          const int big = K == P.check_samples ? 0 : 1;
+          prep_column_term(p, Ys, gs[0], eps, Ys.H);
+          sampled_residual(p, Xs, Ys, fs[0], eps, P.sample_seed, 0, K, smp[0][big], &er, &sr);
+          prep_column_term(p, Xs, fs[0], eps, Xs.H);
+          sampled_residual(p, Ys, Xs, gs[0], eps, P.sample_seed, 1, K, smp[1][big], &ec, &sc);
+          R.pairs_evaluated += (double)K * (double)(n + m);
+          const double hi = std::max(er + 3.0 * sr, ec + 3.0 * sc);
+          const double lo = std::max(er - 3.0 * sr, ec - 3.0 * sc);
+          if (hi < P.tol) {
+            accepted = true;
+            break;
+          }
+          if (lo >= P.tol || K >= P.check_samples_max) break;
+          K = P.check_samples_max;
+        }
+        ++R.checks;
+        R.last_check_samples = K;
+        R.last_check[0] = er;
+        R.last_check[1] = sr;
+        R.last_check[2] = ec;
+        R.last_check[3] = sc;
+        progress("multiscale: check %d after %d coarse updates: row %.4g +- %.3g, column %.4g +- %.3g "
+                 "(%d samples) -> %s", (int)R.checks, (int)R.coarse_iters, er, sr, ec, sc, (int)K,
+                 accepted ? "accepted" : (done || at_eps >= P.coarse_max ? "fine updates" : "more coarse"));
+        if (accepted || done || at_eps >= P.coarse_max) break;
+      }
+      t_lift = now_s();
+      R.seconds_lift = lift_s;
+      R.seconds_coarse = t_lift - t_sorted - lift_s;
+      t_coarse = t_lift - lift_s;
+    }
+    (void)t_coarse;
     for (int k = 2; k < 6; ++k) {
       dev_free(pot[k]);
       pot[k] = nullptr;
     }
-
-    // ---- lift: f from the y cells, g from the x cells
-    float* fs[2] = {(float*)dev_alloc(sizeof(float) * n), (float*)dev_alloc(sizeof(float) * n)};
-    pot[2] = fs[0];
-    pot[3] = fs[1];
-    float* gs[2] = {(float*)dev_alloc(sizeof(float) * m), (float*)dev_alloc(sizeof(float) * m)};
-    pot[4] = gs[0];
-    pot[5] = gs[1];
-    const double eps = P.eps;
-    reset_nonfinite(p);
-    prep_column_term(p, Cy, pot[1], eps, Cy.H);
-    dense_halfstep(p, HalfStep{&Xs, &Cy, Cy.H, fs[0], nullptr, nullptr, eps, eps, false});
-    prep_column_term(p, Cx, pot[0], eps, Cx.H);
-    dense_halfstep(p, HalfStep{&Ys, &Cx, Cx.H, gs[0], nullptr, nullptr, eps, eps, false});
-    R.pairs_evaluated += (double)n * (double)Cy.count + (double)m * (double)Cx.count;
-    {
-      int32_t bad = 0;
-      read_reduction(p, nullptr, &bad);
-      if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite lifted potential");
-    }
-    const double t_lift = now_s();
-    R.seconds_lift = t_lift - t_coarse;
     progress("multiscale: lift done (%.3f s)", R.seconds_lift);
+    R.accepted_by_sample = accepted ? 1 : 0;
 
     // ---- fine loop on the block-pair mask
     block_static(p, Xs, P.B, sx);
@@ -367,10 +575,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     VerifiedList rowV, colV;
     VerifyScratch vscr;
     int cf = 0, cg = 0;
-    int status = SINKHORN_NOT_CONVERGED;
+    int status = accepted ? SINKHORN_OK : SINKHORN_NOT_CONVERGED;
     double Rrow = NAN, Rcol = NAN;
     const double pair_block = (double)P.B * (double)P.B;
-    while (true) {
+    while (!accepted) {
       block_potential_max(p, fs[cf], n, sx);
       block_potential_max(p, gs[cg], m, sy);
       rowL.build(p, sx, sy, eps, delta);
@@ -459,6 +667,56 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     return e.code;
   } catch (...) {
     cleanup();
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+extern "C" int sinkhorn_sample_indices(int64_t count, int32_t k, uint64_t seed, uint64_t stream_id,
+                                       void* stream, int32_t* out) {
+  try {
+    if (!out && k > 0) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (count < 1 || count > INT32_MAX || k < 0) fail(SINKHORN_ERR_INVALID_ARG, "need 1 <= count <= 2^31 - 1 and k >= 0");
+    if (k == 0) return SINKHORN_OK;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_sample_idx, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, st, seed, stream_id,
+                       count, k, out);
+    SK_LAUNCH_CHECK();
+    SK_HIP(hipStreamSynchronize(st));
+    return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+extern "C" int sinkhorn_sampled_residual(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                                         int32_t side, int32_t k, uint64_t seed, double* est,
+                                         double* se) {
+  try {
+    if (!p || !f || !g || !est || !se) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (side != 0 && side != 1) fail(SINKHORN_ERR_INVALID_ARG, "side must be 0 (rows) or 1 (columns)");
+    if (k < 2 || k > (1 << 24)) fail(SINKHORN_ERR_INVALID_ARG, "need 2 <= k <= 2^24");
+    if (p->d > kMaxValuD) fail(SINKHORN_ERR_UNSUPPORTED, "sampled residual needs d <= 8");
+    const Side& rows = side == 0 ? p->X : p->Y;
+    Side& cols = side == 0 ? p->Y : p->X;
+    ensure_partials(p, partial_floats_needed(p, k, round_up(k, kPad), cols.count));
+    prep_column_term(p, cols, side == 0 ? g : f, eps, cols.H);
+    reset_nonfinite(p);
+    SampleSide S;
+    sampled_residual(p, rows, cols, side == 0 ? f : g, eps, seed, (uint64_t)side, k, S, est, se);
+    int32_t bad = 0;
+    read_reduction(p, nullptr, &bad);
+    if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in the sampled check");
+    return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
     set_last_error("unexpected exception");
     return SINKHORN_ERR_HIP;
   }

@@ -65,6 +65,12 @@ FS2_CASES = {
     "w5_n16384_fixed_verify": (5, 16384, dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0,
                                               coarse_max=40, stall_window=1 << 30, max_fine=4,
                                               verify=True)),
+    # adaptive switch with an unreachable tol: both checks (after 20 and 40 centroid updates)
+    # fail and expand to the larger sample, then the fine loop runs its fixed budget
+    "w5_n16384_adaptive": (5, 16384, dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0, coarse_max=40,
+                                          stall_window=1 << 30, max_fine=4, adaptive=True,
+                                          check_every=20, check_samples=1024, check_samples_max=8192,
+                                          sample_seed=11)),
 }
 
 
@@ -81,7 +87,9 @@ def run_fs2(name):
         out, f=r.f, g=r.g, coarse_iters=r.coarse_iters, fine_updates=r.fine_updates,
         R_A_row=r.R_A_row, R_A_col=r.R_A_col, omega=r.omega, certified=r.certified,
         ncells_x=r.ncells_x, ncells_y=r.ncells_y, tiles=np.asarray(r.tiles_history),
-        candidates=np.asarray(r.candidates_history), workload=w, n=n,
+        candidates=np.asarray(r.candidates_history), checks=r.checks,
+        check_history=np.asarray(r.check_history, dtype=np.float64).reshape(-1, 5),
+        accepted_by_sample=r.accepted_by_sample, workload=w, n=n,
         **{k: v for k, v in prm.__dict__.items()},
     )
     print(f"{name}: coarse {r.coarse_iters} fine {r.fine_updates} certified {r.certified} "

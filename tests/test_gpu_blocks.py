@@ -439,3 +439,93 @@ def test_verify_tiles_full_size_sampled(sk):
             col_all = np.count_nonzero(vidx == J) == np.count_nonzero(idx == J)
             assert row_all or col_all, (I, J, top)
     assert checked >= 48
+
+
+# ---- sampled residual checks and the adaptive coarse-to-fine switch (FlashSinkhorn 2, §3.1, §B.2)
+
+from oracle.fs2 import sample_indices as _ref_sample_indices  # noqa: E402
+from oracle.fs2 import sampled_residual as _ref_sampled_residual  # noqa: E402
+
+
+@pytest.mark.parametrize("count,k,seed,stream", [(1000, 1024, 0, 0), (1 << 24, 8192, 11, 1),
+                                                  (7, 4099, 2**63 + 5, 3), (1, 5, 1, 0)])
+def test_sample_indices_bit_exact(sk, count, k, seed, stream):
+    got = sk.sample_indices(count, k, seed, stream).cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, _ref_sample_indices(count, k, seed, stream))
+
+
+@pytest.mark.parametrize("side", [0, 1])
+def test_sampled_residual_matches_oracle(sk, side):
+    c = synth.make(2, n=3000, m=2500)
+    eps = 0.01
+    res = oracle.solve(c.x, c.y, c.a, c.b, 1.0, oracle.Schedule(eps, eps, fixed_iters=3))
+    # both marginals visibly off (a state right after a g-step has a column
+    # residual at the fp32 rounding floor of the half-step, ~1e-7)
+    rng = np.random.default_rng(6)
+    f = (res.f + rng.normal(0, 0.1 * eps, c.n)).astype(np.float32)
+    g = (res.g + rng.normal(0, 0.1 * eps, c.m)).astype(np.float32)
+    k, seed = 1024, 5
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        est, se = P.sampled_residual(eps, _t(f), _t(g), side=side, k=k, seed=seed)
+    if side == 0:
+        ref = _ref_sampled_residual(c.x, c.y, c.a, c.b, f, g, eps, 1.0, _ref_sample_indices(c.n, k, seed, 0))
+    else:
+        ref = _ref_sampled_residual(c.y, c.x, c.b, c.a, g, f, eps, 1.0, _ref_sample_indices(c.m, k, seed, 1))
+    assert est == pytest.approx(ref[0], rel=2e-3) and se == pytest.approx(ref[1], rel=2e-3), (est, se, ref)
+
+
+def test_multiscale_adaptive_fixed_budget_matches_the_oracle(sk):
+    """Adaptive switch with an unreachable tol: both sampled checks run (and
+    expand to the larger sample) on the same draws as the oracle, then the
+    fixed fine budget; check estimates, counts and potentials agree."""
+    path = os.path.join(GOLDEN, "fs2_w5_n16384_adaptive.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_solve_refs.py w5_n16384_adaptive")
+    ref = dict(np.load(path))
+    n = int(ref["n"])
+    c = synth.make(5, n=n, m=n)
+    eps = float(ref["eps"])
+    prm = sk.MultiscaleParams(B=int(ref["B"]), eps=eps, tol=float(ref["tol"]), coarse_tol=float(ref["coarse_tol"]),
+                              coarse_max=int(ref["coarse_max"]), stall_window=int(ref["stall_window"]),
+                              max_fine=int(ref["max_fine"]), adaptive=True, check_every=int(ref["check_every"]),
+                              check_samples=int(ref["check_samples"]),
+                              check_samples_max=int(ref["check_samples_max"]), sample_seed=int(ref["sample_seed"]))
+    _log(f"multiscale adaptive fixed budget n={n}")
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+    assert rep["accepted_by_sample"] == 0 and not bool(ref["accepted_by_sample"])
+    assert rep["checks"] == int(ref["checks"]) == 2
+    assert rep["coarse_iters"] == int(ref["coarse_iters"])
+    assert rep["fine_updates"] == int(ref["fine_updates"]) == prm.max_fine
+    er, sr, ec, sc, k = ref["check_history"][-1]
+    assert rep["last_check_samples"] == int(k) == prm.check_samples_max
+    got = rep["last_check"]
+    assert got[0] == pytest.approx(er, rel=1e-3) and got[1] == pytest.approx(sr, rel=1e-2), (got, er, sr)
+    assert got[2] == pytest.approx(ec, rel=1e-3, abs=1e-9) and got[3] == pytest.approx(sc, rel=1e-2, abs=1e-9)
+    _gauge_close(f, g, ref["f"], ref["g"], 1e-3 * eps)
+
+
+def test_multiscale_adaptive_accepts_an_exact_lift(sk):
+    """Singleton cells (the lift is an ordinary half-step): a lift passes the
+    sampled check, no fine update runs, and the exact residual of the returned
+    potentials is under tol; the oracle takes the same path."""
+    rng = np.random.default_rng(12345)
+    n = 512
+    x = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    y = rng.uniform(0, 1, (n, 2)).astype(np.float32)
+    w = np.full(n, 1.0 / n, np.float32)
+    kw = dict(B=128, eps=0.005, tol=1e-2, p_bits=42, coarse_tol=0.0, stall_window=1 << 30,
+              coarse_iters_per_stage=2, adaptive=True, check_every=3, check_samples=128,
+              check_samples_max=512)
+    from oracle.fs2 import FS2Params
+    ref = oracle.fs2_solve(x, y, w, w, FS2Params(**kw))
+    assert ref.accepted_by_sample
+    with sk.Problem(_t(x), _t(y), _t(w), _t(w), 1.0) as P:
+        f, g, rep = P.solve_multiscale(sk.MultiscaleParams(**kw))
+    assert rep["status"] == sk.OK and rep["accepted_by_sample"] == 1 and rep["fine_updates"] == 0
+    assert rep["ncells_x"] == n and rep["ncells_y"] == n
+    assert abs(rep["checks"] - ref.checks) <= 1, (rep["checks"], ref.checks)
+    R = max(oracle.marginal_residuals(x, y, w, w, f.cpu().numpy(), g.cpu().numpy(), kw["eps"], 1.0))
+    assert R < kw["tol"]
+    if rep["checks"] == ref.checks:
+        _gauge_close(f, g, ref.f, ref.g, 1e-3 * kw["eps"])
