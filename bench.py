@@ -14,9 +14,9 @@ schedule. Inputs are resident in HBM before the timed region.
 Prints ONE JSON line:
   value      = point pairs evaluated by all half-steps / wall time (pair-evals/s)
   roofline   = the pair-loop kernel against the VALU issue rate of the chip,
-               timed with HIP events around each launch on the library's stream
-               in a second run of the same K solves (the events cost a few
-               microseconds per launch, so the first, headline run has none)
+               timed by HIP events that each launch's dispatch records at the
+               kernel's start and end, in a second run of the same K solves
+               (the headline run has no events at all)
   cpu_baseline = the fp64 oracle's half-step on the host cores (bounded sample)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="no HIP events around the pair-kernel launches (no roofline)")
+                    help="no HIP events on the pair-kernel launches (no roofline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--verify", action="store_true",
@@ -267,10 +267,9 @@ def main():
     elapsed = t1 - t0
 
     # second timed region for the roofline: the same steps (workloads 4 and 5:
-    # a bounded run of the same kernels) with a HIP event pair around every
-    # pair-kernel (and materializer) launch on the library's stream; the
-    # events add a few microseconds per launch, so they stay out of the first
-    # region
+    # a bounded run of the same kernels) with a HIP event pair recorded by the
+    # dispatch of every pair-kernel (and materializer) launch at the kernel's
+    # start and end; the events stay out of the first region
     kernel_ms, launches, kpairs = 0.0, 0, 0.0
     mat_ms, mat_launches, mat_pairs = 0.0, 0, 0.0
     if not args.no_kernel_timing:

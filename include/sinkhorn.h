@@ -354,14 +354,15 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
                                 const int32_t* idx, float* T, float* grad);
 
 /* Measurement hook. `kinds` is a bit set of the kernels to time: every later
- * launch of a selected kernel is bracketed by two HIP events recorded on the
- * handle's stream; 0 stops recording.
+ * launch of a selected kernel carries two HIP events that its own dispatch
+ * records at the kernel's start and end (hipExtLaunchKernelGGL), so the time
+ * is the kernel's alone; 0 stops recording.
  *   SINKHORN_PROF_DENSE        dense pair-loop reductions (VALU and MFMA)
  *   SINKHORN_PROF_SPARSE       sparse (block-masked) pair-loop reductions
  *   SINKHORN_PROF_MATERIALIZE  plan-row materializer
  *   SINKHORN_PROF_BARY         dense barycentric pair kernel
  * sinkhorn_profile_read synchronizes the stream and returns (host pointers,
- * any may be NULL) the summed event time of the recorded launches in ms, their
+ * any may be NULL) the summed kernel time of the recorded launches in ms, their
  * number, and the point pairs (materializer: entries) they evaluated; it then
  * clears the record. */
 #define SINKHORN_PROF_DENSE 1

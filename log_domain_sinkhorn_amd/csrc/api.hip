@@ -43,21 +43,23 @@ void check_hip(hipError_t e, const char* what) {
   }
 }
 
-void prof_begin(sinkhorn_problem* p, int32_t kind) {
-  if (!(p->prof & kind)) return;
+ProfEv prof_events(sinkhorn_problem* p, int32_t kind) {
+  ProfEv e;
+  if (!(p->prof & kind)) return e;
   if (p->prof_ev.size() < 2 * (p->prof_used + 1)) {
     for (int k = 0; k < 2; ++k) {
-      hipEvent_t e;
-      SK_HIP(hipEventCreate(&e));
-      p->prof_ev.push_back(e);
+      hipEvent_t ev;
+      SK_HIP(hipEventCreate(&ev));
+      p->prof_ev.push_back(ev);
     }
   }
-  SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used], p->stream));
+  e.start = p->prof_ev[2 * p->prof_used];
+  e.stop = p->prof_ev[2 * p->prof_used + 1];
+  return e;
 }
 
-void prof_end(sinkhorn_problem* p, int32_t kind, double pairs) {
+void prof_done(sinkhorn_problem* p, int32_t kind, double pairs) {
   if (!(p->prof & kind)) return;
-  SK_HIP(hipEventRecord(p->prof_ev[2 * p->prof_used + 1], p->stream));
   ++p->prof_used;
   p->prof_pairs += pairs;
 }

@@ -303,15 +303,15 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
   const bool shifted = A.shift_pot != nullptr;
   {
     const dim3 grid((uint32_t)(A.tiles * A.G));
-    prof_begin(p, SINKHORN_PROF_BARY);
+    const ProfEv pe = prof_events(p, SINKHORN_PROF_BARY);
     if (shifted)
-      hipLaunchKernelGGL((k_bary_valu<D, true>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H,
-                         A.Mp, A.Sp, A.Ap);
+      hipExtLaunchKernelGGL((k_bary_valu<D, true>), grid, dim3(kThreads), 0, p->stream, pe.start,
+                            pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp, A.Ap);
     else
-      hipLaunchKernelGGL((k_bary_valu<D, false>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H,
-                         A.Mp, A.Sp, A.Ap);
+      hipExtLaunchKernelGGL((k_bary_valu<D, false>), grid, dim3(kThreads), 0, p->stream, pe.start,
+                            pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp, A.Ap);
     SK_LAUNCH_CHECK();
-    prof_end(p, SINKHORN_PROF_BARY, (double)p->n * (double)p->m);
+    prof_done(p, SINKHORN_PROF_BARY, (double)p->n * (double)p->m);
     hipLaunchKernelGGL(k_bary_merge<D>, dim3((uint32_t)A.tiles), dim3(kThreads), 0, p->stream, A,
                        (int32_t)shifted);
     SK_LAUNCH_CHECK();

@@ -446,13 +446,14 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
 
 // ---------------------------------------------------------------- sparse half-step
 template <int D>
-void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted) {
+void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted,
+                   const ProfEv& pe) {
   if (shifted)
-    hipLaunchKernelGGL((k_lse_sparse<D, true>), dim3((uint32_t)tiles), dim3(kThreads), 0, p->stream,
-                       A, A.Q, A.H);
+    hipExtLaunchKernelGGL((k_lse_sparse<D, true>), dim3((uint32_t)tiles), dim3(kThreads), 0, p->stream,
+                          pe.start, pe.stop, 0, A, A.Q, A.H);
   else
-    hipLaunchKernelGGL((k_lse_sparse<D, false>), dim3((uint32_t)tiles), dim3(kThreads), 0,
-                       p->stream, A, A.Q, A.H);
+    hipExtLaunchKernelGGL((k_lse_sparse<D, false>), dim3((uint32_t)tiles), dim3(kThreads), 0,
+                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H);
   SK_LAUNCH_CHECK();
 }
 
@@ -482,21 +483,20 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
   A.tile_flag = p->tile_flag;
   A.fallback = 0;
   A.F = make_rowfinal(p, hs);
-  auto launch = [&](const SparseArgs& a, bool sh) {
+  auto launch = [&](const SparseArgs& a, bool sh, const ProfEv& pe) {
     switch (p->d) {
-      case 1: launch_sparse<1>(p, a, tiles, sh); break;
-      case 2: launch_sparse<2>(p, a, tiles, sh); break;
-      case 3: launch_sparse<3>(p, a, tiles, sh); break;
+      case 1: launch_sparse<1>(p, a, tiles, sh, pe); break;
+      case 2: launch_sparse<2>(p, a, tiles, sh, pe); break;
+      case 3: launch_sparse<3>(p, a, tiles, sh, pe); break;
       default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
     }
   };
-  prof_begin(p, SINKHORN_PROF_SPARSE);
-  launch(A, shifted);
-  prof_end(p, SINKHORN_PROF_SPARSE, pairs);
+  launch(A, shifted, prof_events(p, SINKHORN_PROF_SPARSE));
+  prof_done(p, SINKHORN_PROF_SPARSE, pairs);
   if (shifted) {  // exact recompute of flagged tiles (the other workgroups exit at once)
     SparseArgs E = A;
     E.fallback = 1;
-    launch(E, false);
+    launch(E, false, ProfEv{});
   }
   if (A.F.prev) launch_reduce(p, tiles);
 }

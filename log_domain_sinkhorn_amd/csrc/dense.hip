@@ -223,15 +223,15 @@ int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int 
 
 template <int D>
 void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shifted, double pairs) {
-  prof_begin(p, SINKHORN_PROF_DENSE);
+  const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
   if (shifted)
-    hipLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream, A,
-                       A.Q, A.H, A.Mp, A.Sp);
+    hipExtLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
+                          pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
   else
-    hipLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
-                       A, A.Q, A.H, A.Mp, A.Sp);
+    hipExtLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
+                          pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
   SK_LAUNCH_CHECK();
-  prof_end(p, SINKHORN_PROF_DENSE, pairs);
+  prof_done(p, SINKHORN_PROF_DENSE, pairs);
 }
 
 template <int D>

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdint>
@@ -131,8 +132,15 @@ void fill_f32(float* v, int64_t count, float value, hipStream_t st);
 void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st);
 
 // measurement hook (api.hip): call around a pair-loop kernel launch
-void prof_begin(sinkhorn_problem* p, int32_t kind);
-void prof_end(sinkhorn_problem* p, int32_t kind, double pairs);
+// Profiling of one launch of `kind`: events for hipExtLaunchKernelGGL, which
+// the dispatch itself records at the kernel's start and end (null when `kind`
+// is not being profiled); prof_done after the launch counts it.
+struct ProfEv {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+ProfEv prof_events(sinkhorn_problem* p, int32_t kind);
+void prof_done(sinkhorn_problem* p, int32_t kind, double pairs);
 
 // dense.hip
 // Column split of the dense VALU pair kernels for nrows x ncols: G splits of

@@ -271,16 +271,18 @@ __global__ __launch_bounds__(256) void k_check_rows(const int64_t* __restrict__ 
 
 template <int D>
 void launch_valu(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t k,
-                 const double* P, const double* Hd, double kappa, float* T, uint32_t* keys) {
+                 const double* P, const double* Hd, double kappa, float* T, uint32_t* keys,
+                 const ProfEv& pe) {
   const dim3 grid((uint32_t)((k + kRB - 1) / kRB), (uint32_t)((p->m + 255) / 256));
-  hipLaunchKernelGGL((k_materialize_valu<D>), grid, dim3(256), 0, p->stream, p->X.soa, p->X.padded,
-                     p->Y.soa, p->Y.padded, p->m, rows, row0, k, P, Hd, kappa, T, keys);
+  hipExtLaunchKernelGGL((k_materialize_valu<D>), grid, dim3(256), 0, p->stream, pe.start, pe.stop, 0,
+                        p->X.soa, p->X.padded, p->Y.soa, p->Y.padded, p->m, rows, row0, k, P, Hd,
+                        kappa, T, keys);
   SK_LAUNCH_CHECK();
 }
 
 template <int KP>
 void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t k,
-                 const double* P, double twokappa, float* T, uint32_t* keys) {
+                 const double* P, double twokappa, float* T, uint32_t* keys, const ProfEv& pe) {
   const int64_t rtiles = (k + 127) / 128;
   const int64_t ntiles = (p->m + 31) / 32;
   // about two workgroups per CU, each streaming a long column range: shorter
@@ -292,9 +294,9 @@ void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t
   if (want < 1) want = 1;
   const int64_t tps = (ntiles + want - 1) / want;
   const int32_t G = (int32_t)((ntiles + tps - 1) / tps);
-  hipLaunchKernelGGL((k_materialize_mfma<KP>), dim3((uint32_t)(rtiles * G)), dim3(256), 0,
-                     p->stream, p->X.rowmaj, p->Y.rowmaj, p->d, p->m, rows, row0, k, P, twokappa,
-                     G, ntiles, tps, T, keys);
+  hipExtLaunchKernelGGL((k_materialize_mfma<KP>), dim3((uint32_t)(rtiles * G)), dim3(256), 0,
+                        p->stream, pe.start, pe.stop, 0, p->X.rowmaj, p->Y.rowmaj, p->d, p->m, rows,
+                        row0, k, P, twokappa, G, ntiles, tps, T, keys);
   SK_LAUNCH_CHECK();
 }
 
@@ -307,10 +309,10 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
   hipLaunchKernelGGL(k_row_terms, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream, rows,
                      row0, k, p->X.w, f, mf ? p->X.norm2 : nullptr, lam, kappa, P, live, keys);
   SK_LAUNCH_CHECK();
-  prof_begin(p, SINKHORN_PROF_MATERIALIZE);
+  const ProfEv pe = prof_events(p, SINKHORN_PROF_MATERIALIZE);
   if (mf) {
     switch (p->kpad) {
-#define SK_KP(v) case v: launch_mfma<v>(p, rows, row0, k, P, 2.0 * kappa, T, keys); break;
+#define SK_KP(v) case v: launch_mfma<v>(p, rows, row0, k, P, 2.0 * kappa, T, keys, pe); break;
       SK_KP(12) SK_KP(16) SK_KP(20) SK_KP(24) SK_KP(28) SK_KP(32) SK_KP(36)
       SK_KP(40) SK_KP(44) SK_KP(48) SK_KP(52) SK_KP(56) SK_KP(60) SK_KP(64) SK_KP(68)
 #undef SK_KP
@@ -318,18 +320,18 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
     }
   } else {
     switch (p->d) {
-      case 1: launch_valu<1>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 2: launch_valu<2>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 3: launch_valu<3>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 4: launch_valu<4>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 5: launch_valu<5>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 6: launch_valu<6>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 7: launch_valu<7>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
-      case 8: launch_valu<8>(p, rows, row0, k, P, Hd, kappa, T, keys); break;
+      case 1: launch_valu<1>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 2: launch_valu<2>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 3: launch_valu<3>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 4: launch_valu<4>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 5: launch_valu<5>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 6: launch_valu<6>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 7: launch_valu<7>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
+      case 8: launch_valu<8>(p, rows, row0, k, P, Hd, kappa, T, keys, pe); break;
       default: fail(SINKHORN_ERR_UNSUPPORTED, "materializer: unsupported d");
     }
   }
-  prof_end(p, SINKHORN_PROF_MATERIALIZE, (double)k * (double)p->m);
+  prof_done(p, SINKHORN_PROF_MATERIALIZE, (double)k * (double)p->m);
 }
 
 // Column terms for this eps and g: the MFMA path writes H'_j into slot d of y,

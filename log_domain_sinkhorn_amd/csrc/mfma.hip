@@ -390,10 +390,11 @@ MPlan mplan(int64_t nrows, int64_t ncols, int64_t slots) {
 
 template <int KP>
 void launch_kp(sinkhorn_problem* p, const MfmaArgs& A, int64_t blocks, double pairs) {
-  prof_begin(p, SINKHORN_PROF_DENSE);
-  hipLaunchKernelGGL((k_lse_mfma<KP>), dim3((uint32_t)blocks), dim3(256), 0, p->stream, A);
+  const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
+  hipExtLaunchKernelGGL((k_lse_mfma<KP>), dim3((uint32_t)blocks), dim3(256), 0, p->stream, pe.start,
+                        pe.stop, 0, A);
   SK_LAUNCH_CHECK();
-  prof_end(p, SINKHORN_PROF_DENSE, pairs);
+  prof_done(p, SINKHORN_PROF_DENSE, pairs);
 }
 
 }  // namespace
