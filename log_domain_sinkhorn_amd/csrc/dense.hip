@@ -112,17 +112,32 @@ __global__ __launch_bounds__(kThreads) void k_merge(LseArgs A, int32_t shifted) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t np = A.F.np;
+  // all of the lane's partials in one round of loads (G <= kMaxSplit)
+  double mv[kR][kSplitsPerWave];
+  float sv[kR][kSplitsPerWave];
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     const int64_t i = tile * kRowsPerTile + lane + 64 * r;
-    double m = -DBL_MAX, acc = 0.0;
-    if (i < np) {
-      for (int32_t t = wave; t < A.G; t += kW) m = fmax(m, A.Mp[(int64_t)t * np + i]);
-      for (int32_t t = wave; t < A.G; t += kW) {
+#pragma unroll
+    for (int q = 0; q < kSplitsPerWave; ++q) {
+      const int32_t t = wave + kW * q;
+      mv[r][q] = -DBL_MAX;
+      sv[r][q] = 0.0f;
+      if (i < np && t < A.G) {
         const int64_t o = (int64_t)t * np + i;
-        acc += (double)A.Sp[o] * (double)ex2((float)(A.Mp[o] - m));
+        mv[r][q] = A.Mp[o];
+        sv[r][q] = A.Sp[o];
       }
     }
+  }
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    double m = -DBL_MAX, acc = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSplitsPerWave; ++q) m = fmax(m, mv[r][q]);
+#pragma unroll
+    for (int q = 0; q < kSplitsPerWave; ++q)
+      if (wave + kW * q < A.G) acc += (double)sv[r][q] * (double)ex2((float)(mv[r][q] - m));
     L.M[wave][lane + 64 * r] = m;
     sS[wave][lane + 64 * r] = acc;
   }
@@ -139,25 +154,31 @@ __global__ __launch_bounds__(kThreads) void k_merge(LseArgs A, int32_t shifted) 
   finish_tile(A.F, L, tile, mx, sum);
 }
 
-// Sum of count doubles in a fixed order into ctl->residual (one block).
-// The result and the non-finite count also go to the host-mapped mirror, so
-// the host reads them after an event without a copy.
+// Sum of count doubles in a fixed order into ctl->residual (one block):
+// thread t adds part[t], part[t + 256], ...; the 256 sums are then halved
+// pairwise (t + 128 onto t, ..., 1 onto 0; the last six steps by shuffles
+// within wave 0). The result and the non-finite count also go to the
+// host-mapped mirror, so the host reads them after an event without a copy.
 __global__ __launch_bounds__(256) void k_reduce(const double* __restrict__ part, int64_t count,
                                                 Ctl* ctl, Ctl* host) {
   __shared__ double sh[256];
+  const int t = threadIdx.x;
   double acc = 0.0;
-  for (int64_t k = threadIdx.x; k < count; k += 256) acc += part[k];
-  sh[threadIdx.x] = acc;
+  for (int64_t k = t; k < count; k += 256) acc += part[k];
+  sh[t] = acc;
   __syncthreads();
+  if (t < 128) sh[t] += sh[t + 128];
+  __syncthreads();
+  if (t < 64) {
+    double v = sh[t] + sh[t + 64];
 #pragma unroll
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    ctl->residual = sh[0];
-    __hip_atomic_store(&host->residual, sh[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(&host->nonfinite, ctl->nonfinite, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (t == 0) {
+      ctl->residual = v;
+      __hip_atomic_store(&host->residual, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&host->nonfinite, ctl->nonfinite, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
@@ -206,7 +227,7 @@ int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int 
   int64_t maxsplit = A.nchunks / (4 * kW);
   // too few tiles to fill the chip even so: down to one chunk per wave
   if (A.tiles * (maxsplit > 1 ? maxsplit : 1) < slots) maxsplit = A.nchunks / kW;
-  if (maxsplit > 64) maxsplit = 64;
+  if (maxsplit > kMaxSplit) maxsplit = kMaxSplit;
   if (maxsplit < 1) maxsplit = 1;
   const int64_t want = (3 * slots + A.tiles - 1) / A.tiles;
   const bool big = A.nchunks * kChunk * (int64_t)(d + 1) * 4 > kL2Slice;

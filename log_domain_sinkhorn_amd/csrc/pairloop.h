@@ -42,6 +42,8 @@ constexpr int kR = 2;                // rows per lane
 constexpr int kW = 8;                // waves per workgroup
 constexpr int kRowsPerTile = 64 * kR;
 constexpr int kThreads = 64 * kW;
+constexpr int kMaxSplit = 64;                       // column splits per row tile, at most
+constexpr int kSplitsPerWave = kMaxSplit / kW;      // splits one merge wave folds, at most
 constexpr float kBig = 0x1p64f;      // shifted mode: redo a chunk whose sum exceeds this
 constexpr double kTiny = 0x1p-40;    // shifted mode: a row sum below this is redone exactly
 constexpr float kHeadroom = 16.0f;   // shift = estimated LSE - headroom (log2 units)
@@ -297,7 +299,9 @@ __device__ __forceinline__ bool needs_exact(int64_t np, int64_t tile, double sum
 }
 
 // Writes the potentials of a tile's rows (threads t < 128) and its residual
-// partial (fixed-order tree over the workgroup).
+// partial: a fixed-order pairwise tree over the 128 row terms (rows 64..127
+// fold onto 0..63 through LDS, then wave 0 halves by shuffles); the tile's
+// non-finite count goes out in one atomic.
 __device__ __forceinline__ void finish_tile(const RowFinal& F, TileLds& L, int64_t tile, double mx,
                                             double sum) {
   const int t = threadIdx.x;
@@ -306,16 +310,14 @@ __device__ __forceinline__ void finish_tile(const RowFinal& F, TileLds& L, int64
   double term = 0.0;
   int bad = 0;
   if (own) term = finalize_row(F, i, mx, sum, &bad);
-  if (bad) atomicAdd(&F.ctl->nonfinite, bad);
-  if (F.prev) {
-    L.red[t] = term;
-    __syncthreads();
+  if (t >= 64 && t < kRowsPerTile) L.red[t - 64] = term;
+  const int nbad = __syncthreads_count(bad);
+  if (t == 0 && nbad) atomicAdd(&F.ctl->nonfinite, nbad);
+  if (F.prev && t < 64) {
+    double v = term + L.red[t];
 #pragma unroll
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (t < w) L.red[t] += L.red[t + w];
-      __syncthreads();
-    }
-    if (t == 0) F.red_part[tile] = L.red[0];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (t == 0) F.red_part[tile] = v;
   }
 }
 
