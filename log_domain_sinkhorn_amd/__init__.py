@@ -349,6 +349,13 @@ class Problem:
     def __exit__(self, *exc):
         self.close()
 
+    def info(self):
+        """(n, m, d, cost_scale) as the handle holds them (``sinkhorn_problem_info``)."""
+        n, m, d, sc = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_double()
+        _check(lib().sinkhorn_problem_info(self._h, ctypes.byref(n), ctypes.byref(m), ctypes.byref(d),
+                                           ctypes.byref(sc)), "problem_info")
+        return n.value, m.value, d.value, sc.value
+
     def _pot(self, t, k, name):
         return _dev(t, torch.float32, name, (k,))
 

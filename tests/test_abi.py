@@ -61,3 +61,4 @@ def test_invalid_arguments_are_rejected_before_any_device_work():
     assert L.sinkhorn_halfstep_f(None, 0.1, fake, fake, None, None) == sk.ERR_INVALID_ARG
     assert L.sinkhorn_solve(None, None, None, None, None) == sk.ERR_INVALID_ARG
     assert L.sinkhorn_destroy(None) == sk.OK
+    assert L.sinkhorn_problem_info(None, None, None, None, None) == sk.ERR_INVALID_ARG

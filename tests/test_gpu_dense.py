@@ -143,6 +143,14 @@ def test_init_errors(sk):
     assert ei.value.code == sk.ERR_NONFINITE
 
 
+def test_problem_info_reports_the_handles_sizes(sk):
+    c = synth.make(3, n=37, m=53, d=50)
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 0.125) as P:
+        assert P.info() == (37, 53, 50, 0.125)
+        # every output is optional
+        assert sk.lib().sinkhorn_problem_info(P._h, None, None, None, None) == sk.OK
+
+
 def test_fused_row_residual_matches_explicit_plan(sk):
     c = synth.make(2, n=1500, m=1300)
     eps = 5e-3
