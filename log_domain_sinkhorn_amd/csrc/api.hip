@@ -101,6 +101,9 @@ void problem_free(sinkhorn_problem* p) {
   dev_free(p->bary_part);
   dev_free(p->red_part);
   dev_free(p->tile_flag);
+  dev_free(p->order_key);
+  dev_free(p->order_val);
+  dev_free(p->order_temp);
   dev_free(p->ctl);
   host_free(p->host_ctl);
   host_free(p->host_tmp);

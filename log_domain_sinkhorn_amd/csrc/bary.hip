@@ -52,6 +52,7 @@ struct BaryArgs {
   const int32_t* idx;      // sparse: admitted column blocks
   int32_t* tile_flag;      // sparse: tiles left for the exact recompute
   int32_t fallback;        // sparse: 1 = exact recompute of flagged tiles only
+  const int32_t* order;    // sparse: tile of each workgroup (longest lists first), or null
 };
 
 template <int D>
@@ -216,12 +217,13 @@ __global__ __launch_bounds__(kThreads) void k_bary_merge(BaryArgs A, int32_t shi
 
 // Sparse: workgroup = 128-row tile of row block I over its admitted tiles
 // (all columns when it has none); writes the outputs directly. In shifted mode
-// a tile with a too-small row sum is flagged for the fallback launch.
+// a tile with a too-small row sum is flagged for the fallback launch. Tiles
+// are taken in A.order when given (longest lists first; results unchanged).
 template <int D, bool SHIFT>
 __global__ __launch_bounds__(kThreads) void k_bary_sparse(BaryArgs A, const float* __restrict__ Q,
                                                          const float* __restrict__ H) {
   __shared__ BaryLds<D> L;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = A.order ? (int64_t)A.order[blockIdx.x] : (int64_t)blockIdx.x;
   if (!SHIFT && A.fallback && A.tile_flag[tile] == 0) return;  // uniform
   const int64_t I = tile * kRowsPerTile / A.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -321,11 +323,13 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
 template <int D>
 void sparse_bary(sinkhorn_problem* p, BaryArgs& A) {
   const dim3 grid((uint32_t)A.tiles);
+  A.order = heavy_first(p, A.ptr, A.tiles, A.B);
   if (A.shift_pot) {
     hipLaunchKernelGGL((k_bary_sparse<D, true>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H);
     SK_LAUNCH_CHECK();
     BaryArgs E = A;
     E.fallback = 1;
+    E.order = nullptr;
     hipLaunchKernelGGL((k_bary_sparse<D, false>), grid, dim3(kThreads), 0, p->stream, E, E.Q, E.H);
   } else {
     hipLaunchKernelGGL((k_bary_sparse<D, false>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H);

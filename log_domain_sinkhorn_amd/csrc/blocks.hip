@@ -23,6 +23,7 @@
 #include <cmath>
 #include <vector>
 
+#include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 
 #include "pairloop.h"
@@ -229,6 +230,7 @@ struct SparseArgs {
   float lam;               // log2(e) / eps
   float inv_kappa;         // 1 / kappa
   int32_t* tile_flag;      // [tiles] tiles left for the exact recompute
+  const int32_t* order;    // [tiles] tile of each workgroup (heaviest first), or null: in order
   int32_t fallback;        // 1: exact recompute of the flagged tiles only
   RowFinal F;
 };
@@ -237,12 +239,15 @@ struct SparseArgs {
 // share out the admitted column blocks (or, for an empty list, all column
 // chunks) and merge through LDS in wave order. In shifted mode a tile with a
 // too-small row sum is flagged (its residual partial zeroed) and left to the
-// fallback launch, which recomputes exactly the flagged tiles only.
+// fallback launch, which recomputes exactly the flagged tiles only. The
+// workgroups take the tiles in A.order when given (the longest lists first,
+// so that no long tile starts late); every tile writes only its own rows and
+// residual partial, so the order leaves the results unchanged.
 template <int D, bool SHIFT>
 __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const float* __restrict__ Q,
                                                         const float* __restrict__ H) {
   __shared__ TileLds L;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = A.order ? (int64_t)A.order[blockIdx.x] : (int64_t)blockIdx.x;
   if (!SHIFT && A.fallback && A.tile_flag[tile] == 0) return;  // uniform
   const int64_t I = tile * kRowsPerTile / A.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -445,6 +450,58 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
 }
 
 // ---------------------------------------------------------------- sparse half-step
+// Sort key of each row tile: the admitted column blocks of its row block
+// (an empty list means a pass over all columns: the largest key).
+__global__ __launch_bounds__(256) void k_tile_keys(const int64_t* __restrict__ ptr, int64_t tiles,
+                                                   int32_t B, uint32_t* __restrict__ key,
+                                                   int32_t* __restrict__ val) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= tiles) return;
+  const int64_t I = t * kRowsPerTile / B;
+  const int64_t c = ptr[I + 1] - ptr[I];
+  key[t] = c > 0 && c < (int64_t)UINT32_MAX ? (uint32_t)c : UINT32_MAX;
+  val[t] = (int32_t)t;
+}
+
+// The row tiles of a sparse half-step in decreasing order of their lists'
+// length, equal lengths in tile order (a stable radix sort): in this order a
+// launch ends about when its total work is done, while tile order can leave
+// a list tens of times the average running alone at the end.
+const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B) {
+  hipStream_t st = p->stream;
+  if (tiles > p->order_cap) {
+    SK_HIP(hipStreamSynchronize(st));
+    dev_free(p->order_key);
+    dev_free(p->order_val);
+    p->order_key = nullptr;
+    p->order_val = nullptr;
+    p->order_cap = 0;
+    p->order_key = (uint32_t*)dev_alloc(sizeof(uint32_t) * 2 * tiles);
+    p->order_val = (int32_t*)dev_alloc(sizeof(int32_t) * 2 * tiles);
+    p->order_cap = tiles;
+  }
+  uint32_t* kin = p->order_key;
+  uint32_t* kout = p->order_key + p->order_cap;
+  int32_t* vin = p->order_val;
+  int32_t* vout = p->order_val + p->order_cap;
+  hipLaunchKernelGGL(k_tile_keys, dim3((uint32_t)((tiles + 255) / 256)), dim3(256), 0, st, ptr, tiles,
+                     B, kin, vin);
+  SK_LAUNCH_CHECK();
+  size_t need = 0;
+  SK_HIP(rocprim::radix_sort_pairs_desc(nullptr, need, kin, kout, vin, vout, (size_t)tiles, 0, 32, st));
+  if (need > p->order_temp_bytes) {
+    SK_HIP(hipStreamSynchronize(st));
+    dev_free(p->order_temp);
+    p->order_temp = nullptr;
+    p->order_temp_bytes = 0;
+    p->order_temp = dev_alloc(need);
+    p->order_temp_bytes = need;
+  }
+  SK_HIP(rocprim::radix_sort_pairs_desc(p->order_temp, need, kin, kout, vin, vout, (size_t)tiles, 0,
+                                        32, st));
+  return vout;
+}
+
 template <int D>
 void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted,
                    const ProfEv& pe) {
@@ -482,6 +539,7 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
   A.inv_kappa = (float)(1.0 / kappa);
   A.tile_flag = p->tile_flag;
   A.fallback = 0;
+  A.order = heavy_first(p, ptr, tiles, B);
   A.F = make_rowfinal(p, hs);
   auto launch = [&](const SparseArgs& a, bool sh, const ProfEv& pe) {
     switch (p->d) {
@@ -496,6 +554,7 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
   if (shifted) {  // exact recompute of flagged tiles (the other workgroups exit at once)
     SparseArgs E = A;
     E.fallback = 1;
+    E.order = nullptr;
     launch(E, false, ProfEv{});
   }
   if (A.F.prev) launch_reduce(p, tiles);

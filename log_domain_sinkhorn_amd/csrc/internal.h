@@ -108,6 +108,12 @@ struct sinkhorn_problem {
   double* red_part = nullptr;   // [red_cap]
   int64_t red_cap = 0;
   int32_t* tile_flag = nullptr; // [red_cap] tiles marked for the exact recompute, zero between launches
+  // sparse half-steps: dispatch order of the row tiles (heaviest first), grown on demand
+  uint32_t* order_key = nullptr;  // [2 * order_cap] sort keys, in then out
+  int32_t* order_val = nullptr;   // [2 * order_cap] tile indices, in then out
+  int64_t order_cap = 0;
+  void* order_temp = nullptr;     // rocPRIM sort storage
+  size_t order_temp_bytes = 0;
   sk::Ctl* ctl = nullptr;       // device control block
   sk::Ctl* host_ctl = nullptr;  // pinned, host-coherent mirror (the residual kernel writes it)
   sk::Ctl* host_ctl_dev = nullptr;  // device address of host_ctl
@@ -203,6 +209,9 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr);
 void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const int64_t* ptr,
                      const int32_t* idx, double pairs);
 void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_t* idx, int64_t nc);
+// row tiles (128 rows) of a sparse list with block size B, longest lists
+// first (device array of `tiles` indices in the handle's scratch)
+const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B);
 
 // api.hip: annealed dense solve between two sides (X rows, Y columns), f/g
 // in/out, F/G scratch pairs; stall_window > 0 adds the stall stop rule
