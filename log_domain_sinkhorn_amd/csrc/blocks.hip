@@ -450,8 +450,10 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
 }
 
 // ---------------------------------------------------------------- sparse half-step
-// Sort key of each row tile: the admitted column blocks of its row block
-// (an empty list means a pass over all columns: the largest key).
+// Sort key of each row tile: the bit length of its row block's list of
+// admitted column blocks (lists within a factor of two share a key; an
+// empty list means a pass over all columns: the largest key, 63).
+constexpr int kKeyBits = 6;
 __global__ __launch_bounds__(256) void k_tile_keys(const int64_t* __restrict__ ptr, int64_t tiles,
                                                    int32_t B, uint32_t* __restrict__ key,
                                                    int32_t* __restrict__ val) {
@@ -459,14 +461,17 @@ __global__ __launch_bounds__(256) void k_tile_keys(const int64_t* __restrict__ p
   if (t >= tiles) return;
   const int64_t I = t * kRowsPerTile / B;
   const int64_t c = ptr[I + 1] - ptr[I];
-  key[t] = c > 0 && c < (int64_t)UINT32_MAX ? (uint32_t)c : UINT32_MAX;
+  key[t] = c > 0 ? 64u - (uint32_t)__clzll((unsigned long long)c) : (1u << kKeyBits) - 1;
   val[t] = (int32_t)t;
 }
 
-// The row tiles of a sparse half-step in decreasing order of their lists'
-// length, equal lengths in tile order (a stable radix sort): in this order a
-// launch ends about when its total work is done, while tile order can leave
-// a list tens of times the average running alone at the end.
+// The row tiles of a sparse half-step, longest lists first by powers of two
+// and in tile order within a power (a stable radix sort of the bit lengths):
+// the rare lists tens of times the average no longer start late and run
+// alone at the end, while the workgroups running together still take
+// neighbouring row blocks, whose column blocks overlap in L2. Measured at
+// 2^24: 798 ms per launch in tile order, 778 ms with the exact lengths
+// sorted, 765 ms so; on verified lists 446, 460 and 446 ms.
 const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B) {
   hipStream_t st = p->stream;
   if (tiles > p->order_cap) {
@@ -488,7 +493,8 @@ const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tile
                      B, kin, vin);
   SK_LAUNCH_CHECK();
   size_t need = 0;
-  SK_HIP(rocprim::radix_sort_pairs_desc(nullptr, need, kin, kout, vin, vout, (size_t)tiles, 0, 32, st));
+  SK_HIP(rocprim::radix_sort_pairs_desc(nullptr, need, kin, kout, vin, vout, (size_t)tiles, 0,
+                                        kKeyBits, st));
   if (need > p->order_temp_bytes) {
     SK_HIP(hipStreamSynchronize(st));
     dev_free(p->order_temp);
@@ -498,7 +504,7 @@ const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tile
     p->order_temp_bytes = need;
   }
   SK_HIP(rocprim::radix_sort_pairs_desc(p->order_temp, need, kin, kout, vin, vout, (size_t)tiles, 0,
-                                        32, st));
+                                        kKeyBits, st));
   return vout;
 }
 
