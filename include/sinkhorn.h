@@ -357,10 +357,13 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
  * launch of a selected kernel carries two HIP events that its own dispatch
  * records at the kernel's start and end (hipExtLaunchKernelGGL), so the time
  * is the kernel's alone; 0 stops recording.
- *   SINKHORN_PROF_DENSE        dense pair-loop reductions (VALU and MFMA)
+ *   SINKHORN_PROF_DENSE        dense pair-loop reductions: the shifted VALU loop
+ *                              and the MFMA kernel
  *   SINKHORN_PROF_SPARSE       sparse (block-masked) pair-loop reductions
  *   SINKHORN_PROF_MATERIALIZE  plan-row materializer
  *   SINKHORN_PROF_BARY         dense barycentric pair kernel
+ *   SINKHORN_PROF_DENSE_EXACT  dense VALU pair loop in exact mode (residual
+ *                              passes without a shift estimate)
  * sinkhorn_profile_read synchronizes the stream and returns (host pointers,
  * any may be NULL) the summed kernel time of the recorded launches in ms, their
  * number, and the point pairs (materializer: entries) they evaluated; it then
@@ -369,6 +372,7 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
 #define SINKHORN_PROF_SPARSE 2
 #define SINKHORN_PROF_MATERIALIZE 4
 #define SINKHORN_PROF_BARY 8
+#define SINKHORN_PROF_DENSE_EXACT 16
 int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t kinds);
 int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launches,
                           double* pairs);

@@ -49,6 +49,7 @@ PROF_DENSE = 1
 PROF_SPARSE = 2
 PROF_MATERIALIZE = 4
 PROF_BARY = 8
+PROF_DENSE_EXACT = 16
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32

@@ -244,7 +244,8 @@ int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int 
 
 template <int D>
 void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shifted, double pairs) {
-  const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
+  const int32_t kind = shifted ? SINKHORN_PROF_DENSE : SINKHORN_PROF_DENSE_EXACT;
+  const ProfEv pe = prof_events(p, kind);
   if (shifted)
     hipExtLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
                           pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
@@ -252,7 +253,7 @@ void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shif
     hipExtLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
                           pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
   SK_LAUNCH_CHECK();
-  prof_done(p, SINKHORN_PROF_DENSE, pairs);
+  prof_done(p, kind, pairs);
 }
 
 template <int D>

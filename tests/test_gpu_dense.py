@@ -151,6 +151,26 @@ def test_problem_info_reports_the_handles_sizes(sk):
         assert sk.lib().sinkhorn_problem_info(P._h, None, None, None, None) == sk.OK
 
 
+def test_measurement_hook_counts_each_kind(sk):
+    """A half-step with a previous potential runs the shifted loop (dense
+    kind), one without runs the exact loop (its own kind); each launch is
+    counted once with its n*m pairs and a positive kernel time."""
+    c = synth.make(2, n=3000, m=2000)
+    eps = 0.01
+    with _problem(sk, c) as P:
+        g = torch.zeros(c.m, device=DEV)
+        f, _ = P.halfstep_f(eps, g)
+        for kinds, prev, want in ((sk.PROF_DENSE, True, 1), (sk.PROF_DENSE, False, 0),
+                                  (sk.PROF_DENSE_EXACT, False, 1), (sk.PROF_DENSE_EXACT, True, 0)):
+            P.profile_enable(kinds)
+            P.halfstep_f(eps, g, f_prev=f if prev else None)
+            ms, launches, pairs = P.profile_read()
+            P.profile_enable(0)
+            assert launches == want, (kinds, prev, launches)
+            assert pairs == pytest.approx(want * c.n * c.m)
+            assert (ms > 0.0) == (want > 0)
+
+
 def test_fused_row_residual_matches_explicit_plan(sk):
     c = synth.make(2, n=1500, m=1300)
     eps = 5e-3
