@@ -120,6 +120,18 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
 /* Release the handle and its workspace (synchronizes its stream). NULL is a no-op. */
 int sinkhorn_destroy(sinkhorn_problem* p);
 
+/* Device memory the library holds in this process, over all handles (host
+ * outputs; any may be NULL): the bytes allocated now, the peak and the largest
+ * single buffer since the last reset; reset != 0 then sets the peak to the
+ * current amount and the largest buffer to 0. Every device allocation of the
+ * library goes through one allocator, so the figures are exact; buffers the
+ * caller passes in are not counted. For callers that check the working
+ * memory of a call, in the way moscot #846 ("fix(sparsify): materialize
+ * transport-matrix rows ...", its memory measurements) checks that row
+ * extraction no longer grows with n * m * k. Needs no device. */
+int sinkhorn_device_memory(int64_t* current_bytes, int64_t* peak_bytes, int64_t* largest_bytes,
+                           int32_t reset);
+
 /* Sizes of a handle (host outputs; any may be NULL). */
 int sinkhorn_problem_info(const sinkhorn_problem* p, int64_t* n, int64_t* m, int32_t* d,
                           double* cost_scale);

@@ -141,6 +141,7 @@ _SIGS = {
     "sinkhorn_init": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f64, _p], _i32),
     "sinkhorn_destroy": ([_p], _i32),
     "sinkhorn_problem_info": ([_p, _p, _p, _p, _p], _i32),
+    "sinkhorn_device_memory": ([_p, _p, _p, _i32], _i32),
     "sinkhorn_halfstep_f": ([_p, _f64, _p, _p, _p, _p], _i32),
     "sinkhorn_halfstep_g": ([_p, _f64, _p, _p, _p, _p], _i32),
     "sinkhorn_marginal_residual": ([_p, _f64, _p, _p, _p, _p], _i32),
@@ -310,6 +311,15 @@ def morton_order(x: torch.Tensor, y: torch.Tensor):
     _check(lib().sinkhorn_morton_order(_ptr(x), _ptr(y), n, m, d, _stream(x.device), _ptr(cx),
                                        _ptr(px), _ptr(cy), _ptr(py)), "morton_order")
     return cx, px, cy, py
+
+
+def device_memory(reset: bool = False):
+    """(current, peak, largest) device bytes the library holds, over all
+    handles (``sinkhorn_device_memory``); reset=True then starts a new peak."""
+    cur, peak, big = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().sinkhorn_device_memory(ctypes.byref(cur), ctypes.byref(peak), ctypes.byref(big),
+                                        int(bool(reset))), "device_memory")
+    return cur.value, peak.value, big.value
 
 
 class Problem:

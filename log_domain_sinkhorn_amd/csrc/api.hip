@@ -288,6 +288,11 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
 
 }  // namespace sk
 
+namespace sk {
+// setup.hip: the library's device memory (current, peak, largest buffer)
+void device_memory(int64_t* current, int64_t* peak, int64_t* largest, bool reset);
+}  // namespace sk
+
 using namespace sk;
 
 extern "C" {
@@ -380,6 +385,14 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
 int sinkhorn_destroy(sinkhorn_problem* p) {
   return guard([&] {
     problem_free(p);
+    return SINKHORN_OK;
+  });
+}
+
+int sinkhorn_device_memory(int64_t* current_bytes, int64_t* peak_bytes, int64_t* largest_bytes,
+                           int32_t reset) {
+  return guard([&] {
+    device_memory(current_bytes, peak_bytes, largest_bytes, reset != 0);
     return SINKHORN_OK;
   });
 }

@@ -1,7 +1,10 @@
 // Handle set-up: device layouts of the two clouds, weight checks, the fp64
 // mean squared distance, and memory helpers.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <unordered_map>
 
 #include "internal.h"
 
@@ -144,6 +147,15 @@ void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double*
   dev_free(out);
 }
 
+// Device memory held by the library: every allocation goes through
+// dev_alloc, so the current amount, its peak and the largest single buffer
+// are exact (per process, all handles).
+namespace {
+std::mutex g_mem_mu;
+std::unordered_map<void*, size_t> g_mem_size;
+int64_t g_mem_current = 0, g_mem_peak = 0, g_mem_largest = 0;
+}  // namespace
+
 void* dev_alloc(size_t bytes) {
   void* p = nullptr;
   if (bytes == 0) bytes = 256;
@@ -153,11 +165,36 @@ void* dev_alloc(size_t bytes) {
     fail(SINKHORN_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
   }
   check_hip(e, "hipMalloc");
+  std::lock_guard<std::mutex> lock(g_mem_mu);
+  g_mem_size[p] = bytes;
+  g_mem_current += (int64_t)bytes;
+  g_mem_peak = std::max(g_mem_peak, g_mem_current);
+  g_mem_largest = std::max(g_mem_largest, (int64_t)bytes);
   return p;
 }
 
 void dev_free(void* p) {
-  if (p) (void)hipFree(p);
+  if (!p) return;
+  {
+    std::lock_guard<std::mutex> lock(g_mem_mu);
+    auto it = g_mem_size.find(p);
+    if (it != g_mem_size.end()) {
+      g_mem_current -= (int64_t)it->second;
+      g_mem_size.erase(it);
+    }
+  }
+  (void)hipFree(p);
+}
+
+void device_memory(int64_t* current, int64_t* peak, int64_t* largest, bool reset) {
+  std::lock_guard<std::mutex> lock(g_mem_mu);
+  if (current) *current = g_mem_current;
+  if (peak) *peak = g_mem_peak;
+  if (largest) *largest = g_mem_largest;
+  if (reset) {
+    g_mem_peak = g_mem_current;
+    g_mem_largest = 0;
+  }
 }
 
 void* host_alloc(size_t bytes) {

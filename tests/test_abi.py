@@ -62,3 +62,11 @@ def test_invalid_arguments_are_rejected_before_any_device_work():
     assert L.sinkhorn_solve(None, None, None, None, None) == sk.ERR_INVALID_ARG
     assert L.sinkhorn_destroy(None) == sk.OK
     assert L.sinkhorn_problem_info(None, None, None, None, None) == sk.ERR_INVALID_ARG
+
+
+def test_device_memory_needs_no_device():
+    import log_domain_sinkhorn_amd as sk
+
+    cur, peak, big = sk.device_memory(reset=True)
+    assert cur == 0 and peak == 0 and big == 0
+    assert sk.lib().sinkhorn_device_memory(None, None, None, 0) == sk.OK
