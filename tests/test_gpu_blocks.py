@@ -113,6 +113,30 @@ def test_block_screen_full_size_sampled_row_blocks(sk):
         assert np.array_equal(idx[ptr[I]:ptr[I + 1]], col_r[ptr_r[k]:ptr_r[k + 1]]), I
 
 
+def test_block_screen_capacity_overflow_reports_the_needed_count(sk):
+    """A tile-list capacity one short of the need: SINKHORN_ERR_CAPACITY,
+    the needed count in nnz_out, the index array left unwritten."""
+    import ctypes
+
+    n, B, eps = 5000, 128, 1e-3
+    x, y, a, b = _sorted_problem(5, n)
+    f, g = _near_plan_potentials(n, eps, np.random.default_rng(5))
+    delta = 1e-3 / ((n + B - 1) // B)
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        fd, gd = _t(f), _t(g)
+        _, idx = P.block_screen(eps, fd, gd, B, delta)
+        need = int(idx.shape[0])
+        assert need > 1
+        ptr = torch.empty((n + B - 1) // B + 1, dtype=torch.int64, device=DEV)
+        small = torch.full((need - 1,), -7, dtype=torch.int32, device=DEV)
+        nnz = ctypes.c_int64(-1)
+        code = sk.lib().sinkhorn_block_screen(P._h, eps, sk._ptr(fd), sk._ptr(gd), B, delta, 0,
+                                              sk._ptr(ptr), sk._ptr(small), need - 1, ctypes.byref(nnz))
+        assert code == sk.ERR_CAPACITY and nnz.value == need
+        assert bool((small == -7).all())
+        assert b"capacity" in sk.lib().sinkhorn_strerror(code)
+
+
 @pytest.mark.parametrize("prev", [True, False], ids=["shifted", "exact"])
 @pytest.mark.parametrize("n,B,eps", [(16384, 128, 1e-4), (16384, 256, 1e-3), (5000, 128, 1e-3)])
 def test_sparse_halfsteps_match_oracle(sk, n, B, eps, prev):
