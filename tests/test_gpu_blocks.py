@@ -246,6 +246,23 @@ def _dense_check(sk, P, rep, eps, f, g, tol):
     assert max(Rr, Rc) <= R_A + rep["omega"] + fl
 
 
+@pytest.mark.parametrize("B,d", [(256, 3), (128, 2), (128, 1)])
+def test_multiscale_certificate_other_blocks_and_dimensions(sk, B, d):
+    """The certified solve with 256-point blocks, and on clouds of the
+    clustered workload projected to their first d axes: the certificate bounds
+    the exact dense residuals of the returned potentials."""
+    n, eps = 16384, 1e-3
+    c = synth.make(5, n=n, m=n)
+    x = np.ascontiguousarray(c.x[:, :d])
+    y = np.ascontiguousarray(c.y[:, :d])
+    prm = sk.MultiscaleParams(B=B, eps=eps, tol=1e-2)
+    _log(f"multiscale n={n} B={B} d={d}")
+    with sk.Problem(_t(x), _t(y), _t(c.a), _t(c.b), 1.0) as P:
+        f, g, rep = P.solve_multiscale(prm)
+        _log(f"  coarse {rep['coarse_iters']} fine {rep['fine_updates']} cells {rep['ncells_x']}x{rep['ncells_y']}")
+        _dense_check(sk, P, rep, eps, f, g, prm.tol)
+
+
 @pytest.mark.parametrize("eps", [1e-3, 1e-4])
 def test_multiscale_certificate_holds_at_2e18(sk, eps):
     """n = m = 2^18 of the clustered workload: the stop certificate bounds the
