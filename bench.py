@@ -76,27 +76,39 @@ def ops_per_pair(d: int) -> int:
 
 KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h")
 
+# HBM traffic of a workload's dominant kernel: the committed rocprofv3 PMC
+# summary and the sources that kernel is built from (the figure is used only
+# while their digest matches the one recorded with the counters)
+PMC_RECORDS = {
+    2: ("k_lse_valu_w2_n20000_d3_pmc.md", KERNEL_SOURCES),
+    3: ("k_lse_mfma_w3_n50000_m60000_d50_pmc.md", ("mfma.hip", "rowfinal.h", "internal.h")),
+}
 
-def kernel_source_digest() -> str:
-    """sha256 over the sources the dense pair kernel is built from."""
+
+def kernel_source_digest(sources=KERNEL_SOURCES) -> str:
+    """sha256 over the sources a pair kernel is built from."""
     import hashlib
 
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "log_domain_sinkhorn_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def pmc_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed PMC summary, or None
-    when there is none or the kernel source changed since it was taken."""
+def pmc_traffic(kernel: str, workload: int = 2):
+    """HBM bytes per launch of `kernel` from the workload's committed PMC
+    summary, or None when there is none or the kernel source changed since it
+    was taken."""
     import re
 
-    path = os.path.join(ROOT, "profiles", "k_lse_valu_w2_n20000_d3_pmc.md")
+    if workload not in PMC_RECORDS:
+        return None
+    name, sources = PMC_RECORDS[workload]
+    path = os.path.join(ROOT, "profiles", name)
     try:
         text = open(path).read()
-        digest = kernel_source_digest()
+        digest = kernel_source_digest(sources)
     except OSError:
         return None
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+kernel_sources_sha256:\s*([0-9a-f]+)\s+kernel:\s*(\S+)", text)
@@ -355,7 +367,7 @@ def main():
                 "peak": MFMA_F32_PEAK / 1e12,
                 "unit": "TFLOP/s",
                 "frac": achieved / MFMA_F32_PEAK,
-                "traffic": None,
+                "traffic": pmc_traffic(f"k_lse_mfma<{kp}>", args.workload),
                 "flops_per_pair": flops,
                 "kernel": f"k_lse_mfma<{kp}>",
             }
@@ -369,7 +381,7 @@ def main():
                 "peak": VALU_PEAK_OPS / 1e12,
                 "unit": "Tops/s",
                 "frac": achieved / VALU_PEAK_OPS,
-                "traffic": pmc_traffic(kname) if args.workload == 2 else None,
+                "traffic": pmc_traffic(kname, args.workload),
                 "ops_per_pair": ops,
                 "pair_peak": VALU_PEAK_OPS / ops,
                 "kernel": kname,
