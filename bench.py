@@ -184,6 +184,8 @@ def main():
                     help="workload 5: sampled lift checks between batches of coarse updates")
     ap.add_argument("--max-fine", type=int, default=None,
                     help="workload 5: cap on fine updates (profiling runs; the default runs to the certificate)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="run only the kernel-timing region once and print its kernel timing (counter runs)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -264,6 +266,18 @@ def main():
             mat = (lo, P.profile_read() if timing else None)
             P.profile_enable(0)
         return rep, kt, mat
+
+    if args.roofline_only:
+        # only the kernel-timing region, once (for counter runs of the large
+        # workloads); from zero potentials
+        _, kt, _ = step(timing=True, bounded=True)
+        ms, nl, pairs = kt
+        print(json.dumps({"roofline_only": True, "workload": args.workload,
+                          "region": W.get("roofline", "the whole step"),
+                          "pair_kernel": {"launches": nl, "avg_ms": ms / max(nl, 1),
+                                          "pair_evals_per_s": pairs / (ms * 1e-3) if ms else None}}),
+              flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
