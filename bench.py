@@ -194,6 +194,9 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
+    if (args.verify or args.adaptive) and "multiscale" not in WORKLOADS[args.workload]:
+        print("bench.py: --verify and --adaptive apply to the multiscale workload (5) only", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -212,9 +215,6 @@ def main():
     # the cost scale is resolved once, as a number, before anything is timed
     scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
     multiscale = "multiscale" in W
-    if (args.verify or args.adaptive) and not multiscale:
-        print("bench.py: --verify and --adaptive apply to the multiscale workload (5) only", file=sys.stderr)
-        sys.exit(2)
     if multiscale:
         prm = sk.MultiscaleParams(**W["multiscale"])
         if args.max_fine is not None:
