@@ -198,16 +198,18 @@ __global__ void k_reset_ctl(Ctl* ctl) {
   }
 }
 
-// Workgroups of the pair kernel resident on the whole chip at once.
+// Workgroups of the pair kernel resident on the whole chip at once. The
+// per-CU figure is queried once per instantiation (a static initialised
+// under the language's once-only guarantee, so handles on other host
+// threads may ask concurrently; a failed query leaves it to the next call).
 template <int D>
 int64_t resident_slots(sinkhorn_problem* p) {
-  static int per_cu[kMaxValuD + 1] = {};
-  if (per_cu[D] == 0) {
+  static const int per_cu = [] {
     int nb = 0;
     SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_valu<D, true>, kThreads, 0));
-    per_cu[D] = nb > 0 ? nb : 1;
-  }
-  return (int64_t)per_cu[D] * p->num_cu;
+    return nb > 0 ? nb : 1;
+  }();
+  return (int64_t)per_cu * p->num_cu;
 }
 
 constexpr int64_t kXcds = 8;

@@ -334,15 +334,15 @@ struct MPlan {
   int64_t tiles;
 };
 
-// Workgroups of k_lse_mfma<KP> resident on the whole chip at once.
+// Workgroups of k_lse_mfma<KP> resident on the whole chip at once (queried
+// once per instantiation, thread-safe as in the VALU path).
 template <int KP>
 int64_t slots_kp(sinkhorn_problem* p) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
+  static const int per_cu = [] {
     int nb = 0;
     SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_mfma<KP>, 256, 0));
-    per_cu = nb > 0 ? nb : 1;
-  }
+    return nb > 0 ? nb : 1;
+  }();
   return (int64_t)per_cu * p->num_cu;
 }
 
