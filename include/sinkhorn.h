@@ -26,7 +26,9 @@
  *   - All device work is enqueued on the stream given at init (a hipStream_t
  *     passed as void*; NULL means the null stream). Calls that return host
  *     values (residuals, counts, thresholds, reports) synchronize that stream.
- *   - A handle must not be used from two host threads at once.
+ *   - A handle must not be used from two host threads at once; separate
+ *     handles (each on its own stream) may be used from separate threads
+ *     concurrently, and give the same results as when used one at a time.
  *
  * Errors: every function returns an int status. 0 = SINKHORN_OK, positive =
  * success with a note, negative = error. No exception or abort crosses the
