@@ -19,8 +19,9 @@ FlashSinkhorn 2:
     both supports come from the survivors.
   * §3.1 and §B.2 (optional adaptive switch): the coarse stage runs in batches
     of centroid updates; after each, the lifted potentials are accepted when
-    sampled row and column residual estimates plus three standard errors are
-    below tol (1024 sampled indices per side, expanded to 8192 when that
+    est + 3 SE < tol on both sides, est and SE being the sampled estimate of
+    the L1 marginal residual and its standard error (1024 sampled indices per
+    side, expanded to 8192 when that
     interval straddles tol, the same samples at every check); otherwise more
     centroid updates follow until they stall or reach their cap, and the fine
     loop takes over. Sample indices: the raw outputs of Philox4x64-10 keyed
@@ -127,6 +128,9 @@ class FS2Result:
 
 
 def prefix_bits(NB: int, MB: int, d: int) -> int:
+    """Morton prefix length of a cell (§3, §B.1: at most twice as many cells
+    as blocks): the largest p with 2^p <= 2 * max(NB, MB), at most the code
+    length d * 21, so no side has more than 2 * max(NB, MB) cells."""
     return min(d * BITS, int(math.floor(math.log2(2 * max(NB, MB)))))
 
 
@@ -147,14 +151,24 @@ def coarse_solve(cx, cy, mx, my, prm: FS2Params):
         F = halfstep_f(cx, cy, my, G, prm.eps, prm.scale)
         G = halfstep_g(cx, cy, mx, F, prm.eps, prm.scale)
         iters += 1
-        R = max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale))
-        hist.append(R)
-        if R <= prm.coarse_tol:
-            break
-        w = prm.stall_window
-        if len(hist) > w and hist[-1] > (1.0 - prm.stall_rel) * hist[-1 - w]:
+        hist.append(max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale)))
+        if coarse_done(hist, prm):
             break
     return F, G, iters
+
+
+def coarse_done(hist, prm: FS2Params) -> bool:
+    """Stop rule of the centroid updates at the target eps, given the residual
+    history R_1..R_k of those updates (§3.1, §B.2: extra centroid updates run
+    until the coarse error stalls; the cap of 2048 updates is the caller's
+    loop bound). Read here as: stop once R_k <= coarse_tol, or once the last
+    ``stall_window`` updates cut the residual by less than the fraction
+    ``stall_rel``, i.e. R_k > (1 - stall_rel) * R_{k - stall_window}."""
+    R = hist[-1]
+    if R <= prm.coarse_tol:
+        return True
+    w = prm.stall_window
+    return len(hist) > w and R > (1.0 - prm.stall_rel) * hist[-1 - w]
 
 
 def sample_indices(count: int, k: int, seed: int, stream: int) -> np.ndarray:
@@ -216,10 +230,8 @@ def coarse_batch(cx, cy, mx, my, F, G, prm, count: int, anneal: bool):
         F = halfstep_f(cx, cy, my, G, prm.eps, prm.scale)
         G = halfstep_g(cx, cy, mx, F, prm.eps, prm.scale)
         iters += 1
-        R = max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale))
-        hist.append(R)
-        w = prm.stall_window
-        if R <= prm.coarse_tol or (len(hist) > w and hist[-1] > (1.0 - prm.stall_rel) * hist[-1 - w]):
+        hist.append(max(marginal_residuals(cx, cy, mx, my, F, G, prm.eps, prm.scale)))
+        if coarse_done(hist, prm):
             return F, G, annealed, iters, True
     return F, G, annealed, iters, False
 

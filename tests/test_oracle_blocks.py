@@ -132,6 +132,52 @@ def test_sparse_residual_plus_omega_bounds_full_residual(problem):
     assert Fr <= Rr + omega + 1e-12 and Fc <= Rc + omega + 1e-12
 
 
+def _masked_plan_residual(P, Q, wp, wq, f, g, eps, M):
+    """L1 residual of the rows of the plan restricted to the point mask M
+    (scipy cdist for the cost, the plan written out entry by entry)."""
+    C = cdist(P.astype(np.float64), Q.astype(np.float64), "sqeuclidean")
+    pi = (wp.astype(np.float64)[:, None] * wq.astype(np.float64)[None, :]
+          * np.exp((f.astype(np.float64)[:, None] + g.astype(np.float64)[None, :] - C) / eps))
+    rows = np.where(M, pi, 0.0).sum(axis=1)
+    return float(np.abs(rows - wp.astype(np.float64)).sum())
+
+
+def test_sparse_residuals_equal_the_explicitly_masked_plan(problem):
+    """FlashSinkhorn 2, §C.4: the certificate's residual is the one of the plan
+    restricted to the admitted support. Built independently here: a block mask
+    (with a row block and a column block that hold no tile, so both take the
+    dense support), expanded to points with np.kron, and the plan from
+    scipy's cdist."""
+    x, y, a, b, f, g, eps = problem
+    B = 32
+    NB, MB = math.ceil(len(x) / B), math.ceil(len(y) / B)
+    rng = np.random.default_rng(3)
+    Mb = rng.random((NB, MB)) < 0.3
+    Mb[2, :] = False  # row block 2: no admitted tile
+    Mb[:, 5] = False  # column block 5: no admitted tile
+    Mb[7, :] = True   # a full row block
+    ptr = np.concatenate([[0], np.cumsum(Mb.sum(1))]).astype(np.int64)
+    col = np.concatenate([np.nonzero(Mb[I])[0] for I in range(NB)]).astype(np.int32)
+    ptrT = np.concatenate([[0], np.cumsum(Mb.sum(0))]).astype(np.int64)
+    rowT = np.concatenate([np.nonzero(Mb[:, J])[0] for J in range(MB)]).astype(np.int32)
+    Mp = np.kron(Mb, np.ones((B, B), bool))[:len(x), :len(y)]
+    Mr = Mp.copy()
+    Mr[~Mr.any(axis=1)] = True  # rows of a block without tiles: every column
+    Mc = Mp.T.copy()
+    Mc[~Mc.any(axis=1)] = True  # columns of a block without tiles: every row
+    assert not Mr.all() and not Mc.all()
+    want_row = _masked_plan_residual(x, y, a, b, f, g, eps, Mr)
+    want_col = _masked_plan_residual(y, x, b, a, g, f, eps, Mc)
+    Rr, Rc = oracle.sparse_residuals(x, y, a, b, f, g, eps, 1.0, ptr, col, ptrT, rowT, B)
+    assert Rr == pytest.approx(want_row, rel=1e-12, abs=1e-15)
+    assert Rc == pytest.approx(want_col, rel=1e-12, abs=1e-15)
+    # the restriction matters here: the full-support residuals differ
+    full_row = _masked_plan_residual(x, y, a, b, f, g, eps, np.ones_like(Mr))
+    full_col = _masked_plan_residual(y, x, b, a, g, f, eps, np.ones_like(Mc))
+    assert abs(full_row - want_row) > 1e-6 * want_row
+    assert abs(full_col - want_col) > 1e-6 * want_col
+
+
 def test_single_point_blocks_reduce_to_the_plan_threshold(rng):
     """With B = 1 every bound is tight: F = f, G = g, D = C and W = weight, so a
     pair is omitted iff pi_ij <= delta * min(a_i, b_j)."""

@@ -176,3 +176,64 @@ def test_adaptive_switch_falls_back_to_certified_fine_updates(rng):
     assert not res.accepted_by_sample and res.checks >= 1 and res.certified and res.fine_updates > 0
     Fr, Fc = oracle.marginal_residuals(x, y, w, w, res.f, res.g, prm.eps, 1.0)
     assert max(Fr, Fc) <= max(res.R_A_row, res.R_A_col) + res.omega + 1e-12
+
+
+# ---- the coarse stop rule and the cell prefix (FlashSinkhorn 2, §3, §3.1, §B.1, §B.2)
+
+from oracle.fs2 import coarse_done, coarse_solve, prefix_bits  # noqa: E402
+
+
+def _stop_after(history, prm):
+    """Number of centroid updates run when the residuals come out as `history`."""
+    for k in range(1, len(history) + 1):
+        if coarse_done(history[:k], prm):
+            return k
+    return None
+
+
+def test_coarse_stop_rule_on_hand_made_histories():
+    prm = FS2Params(coarse_tol=1e-3, stall_window=10, stall_rel=0.01)
+    # tolerance: stops at the first residual <= coarse_tol (equality included)
+    assert _stop_after([0.5, 0.01, 0.0009, 0.0001], prm) == 3
+    assert _stop_after([0.5, 1e-3], prm) == 2
+    # a plateau at 0.2 after 1, 0.5, 0.25: the window of ten updates first
+    # compares 0.2 with 1.0 (update 11), 0.5 (12), 0.25 (13: 0.2 <= 0.2475),
+    # then with 0.2 itself at update 14 (0.2 > 0.198): stall
+    assert _stop_after([1.0, 0.5, 0.25] + [0.2] * 30, prm) == 14
+    # 0.05% less per update: 0.5% over ten updates, stalls as soon as the
+    # window is full (update 11: 0.9945 > 0.99 * 0.9995)
+    assert _stop_after([1.0 - 0.0005 * k for k in range(1, 40)], prm) == 11
+    # exactly 1% less over the window is progress (stall needs more than 1 - stall_rel)
+    assert _stop_after([1.0] + [0.995] * 9 + [0.99, 0.99], prm) == 12
+    # 20% less per update never stalls and reaches the tolerance at 0.8^31 < 1e-3 (update 32)
+    hist = [0.8 ** k for k in range(1, 60)]
+    assert _stop_after(hist, prm) == 31
+    assert 0.8 ** 30 > 1e-3 >= 0.8 ** 31
+
+
+def test_coarse_stage_runs_the_annealing_then_at_most_coarse_max_updates(rng):
+    x = rng.uniform(0, 1, size=(12, 2))
+    y = rng.uniform(0, 1, size=(9, 2))
+    mx = np.full(12, 1 / 12)
+    my = np.full(9, 1 / 9)
+    # stages 1, 0.5, 0.25, 0.125 above eps = 0.1, two updates each, then the cap of 3
+    prm = FS2Params(eps=0.1, coarse_eps_start=1.0, coarse_factor=0.5, coarse_iters_per_stage=2,
+                    coarse_tol=0.0, coarse_max=3, stall_window=1 << 30)
+    _, _, iters = coarse_solve(x, y, mx, my, prm)
+    assert iters == 4 * 2 + 3
+
+
+def test_prefix_bits_give_at_most_twice_as_many_cells_as_blocks(rng):
+    assert prefix_bits(131072, 131072, 3) == 18  # 2^24 points in blocks of 128
+    assert prefix_bits(1, 1, 3) == 1
+    assert prefix_bits(3, 2, 3) == 2  # 2^2 <= 6 < 2^3
+    assert prefix_bits(4, 1, 3) == 3
+    assert prefix_bits(1 << 40, 1, 1) == 21  # at most the code length
+    for n in (300, 1000, 5000):
+        x = rng.uniform(0, 1, size=(n, 3)).astype(np.float32)
+        codes, perm, _, _ = oracle.morton_order(x, x)
+        NB = (n + 127) // 128
+        p = prefix_bits(NB, NB, 3)
+        off, _, _ = oracle.cells(codes, x[perm], np.full(n, 1 / n, np.float32), p)
+        assert len(off) - 1 <= 2 * NB
+        assert 2 ** p <= 2 * NB < 2 ** (p + 1)
