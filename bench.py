@@ -74,7 +74,7 @@ def ops_per_pair(d: int) -> int:
     return 2 * d + 2
 
 
-KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h")
+KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h", "launch_plan.h")
 
 # HBM traffic of a workload's dominant kernel: the committed rocprofv3 PMC
 # summary and the sources that kernel is built from (the figure is used only

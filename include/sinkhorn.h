@@ -112,9 +112,9 @@ int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m,
  * (negative weights are not checked and give undefined results); returns
  * SINKHORN_ERR_MASS if |sum a - sum b| > 1e-5 * max(sum a, sum b), and
  * SINKHORN_ERR_NONFINITE if a coordinate or weight is NaN or infinite.
- * The handle (host pointer) is written to *out. The moscot #846 materializer is
- * "a callable over row indices built once per call", with geometry resolution
- * hoisted out of the row loop; the handle plays that role. */
+ * The handle (host pointer) is written to *out. In moscot #846 the row
+ * materializer is built once and then called per batch of row indices, the
+ * geometry resolved before the row loop; the handle plays that role. */
 int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const float* a,
                   const float* b, int64_t n, int64_t m, int32_t d, double cost_scale,
                   void* stream);
@@ -268,8 +268,8 @@ typedef struct {
   /* Adaptive coarse-to-fine switch (FlashSinkhorn 2, §3.1, §B.2), when nonzero: the coarse
    * stage runs in batches of check_every centroid updates (the first after the annealing
    * stages), each ending early on coarse_tol or a stall; after each batch the potentials are
-   * lifted and accepted, with no fine update, when the sampled row and column residual
-   * estimates plus three standard errors are below tol (check_samples indices per side,
+   * lifted and accepted, with no fine update, when est + 3 SE < tol holds on both sides
+   * (est, SE: sampled L1 residual estimate and its standard error; check_samples indices per side,
    * check_samples_max when that interval straddles tol; the same indices at every check).
    * Otherwise batches continue until the coarse stage converges, stalls or reaches
    * coarse_max, and the certified fine loop follows. Sample k of a side of size c is

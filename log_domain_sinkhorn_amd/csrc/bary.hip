@@ -314,7 +314,7 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
                             pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp, A.Ap);
     SK_LAUNCH_CHECK();
     prof_done(p, SINKHORN_PROF_BARY, (double)p->n * (double)p->m);
-    hipLaunchKernelGGL(k_bary_merge<D>, dim3((uint32_t)A.tiles), dim3(kThreads), 0, p->stream, A,
+    hipLaunchKernelGGL(k_bary_merge<D>, grid1(A.tiles, kThreads), dim3(kThreads), 0, p->stream, A,
                        (int32_t)shifted);
     SK_LAUNCH_CHECK();
   }

@@ -345,7 +345,7 @@ void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& o
   out.lw = (double*)dev_alloc(sizeof(double) * out.nb);
   out.F = (double*)dev_alloc(sizeof(double) * out.nb);
   double* W = (double*)dev_alloc(sizeof(double) * out.nb);
-  hipLaunchKernelGGL(k_block_static, dim3((uint32_t)out.nb), dim3(64), 0, p->stream, s.soa,
+  hipLaunchKernelGGL(k_block_static, grid1(out.nb, 64), dim3(64), 0, p->stream, s.soa,
                      s.padded, p->d, s.w, s.count, B, out.lo, out.hi, W, out.nb);
   SK_LAUNCH_CHECK();
   std::vector<double> h((size_t)out.nb);
@@ -359,7 +359,7 @@ void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& o
   out.ghi = (double*)dev_alloc(sizeof(double) * 3 * out.ng);
   out.glw = (double*)dev_alloc(sizeof(double) * out.ng);
   out.gF = (double*)dev_alloc(sizeof(double) * out.ng);
-  hipLaunchKernelGGL(k_group_static, dim3((uint32_t)((out.ng + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(k_group_static, grid1(((out.ng + 255) / 256), 256), dim3(256), 0,
                      p->stream, out.lo, out.hi, out.lw, out.nb, p->d, out.ng, out.glo, out.ghi,
                      out.glw);
   SK_LAUNCH_CHECK();
@@ -367,9 +367,9 @@ void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& o
 }
 
 void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, BlockSummary& s) {
-  hipLaunchKernelGGL(k_block_max, dim3((uint32_t)s.nb), dim3(64), 0, p->stream, pot, count, s.B, s.F);
+  hipLaunchKernelGGL(k_block_max, grid1(s.nb, 64), dim3(64), 0, p->stream, pot, count, s.B, s.F);
   SK_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_group_max, dim3((uint32_t)((s.ng + 255) / 256)), dim3(256), 0, p->stream, s.F,
+  hipLaunchKernelGGL(k_group_max, grid1(((s.ng + 255) / 256), 256), dim3(256), 0, p->stream, s.F,
                      s.nb, s.ng, s.gF);
   SK_LAUNCH_CHECK();
 }
@@ -439,7 +439,7 @@ int64_t screen_tiles(sinkhorn_problem* p, const BlockSummary& rows, const BlockS
 int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
   uint32_t* d = (uint32_t*)dev_alloc(sizeof(uint32_t));
   zero_i32((int32_t*)d, 1, p->stream);
-  hipLaunchKernelGGL(k_count_empty, dim3((uint32_t)((nr + 255) / 256)), dim3(256), 0, p->stream, ptr,
+  hipLaunchKernelGGL(k_count_empty, grid1(((nr + 255) / 256), 256), dim3(256), 0, p->stream, ptr,
                      nr, d);
   SK_LAUNCH_CHECK();
   uint32_t h = 0;
@@ -489,7 +489,7 @@ const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tile
   uint32_t* kout = p->order_key + p->order_cap;
   int32_t* vin = p->order_val;
   int32_t* vout = p->order_val + p->order_cap;
-  hipLaunchKernelGGL(k_tile_keys, dim3((uint32_t)((tiles + 255) / 256)), dim3(256), 0, st, ptr, tiles,
+  hipLaunchKernelGGL(k_tile_keys, grid1(((tiles + 255) / 256), 256), dim3(256), 0, st, ptr, tiles,
                      B, kin, vin);
   SK_LAUNCH_CHECK();
   size_t need = 0;
@@ -512,10 +512,10 @@ template <int D>
 void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted,
                    const ProfEv& pe) {
   if (shifted)
-    hipExtLaunchKernelGGL((k_lse_sparse<D, true>), dim3((uint32_t)tiles), dim3(kThreads), 0, p->stream,
+    hipExtLaunchKernelGGL((k_lse_sparse<D, true>), grid1(tiles, kThreads), dim3(kThreads), 0, p->stream,
                           pe.start, pe.stop, 0, A, A.Q, A.H);
   else
-    hipExtLaunchKernelGGL((k_lse_sparse<D, false>), dim3((uint32_t)tiles), dim3(kThreads), 0,
+    hipExtLaunchKernelGGL((k_lse_sparse<D, false>), grid1(tiles, kThreads), dim3(kThreads), 0,
                           p->stream, pe.start, pe.stop, 0, A, A.Q, A.H);
   SK_LAUNCH_CHECK();
 }
@@ -569,7 +569,7 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
 void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_t* idx, int64_t nc) {
   uint32_t* d = (uint32_t*)dev_alloc(sizeof(uint32_t));
   zero_i32((int32_t*)d, 1, p->stream);
-  hipLaunchKernelGGL(k_check_csr, dim3((uint32_t)((nr + 255) / 256)), dim3(256), 0, p->stream, ptr,
+  hipLaunchKernelGGL(k_check_csr, grid1(((nr + 255) / 256), 256), dim3(256), 0, p->stream, ptr,
                      nr, idx, nc, d);
   SK_LAUNCH_CHECK();
   uint32_t h = 0;

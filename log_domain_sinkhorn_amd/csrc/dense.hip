@@ -215,32 +215,19 @@ int64_t resident_slots(sinkhorn_problem* p) {
 constexpr int64_t kXcds = 8;
 constexpr int64_t kL2Slice = 2 << 20;  // column bytes an XCD's L2 keeps comfortably
 
-// Column splits G per row tile, a power of two (the kernels split the block
-// index with a mask and a shift): at least 4 chunks per wave (1 when the
-// tiles are too few to fill the chip), at most 64. The workgroups run in
-// rounds of `slots` and finish unevenly, so aim at three rounds or more for
-// the load to even out. Workgroups are dealt to the XCDs in turn, so with G
-// a multiple of 8 each XCD streams its own column splits: preferred whenever
-// the column data would not fit an XCD's L2 whole, or G reaches 8 anyway.
-// Trailing splits may be empty; they leave an empty partial.
+// Column splits G per row tile (plan_dense_split: a power of two, at least 4
+// chunks per wave, about three rounds of the resident workgroups, a multiple
+// of the 8 XCDs when the columns outgrow an XCD's L2, and a grid that fits
+// one dispatch). Trailing splits may be empty; they leave an empty partial.
 int64_t plan_split(LseArgs& A, int64_t nrows, int64_t ncols, int64_t slots, int d) {
-  A.nchunks = (ncols + kChunk - 1) / kChunk;
-  A.tiles = (nrows + kRowsPerTile - 1) / kRowsPerTile;
-  int64_t maxsplit = A.nchunks / (4 * kW);
-  // too few tiles to fill the chip even so: down to one chunk per wave
-  if (A.tiles * (maxsplit > 1 ? maxsplit : 1) < slots) maxsplit = A.nchunks / kW;
-  if (maxsplit > kMaxSplit) maxsplit = kMaxSplit;
-  if (maxsplit < 1) maxsplit = 1;
-  const int64_t want = (3 * slots + A.tiles - 1) / A.tiles;
-  const bool big = A.nchunks * kChunk * (int64_t)(d + 1) * 4 > kL2Slice;
-  int64_t G = 1;
-  while (2 * G <= maxsplit && G < want) G *= 2;  // smallest power of two >= want, capped
-  if (big && G < kXcds && kXcds <= maxsplit) G = kXcds;
-  int32_t lg = 0;
-  while ((int64_t(1) << lg) < G) ++lg;
-  A.G = (int32_t)G;
-  A.glog = lg;
-  A.cps = (A.nchunks + G - 1) / G;
+  const DenseSplit s = plan_dense_split(nrows, ncols, slots, d, kChunk, kRowsPerTile, kW, kThreads,
+                                        kMaxSplit, kXcds, kL2Slice);
+  if (!s.ok) fail(SINKHORN_ERR_UNSUPPORTED, "too many row tiles for one dispatch");
+  A.nchunks = s.nchunks;
+  A.tiles = s.tiles;
+  A.G = s.G;
+  A.glog = s.glog;
+  A.cps = s.cps;
   return A.tiles * A.G;
 }
 
@@ -249,10 +236,10 @@ void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shif
   const int32_t kind = shifted ? SINKHORN_PROF_DENSE : SINKHORN_PROF_DENSE_EXACT;
   const ProfEv pe = prof_events(p, kind);
   if (shifted)
-    hipExtLaunchKernelGGL((k_lse_valu<D, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
+    hipExtLaunchKernelGGL((k_lse_valu<D, true>), grid1(blocks, kThreads), dim3(kThreads), 0, p->stream,
                           pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
   else
-    hipExtLaunchKernelGGL((k_lse_valu<D, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, p->stream,
+    hipExtLaunchKernelGGL((k_lse_valu<D, false>), grid1(blocks, kThreads), dim3(kThreads), 0, p->stream,
                           pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
   SK_LAUNCH_CHECK();
   prof_done(p, kind, pairs);
@@ -261,13 +248,12 @@ void launch_lse(sinkhorn_problem* p, const LseArgs& A, int64_t blocks, bool shif
 template <int D>
 void run_halfstep(sinkhorn_problem* p, const HalfStep& hs, LseArgs& A, bool shifted, double pairs) {
   const int64_t blocks = plan_split(A, hs.rows->count, hs.cols->count, resident_slots<D>(p), D);
-  if (blocks >= (int64_t)UINT32_MAX) fail(SINKHORN_ERR_UNSUPPORTED, "too many row tiles");
   // fp64 maxima: two float slots per partial
   if (2 * (int64_t)A.G * hs.rows->count > p->part_cap)
     fail(SINKHORN_ERR_HIP, "partial buffer too small");
   if (row_groups(hs.rows->count) > p->red_cap) fail(SINKHORN_ERR_HIP, "reduction buffer too small");
   launch_lse<D>(p, A, blocks, shifted, pairs);
-  hipLaunchKernelGGL(k_merge<D>, dim3((uint32_t)A.tiles), dim3(kThreads), 0, p->stream, A,
+  hipLaunchKernelGGL(k_merge<D>, grid1(A.tiles, kThreads), dim3(kThreads), 0, p->stream, A,
                      (int32_t)shifted);
   SK_LAUNCH_CHECK();
   if (A.F.prev) launch_reduce(p, A.tiles);
@@ -354,7 +340,7 @@ void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, d
     return;
   }
   const int64_t blocks = (side.count + 255) / 256;
-  hipLaunchKernelGGL(k_column_term, dim3((uint32_t)blocks), dim3(256), 0, p->stream, side.w, pot,
+  hipLaunchKernelGGL(k_column_term, grid1(blocks, 256), dim3(256), 0, p->stream, side.w, pot,
                      side.count, kLog2e / eps, H);
   SK_LAUNCH_CHECK();
 }

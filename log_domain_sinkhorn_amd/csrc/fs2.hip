@@ -120,7 +120,7 @@ void build_cells(sinkhorn_problem* p, const Side& sorted, const uint64_t* codes,
   int64_t* off = nullptr;
   void* temp = nullptr;
   try {
-    hipLaunchKernelGGL(k_cell_flags, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, codes, n,
+    hipLaunchKernelGGL(k_cell_flags, grid1(((n + 255) / 256), 256), dim3(256), 0, st, codes, n,
                        shift, flags);
     SK_LAUNCH_CHECK();
     size_t tb = 0;
@@ -131,11 +131,11 @@ void build_cells(sinkhorn_problem* p, const Side& sorted, const uint64_t* codes,
     SK_HIP(hipMemcpyAsync(&ncell, incl + n - 1, sizeof(int32_t), hipMemcpyDeviceToHost, st));
     SK_HIP(hipStreamSynchronize(st));
     off = (int64_t*)dev_alloc(sizeof(int64_t) * (ncell + 1));
-    hipLaunchKernelGGL(k_cell_offsets, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, flags,
+    hipLaunchKernelGGL(k_cell_offsets, grid1(((n + 255) / 256), 256), dim3(256), 0, st, flags,
                        incl, n, off);
     SK_LAUNCH_CHECK();
     alloc_side(cells, ncell, p->d, st);
-    hipLaunchKernelGGL(k_cell_records, dim3((uint32_t)((ncell + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_cell_records, grid1(((ncell + 255) / 256), 256), dim3(256), 0, st,
                        sorted.soa, sorted.padded, sorted.w, off, (int64_t)ncell, p->d, cells.soa,
                        cells.padded, cells.w);
     SK_LAUNCH_CHECK();
@@ -431,10 +431,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
                     codes[1], perm[1]);
     alloc_side(Xs, n, d, st);
     alloc_side(Ys, m, d, st);
-    hipLaunchKernelGGL(k_gather, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p->X.soa,
+    hipLaunchKernelGGL(k_gather, grid1(((n + 255) / 256), 256), dim3(256), 0, st, p->X.soa,
                        p->X.padded, p->X.w, perm[0], n, d, Xs.soa, Xs.padded, Xs.w);
     SK_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_gather, dim3((uint32_t)((m + 255) / 256)), dim3(256), 0, st, p->Y.soa,
+    hipLaunchKernelGGL(k_gather, grid1(((m + 255) / 256), 256), dim3(256), 0, st, p->Y.soa,
                        p->Y.padded, p->Y.w, perm[1], m, d, Ys.soa, Ys.padded, Ys.w);
     SK_LAUNCH_CHECK();
     build_cells(p, Xs, codes[0], p_bits, Cx);
@@ -648,10 +648,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     R.R_A_row = Rrow;
     R.R_A_col = Rcol;
     // ---- back to the caller's order
-    hipLaunchKernelGGL(k_scatter, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, fs[cf],
+    hipLaunchKernelGGL(k_scatter, grid1(((n + 255) / 256), 256), dim3(256), 0, st, fs[cf],
                        perm[0], n, f);
     SK_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_scatter, dim3((uint32_t)((m + 255) / 256)), dim3(256), 0, st, gs[cg],
+    hipLaunchKernelGGL(k_scatter, grid1(((m + 255) / 256), 256), dim3(256), 0, st, gs[cg],
                        perm[1], m, g);
     SK_LAUNCH_CHECK();
     SK_HIP(hipStreamSynchronize(st));
@@ -679,7 +679,7 @@ extern "C" int sinkhorn_sample_indices(int64_t count, int32_t k, uint64_t seed, 
     if (count < 1 || count > INT32_MAX || k < 0) fail(SINKHORN_ERR_INVALID_ARG, "need 1 <= count <= 2^31 - 1 and k >= 0");
     if (k == 0) return SINKHORN_OK;
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(k_sample_idx, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, st, seed, stream_id,
+    hipLaunchKernelGGL(k_sample_idx, grid1(((k + 255) / 256), 256), dim3(256), 0, st, seed, stream_id,
                        count, k, out);
     SK_LAUNCH_CHECK();
     SK_HIP(hipStreamSynchronize(st));

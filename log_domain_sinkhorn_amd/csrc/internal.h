@@ -9,6 +9,7 @@
 #include <string>
 #include <vector>
 
+#include "launch_plan.h"
 #include "sinkhorn.h"
 
 namespace sk {
@@ -28,6 +29,17 @@ void progress(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 
 #define SK_HIP(call) ::sk::check_hip((call), #call)
 #define SK_LAUNCH_CHECK() ::sk::check_hip(hipGetLastError(), "kernel launch")
+
+// Grid of a 1-D launch of `blocks` workgroups of `threads` work-items;
+// SINKHORN_ERR_UNSUPPORTED when it exceeds what one dispatch can hold
+// (launch_plan.h), instead of a launch that would drop workgroups.
+inline dim3 grid1(int64_t blocks, int64_t threads) {
+  if (!grid_fits(blocks, threads))
+    fail(SINKHORN_ERR_UNSUPPORTED, "launch of " + std::to_string(blocks) + " x " +
+                                       std::to_string(threads) +
+                                       " work-items exceeds one dispatch (2^32 - 1)");
+  return dim3((uint32_t)blocks);
+}
 
 // ---------------------------------------------------------------- constants
 constexpr double kLog2e = 1.4426950408889634074;  // 1 / ln 2

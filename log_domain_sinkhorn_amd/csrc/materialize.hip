@@ -294,7 +294,7 @@ void launch_mfma(sinkhorn_problem* p, const int64_t* rows, int64_t row0, int64_t
   if (want < 1) want = 1;
   const int64_t tps = (ntiles + want - 1) / want;
   const int32_t G = (int32_t)((ntiles + tps - 1) / tps);
-  hipExtLaunchKernelGGL((k_materialize_mfma<KP>), dim3((uint32_t)(rtiles * G)), dim3(256), 0,
+  hipExtLaunchKernelGGL((k_materialize_mfma<KP>), grid1((rtiles * G), 256), dim3(256), 0,
                         p->stream, pe.start, pe.stop, 0, p->X.rowmaj, p->Y.rowmaj, p->d, p->m, rows,
                         row0, k, P, twokappa, G, ntiles, tps, T, keys);
   SK_LAUNCH_CHECK();
@@ -306,7 +306,7 @@ void rows_pass(sinkhorn_problem* p, double eps, const float* f, const int64_t* r
   const double lam = kLog2e / eps;
   const double kappa = p->scale * lam;
   const bool mf = p->d > kMaxValuD;
-  hipLaunchKernelGGL(k_row_terms, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream, rows,
+  hipLaunchKernelGGL(k_row_terms, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream, rows,
                      row0, k, p->X.w, f, mf ? p->X.norm2 : nullptr, lam, kappa, P, live, keys);
   SK_LAUNCH_CHECK();
   const ProfEv pe = prof_events(p, SINKHORN_PROF_MATERIALIZE);
@@ -340,7 +340,7 @@ void column_terms(sinkhorn_problem* p, double eps, const float* g, double* Hd) {
   if (p->d > kMaxValuD) {
     mfma_column_term(p, p->Y, g, eps);
   } else {
-    hipLaunchKernelGGL(k_col_terms, dim3((uint32_t)((p->m + 255) / 256)), dim3(256), 0, p->stream,
+    hipLaunchKernelGGL(k_col_terms, grid1(((p->m + 255) / 256), 256), dim3(256), 0, p->stream,
                        p->Y.w, g, p->m, kLog2e / eps, Hd);
     SK_LAUNCH_CHECK();
   }
@@ -430,7 +430,7 @@ int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, c
     s.keys = (uint32_t*)dev_alloc(sizeof(uint32_t) * (k + 1));
     hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(64), 0, p->stream, s.keys + k, 0u);
     SK_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_check_rows, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+    hipLaunchKernelGGL(k_check_rows, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream,
                        rows, k, p->n, s.keys + k);
     SK_LAUNCH_CHECK();
     SK_HIP(hipMemcpyAsync(p->host_tmp, s.keys + k, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
@@ -442,7 +442,7 @@ int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, c
     column_terms(p, eps, g, s.Hd);
     rows_pass(p, eps, f, rows, 0, k, s.P, nullptr, s.keys, s.Hd, T);
     if (row_max) {
-      hipLaunchKernelGGL(k_keys_to_max, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+      hipLaunchKernelGGL(k_keys_to_max, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream,
                          s.keys, k, row_max);
       SK_LAUNCH_CHECK();
     }
@@ -475,7 +475,7 @@ int sinkhorn_min_row(sinkhorn_problem* p, double eps, const float* f, const floa
     for (int64_t r0 = 0; r0 < p->n; r0 += kb) {
       const int64_t k = p->n - r0 < kb ? p->n - r0 : kb;
       rows_pass(p, eps, f, nullptr, r0, k, s.P, s.live, s.keys, s.Hd, nullptr);
-      hipLaunchKernelGGL(k_min_live, dim3((uint32_t)((k + 255) / 256)), dim3(256), 0, p->stream,
+      hipLaunchKernelGGL(k_min_live, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream,
                          s.keys, s.live, k, best);
       SK_LAUNCH_CHECK();
     }
@@ -541,7 +541,7 @@ int sinkhorn_sparsify(sinkhorn_problem* p, double eps, const float* f, const flo
       for (int64_t r0 = 0; r0 < n; r0 += batch) {
         const int64_t k = n - r0 < batch ? n - r0 : batch;
         rows_pass(p, eps, f, nullptr, r0, k, s.P, nullptr, s.keys, s.Hd, T);
-        hipLaunchKernelGGL(k_row_count, dim3((uint32_t)k), dim3(256), 0, p->stream, T, m, threshold,
+        hipLaunchKernelGGL(k_row_count, grid1(k, 256), dim3(256), 0, p->stream, T, m, threshold,
                            counts);
         SK_LAUNCH_CHECK();
         // row_ptr[r0 .. r0 + k) = total + exclusive prefix of the batch counts
@@ -557,7 +557,7 @@ int sinkhorn_sparsify(sinkhorn_problem* p, double eps, const float* f, const flo
         memcpy(&cnt, &p->host_tmp[1], sizeof(int64_t));
         const int64_t after = last + cnt;
         if (fill && after <= cap) {
-          hipLaunchKernelGGL(k_row_fill, dim3((uint32_t)k), dim3(256), 0, p->stream, T, m, threshold,
+          hipLaunchKernelGGL(k_row_fill, grid1(k, 256), dim3(256), 0, p->stream, T, m, threshold,
                              row_ptr + r0, col, val);
           SK_LAUNCH_CHECK();
         }

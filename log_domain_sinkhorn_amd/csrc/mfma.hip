@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256 * kMergeGroups) void k_merge_splits(RowFinal F,
 
 void merge_splits(sinkhorn_problem* p, const RowFinal& F, int32_t G) {
   const int64_t nblocks = (F.np + 255) / 256;
-  hipLaunchKernelGGL(k_merge_splits, dim3((uint32_t)nblocks), dim3(256 * kMergeGroups), 0,
+  hipLaunchKernelGGL(k_merge_splits, grid1(nblocks, 256 * kMergeGroups), dim3(256 * kMergeGroups), 0,
                      p->stream, F, G, p->Mpart, p->Spart);
   SK_LAUNCH_CHECK();
   if (F.prev) launch_reduce(p, nblocks);
@@ -382,6 +382,9 @@ MPlan mplan(int64_t nrows, int64_t ncols, int64_t slots) {
   const int64_t maxsplit = mp.ntiles / 8 > 1 ? mp.ntiles / 8 : 1;
   if (want > 64) want = 64;
   if (want > maxsplit) want = maxsplit;
+  // tiles * G workgroups must fit one dispatch
+  const int64_t fit = max_blocks_1d(256) / mp.tiles;
+  if (want > fit) want = fit;
   if (want < 1) want = 1;
   mp.tps = (mp.ntiles + want - 1) / want;
   mp.G = (int32_t)((mp.ntiles + mp.tps - 1) / mp.tps);
@@ -391,7 +394,7 @@ MPlan mplan(int64_t nrows, int64_t ncols, int64_t slots) {
 template <int KP>
 void launch_kp(sinkhorn_problem* p, const MfmaArgs& A, int64_t blocks, double pairs) {
   const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
-  hipExtLaunchKernelGGL((k_lse_mfma<KP>), dim3((uint32_t)blocks), dim3(256), 0, p->stream, pe.start,
+  hipExtLaunchKernelGGL((k_lse_mfma<KP>), grid1(blocks, 256), dim3(256), 0, p->stream, pe.start,
                         pe.stop, 0, A);
   SK_LAUNCH_CHECK();
   prof_done(p, SINKHORN_PROF_DENSE, pairs);
@@ -420,7 +423,7 @@ void setup_mfma(sinkhorn_problem* p, const float* x, const float* y) {
     const float* pts = side == 0 ? x : y;
     s.rowmaj = (float*)dev_alloc(sizeof(float) * s.padded * p->kpad);
     s.norm2 = (float*)dev_alloc(sizeof(float) * s.padded);
-    hipLaunchKernelGGL(k_centre, dim3((uint32_t)((s.padded + 255) / 256)), dim3(256), 0, p->stream,
+    hipLaunchKernelGGL(k_centre, grid1(((s.padded + 255) / 256), 256), dim3(256), 0, p->stream,
                        pts, s.count, d, p->kpad, s.padded, dc, s.rowmaj, s.norm2);
     SK_LAUNCH_CHECK();
   }
@@ -430,7 +433,7 @@ void setup_mfma(sinkhorn_problem* p, const float* x, const float* y) {
 
 void mfma_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps) {
   const double kappa = p->scale * kLog2e / eps;
-  hipLaunchKernelGGL(k_column_term_mfma, dim3((uint32_t)((side.count + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(k_column_term_mfma, grid1(((side.count + 255) / 256), 256), dim3(256), 0,
                      p->stream, side.w, pot, side.norm2, side.count, kLog2e / eps,
                      1.0 / (2.0 * kappa), side.rowmaj + p->d, p->kpad);
   SK_LAUNCH_CHECK();

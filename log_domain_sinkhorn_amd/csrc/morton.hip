@@ -93,7 +93,7 @@ void bbox(const float* pts, int64_t ps, int64_t as, int64_t count, int32_t d, hi
   const int64_t per_block = (int64_t)kBoxBlock * kBoxPer;
   const int64_t blocks = (count + per_block - 1) / per_block;
   float* part = (float*)dev_alloc(sizeof(float) * blocks * 2 * d);
-  hipLaunchKernelGGL(k_bbox, dim3((uint32_t)blocks), dim3(kBoxBlock), 0, st, pts, ps, as, count, d,
+  hipLaunchKernelGGL(k_bbox, grid1(blocks, kBoxBlock), dim3(kBoxBlock), 0, st, pts, ps, as, count, d,
                      part);
   SK_LAUNCH_CHECK();
   std::vector<float> h((size_t)(blocks * 2 * d));
@@ -140,7 +140,7 @@ void morton_sort_strided(const float* x, int64_t xps, int64_t xas, const float* 
       const int64_t count = side == 0 ? n : m;
       uint64_t* kout = side == 0 ? codes_x : codes_y;
       int32_t* vout = side == 0 ? perm_x : perm_y;
-      hipLaunchKernelGGL(k_codes, dim3((uint32_t)((count + 255) / 256)), dim3(256), 0, st, pts, ps,
+      hipLaunchKernelGGL(k_codes, grid1(((count + 255) / 256), 256), dim3(256), 0, st, pts, ps,
                          as, count, d, box, ktmp, vtmp);
       SK_LAUNCH_CHECK();
       size_t tb = temp_bytes;

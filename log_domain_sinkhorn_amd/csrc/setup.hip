@@ -138,7 +138,7 @@ void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double*
   hipLaunchKernelGGL(k_moments, dim3((uint32_t)nchunk, (uint32_t)d), dim3(256), 0, st, pts, count,
                      d, chunk, part);
   SK_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_moments_reduce, dim3((uint32_t)((d + 255) / 256)), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(k_moments_reduce, grid1(((d + 255) / 256), 256), dim3(256), 0, st, part,
                      nchunk, d, out);
   SK_LAUNCH_CHECK();
   SK_HIP(hipMemcpyAsync(host_out, out, sizeof(double) * 2 * d, hipMemcpyDeviceToHost, st));
@@ -222,7 +222,7 @@ void host_free(void* p) {
 }
 
 void zero_i32(int32_t* v, int32_t count, hipStream_t st) {
-  hipLaunchKernelGGL(k_zero_i32, dim3((uint32_t)((count + 255) / 256)), dim3(256), 0, st, v, count);
+  hipLaunchKernelGGL(k_zero_i32, grid1(((count + 255) / 256), 256), dim3(256), 0, st, v, count);
   SK_LAUNCH_CHECK();
 }
 

@@ -240,7 +240,7 @@ template <int D>
 void launch_verify(hipStream_t st, const VerifyArgs& A) {
   constexpr int64_t kMaxGroups = 1 << 20;  // 2^28 work-items
   const int64_t want = (A.nnz + 3) / 4;
-  hipLaunchKernelGGL((k_verify<D>), dim3((uint32_t)(want < kMaxGroups ? want : kMaxGroups)), dim3(256),
+  hipLaunchKernelGGL((k_verify<D>), grid1((want < kMaxGroups ? want : kMaxGroups), 256), dim3(256),
                      0, st, A);
   SK_LAUNCH_CHECK();
 }
@@ -324,9 +324,9 @@ int64_t verify_tiles(sinkhorn_problem* p, const Side& rows, const Side& cols, co
       case 3: launch_verify<3>(st, A); break;
       default: fail(SINKHORN_ERR_UNSUPPORTED, "tile verification needs d <= 3");
     }
-    hipLaunchKernelGGL(k_row_fallback, dim3((uint32_t)nb), dim3(64), 0, st, ptr, nb, s.keep);
+    hipLaunchKernelGGL(k_row_fallback, grid1(nb, 64), dim3(64), 0, st, ptr, nb, s.keep);
     SK_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_zero_i32v, dim3((uint32_t)((mb + 255) / 256)), dim3(256), 0, st, s.colany, mb);
+    hipLaunchKernelGGL(k_zero_i32v, grid1(((mb + 255) / 256), 256), dim3(256), 0, st, s.colany, mb);
     SK_LAUNCH_CHECK();
     const uint32_t eb = (uint32_t)((nnz + 255) / 256);
     hipLaunchKernelGGL(k_col_mark, dim3(eb), dim3(256), 0, st, idx, nnz, s.keep, s.colany);
@@ -334,7 +334,7 @@ int64_t verify_tiles(sinkhorn_problem* p, const Side& rows, const Side& cols, co
     hipLaunchKernelGGL(k_col_fallback, dim3(eb), dim3(256), 0, st, idx, nnz, s.colany, s.keep);
     SK_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_keep_count, dim3((uint32_t)(nb + 1)), dim3(64), 0, st, ptr, nb, s.keep, s.cnt);
+  hipLaunchKernelGGL(k_keep_count, grid1((nb + 1), 64), dim3(64), 0, st, ptr, nb, s.keep, s.cnt);
   SK_LAUNCH_CHECK();
   size_t tb = 0;
   SK_HIP(rocprim::exclusive_scan(nullptr, tb, s.cnt, vptr, (int64_t)0, (size_t)(nb + 1),
@@ -358,7 +358,7 @@ int64_t verify_tiles(sinkhorn_problem* p, const Side& rows, const Side& cols, co
   SK_HIP(hipStreamSynchronize(st));
   if (kept < 0 || kept > nnz) fail(SINKHORN_ERR_HIP, "tile verification: bad kept count");
   if (nb > 0) {
-    hipLaunchKernelGGL(k_keep_fill, dim3((uint32_t)nb), dim3(64), 0, st, ptr, nb, idx, s.keep, vptr,
+    hipLaunchKernelGGL(k_keep_fill, grid1(nb, 64), dim3(64), 0, st, ptr, nb, idx, s.keep, vptr,
                        vidx, s.vrow);
     SK_LAUNCH_CHECK();
   }
@@ -367,7 +367,7 @@ int64_t verify_tiles(sinkhorn_problem* p, const Side& rows, const Side& cols, co
     SK_HIP(rocprim::radix_sort_pairs(s.temp, sb2, vidx, s.skey, s.vrow, tidx, (size_t)kept, 0,
                                      ebits, st));
   }
-  hipLaunchKernelGGL(k_col_bounds, dim3((uint32_t)((mb + 1 + 255) / 256)), dim3(256), 0, st, s.skey,
+  hipLaunchKernelGGL(k_col_bounds, grid1(((mb + 1 + 255) / 256), 256), dim3(256), 0, st, s.skey,
                      kept, mb, tptr);
   SK_LAUNCH_CHECK();
   return kept;

@@ -25,6 +25,8 @@ CASES = {
     "w2_n1000_tol": (2, 1000, 1000, dict(eps_start=1.0, eps_target=1e-3, tol=1e-3, max_iters=5000), "one"),
     "w4_n1000_tol": (4, 1000, 1000, dict(eps_start=1.0, eps_target=1e-4, tol=1e-3, max_iters=5000), "one"),
     "w3_n1500_tol": (3, 1500, 1800, dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=5000), "mean"),
+    # the full 20000 x 20000 workload (a few hours of fp64 numpy on a few cores)
+    "w2_full_tol": (2, None, None, dict(eps_start=1.0, eps_target=1e-3, tol=1e-3, max_iters=5000), "one"),
 }
 
 

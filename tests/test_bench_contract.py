@@ -32,11 +32,21 @@ def test_ops_per_pair_counts_the_shifted_loop():
 
 
 def test_traffic_records_match_their_kernel_and_sources(tmp_path, monkeypatch):
-    # the committed records resolve for their own workload and kernel only
-    assert bench.pmc_traffic("k_lse_valu<3,true>", 2) is not None
-    assert bench.pmc_traffic("k_lse_mfma<52>", 3) is not None
-    assert bench.pmc_traffic("k_lse_valu<3,true>", 4) is None
-    assert bench.pmc_traffic("k_lse_valu<2,true>", 2) is None
+    # every committed record names its kernel and the digest of the sources it
+    # was taken with; it resolves only for that kernel and only while the
+    # sources still have that digest
+    import re
+
+    for w, (name, sources) in bench.PMC_RECORDS.items():
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+kernel_sources_sha256:\s*([0-9a-f]+)"
+                      r"\s+kernel:\s*(\S+)", text)
+        assert m, name
+        fresh = m.group(2) == bench.kernel_source_digest(sources)
+        got = bench.pmc_traffic(m.group(3), w)
+        assert got == (float(m.group(1)) if fresh else None)
+        assert bench.pmc_traffic(m.group(3) + "x", w) is None
+    assert bench.pmc_traffic("k_lse_valu<3,true>", 99) is None
     # a record whose digest no longer matches the sources is ignored
     prof = tmp_path / "profiles"
     prof.mkdir()
