@@ -178,6 +178,23 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sched, float* f
 int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, const float* g,
                               const int64_t* rows, int64_t k, float* T, float* row_max);
 
+/* sinkhorn_materialize_rows for callers that cannot allocate device memory
+ * during the call (code that must not call hipMalloc: tight serving loops
+ * over row batches, harnesses that forbid allocation). Same arguments,
+ * results and synchronization as sinkhorn_materialize_rows (the same kernels,
+ * so the same values bit for bit), but the call allocates nothing: its
+ * per-call buffers (row terms, row-maximum keys and, for d <= 8, fp64 column
+ * terms) live in one fixed array in the library's device memory, 16.8 MB per
+ * GPU, set up by sinkhorn_init and held until the process ends. Limits:
+ * k <= 4096 rows per call, and m <= 2^21 columns when d <= 8 (no limit on m
+ * for d > 8); beyond them the call returns SINKHORN_ERR_INVALID_ARG and does
+ * nothing. Every call on one GPU shares that array: calls that overlap in
+ * time on the same GPU (other host threads, other streams) race and give
+ * undefined results; calls one after the other are independent. */
+int sinkhorn_materialize_rows_noalloc(sinkhorn_problem* p, double eps, const float* f,
+                                      const float* g, const int64_t* rows, int64_t k, float* T,
+                                      float* row_max);
+
 /* min over rows with a_i > 0 of max_j T_ij (moscot #846, "Behavioural changes":
  * the largest threshold that keeps every row non-empty, exact and independent
  * of the batch; rows without mass take no part). Computed in row batches

@@ -147,6 +147,7 @@ _SIGS = {
     "sinkhorn_marginal_residual": ([_p, _f64, _p, _p, _p, _p], _i32),
     "sinkhorn_solve": ([_p, _p, _p, _p, _p], _i32),
     "sinkhorn_materialize_rows": ([_p, _f64, _p, _p, _p, _i64, _p, _p], _i32),
+    "sinkhorn_materialize_rows_noalloc": ([_p, _f64, _p, _p, _p, _i64, _p, _p], _i32),
     "sinkhorn_min_row": ([_p, _f64, _p, _p, _p], _i32),
     "sinkhorn_morton_order": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_block_screen": ([_p, _f64, _p, _p, _i32, _f64, _i32, _p, _p, _i64, _p], _i32),
@@ -428,6 +429,21 @@ class Problem:
             _dev(row_max, torch.float32, "row_max", (k,))
         _check(lib().sinkhorn_materialize_rows(self._h, float(eps), _ptr(f), _ptr(g), _ptr(rows), k,
                                                _ptr(T), _ptr(row_max)), "materialize_rows")
+        return T, row_max
+
+    def materialize_rows_noalloc(self, eps, f, g, rows, T, row_max=None):
+        """materialize_rows into caller buffers with no allocation in the call
+        (T [k, m] fp32 is required; k <= 4096, m <= 2^21 when d <= 8)."""
+        self._pot(f, self.n, "f")
+        self._pot(g, self.m, "g")
+        _dev(rows, torch.int64, "rows")
+        k = rows.shape[0]
+        _dev(T, torch.float32, "T", (k, self.m))
+        if row_max is not None:
+            _dev(row_max, torch.float32, "row_max", (k,))
+        _check(lib().sinkhorn_materialize_rows_noalloc(self._h, float(eps), _ptr(f), _ptr(g), _ptr(rows),
+                                                       k, _ptr(T), _ptr(row_max)),
+               "materialize_rows_noalloc")
         return T, row_max
 
     def min_row(self, eps, f, g) -> float:

@@ -347,8 +347,10 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       {
         int dev = 0;
         SK_HIP(hipGetDevice(&dev));
+        p->device = dev;
         SK_HIP(hipDeviceGetAttribute(&p->num_cu, hipDeviceAttributeMultiprocessorCount, dev));
         if (p->num_cu < 1) p->num_cu = 1;
+        static_scratch_setup(dev);
       }
       p->host_tmp = (double*)host_alloc(sizeof(double) * 8);
       side_init(p, p->X, x, a, n);

@@ -129,6 +129,7 @@ struct sinkhorn_problem {
   sk::Ctl* ctl = nullptr;       // device control block
   sk::Ctl* host_ctl = nullptr;  // pinned, host-coherent mirror (the residual kernel writes it)
   sk::Ctl* host_ctl_dev = nullptr;  // device address of host_ctl
+  int32_t device = 0;           // the HIP device the handle was created on
   int32_t num_cu = 0;           // compute units of the device
   double* host_tmp = nullptr;   // [8] pinned scratch
   // solve scratch: double-buffered potentials
@@ -244,6 +245,10 @@ void morton_sort(const float* x, const float* y, int64_t n, int64_t m, int32_t d
 void morton_sort_soa(const float* x, int64_t xpad, const float* y, int64_t ypad, int64_t n,
                      int64_t m, int32_t d, hipStream_t st, uint64_t* codes_x, int32_t* perm_x,
                      uint64_t* codes_y, int32_t* perm_y);
+
+// materialize.hip: records the device address of the static scratch of the
+// allocation-free materializer for `device` (the current device), once
+void static_scratch_setup(int device);
 
 double device_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m, int32_t d,
                             hipStream_t st);

@@ -14,6 +14,9 @@
 #include <cfloat>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
 
 #include <rocprim/device/device_scan.hpp>
 
@@ -398,6 +401,69 @@ __global__ void k_set_i64(int64_t* p, int64_t v) {
   if (threadIdx.x == 0) *p = v;
 }
 
+void materialize_checks(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                        const int64_t* rows, int64_t k, const float* T) {
+  if (!p || !f || !g || !rows || !T) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+  if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (k < 0) fail(SINKHORN_ERR_INVALID_ARG, "k must be >= 0");
+}
+
+// Rows rows[0..k) of the plan into T [k][m] (and their maxima into row_max
+// when non-null), with the per-call buffers P [k] and keys [k + 1] (device)
+// and, for d <= 8, Hd [m]; every value they hold is written here before it is
+// read. Checks the row indices first (one synchronization) and synchronizes
+// at the end.
+void materialize_into(sinkhorn_problem* p, double eps, const float* f, const float* g,
+                      const int64_t* rows, int64_t k, float* T, float* row_max, double* P,
+                      uint32_t* keys, double* Hd) {
+  hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(64), 0, p->stream, keys + k, 0u);
+  SK_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_check_rows, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream, rows, k,
+                     p->n, keys + k);
+  SK_LAUNCH_CHECK();
+  SK_HIP(hipMemcpyAsync(p->host_tmp, keys + k, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
+  SK_HIP(hipStreamSynchronize(p->stream));
+  uint32_t nbad;
+  memcpy(&nbad, p->host_tmp, sizeof(uint32_t));
+  if (nbad) fail(SINKHORN_ERR_INVALID_ARG, "row index outside [0, n)");
+  column_terms(p, eps, g, Hd);
+  rows_pass(p, eps, f, rows, 0, k, P, nullptr, keys, Hd, T);
+  if (row_max) {
+    hipLaunchKernelGGL(k_keys_to_max, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream, keys,
+                       k, row_max);
+    SK_LAUNCH_CHECK();
+  }
+  SK_HIP(hipStreamSynchronize(p->stream));
+}
+
+// ---- the allocation-free variant's device memory
+//
+// One array per GPU, in the code object's data, held until the process ends:
+// the row terms P, the fp64 column terms Hd and the row-maximum keys of one
+// call of sinkhorn_materialize_rows_noalloc. Host code never uses the
+// array's name as an address (on the host it only names the symbol): every
+// use goes through the device address hipGetSymbolAddress returned for the
+// GPU, recorded once per device.
+constexpr int64_t kStaticRows = 4096;              // rows per call, at most
+constexpr int64_t kStaticCols = int64_t(1) << 21;  // columns per call when d <= 8, at most
+constexpr int64_t kStaticOffP = 0;
+constexpr int64_t kStaticOffHd = kStaticOffP + kStaticRows * 8;
+constexpr int64_t kStaticOffKeys = kStaticOffHd + kStaticCols * 8;
+constexpr int64_t kStaticBytes = kStaticOffKeys + (kStaticRows + 64) * 4;
+
+__device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, unsigned char*> g_scratch;  // device -> address of its copy of scratch
+
+unsigned char* static_scratch(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(device);
+  if (it == g_scratch.end())
+    fail(SINKHORN_ERR_HIP, "static scratch of device " + std::to_string(device) + " not set up");
+  return it->second;
+}
+
 struct Scratch {
   double* P = nullptr;
   double* Hd = nullptr;
@@ -412,6 +478,20 @@ struct Scratch {
 };
 
 }  // namespace
+
+// The device address of the current device's copy of the static scratch,
+// looked up once per device; called by sinkhorn_init with the handle's device
+// current.
+void static_scratch_setup(int device) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch.count(device)) return;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  check_hip(e, "hipGetSymbolAddress(scratch)");
+  if (!ptr) fail(SINKHORN_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+  g_scratch[device] = static_cast<unsigned char*>(ptr);
+}
+
 }  // namespace sk
 
 using namespace sk;
@@ -421,32 +501,41 @@ extern "C" {
 int sinkhorn_materialize_rows(sinkhorn_problem* p, double eps, const float* f, const float* g,
                               const int64_t* rows, int64_t k, float* T, float* row_max) {
   try {
-    if (!p || !f || !g || !rows || !T) fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
-    if (!(std::isfinite(eps) && eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
-    if (k < 0) fail(SINKHORN_ERR_INVALID_ARG, "k must be >= 0");
+    materialize_checks(p, eps, f, g, rows, k, T);
     if (k == 0) return SINKHORN_OK;
     Scratch s;
     s.P = (double*)dev_alloc(sizeof(double) * k);
     s.keys = (uint32_t*)dev_alloc(sizeof(uint32_t) * (k + 1));
-    hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(64), 0, p->stream, s.keys + k, 0u);
-    SK_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_check_rows, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream,
-                       rows, k, p->n, s.keys + k);
-    SK_LAUNCH_CHECK();
-    SK_HIP(hipMemcpyAsync(p->host_tmp, s.keys + k, sizeof(uint32_t), hipMemcpyDeviceToHost, p->stream));
-    SK_HIP(hipStreamSynchronize(p->stream));
-    uint32_t nbad;
-    memcpy(&nbad, p->host_tmp, sizeof(uint32_t));
-    if (nbad) fail(SINKHORN_ERR_INVALID_ARG, "row index outside [0, n)");
     if (p->d <= kMaxValuD) s.Hd = (double*)dev_alloc(sizeof(double) * p->m);
-    column_terms(p, eps, g, s.Hd);
-    rows_pass(p, eps, f, rows, 0, k, s.P, nullptr, s.keys, s.Hd, T);
-    if (row_max) {
-      hipLaunchKernelGGL(k_keys_to_max, grid1(((k + 255) / 256), 256), dim3(256), 0, p->stream,
-                         s.keys, k, row_max);
-      SK_LAUNCH_CHECK();
-    }
-    SK_HIP(hipStreamSynchronize(p->stream));
+    materialize_into(p, eps, f, g, rows, k, T, row_max, s.P, s.keys, s.Hd);
+    return SINKHORN_OK;
+  } catch (const Failure& e) {
+    set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}
+
+int sinkhorn_materialize_rows_noalloc(sinkhorn_problem* p, double eps, const float* f,
+                                      const float* g, const int64_t* rows, int64_t k, float* T,
+                                      float* row_max) {
+  try {
+    materialize_checks(p, eps, f, g, rows, k, T);
+    if (k > kStaticRows)
+      fail(SINKHORN_ERR_INVALID_ARG, "materialize_rows_noalloc: k = " + std::to_string(k) +
+                                         " rows exceed its limit of " + std::to_string(kStaticRows));
+    if (p->d <= kMaxValuD && p->m > kStaticCols)
+      fail(SINKHORN_ERR_INVALID_ARG, "materialize_rows_noalloc: m = " + std::to_string(p->m) +
+                                         " columns exceed its limit of " +
+                                         std::to_string(kStaticCols) + " for d <= 8");
+    if (k == 0) return SINKHORN_OK;
+    unsigned char* base = static_scratch(p->device);
+    double* P = reinterpret_cast<double*>(base + kStaticOffP);
+    double* Hd = reinterpret_cast<double*>(base + kStaticOffHd);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(base + kStaticOffKeys);
+    materialize_into(p, eps, f, g, rows, k, T, row_max, P, keys, p->d <= kMaxValuD ? Hd : nullptr);
     return SINKHORN_OK;
   } catch (const Failure& e) {
     set_last_error(e.msg);
