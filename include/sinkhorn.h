@@ -79,7 +79,10 @@ typedef struct {
   int32_t check_every;
 } sinkhorn_schedule;
 
-/* Filled by sinkhorn_solve / sinkhorn_solve_multiscale (host struct). */
+/* Filled by sinkhorn_solve (host struct). history / history_cap are inputs:
+ * a host buffer (may be NULL with history_cap = 0) that receives the row
+ * residuals of the last history_cap checks at eps_target, oldest first;
+ * history_len returns how many checks there were (it may exceed the cap). */
 typedef struct {
   int64_t halfsteps;       /* dense or sparse potential updates launched */
   int64_t iters;           /* full iterations, all stages */
@@ -90,6 +93,12 @@ typedef struct {
   double seconds;          /* host wall time of the call */
   int32_t stages;          /* annealing stages run (eps_target not counted) */
   int32_t converged;       /* 1 if the stop test passed */
+  double* history;         /* in: host buffer for the residual history, or NULL */
+  int32_t history_cap;     /* in: its capacity in doubles (0 with NULL) */
+  int32_t history_len;     /* out: residual checks made at eps_target */
+  double seconds_per_halfstep;  /* out: seconds / halfsteps (host wall time) */
+  int64_t workspace_bytes;      /* out: device bytes the handle holds (its O((n + m) d) workspace) */
+  int64_t peak_extra_bytes;     /* out: most device memory the call held beyond the handle's */
 } sinkhorn_report;
 
 /* Human-readable name of a status code. Never NULL. */
@@ -114,10 +123,22 @@ int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m,
  * SINKHORN_ERR_NONFINITE if a coordinate or weight is NaN or infinite.
  * The handle (host pointer) is written to *out. In moscot #846 the row
  * materializer is built once and then called per batch of row indices, the
- * geometry resolved before the row loop; the handle plays that role. */
+ * geometry resolved before the row loop; the handle plays that role.
+ * flags: 0, or SINKHORN_FLAG_FP32_PAIRS (below); other bits are refused. */
 int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const float* a,
                   const float* b, int64_t n, int64_t m, int32_t d, double cost_scale,
-                  void* stream);
+                  uint32_t flags, void* stream);
+
+/* For d <= 3 the dense half-steps (and the dense solve's potentials between
+ * them) compute in fp64 up to the shifted exponent, whose exp2 is fp32
+ * (FlashSinkhorn 2, §A.1: the arithmetic's precision moves the potentials):
+ * with |potential| >> eps an fp32 column term, row shift or stored potential
+ * rounds each half-step by ~1e-5 eps in a way that depends on the iterate,
+ * and thousands of iterations at small eps integrate it (2e-2 eps after 2229
+ * iterations at eps = 1e-4). This flag selects the fp32 pair loop instead:
+ * about 1.4x faster on this chip, and within 1e-5 max(eps, |f|) per
+ * half-step, but its solves drift as described. d > 3 always runs fp32. */
+#define SINKHORN_FLAG_FP32_PAIRS 1u
 
 /* Release the handle and its workspace (synchronizes its stream). NULL is a no-op. */
 int sinkhorn_destroy(sinkhorn_problem* p);

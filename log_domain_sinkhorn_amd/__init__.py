@@ -81,6 +81,12 @@ class _ReportC(ctypes.Structure):
         ("seconds", _f64),
         ("stages", _i32),
         ("converged", _i32),
+        ("history", ctypes.POINTER(_f64)),
+        ("history_cap", _i32),
+        ("history_len", _i32),
+        ("seconds_per_halfstep", _f64),
+        ("workspace_bytes", _i64),
+        ("peak_extra_bytes", _i64),
     ]
 
 
@@ -138,7 +144,7 @@ _SIGS = {
     "sinkhorn_strerror": ([_i32], ctypes.c_char_p),
     "sinkhorn_last_error": ([], ctypes.c_char_p),
     "sinkhorn_mean_sqeuclid": ([_p, _p, _i64, _i64, _i32, _p, _p], _i32),
-    "sinkhorn_init": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f64, _p], _i32),
+    "sinkhorn_init": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f64, ctypes.c_uint32, _p], _i32),
     "sinkhorn_destroy": ([_p], _i32),
     "sinkhorn_problem_info": ([_p, _p, _p, _p, _p], _i32),
     "sinkhorn_device_memory": ([_p, _p, _p, _i32], _i32),
@@ -314,6 +320,9 @@ def morton_order(x: torch.Tensor, y: torch.Tensor):
     return cx, px, cy, py
 
 
+FLAG_FP32_PAIRS = 1
+
+
 def device_memory(reset: bool = False):
     """(current, peak, largest) device bytes the library holds, over all
     handles (``sinkhorn_device_memory``); reset=True then starts a new peak."""
@@ -326,7 +335,7 @@ def device_memory(reset: bool = False):
 class Problem:
     """A problem handle (``sinkhorn_init``) over device clouds x [n,d], y [m,d]."""
 
-    def __init__(self, x, y, a=None, b=None, cost_scale: float = 1.0):
+    def __init__(self, x, y, a=None, b=None, cost_scale: float = 1.0, flags: int = 0):
         _dev(x, torch.float32, "x")
         _dev(y, torch.float32, "y")
         if x.dim() != 2 or y.dim() != 2 or x.shape[1] != y.shape[1]:
@@ -339,9 +348,11 @@ class Problem:
             _dev(b, torch.float32, "b", (self.m,))
         self.device = x.device
         self.cost_scale = float(cost_scale)
+        self.flags = int(flags)
         h = ctypes.c_void_p()
         _check(lib().sinkhorn_init(ctypes.byref(h), _ptr(x), _ptr(y), _ptr(a), _ptr(b), self.n,
-                                   self.m, self.d, self.cost_scale, _stream(self.device)), "init")
+                                   self.m, self.d, self.cost_scale, self.flags, _stream(self.device)),
+               "init")
         self._h = h
 
     def close(self):
@@ -404,16 +415,21 @@ class Problem:
                                                 ctypes.byref(r), ctypes.byref(c)), "marginal_residual")
         return r.value, c.value
 
-    def solve(self, sched: Schedule, f=None, g=None):
+    def solve(self, sched: Schedule, f=None, g=None, history: int = 256):
         """Annealed dense solve. Returns (f, g, report dict); report['status']
-        is OK or NOT_CONVERGED."""
+        is OK or NOT_CONVERGED; report['history'] holds the row residuals of
+        the last `history` checks at eps_target."""
         f = torch.zeros(self.n, dtype=torch.float32, device=self.device) if f is None else self._pot(f, self.n, "f")
         g = torch.zeros(self.m, dtype=torch.float32, device=self.device) if g is None else self._pot(g, self.m, "g")
         sc = sched._c()
         rep = _ReportC()
+        buf = (_f64 * max(1, history))()
+        rep.history = ctypes.cast(buf, ctypes.POINTER(_f64))
+        rep.history_cap = int(history)
         st = _check(lib().sinkhorn_solve(self._h, ctypes.byref(sc), _ptr(f), _ptr(g), ctypes.byref(rep)),
                     "solve")
         out = _struct_dict(rep)
+        out["history"] = list(buf[:min(rep.history_len, history)])
         out["status"] = st
         return f, g, out
 

@@ -1,5 +1,6 @@
 // C ABI entry points: argument checks, handle life cycle, half-steps, the
 // exact residual and the annealed dense solve driver.
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -110,7 +111,10 @@ void problem_free(sinkhorn_problem* p) {
   for (int k = 0; k < 2; ++k) {
     dev_free(p->fbuf[k]);
     dev_free(p->gbuf[k]);
+    dev_free(p->fbuf64[k]);
+    dev_free(p->gbuf64[k]);
   }
+  dev_free(p->shift64);
   if (p->ev) (void)hipEventDestroy(p->ev);
   for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   delete p;
@@ -125,16 +129,30 @@ void halfstep(sinkhorn_problem* p, bool fside, double eps, const float* other, f
   require(out != other && (prev == nullptr || out != prev), "output aliases an input");
   Side& rows = fside ? p->X : p->Y;
   Side& cols = fside ? p->Y : p->X;
-  prep_column_term(p, cols, other, eps, cols.H);
-  reset_nonfinite(p);
-  HalfStep hs{&rows, &cols, cols.H, out, prev, nullptr, eps, eps, prev != nullptr && l1 != nullptr};
-  hs.shift_pot = prev;  // the previous potential estimates the row shifts
-  dense_halfstep(p, hs);
+  const bool residual = prev != nullptr && l1 != nullptr;
+  if (p->precise) {
+    prep_column_term64(p, cols, other, nullptr, eps, cols.H64);
+    reset_nonfinite(p);
+    const double* shift = nullptr;
+    if (prev) {  // the previous potential estimates the row shifts
+      widen_f32(prev, rows.count, p->shift64, p->stream);
+      shift = p->shift64;
+    }
+    HalfStep64 hs{&rows, &cols, cols.H64, out, nullptr, prev, nullptr, nullptr, eps, eps, residual,
+                  shift};
+    dense_halfstep64(p, hs);
+  } else {
+    prep_column_term(p, cols, other, eps, cols.H);
+    reset_nonfinite(p);
+    HalfStep hs{&rows, &cols, cols.H, out, prev, nullptr, eps, eps, residual};
+    hs.shift_pot = prev;  // the previous potential estimates the row shifts
+    dense_halfstep(p, hs);
+  }
   if (l1) {
     double v = 0.0;
     int32_t bad = 0;
     read_reduction(p, &v, &bad);
-    *l1 = hs.residual ? v : NAN;
+    *l1 = residual ? v : NAN;
     if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential in half-step");
   }
 }
@@ -160,21 +178,66 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
   const auto t0 = std::chrono::steady_clock::now();
   hipStream_t st = p->stream;
   const double pairs = (double)X.count * (double)Y.count;
-  copy_f32(f, X.count, F[0], st);
-  copy_f32(g, Y.count, G[0], st);
+  // the handle's own clouds on the fp64 path iterate with fp64 potentials,
+  // column terms and pair arithmetic (dense64.hip); other sides (the
+  // multiscale cells) in fp32
+  const bool precise = p->precise && &X == &p->X && &Y == &p->Y;
+  double* F64[2] = {p->fbuf64[0], p->fbuf64[1]};
+  double* G64[2] = {p->gbuf64[0], p->gbuf64[1]};
+  if (precise) {
+    widen_f32(f, X.count, F64[0], st);
+    widen_f32(g, Y.count, G64[0], st);
+  } else {
+    copy_f32(f, X.count, F[0], st);
+    copy_f32(g, Y.count, G[0], st);
+  }
   reset_nonfinite(p);
   int cur = 0;
   SolveOut o;
 
+  // f-step from state `from` into state 1 - from (fused residual of state
+  // `from` when `residual`; with `hnext`, the next column term of X for eps)
+  auto fstep = [&](int from, double eps, bool residual, bool hnext) {
+    if (precise) {
+      HalfStep64 hs{&X, &Y, Y.H64, nullptr, F64[1 - from], nullptr, F64[from],
+                    hnext ? X.H64 : nullptr, eps, eps, residual, F64[from]};
+      dense_halfstep64(p, hs);
+    } else {
+      HalfStep hs{&X, &Y, Y.H, F[1 - from], F[from], hnext ? X.H : nullptr, eps, eps, residual};
+      hs.shift_pot = F[from];
+      dense_halfstep(p, hs);
+    }
+  };
+  // g-step from state `from` (the next column term of Y for eps_next)
+  auto gstep = [&](int from, double eps, double eps_next, bool residual, bool hnext) {
+    if (precise) {
+      HalfStep64 hs{&Y, &X, X.H64, nullptr, G64[1 - from], nullptr, G64[from],
+                    hnext ? Y.H64 : nullptr, eps, eps_next, residual, G64[from]};
+      dense_halfstep64(p, hs);
+    } else {
+      HalfStep hs{&Y, &X, X.H, G[1 - from], G[from], hnext ? Y.H : nullptr, eps, eps_next, residual};
+      hs.shift_pot = G[from];
+      dense_halfstep(p, hs);
+    }
+  };
+  auto yterm = [&](int state, double eps) {
+    if (precise)
+      prep_column_term64(p, Y, nullptr, G64[state], eps, Y.H64);
+    else
+      prep_column_term(p, Y, G[state], eps, Y.H);
+  };
+  auto xterm = [&](int state, double eps) {
+    if (precise)
+      prep_column_term64(p, X, nullptr, F64[state], eps, X.H64);
+    else
+      prep_column_term(p, X, F[state], eps, X.H);
+  };
+
   // one full iteration from state `cur`; eps_next is the eps of the f-step that follows
   auto iterate = [&](double eps, double eps_next, bool residual) {
-    HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], X.H, eps, eps, residual};
-    fs.shift_pot = F[cur];
-    dense_halfstep(p, fs);
+    fstep(cur, eps, residual, true);
     if (residual) SK_HIP(hipEventRecord(p->ev, st));  // the reduction wrote host_ctl
-    HalfStep gs{&Y, &X, X.H, G[1 - cur], G[cur], Y.H, eps, eps_next, false};
-    gs.shift_pot = G[cur];
-    dense_halfstep(p, gs);
+    gstep(cur, eps, eps_next, false, true);
     o.halfsteps += 2;
     cur = 1 - cur;
   };
@@ -186,7 +249,7 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
     const double nxt = eps * s.eps_factor;
     const double eps_after = nxt > s.eps_target ? nxt : s.eps_target;
     if (s.iters_per_stage > 0) {
-      if (first) prep_column_term(p, Y, G[cur], eps, Y.H);
+      if (first) yterm(cur, eps);
       first = false;
       for (int32_t k = 0; k < s.iters_per_stage; ++k) {
         const bool last = k + 1 == s.iters_per_stage;
@@ -200,7 +263,7 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
     eps = nxt;
   }
   eps = s.eps_target;
-  if (first) prep_column_term(p, Y, G[cur], eps, Y.H);
+  if (first) yterm(cur, eps);
 
   int ret = cur;
   if (s.fixed_iters > 0) {
@@ -213,21 +276,20 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
     o.converged = 1;
   } else {
     const int32_t every = s.check_every > 1 ? s.check_every : 1;
-    std::vector<double> hist;
     // iteration k checks the state left by iteration k-1
     for (int64_t k = 1;; ++k) {
       const int64_t prev_done = k - 1;
       const bool check = prev_done >= 1 && prev_done % every == 0;
       if (prev_done >= s.max_iters) {
         // only the residual of the final state is still needed
-        HalfStep fs{&X, &Y, Y.H, F[1 - cur], F[cur], nullptr, eps, eps, true};
-        dense_halfstep(p, fs);
+        fstep(cur, eps, true, false);
         ++o.halfsteps;
         double v;
         int32_t bad;
         read_reduction(p, &v, &bad);
         if (bad) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
         o.row_l1 = v;
+        o.history.push_back(v);
         ret = cur;
         o.converged = v <= s.tol ? 1 : 0;
         o.seconds = seconds_since(t0);
@@ -239,6 +301,7 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
         SK_HIP(hipEventSynchronize(p->ev));
         if (p->host_ctl->nonfinite) fail(SINKHORN_ERR_NONFINITE, "non-finite potential during solve");
         const double v = p->host_ctl->residual;
+        std::vector<double>& hist = o.history;
         hist.push_back(v);
         if (hist.size() % 100 == 0)
           progress("solve: %d iterations at eps %.4g, row residual %.4g (%.3f s)", (int)o.iters, eps,
@@ -262,25 +325,28 @@ SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, 
   // residuals of the returned state (the row side is known in the tol mode)
   {
     if (std::isnan(o.row_l1)) {
-      prep_column_term(p, Y, G[ret], eps, Y.H);
+      yterm(ret, eps);
       reset_nonfinite(p);
-      HalfStep fs{&X, &Y, Y.H, F[1 - ret], F[ret], nullptr, eps, eps, true};
-      dense_halfstep(p, fs);
+      fstep(ret, eps, true, false);
       read_reduction(p, &o.row_l1, nullptr);
       ++o.halfsteps;
     }
-    prep_column_term(p, X, F[ret], eps, X.H);
+    xterm(ret, eps);
     reset_nonfinite(p);
-    HalfStep gs{&Y, &X, X.H, G[1 - ret], G[ret], nullptr, eps, eps, true};
-    dense_halfstep(p, gs);
+    gstep(ret, eps, eps, true, false);
     read_reduction(p, &o.col_l1, nullptr);
     ++o.halfsteps;
   }
   if (o.seconds == 0.0) o.seconds = seconds_since(t0);
   progress("solve: %d iterations at eps %.4g, row residual %.4g, column residual %.4g (%.3f s)",
            (int)o.iters, eps, o.row_l1, o.col_l1, o.seconds);
-  copy_f32(F[ret], X.count, f, st);
-  copy_f32(G[ret], Y.count, g, st);
+  if (precise) {
+    narrow_f64(F64[ret], X.count, f, st);
+    narrow_f64(G64[ret], Y.count, g, st);
+  } else {
+    copy_f32(F[ret], X.count, f, st);
+    copy_f32(G[ret], Y.count, g, st);
+  }
   SK_HIP(hipStreamSynchronize(st));
   o.pairs = pairs * (double)o.halfsteps;
   return o;
@@ -326,7 +392,7 @@ int sinkhorn_mean_sqeuclid(const float* x, const float* y, int64_t n, int64_t m,
 
 int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const float* a,
                   const float* b, int64_t n, int64_t m, int32_t d, double cost_scale,
-                  void* stream) {
+                  uint32_t flags, void* stream) {
   return guard([&] {
     require(out != nullptr, "null output handle");
     *out = nullptr;
@@ -334,12 +400,16 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
     require(n >= 1 && m >= 1, "n and m must be >= 1");
     require(d >= 1 && d <= kMaxMfmaD, "d must be in [1, 63]");
     require(std::isfinite(cost_scale) && cost_scale > 0.0, "cost_scale must be finite and > 0");
+    require((flags & ~(uint32_t)SINKHORN_FLAG_FP32_PAIRS) == 0, "unknown flags");
+    const int64_t bytes0 = thread_alloc_current();
     sinkhorn_problem* p = new sinkhorn_problem();
     try {
       p->n = n;
       p->m = m;
       p->d = d;
       p->scale = cost_scale;
+      p->flags = flags;
+      p->precise = d <= 3 && !(flags & SINKHORN_FLAG_FP32_PAIRS);
       p->stream = (hipStream_t)stream;
       p->ctl = (Ctl*)dev_alloc(sizeof(Ctl));
       p->host_ctl = (Ctl*)host_alloc_coherent(sizeof(Ctl));
@@ -353,8 +423,8 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
         static_scratch_setup(dev);
       }
       p->host_tmp = (double*)host_alloc(sizeof(double) * 8);
-      side_init(p, p->X, x, a, n);
-      side_init(p, p->Y, y, b, m);
+      side_init(p, p->X, x, a, n, p->precise);
+      side_init(p, p->Y, y, b, m, p->precise);
       const double sa = p->X.wsum, sb = p->Y.wsum;
       if (std::fabs(sa - sb) > 1e-5 * std::fmax(sa, sb))
         fail(SINKHORN_ERR_MASS, "sum(a) = " + std::to_string(sa) + " differs from sum(b) = " +
@@ -362,6 +432,9 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       if (d > kMaxValuD) setup_mfma(p, x, y);
       p->part_cap = std::max(partial_floats_needed(p, n, p->X.padded, m),
                              partial_floats_needed(p, m, p->Y.padded, n));
+      if (p->precise)
+        p->part_cap = std::max(p->part_cap, std::max(dense64_partial_floats(p, n, m),
+                                                     dense64_partial_floats(p, m, n)));
       p->Mpart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->Spart = (float*)dev_alloc(sizeof(float) * p->part_cap);
       p->red_cap = std::max(row_groups(n), row_groups(m)) + 16;
@@ -372,9 +445,15 @@ int sinkhorn_init(sinkhorn_problem** out, const float* x, const float* y, const 
       for (int k = 0; k < 2; ++k) {
         p->fbuf[k] = (float*)dev_alloc(sizeof(float) * n);
         p->gbuf[k] = (float*)dev_alloc(sizeof(float) * m);
+        if (p->precise) {
+          p->fbuf64[k] = (double*)dev_alloc(sizeof(double) * n);
+          p->gbuf64[k] = (double*)dev_alloc(sizeof(double) * m);
+        }
       }
+      if (p->precise) p->shift64 = (double*)dev_alloc(sizeof(double) * std::max(n, m));
       SK_HIP(hipEventCreateWithFlags(&p->ev, hipEventDisableTiming));
       SK_HIP(hipStreamSynchronize(p->stream));
+      p->workspace_bytes = thread_alloc_current() - bytes0;
     } catch (...) {
       problem_free(p);
       throw;
@@ -449,6 +528,10 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
     require(p && sc && f && g, "null pointer");
     float* F[2] = {p->fbuf[0], p->fbuf[1]};
     float* G[2] = {p->gbuf[0], p->gbuf[1]};
+    if (rep) require(rep->history_cap >= 0 && (rep->history_cap == 0 || rep->history),
+                     "report history buffer");
+    const int64_t base = thread_alloc_current();
+    thread_alloc_mark();
     const SolveOut o = dense_solve(p, p->X, p->Y, f, g, F, G, *sc, 0, 0.0);
     if (rep) {
       rep->halfsteps = o.halfsteps;
@@ -460,6 +543,13 @@ int sinkhorn_solve(sinkhorn_problem* p, const sinkhorn_schedule* sc, float* f, f
       rep->seconds = o.seconds;
       rep->stages = o.stages;
       rep->converged = o.converged;
+      rep->seconds_per_halfstep = o.halfsteps > 0 ? o.seconds / (double)o.halfsteps : 0.0;
+      rep->workspace_bytes = p->workspace_bytes;
+      rep->peak_extra_bytes = thread_alloc_peak() - base;
+      const int64_t len = (int64_t)o.history.size();
+      rep->history_len = (int32_t)len;
+      const int64_t keep = std::min<int64_t>(len, rep->history_cap);
+      for (int64_t k = 0; k < keep; ++k) rep->history[k] = o.history[len - keep + k];
     }
     return o.status;
   });

@@ -62,6 +62,12 @@ inline int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
 // ---------------------------------------------------------------- device memory
 void* dev_alloc(size_t bytes);
 void dev_free(void* p);
+// device bytes allocated minus freed by the calling host thread, and the
+// largest value that count reached since thread_alloc_mark() (which starts
+// a new interval at the current count)
+int64_t thread_alloc_current();
+void thread_alloc_mark();
+int64_t thread_alloc_peak();
 void* host_alloc(size_t bytes);  // pinned
 void* host_alloc_coherent(size_t bytes);  // pinned, mapped, coherent with device writes
 void host_free(void* p);
@@ -75,6 +81,8 @@ struct Side {
   float* norm2 = nullptr;  // [padded] ||centred point||^2 (MFMA path)
   float* w = nullptr;      // [count] weights
   float* H = nullptr;      // [padded] column term of this side, -inf padding
+  double* soa64 = nullptr; // [d][padded] coordinates widened to fp64 (fp64 half-steps, d <= 3)
+  double* H64 = nullptr;   // [padded] fp64 column term, -inf padding (fp64 half-steps)
   double wsum = 0.0;
 };
 
@@ -99,6 +107,25 @@ struct HalfStep {
   // previous potential of the row side: enables the shifted pair loop (its
   // fixed per-row shift is estimated from it); null runs the exact loop
   const float* shift_pot = nullptr;
+};
+
+// One dense half-step with fp64 potentials, column terms and pair
+// arithmetic (dense64.hip, d <= 3).
+struct HalfStep64 {
+  const Side* rows;
+  const Side* cols;
+  const double* Hcols;      // fp64 column term (log2 units) of the column side
+  float* out32;             // new potential of the row side, fp32 (nullable)
+  double* out64;            // the same in fp64 (nullable)
+  const float* prev32;      // previous potential for the residual (nullable) ...
+  const double* prev64;     // ... or this one (nullable)
+  double* Hnext;            // nullable: fp64 column term of the row side for the next step
+  double eps;               // eps of this half-step
+  double eps_next;          // eps used for Hnext
+  bool residual;
+  // previous potential of the row side (fp64): sets each row's shift; null
+  // runs the exact two-pass form
+  const double* shift_pot;
 };
 
 }  // namespace sk
@@ -135,6 +162,14 @@ struct sinkhorn_problem {
   // solve scratch: double-buffered potentials
   float* fbuf[2] = {nullptr, nullptr};
   float* gbuf[2] = {nullptr, nullptr};
+  // fp64 dense path (d <= 3 unless SINKHORN_FLAG_FP32_PAIRS): the solve's
+  // fp64 potentials and a row-shift scratch
+  bool precise = false;
+  uint32_t flags = 0;
+  double* fbuf64[2] = {nullptr, nullptr};
+  double* gbuf64[2] = {nullptr, nullptr};
+  double* shift64 = nullptr;  // [max(n, m)]
+  int64_t workspace_bytes = 0;  // device bytes the handle holds
   hipEvent_t ev = nullptr;
   // measurement hook: event pairs around pair-loop kernel launches
   int32_t prof = 0;                 // SINKHORN_PROF_* kinds being timed
@@ -147,6 +182,9 @@ namespace sk {
 
 // setup.hip helpers
 void zero_i32(int32_t* v, int32_t count, hipStream_t st);
+void fill_f64(double* v, int64_t count, double value, hipStream_t st);
+void widen_f32(const float* src, int64_t count, double* dst, hipStream_t st);
+void narrow_f64(const double* src, int64_t count, float* dst, hipStream_t st);
 void fill_f32(float* v, int64_t count, float value, hipStream_t st);
 void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st);
 
@@ -176,6 +214,11 @@ int64_t partial_floats_needed(sinkhorn_problem* p, int64_t nrows, int64_t rows_p
 void prep_column_term(sinkhorn_problem* p, const Side& side, const float* pot, double eps,
                       float* H);
 void dense_halfstep(sinkhorn_problem* p, const HalfStep& hs);
+// dense64.hip
+void dense_halfstep64(sinkhorn_problem* p, const HalfStep64& hs);
+void prep_column_term64(sinkhorn_problem* p, const Side& side, const float* pot32,
+                        const double* pot64, double eps, double* H);
+int64_t dense64_partial_floats(sinkhorn_problem* p, int64_t nrows, int64_t ncols);
 // enqueue the copy of the control block to its pinned mirror
 void copy_ctl(sinkhorn_problem* p);
 // returns (residual sum, nonfinite count) after a synchronizing read
@@ -185,7 +228,9 @@ void reset_nonfinite(sinkhorn_problem* p);
 int64_t row_groups(int64_t rows);
 
 // setup.hip
-void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count);
+// with64: also the fp64 coordinates and column term of the fp64 half-steps
+void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count,
+               bool with64);
 void side_free(Side& s);
 // per-dimension (sum, sum of squares) of a device cloud [count][d] -> host [d][2]
 void moments(const float* pts, int64_t count, int32_t d, hipStream_t st, double* host_out);
@@ -234,6 +279,7 @@ struct SolveOut {
   int32_t stages = 0, converged = 0;
   bool stalled = false;
   int status = SINKHORN_OK;
+  std::vector<double> history;  // row residual at every check at eps_target
 };
 SolveOut dense_solve(sinkhorn_problem* p, Side& X, Side& Y, float* f, float* g, float* F[2],
                      float* G[2], const sinkhorn_schedule& s, int32_t stall_window,

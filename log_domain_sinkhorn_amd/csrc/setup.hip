@@ -25,6 +25,23 @@ __global__ __launch_bounds__(256) void k_fill(float* __restrict__ v, int64_t cou
   if (i < count) v[i] = value;
 }
 
+__global__ __launch_bounds__(256) void k_fill64(double* __restrict__ v, int64_t count, double value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) v[i] = value;
+}
+
+__global__ __launch_bounds__(256) void k_widen(const float* __restrict__ src, int64_t count,
+                                               double* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) dst[i] = (double)src[i];
+}
+
+__global__ __launch_bounds__(256) void k_narrow(const double* __restrict__ src, int64_t count,
+                                                float* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) dst[i] = (float)src[i];
+}
+
 __global__ __launch_bounds__(256) void k_copy(const float* __restrict__ src, int64_t count,
                                               float* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -154,7 +171,12 @@ namespace {
 std::mutex g_mem_mu;
 std::unordered_map<void*, size_t> g_mem_size;
 int64_t g_mem_current = 0, g_mem_peak = 0, g_mem_largest = 0;
+thread_local int64_t t_current = 0, t_peak = 0;
 }  // namespace
+
+int64_t thread_alloc_current() { return t_current; }
+void thread_alloc_mark() { t_peak = t_current; }
+int64_t thread_alloc_peak() { return t_peak; }
 
 void* dev_alloc(size_t bytes) {
   void* p = nullptr;
@@ -170,6 +192,8 @@ void* dev_alloc(size_t bytes) {
   g_mem_current += (int64_t)bytes;
   g_mem_peak = std::max(g_mem_peak, g_mem_current);
   g_mem_largest = std::max(g_mem_largest, (int64_t)bytes);
+  t_current += (int64_t)bytes;
+  t_peak = std::max(t_peak, t_current);
   return p;
 }
 
@@ -180,6 +204,7 @@ void dev_free(void* p) {
     auto it = g_mem_size.find(p);
     if (it != g_mem_size.end()) {
       g_mem_current -= (int64_t)it->second;
+      t_current -= (int64_t)it->second;
       g_mem_size.erase(it);
     }
   }
@@ -238,7 +263,26 @@ void copy_f32(const float* src, int64_t count, float* dst, hipStream_t st) {
   SK_LAUNCH_CHECK();
 }
 
-void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count) {
+void fill_f64(double* v, int64_t count, double value, hipStream_t st) {
+  if (count <= 0) return;
+  hipLaunchKernelGGL(k_fill64, grid1((count + 255) / 256, 256), dim3(256), 0, st, v, count, value);
+  SK_LAUNCH_CHECK();
+}
+
+void widen_f32(const float* src, int64_t count, double* dst, hipStream_t st) {
+  if (count <= 0) return;
+  hipLaunchKernelGGL(k_widen, grid1((count + 255) / 256, 256), dim3(256), 0, st, src, count, dst);
+  SK_LAUNCH_CHECK();
+}
+
+void narrow_f64(const double* src, int64_t count, float* dst, hipStream_t st) {
+  if (count <= 0) return;
+  hipLaunchKernelGGL(k_narrow, grid1((count + 255) / 256, 256), dim3(256), 0, st, src, count, dst);
+  SK_LAUNCH_CHECK();
+}
+
+void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, int64_t count,
+               bool with64) {
   const int32_t d = p->d;
   hipStream_t st = p->stream;
   s.count = count;
@@ -255,6 +299,12 @@ void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, i
     hipLaunchKernelGGL(k_to_soa, dim3(blocks_for(s.padded)), dim3(256), 0, st, pts, count, d,
                        s.padded, s.soa);
     SK_LAUNCH_CHECK();
+    if (with64) {  // the fp64 half-steps read widened coordinates and an fp64 column term
+      s.soa64 = (double*)dev_alloc(sizeof(double) * (size_t)d * s.padded);
+      widen_f32(s.soa, (int64_t)d * s.padded, s.soa64, st);
+      s.H64 = (double*)dev_alloc(sizeof(double) * s.padded);
+      fill_f64(s.H64, s.padded, -INFINITY, st);
+    }
   }
   // weight sum and finiteness of coordinates and weights
   const uint32_t nb = blocks_for(count);
@@ -281,6 +331,8 @@ void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, i
 
 void side_free(Side& s) {
   dev_free(s.soa);
+  dev_free(s.soa64);
+  dev_free(s.H64);
   dev_free(s.rowmaj);
   dev_free(s.norm2);
   dev_free(s.w);

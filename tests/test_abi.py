@@ -50,13 +50,16 @@ def test_invalid_arguments_are_rejected_before_any_device_work():
     L = sk.lib()
     h = ctypes.c_void_p()
     # null coordinates, bad sizes, bad scale: rejected on the host
-    assert L.sinkhorn_init(ctypes.byref(h), None, None, None, None, 10, 10, 3, 1.0, None) == sk.ERR_INVALID_ARG
+    assert L.sinkhorn_init(ctypes.byref(h), None, None, None, None, 10, 10, 3, 1.0, 0, None) == sk.ERR_INVALID_ARG
     fake = ctypes.c_void_p(16)
-    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 0, 10, 3, 1.0, None) == sk.ERR_INVALID_ARG
-    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 0, 1.0, None) == sk.ERR_INVALID_ARG
-    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 3, float("nan"), None) == sk.ERR_INVALID_ARG
-    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 3, -1.0, None) == sk.ERR_INVALID_ARG
+    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 0, 10, 3, 1.0, 0, None) == sk.ERR_INVALID_ARG
+    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 0, 1.0, 0, None) == sk.ERR_INVALID_ARG
+    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 3, float("nan"), 0, None) == sk.ERR_INVALID_ARG
+    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 3, -1.0, 0, None) == sk.ERR_INVALID_ARG
     assert b"cost_scale" in L.sinkhorn_last_error()
+    # unknown flag bits
+    assert L.sinkhorn_init(ctypes.byref(h), fake, fake, None, None, 10, 10, 3, 1.0, 2, None) == sk.ERR_INVALID_ARG
+    assert b"flags" in L.sinkhorn_last_error()
     # null handle
     assert L.sinkhorn_halfstep_f(None, 0.1, fake, fake, None, None) == sk.ERR_INVALID_ARG
     assert L.sinkhorn_solve(None, None, None, None, None) == sk.ERR_INVALID_ARG
