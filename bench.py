@@ -1,25 +1,40 @@
 #!/usr/bin/env python3
 """Throughput of the online log-domain Sinkhorn hot path on one MI355X.
 
-Default workload (the one the headline metric is quoted on): n = m = 20000
-points in d = 3, each cloud an 8-component Gaussian mixture (sigma 0.05),
-Dirichlet(1) weights, squared-Euclidean cost (scale 1), eps annealed from 1.0
-by halving (10 full iterations per stage) down to 1e-3, then iterated at 1e-3
-until the L1 marginal residual is <= 1e-3.
+Default workload: the largest one, n = m = 2^24 points in d = 3 (64-component
+Gaussian mixtures), solved block-sparse and multiscale: Morton order, cells,
+annealed coarse solve on the cells, lift, then fine updates on block pairs
+screened with block potential maxima, at eps = 1e-4, to the certified L1
+marginal residual 1e-2. Other workloads with --workload W (1-4: the dense
+online half-step; 3: d = 50 on the fp32 MFMA cross term).
 
-One step = one full solve from zero potentials: every f- and g-half-step
-(online tiled log-sum-exp on the GPU), the fused residual checks and the
-schedule. Inputs are resident in HBM before the timed region.
+What is timed (inputs resident in HBM, handle initialised):
+  * wall_time_to_residual_s: one whole solve from zero potentials to its stop
+    test (W = 5: the certificate; W = 1..4: the schedule's residual test);
+  * the K timed steps (after W untimed ones), bracketed by synchronizations:
+      W = 1, 2, 3: one whole solve per step (3: then every plan row
+                   materialized in batches of 1024 and min_row);
+      W = 4:       one full iteration (f- then g-half-step) at eps = 1e-4,
+                   continuing from the solved potentials;
+      W = 5:       one fine update (both tile lists screened, sparse f- and
+                   g-half-step, admitted residual), continuing from the
+                   certified potentials (warm-started multiscale calls).
+  value = n * m * (half-steps in the timed steps) / elapsed: the metric's
+  n*m/t per half-step. For W = 5 this counts every half-step as n*m pairs
+  (what a dense half-step would evaluate); the pairs the sparse half-steps
+  actually visited are reported beside it.
 
-Prints ONE JSON line:
-  value      = point pairs evaluated by all half-steps / wall time (pair-evals/s)
-  roofline   = the pair-loop kernel against the VALU issue rate of the chip,
-               timed by HIP events that each launch's dispatch records at the
-               kernel's start and end, in a second run of the same K solves
-               (the headline run has no events at all)
-  cpu_baseline = the fp64 oracle's half-step on the host cores (bounded sample)
+Prints ONE JSON line, with
+  roofline     = the dominant kernel against the chip's peak for its
+                 instruction mix, from unit counts and clock (256 CUs,
+                 2.4 GHz; fp32 vector 157.3 TFLOP/s = 128 FMA lanes per CU per
+                 clock, fp64 vector 78.6 = 64; fp32 MFMA 157.3; HBM 8 TB/s),
+                 its kernel time taken by HIP events that each launch's own
+                 dispatch records at the kernel's start and end;
+  issue_ceiling = the same mix measured by the library's probe kernels;
+  cpu_baseline = the fp64 oracle's half-step on the host cores (bounded sample).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 """
 import argparse
 import json
@@ -30,16 +45,18 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# chip constants (MI355X): 256 CUs, 64 lanes of fp32 VALU issue per CU per clock
+# MI355X: 256 CUs at 2.4 GHz. fp32 vector 157.3 TFLOP/s = 256 * 2.4e9 * 128
+# lanes * 2 (FMA); fp64 vector 78.6 TFLOP/s: 64 lanes. Nothing here uses
+# packed fp32 instructions: the 128 fp32 lanes per clock are issue slots of
+# ordinary VALU instructions, which this part fills beyond 64 per clock when
+# the instruction mix allows (the probe kernels reach 5.5e13/s).
 CUS = 256
 CLOCK_HZ = 2.4e9
-VALU_LANES_PER_CU = 64
-VALU_PEAK_OPS = CUS * VALU_LANES_PER_CU * CLOCK_HZ  # 3.93e13 lane-ops/s (no packed fp32)
+FP32_VALU_PEAK = CUS * 128 * CLOCK_HZ  # 7.86e13 fp32 lane-instructions/s
+FP64_VALU_PEAK = CUS * 64 * CLOCK_HZ   # 3.93e13 fp64 lane-instructions/s
 MFMA_F32_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
 HBM_PEAK = 8.0e12  # bytes/s
 
-# steps / warmup: defaults per workload (a full solve of 4 or 5 takes minutes).
-# roofline: how the second, event-timed region runs (None: the same steps).
 WORKLOADS = {
     1: dict(sched=dict(eps_start=0.01, eps_target=0.01, fixed_iters=200), steps=5, warmup=1,
             desc="w1: n=m=1000 d=2, x~U[0,1]^2, y~N(0.5,0.1^2), uniform weights, eps=0.01, 200 iterations"),
@@ -53,11 +70,10 @@ WORKLOADS = {
                  "cost / mean cost, eps=0.05 to L1 residual 1e-3, then every plan row materialized in batches "
                  "of 1024 and min_i max_j T_ij"),
     4: dict(sched=dict(eps_start=1.0, eps_target=1e-4, eps_factor=0.5, iters_per_stage=10,
-                       tol=1e-3, max_iters=20000), steps=1, warmup=0,
-            roofline=dict(eps_start=1e-4, eps_target=1e-4, fixed_iters=5),
+                       tol=1e-3, max_iters=20000), steps=20, warmup=5, continuation=True,
             desc="w4: n=m=1e6 d=3, x~U[0,1]^3, y=jittered 100^3 grid, uniform weights, "
                  "eps 1->1e-4 halving x10/stage, then to L1 residual 1e-3"),
-    5: dict(multiscale=dict(B=128, eps=1e-4, tol=1e-2), steps=1, warmup=0, roofline=dict(max_fine=3),
+    5: dict(multiscale=dict(B=128, eps=1e-4, tol=1e-2), steps=20, warmup=5,
             desc="w5: n=m=2^24 d=3, 64-component GMM in [0,1]^3 (sigma U[0.01,0.05]), y = shifted means, "
                  "uniform weights; Morton order, B=128 blocks, cells <= 2x blocks, coarse annealed centroid "
                  "solve + lift, fine loop on block pairs screened with block potential maxima "
@@ -66,15 +82,26 @@ WORKLOADS = {
 
 
 def ops_per_pair(d: int) -> int:
-    """Vector-ALU instructions per pair that the difference-form half-step
-    needs with a fixed per-row shift: d subs and d fmas for the shifted squared
-    distance (the shift folded into the first fma), 1 fma for the exponent and
-    1 add into the sum. The exp2 of each pair issues on the transcendental unit
-    alongside and is not counted against the VALU issue rate."""
+    """fp32 VALU instructions per pair of the shifted pair loop: d subs and d
+    fmas for the shifted squared distance (the shift folded into the first
+    fma), 1 fma for the exponent and 1 add into the sum. The exp2 issues on
+    the transcendental unit alongside (its own rate is ~4x lower than the
+    VALU's, and the loop needs one per 8 VALU instructions)."""
     return 2 * d + 2
 
 
+def slots_per_pair(d: int, fp64: bool) -> int:
+    """fp32 issue slots per pair: the fp32 loop's ops_per_pair, or for the
+    fp64 loop its 2d + 2 fp64-class instructions (d adds, d fmas, 1 exponent
+    fma, 1 conversion; two slots each at half the fp32 lane rate) plus the
+    fp32 add."""
+    return 2 * (2 * d + 2) + 1 if fp64 else ops_per_pair(d)
+
+
 KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h", "launch_plan.h")
+KERNEL_SOURCES_64 = ("dense64.hip", "pairloop64.h", "pairloop.h", "rowfinal.h", "internal.h",
+                     "launch_plan.h")
+SPARSE_SOURCES = ("blocks.hip", "pairloop.h", "rowfinal.h", "internal.h", "launch_plan.h")
 
 # HBM traffic of a workload's dominant kernel: the committed rocprofv3 PMC
 # summary and the sources that kernel is built from (the figure is used only
@@ -153,6 +180,26 @@ def cpu_baseline(c, eps, scale=1.0, budget_s=12.0):
     }
 
 
+PROBES = ("FMA_F32", "SUB_F32", "FMAC_F32", "EXP_F32", "PAIR_F32", "PAIR_F32_NOEXP", "FMA_F64",
+          "ADD_F64", "CVT_F32_F64", "PAIR_F64")
+
+
+def issue_rates(kinds=PROBES, iters=200000):
+    """Measured issue rates of the probe kernels (lane-instructions/s of the
+    counted class, pairs/s for the pair probes), the best of three runs each."""
+    import log_domain_sinkhorn_amd as sk
+
+    out = {}
+    for name in kinds:
+        kind = getattr(sk, "PROBE_" + name)
+        it = iters if "PAIR" not in name else iters // 8
+        best = max((sk.probe_issue_rate(kind, it) for _ in range(3)), key=lambda r: r[0])
+        peak = FP64_VALU_PEAK if name.endswith("F64") and "PAIR" not in name else FP32_VALU_PEAK
+        out[name] = {"lane_instr_per_s": best[0], "pairs_per_s": best[1] or None, "kernel_ms": best[2],
+                     "frac_of_lane_peak": best[0] / peak}
+    return out
+
+
 def copy_calibration(mib: int, reps: int = 5):
     """A plain device copy of `mib` MiB (reads and writes that many bytes per
     launch) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -167,12 +214,36 @@ def copy_calibration(mib: int, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": reps}), flush=True)
 
 
+def note(msg):
+    """A progress line on stderr (the run's own steps)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alu_roofline(kname, pairs, ms, d, fp64, workload):
+    rate = pairs / (ms * 1e-3)
+    slots = slots_per_pair(d, fp64)
+    achieved = rate * slots
+    return {
+        "bound": "alu",
+        "achieved": achieved / 1e12,
+        "peak": FP32_VALU_PEAK / 1e12,
+        "unit": "Tops/s",
+        "frac": achieved / FP32_VALU_PEAK,
+        "traffic": pmc_traffic(kname, workload),
+        "ops_per_pair": slots,
+        "ops": (f"fp32 issue slots per pair: {slots} fp32 VALU" if not fp64 else
+                f"fp32 issue slots per pair: {2 * d + 2} fp64 VALU at 2 slots + 1 fp32 add"),
+        "pair_peak": FP32_VALU_PEAK / slots,
+        "kernel": kname,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", type=int, default=5, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="no HIP events on the pair-kernel launches (no roofline)")
@@ -182,19 +253,28 @@ def main():
                     help="workload 5: verify the screened tiles (exact shares) before each fine update")
     ap.add_argument("--adaptive", action="store_true",
                     help="workload 5: sampled lift checks between batches of coarse updates")
-    ap.add_argument("--max-fine", type=int, default=None,
-                    help="workload 5: cap on fine updates (profiling runs; the default runs to the certificate)")
+    ap.add_argument("--fp32-pairs", action="store_true",
+                    help="dense d <= 3 half-steps in the fp32 pair loop (SINKHORN_FLAG_FP32_PAIRS)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the issue-rate probe kernels and print their rates")
     ap.add_argument("--roofline-only", action="store_true",
-                    help="run only the kernel-timing region once and print its kernel timing (counter runs)")
+                    help="only the kernel-timing region, from a continuation state reached without "
+                         "the full solve (counter runs)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.probe:
+        print(json.dumps({"issue_rates": issue_rates(), "fp32_lane_peak": FP32_VALU_PEAK,
+                          "fp64_lane_peak": FP64_VALU_PEAK}), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
-    if (args.verify or args.adaptive) and "multiscale" not in WORKLOADS[args.workload]:
+    W = WORKLOADS[args.workload]
+    multiscale = "multiscale" in W
+    if (args.verify or args.adaptive) and not multiscale:
         print("bench.py: --verify and --adaptive apply to the multiscale workload (5) only", file=sys.stderr)
         sys.exit(2)
 
@@ -203,123 +283,128 @@ def main():
     import log_domain_sinkhorn_amd as sk
     import synth
 
-    W = WORKLOADS[args.workload]
     if args.steps is None:
         args.steps = W["steps"]
     if args.warmup is None:
         args.warmup = W["warmup"]
+    note(f"workload {args.workload}: generating inputs")
     c = synth.make(args.workload)
     dev = torch.device("cuda:0")
     x, y = torch.from_numpy(c.x).to(dev), torch.from_numpy(c.y).to(dev)
     a, b = torch.from_numpy(c.a).to(dev), torch.from_numpy(c.b).to(dev)
     # the cost scale is resolved once, as a number, before anything is timed
     scale = 1.0 / sk.mean_sqeuclid(x, y) if W.get("scale") == "mean" else 1.0
-    multiscale = "multiscale" in W
+    flags = sk.FLAG_FP32_PAIRS if args.fp32_pairs else 0
+    fp64 = c.d <= 3 and not args.fp32_pairs and not multiscale
+    P = sk.Problem(x, y, a, b, scale, flags=flags)
+    f = torch.zeros(c.n, dtype=torch.float32, device=dev)
+    g = torch.zeros(c.m, dtype=torch.float32, device=dev)
+    extra = {}
+    continuing = multiscale or bool(W.get("continuation"))
+    batch = W.get("materialize", 0)
+
     if multiscale:
         prm = sk.MultiscaleParams(**W["multiscale"])
-        if args.max_fine is not None:
-            prm.max_fine = args.max_fine
         prm.verify = bool(args.verify)
         prm.adaptive = bool(args.adaptive)
         eps = prm.eps
         kind = sk.PROF_SPARSE
+        cont = dict(prm.__dict__, warm_start=True, adaptive=False, tol=1e-30)
+
+        def solve_once():
+            f.zero_()
+            g.zero_()
+            return P.solve_multiscale(prm, f, g)
+
+        def run_steps(k):
+            # k fine updates from (f, g), continuing in place; the last f-step
+            # gives the admitted residual of the returned state
+            _, _, rep = P.solve_multiscale(sk.MultiscaleParams(**dict(cont, max_fine=k)), f, g)
+            assert rep["fine_updates"] == k, rep["fine_updates"]
+            return rep, 2 * k + 1
     else:
         sched = sk.Schedule(**W["sched"])
         eps = float(W["sched"]["eps_target"])
         kind = sk.PROF_DENSE
-    P = sk.Problem(x, y, a, b, scale)
-    f = torch.zeros(c.n, dtype=torch.float32, device=dev)
-    g = torch.zeros(c.m, dtype=torch.float32, device=dev)
-    batch = W.get("materialize", 0)
-    if batch:
-        T = torch.empty((batch, c.m), dtype=torch.float32, device=dev)
-        rmax = torch.empty(batch, dtype=torch.float32, device=dev)
-        row_ids = torch.arange(c.n, dtype=torch.int64, device=dev)
+        if batch:
+            T = torch.empty((batch, c.m), dtype=torch.float32, device=dev)
+            rmax = torch.empty(batch, dtype=torch.float32, device=dev)
+            row_ids = torch.arange(c.n, dtype=torch.int64, device=dev)
 
-    def step(timing=False, bounded=False, warm=False):
-        if not warm:
+        def solve_once():
             f.zero_()
             g.zero_()
-        P.profile_enable(kind if timing else 0)
-        if multiscale:
-            q = prm
-            if bounded and "roofline" in W:
-                q = sk.MultiscaleParams(**{**prm.__dict__, **W["roofline"]})
-            f_, g_, rep = P.solve_multiscale(q, f, g)
-            f.copy_(f_)
-            g.copy_(g_)
-            rep = dict(rep, pairs_evaluated=rep["pairs_evaluated"], seconds=rep["seconds_total"])
-        else:
-            sc = sk.Schedule(**W["roofline"]) if bounded and "roofline" in W else sched
-            _, _, rep = P.solve(sc, f, g)
-        kt = P.profile_read() if timing else None
-        P.profile_enable(0)
-        mat = None
-        if batch:
-            # every plan row, batch by batch; min over rows of the row maxima
-            P.profile_enable(sk.PROF_MATERIALIZE if timing else 0)
-            lo = torch.full((), float("inf"), device=dev)
+            return P.solve(sched, f, g)
+
+        def materialize_all():
+            # every plan row, batch by batch, and the min_row threshold
             for r0 in range(0, c.n, batch):
                 k = min(batch, c.n - r0)
                 P.materialize_rows(eps, f, g, row_ids[r0:r0 + k], T=T[:k], row_max=rmax[:k])
-                lo = torch.minimum(lo, rmax[:k].min())
-            mat = (lo, P.profile_read() if timing else None)
-            P.profile_enable(0)
-        return rep, kt, mat
+            return P.min_row(eps, f, g)
+
+        if continuing:
+            def run_steps(k):
+                # k full iterations at eps_target, continuing from (f, g); the
+                # count includes the two residual half-steps the solve ends with
+                _, _, rep = P.solve(sk.Schedule(eps, eps, fixed_iters=k), f, g)
+                return rep, rep["halfsteps"]
+        else:
+            def run_steps(k):
+                hs, rep = 0, None
+                for _ in range(k):
+                    _, _, rep = solve_once()
+                    hs += rep["halfsteps"]
+                    if batch:
+                        extra["min_row"] = materialize_all()
+                return rep, hs
 
     if args.roofline_only:
-        # only the kernel-timing region, once (for counter runs of the large
-        # workloads); from zero potentials
-        _, kt, _ = step(timing=True, bounded=True)
-        ms, nl, pairs = kt
+        if multiscale:
+            solve_once()
+        elif continuing:
+            P.solve(sk.Schedule(eps, eps, fixed_iters=3), f, g)  # a state at eps_target
+        P.profile_enable(kind)
+        run_steps(3 if continuing else 1)
+        ms, nl, pairs = P.profile_read()
+        P.profile_enable(0)
         print(json.dumps({"roofline_only": True, "workload": args.workload,
-                          "region": W.get("roofline", "the whole step"),
                           "pair_kernel": {"launches": nl, "avg_ms": ms / max(nl, 1),
                                           "pair_evals_per_s": pairs / (ms * 1e-3) if ms else None}}),
               flush=True)
         return
 
-    for _ in range(args.warmup):
-        step()
+    # one whole solve from zero potentials: the wall time to the residual
+    note("one whole solve to the stop test")
     torch.cuda.synchronize()
+    t = time.perf_counter()
+    _, _, srep = solve_once()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t
+    if batch:
+        extra["min_row"] = materialize_all()
+    note(f"solve done in {wall:.1f} s; {args.warmup} warm-up and {args.steps} timed steps")
 
-    # timed region: K steps, nothing else on the stream
-    reps = []
+    if args.warmup > 0:
+        run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        reps.append(step())
+    trep, halfsteps = run_steps(args.steps)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
+    note(f"timed steps done in {elapsed:.1f} s")
 
-    # second timed region for the roofline: the same steps (workloads 4 and 5:
-    # a bounded run of the same kernels) with a HIP event pair recorded by the
-    # dispatch of every pair-kernel (and materializer) launch at the kernel's
-    # start and end; the events stay out of the first region. The bounded
-    # dense run (workload 4) starts from the potentials the timed solve
-    # returned, the state most of its half-steps run in (from zero potentials
-    # at the target eps the row shifts are poor and more chunks are redone);
-    # the bounded multiscale run starts from zero like the solve.
-    kernel_ms, launches, kpairs = 0.0, 0, 0.0
-    mat_ms, mat_launches, mat_pairs = 0.0, 0, 0.0
+    # kernel timing: the same steps again (3 of them for the continuing
+    # workloads) with a HIP event pair recorded by the dispatch of every
+    # pair-kernel launch at the kernel's start and end
+    kt = None
     if not args.no_kernel_timing:
-        warm = not multiscale and "roofline" in W
-        for _ in range(args.steps):
-            _, kt, mat = step(timing=True, bounded=True, warm=warm)
-            kernel_ms += kt[0]
-            launches += kt[1]
-            kpairs += kt[2]
-            if mat:
-                mat_ms += mat[1][0]
-                mat_launches += mat[1][1]
-                mat_pairs += mat[1][2]
-    timed = launches > 0 and kernel_ms > 0
+        P.profile_enable(kind)
+        run_steps(3 if continuing else 1)
+        kt = P.profile_read()
+        P.profile_enable(0)
 
-    solve_pairs = sum(r[0]["pairs_evaluated"] for r in reps)
-    mat_entries = (c.n * c.m if batch else 0) * args.steps
-    value = (solve_pairs + mat_entries) / elapsed
-    last = reps[-1][0]
+    value = c.n * c.m * halfsteps / elapsed
     out = {
         "metric": "pair-evals/s per Sinkhorn half-step (n*m/t) + wall-time to L1 residual 1e-3",
         "value": value,
@@ -331,7 +416,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64+f32" if fp64 else "f32",
         "data": "synthetic",
         "config": {
             "workload": W["desc"],
@@ -339,112 +424,57 @@ def main():
             "m": c.m,
             "d": c.d,
             "cost_scale": scale,
-            "step": ("one multiscale solve (Morton order, cells, coarse solve, lift, fine loop) to the "
-                     "certified stop" if multiscale else "one solve from zero potentials to the stop test")
-                    + (", then all plan rows materialized" if batch else ""),
+            "step": ("one fine update from the certified potentials (both tile lists screened, sparse f- "
+                     "and g-half-step, admitted residual)" if multiscale else
+                     "one full iteration at eps_target from the solved potentials" if continuing
+                     else "one solve from zero potentials to the stop test"
+                     + (", then all plan rows materialized and min_row" if batch else "")),
+            "pair_arithmetic": "fp64 up to the exponent (d <= 3)" if fp64 else "fp32",
         },
-        "wall_time_to_residual_s": sum(r[0]["seconds"] for r in reps) / len(reps),
+        "wall_time_to_residual_s": wall,
+        "halfsteps_timed": halfsteps,
     }
     if multiscale:
-        for k in ("certified", "coarse_iters", "fine_updates", "ncells_x", "ncells_y", "last_tiles",
-                  "last_candidates", "R_A_row", "R_A_col", "omega", "seconds_sort", "seconds_coarse",
-                  "seconds_lift", "seconds_fine"):
-            out[k] = last[k]
-        out["verify"] = bool(prm.verify)
-        out["adaptive"] = bool(prm.adaptive)
+        out["evaluated_pair_evals_per_s"] = trep["pairs_evaluated"] / elapsed
+        out["solve"] = {k: srep[k] for k in (
+            "certified", "coarse_iters", "fine_updates", "ncells_x", "ncells_y", "last_tiles",
+            "last_candidates", "R_A_row", "R_A_col", "omega", "seconds_total", "seconds_sort",
+            "seconds_coarse", "seconds_lift", "seconds_fine", "pairs_evaluated", "peak_extra_bytes")}
+        out["solve"]["verify"] = bool(prm.verify)
+        out["solve"]["adaptive"] = bool(prm.adaptive)
         if prm.adaptive:
-            out.update(accepted_by_sample=bool(last["accepted_by_sample"]), checks=last["checks"],
-                       last_check=dict(zip(("row", "row_se", "col", "col_se"), last["last_check"]),
-                                       samples=last["last_check_samples"]))
+            out["solve"].update(accepted_by_sample=bool(srep["accepted_by_sample"]), checks=srep["checks"])
     else:
-        out.update(halfsteps_per_solve=last["halfsteps"], iters_per_solve=last["iters"],
-                   final_row_l1=last["row_l1"], final_col_l1=last["col_l1"])
-    if "roofline" in W and timed:
-        out["roofline_region"] = ("bounded run of the same kernels: " + json.dumps(W["roofline"]))
-    if batch:
-        out["min_row_max"] = float(reps[-1][2][0])
-    mfma = c.d > 8
-    if timed:
-        out["pair_kernel"] = {
-            "launches": launches,
-            "avg_ms": kernel_ms / launches,
-            "pairs_per_launch": kpairs / launches,
-            "pair_evals_per_s": kpairs / (kernel_ms * 1e-3),
-        }
-        if mfma:
+        out["solve"] = {k: srep[k] for k in ("halfsteps", "iters", "final_iters", "row_l1", "col_l1",
+                                              "seconds", "seconds_per_halfstep", "workspace_bytes",
+                                              "peak_extra_bytes")}
+        out["solve"]["history_tail"] = srep["history"][-5:]
+        if "min_row" in extra:
+            out["min_row"] = extra["min_row"]
+    if kt and kt[1] > 0 and kt[0] > 0:
+        ms, nl, pairs = kt
+        out["pair_kernel"] = {"launches": nl, "avg_ms": ms / nl, "pairs_per_launch": pairs / nl,
+                              "pair_evals_per_s": pairs / (ms * 1e-3)}
+        if c.d > 8:
             kp = (c.d + 1 + 3) // 4 * 4
             flops = 2.0 * c.d  # the cross term x . y, algorithmic
-            achieved = kpairs * flops / (kernel_ms * 1e-3)
-            out["roofline"] = {
-                "bound": "mfma",
-                "achieved": achieved / 1e12,
-                "peak": MFMA_F32_PEAK / 1e12,
-                "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F32_PEAK,
-                "traffic": pmc_traffic(f"k_lse_mfma<{kp}>", args.workload),
-                "flops_per_pair": flops,
-                "kernel": f"k_lse_mfma<{kp}>",
-            }
+            achieved = pairs * flops / (ms * 1e-3)
+            out["roofline"] = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_F32_PEAK / 1e12,
+                               "unit": "TFLOP/s", "frac": achieved / MFMA_F32_PEAK,
+                               "traffic": pmc_traffic(f"k_lse_mfma<{kp}>", args.workload),
+                               "flops_per_pair": flops, "kernel": f"k_lse_mfma<{kp}>"}
         else:
-            kname = f"k_lse_sparse<{c.d},true>" if multiscale else f"k_lse_valu<{c.d},true>"
-            ops = ops_per_pair(c.d)
-            achieved = kpairs * ops / (kernel_ms * 1e-3)
-            out["roofline"] = {
-                "bound": "alu",
-                "achieved": achieved / 1e12,
-                "peak": VALU_PEAK_OPS / 1e12,
-                "unit": "Tops/s",
-                "frac": achieved / VALU_PEAK_OPS,
-                "traffic": pmc_traffic(kname, args.workload),
-                "ops_per_pair": ops,
-                "pair_peak": VALU_PEAK_OPS / ops,
-                "kernel": kname,
-            }
-        if mat_launches:
-            wbytes = mat_pairs * 4.0
-            out["materializer"] = {
-                "launches": mat_launches,
-                "avg_ms": mat_ms / mat_launches,
-                "entries_per_launch": mat_pairs / mat_launches,
-                "write_GBps": wbytes / (mat_ms * 1e-3) / 1e9,
-                "hbm_frac": wbytes / (mat_ms * 1e-3) / HBM_PEAK,
-            }
-    if batch and not args.no_kernel_timing:
-        # the consumer of the row materializer: sparsify at min_row on the device
-        thr = P.min_row(eps, f, g)
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        ptr, col, val = P.sparsify(eps, f, g, thr, batch=batch)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t
-        out["sparsify"] = {
-            "threshold": thr,
-            "nnz": int(ptr[-1].item()),
-            "seconds": dt,
-            "note": "count pass, then the entries (two materializations per batch), min_row threshold",
-        }
-    if not multiscale and c.d <= 8 and not args.no_kernel_timing:
-        # barycentric projection + source gradient at the solved potentials
-        # (the f-step's loop with d weighted sums: 2d+2 + d VALU per pair)
-        reps_b = 3 if c.n * c.m <= 1e10 else 1
-        P.barycentric(eps, g, f_hint=f)  # first call: module load, buffers
-        torch.cuda.synchronize()
-        P.profile_enable(sk.PROF_BARY)
-        for _ in range(reps_b):
-            P.barycentric(eps, g, f_hint=f)
-        bms, bl, bp = P.profile_read()
-        P.profile_enable(0)
-        bops = ops_per_pair(c.d) + c.d
-        out["barycentric"] = {
-            "launches": bl,
-            "avg_ms": bms / bl,
-            "pair_evals_per_s": bp / (bms * 1e-3),
-            "ops_per_pair": bops,
-            "valu_frac": bp * bops / (bms * 1e-3) / VALU_PEAK_OPS,
-            "kernel": f"k_bary_valu<{c.d},true>",
-        }
+            kname = (f"k_lse_sparse<{c.d},true>" if multiscale else
+                     f"k_lse_valu64<{c.d}>" if fp64 else f"k_lse_valu<{c.d},true>")
+            out["roofline"] = alu_roofline(kname, pairs, ms, c.d, fp64, args.workload)
+            # the same instruction mix measured by the probe kernels
+            name = "PAIR_F64" if fp64 else "PAIR_F32"
+            pr = issue_rates((name,))
+            out["issue_ceiling"] = {"probe": name, "pairs_per_s": pr[name]["pairs_per_s"],
+                                    "kernel_over_probe": (pairs / (ms * 1e-3)) / pr[name]["pairs_per_s"]}
     P.close()
     if not args.no_cpu_baseline:
+        note("cpu baseline (the fp64 oracle on the host)")
         out["cpu_baseline"] = cpu_baseline(c, eps, scale)
     print(json.dumps(out), flush=True)
 

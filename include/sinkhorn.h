@@ -234,6 +234,17 @@ int sinkhorn_morton_order(const float* x, const float* y, int64_t n, int64_t m, 
                           void* stream, uint64_t* codes_x, int32_t* perm_x, uint64_t* codes_y,
                           int32_t* perm_y);
 
+/* The same Morton order for one side of a handle (side 0: x, 1: y), from
+ * the handle's own copies of the clouds: both sides are quantized over the
+ * bounding box of x and y together, exactly as sinkhorn_morton_order does,
+ * so codes_out [count] (device, sorted) and perm_out [count] (device,
+ * original index of each sorted point) equal that call's outputs for the
+ * side. d <= 3 (SINKHORN_ERR_UNSUPPORTED otherwise). Allocates the other
+ * side's codes and order for the duration of the call; synchronizes the
+ * handle's stream. */
+int sinkhorn_morton_sort(sinkhorn_problem* p, int32_t side, int32_t* perm_out,
+                         uint64_t* codes_out);
+
 /* Block-pair screen (FlashSinkhorn 2, §3.2 and §B.3: block-level potential
  * maxima and bounding boxes; §A.3: an omitted tile drops at most
  * delta_rel * a_i per row and delta_rel * b_j per column). Blocks are B
@@ -318,6 +329,9 @@ typedef struct {
   int32_t check_samples;
   int32_t check_samples_max;
   uint64_t sample_seed;
+  /* Continuation, when nonzero: no cells, coarse stage or lift; the fine
+   * loop starts from f and g as given (caller's order) and runs as above. */
+  int32_t warm_start;
 } sinkhorn_multiscale_params;
 
 typedef struct {
@@ -336,6 +350,7 @@ typedef struct {
   int64_t last_check_samples;  /* samples per side of the last check */
   double last_check[4];        /* its row estimate, row standard error, column estimate, column
                                   standard error */
+  int64_t peak_extra_bytes;    /* most device memory the call held beyond the handle's */
 } sinkhorn_multiscale_report;
 
 /* Block-sparse multiscale solve for d <= 3 (FlashSinkhorn 2): Morton sort,
@@ -343,8 +358,9 @@ typedef struct {
  * on the cells, lift of the coarse potentials to the points, then fine updates
  * that each rebuild the block-pair mask and run the sparse f- and g-steps,
  * stopping when the certificate max(R_A,row, R_A,col) + Omega <= tol holds.
- * f [n], g [m] (device) receive the potentials in the caller's order;
- * rep (host) may be NULL. Returns SINKHORN_NOT_CONVERGED at the fine cap. */
+ * f [n], g [m] (device) receive the potentials in the caller's order (with
+ * warm_start they also give the starting potentials); rep (host) may be
+ * NULL. Returns SINKHORN_NOT_CONVERGED at the fine cap. */
 int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_multiscale_params* prm,
                               float* f, float* g, sinkhorn_multiscale_report* rep);
 
@@ -428,6 +444,46 @@ int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
 int sinkhorn_profile_enable(sinkhorn_problem* p, int32_t kinds);
 int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launches,
                           double* pairs);
+
+/* Issue-rate probe: the vector-ALU ceiling of this device for the pair
+ * kernels' instruction mix, measured rather than taken from a data sheet
+ * (FlashSinkhorn 2, §C.6 accounts for its kernels' cost in instructions per
+ * pair). Runs one probe kernel of `iters` iterations on `stream` (NULL: the
+ * null stream) over 8 waves per SIMD of every compute unit and returns (host
+ * pointers, any may be NULL) the lane-instructions retired per second of the
+ * counted class, the point pairs per second for the pair probes (0
+ * otherwise) and the kernel time in ms (HIP events around the launch, after
+ * one warm-up launch). Kinds (each iteration four independent chains):
+ *   SINKHORN_PROBE_FMA_F32        v_fma_f32 on VGPRs; counts the FMAs
+ *   SINKHORN_PROBE_EXP_F32        v_exp_f32 alone; counts the exps
+ *   SINKHORN_PROBE_FMA_F64        v_fma_f64 on VGPRs; counts the FMAs
+ *   SINKHORN_PROBE_PAIR_F32       one d = 3 pair of the dense half-step's fp32
+ *                                 loop: 3 v_sub_f32 (scalar operand), v_fma_f32,
+ *                                 2 v_fmac_f32, v_fma_f32 (scalar operand),
+ *                                 v_exp_f32, v_add_f32; counts the 8 non-exp
+ *   SINKHORN_PROBE_PAIR_F32_NOEXP the same without the v_exp_f32
+ *   SINKHORN_PROBE_PAIR_F64       the same pair in fp64 up to the exponent:
+ *                                 3 v_add_f64, 4 v_fma_f64, v_cvt_f32_f64,
+ *                                 v_exp_f32, v_add_f32; counts the 9 non-exp
+ *   SINKHORN_PROBE_SUB_F32        v_sub_f32 with a scalar operand
+ *   SINKHORN_PROBE_FMAC_F32       v_fmac_f32 (accumulator in the destination)
+ *   SINKHORN_PROBE_ADD_F64        v_add_f64 with a scalar operand
+ *   SINKHORN_PROBE_CVT_F32_F64    v_cvt_f32_f64 (the CVT probe also sums its
+ *                                 results: 4 v_add_f32 per 4 conversions,
+ *                                 not counted)
+ * Synchronizes `stream`. */
+#define SINKHORN_PROBE_FMA_F32 0
+#define SINKHORN_PROBE_EXP_F32 1
+#define SINKHORN_PROBE_FMA_F64 2
+#define SINKHORN_PROBE_PAIR_F32 3
+#define SINKHORN_PROBE_PAIR_F32_NOEXP 4
+#define SINKHORN_PROBE_PAIR_F64 5
+#define SINKHORN_PROBE_SUB_F32 6
+#define SINKHORN_PROBE_FMAC_F32 7
+#define SINKHORN_PROBE_ADD_F64 8
+#define SINKHORN_PROBE_CVT_F32_F64 9
+int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stream, double* lane_instr_per_s,
+                              double* pairs_per_s, double* kernel_ms);
 
 #ifdef __cplusplus
 }

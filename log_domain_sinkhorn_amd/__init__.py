@@ -111,6 +111,7 @@ class _MultiscaleParamsC(ctypes.Structure):
         ("check_samples", _i32),
         ("check_samples_max", _i32),
         ("sample_seed", ctypes.c_uint64),
+        ("warm_start", _i32),
     ]
 
 
@@ -136,6 +137,7 @@ class _MultiscaleReportC(ctypes.Structure):
         ("checks", _i64),
         ("last_check_samples", _i64),
         ("last_check", _f64 * 4),
+        ("peak_extra_bytes", _i64),
     ]
 
 
@@ -156,6 +158,7 @@ _SIGS = {
     "sinkhorn_materialize_rows_noalloc": ([_p, _f64, _p, _p, _p, _i64, _p, _p], _i32),
     "sinkhorn_min_row": ([_p, _f64, _p, _p, _p], _i32),
     "sinkhorn_morton_order": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _p], _i32),
+    "sinkhorn_morton_sort": ([_p, _i32, _p, _p], _i32),
     "sinkhorn_block_screen": ([_p, _f64, _p, _p, _i32, _f64, _i32, _p, _p, _i64, _p], _i32),
     "sinkhorn_verify_tiles": ([_p, _f64, _p, _p, _i32, _f64, _p, _p, _p, _p, _p, _p, _p], _i32),
     "sinkhorn_sparse_halfstep_f": ([_p, _f64, _p, _i32, _p, _p, _p, _p, _p], _i32),
@@ -168,6 +171,7 @@ _SIGS = {
     "sinkhorn_sampled_residual": ([_p, _f64, _p, _p, _i32, _i32, ctypes.c_uint64, _p, _p], _i32),
     "sinkhorn_profile_enable": ([_p, _i32], _i32),
     "sinkhorn_profile_read": ([_p, _p, _p, _p], _i32),
+    "sinkhorn_probe_issue_rate": ([_i32, _i32, _p, _p, _p, _p], _i32),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -268,6 +272,7 @@ class MultiscaleParams:
     check_samples: int = 1024
     check_samples_max: int = 8192
     sample_seed: int = 0
+    warm_start: bool = False
 
     def _c(self) -> _MultiscaleParamsC:
         return _MultiscaleParamsC(self.B, self.p_bits, self.eps, self.tol, self.delta_scale,
@@ -275,7 +280,8 @@ class MultiscaleParams:
                                   self.coarse_iters_per_stage, self.coarse_tol, self.coarse_max,
                                   self.stall_window, self.stall_rel, self.max_fine,
                                   int(bool(self.verify)), int(bool(self.adaptive)), self.check_every,
-                                  self.check_samples, self.check_samples_max, self.sample_seed)
+                                  self.check_samples, self.check_samples_max, self.sample_seed,
+                                  int(bool(self.warm_start)))
 
 
 def _struct_dict(s) -> dict:
@@ -320,7 +326,18 @@ def morton_order(x: torch.Tensor, y: torch.Tensor):
     return cx, px, cy, py
 
 
+(PROBE_FMA_F32, PROBE_EXP_F32, PROBE_FMA_F64, PROBE_PAIR_F32, PROBE_PAIR_F32_NOEXP, PROBE_PAIR_F64,
+ PROBE_SUB_F32, PROBE_FMAC_F32, PROBE_ADD_F64, PROBE_CVT_F32_F64) = range(10)
 FLAG_FP32_PAIRS = 1
+
+
+def probe_issue_rate(kind: int, iters: int = 20000, device="cuda:0"):
+    """(lane-instructions/s, pairs/s, kernel ms) of an issue-rate probe kernel."""
+    rate, pairs, ms = _f64(), _f64(), _f64()
+    with torch.cuda.device(device):
+        _check(lib().sinkhorn_probe_issue_rate(int(kind), int(iters), _stream(device), ctypes.byref(rate),
+                                               ctypes.byref(pairs), ctypes.byref(ms)), "probe_issue_rate")
+    return rate.value, pairs.value, ms.value
 
 
 def device_memory(reset: bool = False):
@@ -469,6 +486,14 @@ class Problem:
         _check(lib().sinkhorn_min_row(self._h, float(eps), _ptr(f), _ptr(g), ctypes.byref(out)),
                "min_row")
         return out.value
+
+    def morton_sort(self, side: int):
+        """(codes int64 holding the uint64 bits, perm int32) of side 0 (x) or 1 (y)."""
+        count = self.n if side == 0 else self.m
+        codes = torch.empty(count, dtype=torch.int64, device=self.device)
+        perm = torch.empty(count, dtype=torch.int32, device=self.device)
+        _check(lib().sinkhorn_morton_sort(self._h, int(side), _ptr(perm), _ptr(codes)), "morton_sort")
+        return codes, perm
 
     def block_screen(self, eps, f, g, B, delta_rel, transpose=False, cap=None):
         """Admitted tiles as (ptr int64, idx int32) device tensors."""

@@ -49,6 +49,13 @@ __global__ __launch_bounds__(256) void k_scatter(const float* __restrict__ in,
   if (i < count) out[perm[i]] = in[i];
 }
 
+__global__ __launch_bounds__(256) void k_gather_pot(const float* __restrict__ in,
+                                                    const int32_t* __restrict__ perm, int64_t count,
+                                                    float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) out[i] = in[perm[i]];
+}
+
 __global__ __launch_bounds__(256) void k_cell_flags(const uint64_t* __restrict__ codes,
                                                     int64_t count, int32_t shift,
                                                     int32_t* __restrict__ flags) {
@@ -403,6 +410,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     if (!(std::isfinite(P.eps) && P.eps > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (!(P.tol > 0.0) || !(P.delta_scale > 0.0)) fail(SINKHORN_ERR_INVALID_ARG, "tol and delta_scale must be > 0");
     if (P.max_fine < 0 || P.coarse_max < 1) fail(SINKHORN_ERR_INVALID_ARG, "bad iteration caps");
+    if (P.warm_start && P.adaptive) fail(SINKHORN_ERR_INVALID_ARG, "warm_start excludes the adaptive switch");
     if (P.verify && P.B != kVerifyB) fail(SINKHORN_ERR_UNSUPPORTED, "tile verification needs B = 128");
     if (P.adaptive && (P.check_every < 1 || P.check_samples < 2 || P.check_samples_max < P.check_samples ||
                        P.check_samples_max > (1 << 24)))
@@ -420,6 +428,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     if (p_bits > 21 * d) p_bits = 21 * d;
     sinkhorn_multiscale_report R{};
     R.omega = omega;
+    const int64_t bytes0 = thread_alloc_current();
+    thread_alloc_mark();
 
     // ---- Morton order and sorted sides
     for (int k = 0; k < 2; ++k) {
@@ -437,8 +447,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     hipLaunchKernelGGL(k_gather, grid1(((m + 255) / 256), 256), dim3(256), 0, st, p->Y.soa,
                        p->Y.padded, p->Y.w, perm[1], m, d, Ys.soa, Ys.padded, Ys.w);
     SK_LAUNCH_CHECK();
-    build_cells(p, Xs, codes[0], p_bits, Cx);
-    build_cells(p, Ys, codes[1], p_bits, Cy);
+    if (!P.warm_start) {
+      build_cells(p, Xs, codes[0], p_bits, Cx);
+      build_cells(p, Ys, codes[1], p_bits, Cy);
+    }
     R.ncells_x = Cx.count;
     R.ncells_y = Cy.count;
     SK_HIP(hipStreamSynchronize(st));
@@ -451,10 +463,12 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     auto need = [&](int64_t rows, int64_t cols) {
       ensure_partials(p, partial_floats_needed(p, rows, round_up(rows, kPad), cols));
     };
-    need(Cx.count, Cy.count);
-    need(Cy.count, Cx.count);
-    need(n, Cy.count);
-    need(m, Cx.count);
+    if (!P.warm_start) {
+      need(Cx.count, Cy.count);
+      need(Cy.count, Cx.count);
+      need(n, Cy.count);
+      need(m, Cx.count);
+    }
     pot[0] = (float*)dev_alloc(sizeof(float) * Cx.count);  // F
     pot[1] = (float*)dev_alloc(sizeof(float) * Cy.count);  // G
     pot[2] = (float*)dev_alloc(sizeof(float) * Cx.count);
@@ -495,7 +509,16 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     };
     bool accepted = false;
     double t_coarse, t_lift;
-    if (!P.adaptive) {
+    if (P.warm_start) {
+      // the fine loop starts from the caller's potentials (in Morton order)
+      hipLaunchKernelGGL(k_gather_pot, grid1((n + 255) / 256, 256), dim3(256), 0, st, f, perm[0], n,
+                         fs[0]);
+      SK_LAUNCH_CHECK();
+      hipLaunchKernelGGL(k_gather_pot, grid1((m + 255) / 256, 256), dim3(256), 0, st, g, perm[1], m,
+                         gs[0]);
+      SK_LAUNCH_CHECK();
+      t_coarse = t_lift = now_s();
+    } else if (!P.adaptive) {
       const SolveOut co = dense_solve(p, Cx, Cy, pot[0], pot[1], CF, CG, cs, P.stall_window, P.stall_rel);
       R.coarse_iters = co.iters;
       R.pairs_evaluated += co.pairs;
@@ -658,6 +681,7 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     const double t_end = now_s();
     R.seconds_fine = t_end - t_lift;
     R.seconds_total = t_end - t_start;
+    R.peak_extra_bytes = thread_alloc_peak() - bytes0;
     if (rep) *rep = R;
     cleanup();
     return status;

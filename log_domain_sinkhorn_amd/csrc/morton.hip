@@ -190,3 +190,41 @@ extern "C" int sinkhorn_morton_order(const float* x, const float* y, int64_t n, 
     return SINKHORN_ERR_HIP;
   }
 }
+
+extern "C" int sinkhorn_morton_sort(sinkhorn_problem* p, int32_t side, int32_t* perm_out,
+                                    uint64_t* codes_out) {
+  uint64_t* other_codes = nullptr;
+  int32_t* other_perm = nullptr;
+  try {
+    if (!p || !perm_out || !codes_out) sk::fail(SINKHORN_ERR_INVALID_ARG, "null pointer");
+    if (side != 0 && side != 1) sk::fail(SINKHORN_ERR_INVALID_ARG, "side must be 0 (x) or 1 (y)");
+    if (p->d > 3 || !p->X.soa || !p->Y.soa)
+      sk::fail(SINKHORN_ERR_UNSUPPORTED, "Morton codes are built for d <= 3");
+    if (p->n > INT32_MAX || p->m > INT32_MAX)
+      sk::fail(SINKHORN_ERR_INVALID_ARG, "n and m must be < 2^31");
+    // both sides share one bounding box, so both are quantized; the other
+    // side's codes and order go to temporary buffers
+    const int64_t other = side == 0 ? p->m : p->n;
+    other_codes = (uint64_t*)sk::dev_alloc(sizeof(uint64_t) * other);
+    other_perm = (int32_t*)sk::dev_alloc(sizeof(int32_t) * other);
+    uint64_t* cx = side == 0 ? codes_out : other_codes;
+    int32_t* px = side == 0 ? perm_out : other_perm;
+    uint64_t* cy = side == 1 ? codes_out : other_codes;
+    int32_t* py = side == 1 ? perm_out : other_perm;
+    sk::morton_sort_soa(p->X.soa, p->X.padded, p->Y.soa, p->Y.padded, p->n, p->m, p->d, p->stream,
+                        cx, px, cy, py);
+    sk::dev_free(other_codes);
+    sk::dev_free(other_perm);
+    return SINKHORN_OK;
+  } catch (const sk::Failure& e) {
+    sk::dev_free(other_codes);
+    sk::dev_free(other_perm);
+    sk::set_last_error(e.msg);
+    return e.code;
+  } catch (...) {
+    sk::dev_free(other_codes);
+    sk::dev_free(other_perm);
+    sk::set_last_error("unexpected exception");
+    return SINKHORN_ERR_HIP;
+  }
+}

@@ -54,6 +54,22 @@ def test_morton_codes_and_order_bit_exact(sk, w, n, m):
         assert np.array_equal(g_, r_), what
 
 
+@pytest.mark.parametrize("w,n,m", [(5, 5000, 4321), (2, 1, 7), (1, 3001, 517)])
+def test_handle_morton_sort_equals_the_standalone_order(sk, w, n, m):
+    """The handle form (one side of a handle's clouds) gives the oracle's codes
+    and order bit for bit, like the standalone call over both clouds."""
+    c = synth.make(w, n=n, m=m)
+    ref = oracle.morton_order(c.x, c.y)
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        cx, px = P.morton_sort(0)
+        cy, py = P.morton_sort(1)
+    got = (cx.cpu().numpy().view(np.uint64), px.cpu().numpy(), cy.cpu().numpy().view(np.uint64),
+           py.cpu().numpy())
+    for g_, r_, what in zip(got, ref, ("codes_x", "perm_x", "codes_y", "perm_y")):
+        assert np.array_equal(g_.astype(np.int64) if what.startswith("perm") else g_,
+                              r_.astype(np.int64) if what.startswith("perm") else r_), what
+
+
 def _sorted_problem(w, n, seed_shift=0.0):
     c = synth.make(w, n=n, m=n)
     _, px, _, py = oracle.morton_order(c.x, c.y)
@@ -211,6 +227,29 @@ def test_multiscale_fixed_budget_matches_the_oracle(sk):
     assert abs(rep["last_tiles"] - tiles) <= max(2, tiles // 1000), (rep["last_tiles"], tiles)
     _gauge_close(f, g, ref["f"], ref["g"], 1e-3 * eps)
     assert rep["R_A_row"] == pytest.approx(float(ref["R_A_row"]), rel=1e-2)
+
+
+def test_multiscale_warm_start_continues_the_fine_loop_bit_for_bit(sk):
+    """A warm-started solve (no cells, coarse stage or lift) from the state an
+    earlier solve returned continues its fine loop exactly: 2 updates, then 3
+    more from the returned potentials, equal 5 updates in one call bit for
+    bit; with no update allowed the potentials come back unchanged and the
+    admitted residual is the one the first call reported."""
+    n = 16384
+    c = synth.make(5, n=n, m=n)
+    base = dict(B=128, eps=1e-3, tol=1e-30, coarse_tol=0.0, coarse_max=40, stall_window=1 << 30)
+    with sk.Problem(_t(c.x), _t(c.y), _t(c.a), _t(c.b), 1.0) as P:
+        f5, g5, r5 = P.solve_multiscale(sk.MultiscaleParams(**base, max_fine=5))
+        f2, g2, r2 = P.solve_multiscale(sk.MultiscaleParams(**base, max_fine=2))
+        f0, g0, r0 = P.solve_multiscale(sk.MultiscaleParams(**base, max_fine=0, warm_start=True),
+                                        f2.clone(), g2.clone())
+        assert torch.equal(f0, f2) and torch.equal(g0, g2)
+        assert r0["R_A_row"] == r2["R_A_row"] and r0["ncells_x"] == 0 and r0["coarse_iters"] == 0
+        fw, gw, rw = P.solve_multiscale(sk.MultiscaleParams(**base, max_fine=3, warm_start=True),
+                                        f2.clone(), g2.clone())
+    assert rw["status"] == sk.NOT_CONVERGED and rw["fine_updates"] == 3
+    assert torch.equal(fw, f5) and torch.equal(gw, g5)
+    assert rw["R_A_row"] == r5["R_A_row"] and rw["last_tiles"] == r5["last_tiles"]
 
 
 @pytest.mark.parametrize("verify", [False, True], ids=["screened", "verified"])
