@@ -36,8 +36,17 @@ def _f64(v) -> np.ndarray:
 
 
 def _threads() -> int:
-    env = os.environ.get("ORACLE_THREADS")
-    return max(1, int(env)) if env else max(1, os.cpu_count() or 1)
+    """Worker threads: ORACLE_THREADS, else OMP_NUM_THREADS, else the CPUs
+    this process may run on (the thread count never changes a result: every
+    chunk is computed alone and the chunks are combined in order)."""
+    for var in ("ORACLE_THREADS", "OMP_NUM_THREADS"):
+        env = os.environ.get(var, "").strip()
+        if env.isdigit():
+            return max(1, int(env))
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
 
 
 def _chunks(count: int, width: int):

@@ -8,6 +8,7 @@ import pytest
 from scipy.spatial.distance import cdist
 
 import oracle
+import synth
 
 
 def _clustered(rng, n, m):
@@ -368,3 +369,33 @@ def test_compacted_lists_are_transposes(problem):
     for J in range(MB):
         r = rowsT[ptrT[J]:ptrT[J + 1]]
         assert (np.diff(r) > 0).all()
+
+
+def test_process_pool_screen_digests_equal_the_single_process_screen():
+    """The full-size GPU checks compare tile lists against the oracle's screen
+    run over worker processes by row-block ranges: those digests must be the
+    single-process screen's, range by range."""
+    import oracle_pool
+
+    n, B, eps = 16384, 128, 1e-3
+    c = synth.make(5, n=n, m=n)
+    _, px, _, py = oracle.morton_order(c.x, c.y)
+    x, y, a, b = c.x[px], c.y[py], c.a[px], c.b[py]
+    rng = np.random.default_rng(4)
+    base = eps * math.log(n) / 2
+    f = (base + rng.normal(0, 0.3 * eps, n)).astype(np.float32)
+    g = (base + rng.normal(0, 0.3 * eps, n)).astype(np.float32)
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    delta = 1e-3 / (n // B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    assert 0 < len(col) < (n // B) ** 2
+    got = oracle_pool.screen_digests(sx, sy, eps, 1.0, delta, width=24, procs=2)
+    assert [(lo, hi) for lo, hi, _, _ in got] == oracle_pool.spans(n // B, 24)
+    for lo, hi, counts, h in got:
+        want_counts, want_h = oracle_pool.digest(ptr, col, lo, hi)
+        assert np.array_equal(counts, want_counts) and h == want_h
+    # a single changed tile index changes its range's digest
+    col2 = col.copy()
+    col2[len(col2) // 2] ^= 1
+    assert any(oracle_pool.digest(ptr, col2, lo, hi)[1] != h for lo, hi, _, h in got)
