@@ -109,6 +109,7 @@ SPARSE_SOURCES = ("blocks.hip", "pairloop.h", "rowfinal.h", "internal.h", "launc
 PMC_RECORDS = {
     2: ("k_lse_valu_w2_n20000_d3_pmc.md", KERNEL_SOURCES),
     3: ("k_lse_mfma_w3_n50000_m60000_d50_pmc.md", ("mfma.hip", "rowfinal.h", "internal.h")),
+    5: ("k_lse_sparse_w5_n16777216_eps1e-4_pmc.md", SPARSE_SOURCES),
 }
 
 
@@ -181,7 +182,7 @@ def cpu_baseline(c, eps, scale=1.0, budget_s=12.0):
 
 
 PROBES = ("FMA_F32", "SUB_F32", "FMAC_F32", "EXP_F32", "PAIR_F32", "PAIR_F32_NOEXP", "FMA_F64",
-          "ADD_F64", "CVT_F32_F64", "PAIR_F64")
+          "ADD_F64", "CVT_F32_F64", "PAIR_F64", "PAIR_TILE_F32")
 
 
 def issue_rates(kinds=PROBES, iters=200000):
