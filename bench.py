@@ -81,21 +81,32 @@ WORKLOADS = {
 }
 
 
-def ops_per_pair(d: int) -> int:
-    """fp32 VALU instructions per pair of the shifted pair loop: d subs and d
-    fmas for the shifted squared distance (the shift folded into the first
-    fma), 1 fma for the exponent and 1 add into the sum. The exp2 issues on
-    the transcendental unit alongside (its own rate is ~4x lower than the
-    VALU's, and the loop needs one per 8 VALU instructions)."""
-    return 2 * d + 2
+# Issue slots per pair, in fp32 VALU lane-instruction slots of the chip's fp32
+# lane rate: an fp32 VALU instruction takes 1, an fp64 one 2 (the fp64 rate is
+# half the fp32 rate) and v_exp_f32 4 (transcendentals issue at a quarter of
+# the rate; the probe measures 93% of that alone and shows the exp does not
+# overlap the other VALU work). The counts are the arithmetic each form does
+# per pair, without loop control, chunk loads or the per-row and per-tile work.
+def slots_per_pair(d: int, form: str) -> int:
+    """form: 'f32' (the shifted difference form: d sub, d fma, 1 fma for the
+    exponent, 1 add, 1 exp2), 'f64' (the same in fp64 up to the exponent: d
+    add, d + 1 fma in fp64, 1 conversion, then the exp2 and the fp32 add),
+    'local' (the tile-local expanded form of the sparse half-step: 1 mul and
+    d - 1 fma for the dot product, the exp2, 1 fma into the tile sum)."""
+    if form == "f32":
+        return (2 * d + 2) + 4
+    if form == "f64":
+        return 2 * (2 * d + 1) + 2 + 1 + 4
+    if form == "local":
+        return (d + 1) + 4
+    raise ValueError(form)
 
 
-def slots_per_pair(d: int, fp64: bool) -> int:
-    """fp32 issue slots per pair: the fp32 loop's ops_per_pair, or for the
-    fp64 loop its 2d + 2 fp64-class instructions (d adds, d fmas, 1 exponent
-    fma, 1 conversion; two slots each at half the fp32 lane rate) plus the
-    fp32 add."""
-    return 2 * (2 * d + 2) + 1 if fp64 else ops_per_pair(d)
+SLOT_TEXT = {
+    "f32": "2d+2 fp32 VALU + 1 exp2 (4 slots) per pair",
+    "f64": "2d+1 fp64 VALU (2 slots each) + 1 fp64-to-fp32 conversion (2) + 1 fp32 add + 1 exp2 (4) per pair",
+    "local": "d+1 fp32 VALU + 1 exp2 (4 slots) per pair",
+}
 
 
 KERNEL_SOURCES = ("dense.hip", "pairloop.h", "rowfinal.h", "internal.h", "launch_plan.h")
@@ -220,9 +231,9 @@ def note(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def alu_roofline(kname, pairs, ms, d, fp64, workload):
+def alu_roofline(kname, pairs, ms, d, form, workload):
     rate = pairs / (ms * 1e-3)
-    slots = slots_per_pair(d, fp64)
+    slots = slots_per_pair(d, form)
     achieved = rate * slots
     return {
         "bound": "alu",
@@ -232,8 +243,7 @@ def alu_roofline(kname, pairs, ms, d, fp64, workload):
         "frac": achieved / FP32_VALU_PEAK,
         "traffic": pmc_traffic(kname, workload),
         "ops_per_pair": slots,
-        "ops": (f"fp32 issue slots per pair: {slots} fp32 VALU" if not fp64 else
-                f"fp32 issue slots per pair: {2 * d + 2} fp64 VALU at 2 slots + 1 fp32 add"),
+        "ops": f"{slots} fp32 issue slots per pair at d = {d}: " + SLOT_TEXT[form],
         "pair_peak": FP32_VALU_PEAK / slots,
         "kernel": kname,
     }
@@ -467,9 +477,10 @@ def main():
         else:
             kname = (f"k_lse_sparse<{c.d},true>" if multiscale else
                      f"k_lse_valu64<{c.d}>" if fp64 else f"k_lse_valu<{c.d},true>")
-            out["roofline"] = alu_roofline(kname, pairs, ms, c.d, fp64, args.workload)
+            form = "local" if multiscale else "f64" if fp64 else "f32"
+            out["roofline"] = alu_roofline(kname, pairs, ms, c.d, form, args.workload)
             # the same instruction mix measured by the probe kernels
-            name = "PAIR_F64" if fp64 else "PAIR_F32"
+            name = "PAIR_TILE_F32" if multiscale else "PAIR_F64" if fp64 else "PAIR_F32"
             pr = issue_rates((name,))
             out["issue_ceiling"] = {"probe": name, "pairs_per_s": pr[name]["pairs_per_s"],
                                     "kernel_over_probe": (pairs / (ms * 1e-3)) / pr[name]["pairs_per_s"]}

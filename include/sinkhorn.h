@@ -471,6 +471,10 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
  *   SINKHORN_PROBE_CVT_F32_F64    v_cvt_f32_f64 (the CVT probe also sums its
  *                                 results: 4 v_add_f32 per 4 conversions,
  *                                 not counted)
+ *   SINKHORN_PROBE_PAIR_TILE_F32  one pair of a tile-local expanded form:
+ *                                 v_mul_f32 + 2 v_fmac_f32 (scalar column
+ *                                 offsets), v_exp_f32, v_fmac_f32 (scalar
+ *                                 column weight); counts the 4 non-exp
  * Synchronizes `stream`. */
 #define SINKHORN_PROBE_FMA_F32 0
 #define SINKHORN_PROBE_EXP_F32 1
@@ -482,6 +486,7 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
 #define SINKHORN_PROBE_FMAC_F32 7
 #define SINKHORN_PROBE_ADD_F64 8
 #define SINKHORN_PROBE_CVT_F32_F64 9
+#define SINKHORN_PROBE_PAIR_TILE_F32 10
 int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stream, double* lane_instr_per_s,
                               double* pairs_per_s, double* kernel_ms);
 

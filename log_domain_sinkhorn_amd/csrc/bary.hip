@@ -224,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void k_bary_sparse(BaryArgs A, const floa
                                                          const float* __restrict__ H) {
   __shared__ BaryLds<D> L;
   const int64_t tile = A.order ? (int64_t)A.order[blockIdx.x] : (int64_t)blockIdx.x;
+  if (tile < 0) return;                                         // an empty slot (uniform)
   if (!SHIFT && A.fallback && A.tile_flag[tile] == 0) return;  // uniform
   const int64_t I = tile * kRowsPerTile / A.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -322,15 +323,17 @@ void dense_bary(sinkhorn_problem* p, BaryArgs& A) {
 
 template <int D>
 void sparse_bary(sinkhorn_problem* p, BaryArgs& A) {
-  const dim3 grid((uint32_t)A.tiles);
-  A.order = heavy_first(p, A.ptr, A.tiles, A.B);
+  int64_t slots = A.tiles;
+  A.order = heavy_first(p, A.ptr, A.tiles, A.B, (p->m + A.B - 1) / A.B, &slots);
+  const dim3 grid = grid1(slots, kThreads);
   if (A.shift_pot) {
     hipLaunchKernelGGL((k_bary_sparse<D, true>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H);
     SK_LAUNCH_CHECK();
     BaryArgs E = A;
     E.fallback = 1;
     E.order = nullptr;
-    hipLaunchKernelGGL((k_bary_sparse<D, false>), grid, dim3(kThreads), 0, p->stream, E, E.Q, E.H);
+    hipLaunchKernelGGL((k_bary_sparse<D, false>), grid1(A.tiles, kThreads), dim3(kThreads), 0,
+                       p->stream, E, E.Q, E.H);
   } else {
     hipLaunchKernelGGL((k_bary_sparse<D, false>), grid, dim3(kThreads), 0, p->stream, A, A.Q, A.H);
   }

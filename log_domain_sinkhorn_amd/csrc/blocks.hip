@@ -31,6 +31,100 @@
 namespace sk {
 namespace {
 
+// Tile-local frame, static part: one wave per block of B points; the block
+// centre o = (lo + hi) / 2 per axis (fp32), every point's offset from it and
+// the block radius max |y_j - o| (rounded up by 2^-20 relative), zero offsets
+// on padding up to the side's stride.
+template <int D>
+__global__ __launch_bounds__(64) void k_frame_build(const float* __restrict__ soa, int64_t stride,
+                                                    int64_t count, int32_t B, float* __restrict__ off,
+                                                    float* __restrict__ ctr) {
+  const int64_t J = blockIdx.x;
+  const int64_t s = J * B;
+  const int64_t e = s + B < count ? s + B : count;
+  const int64_t ep = s + B < stride ? s + B : stride;
+  float l[D], h[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    l[k] = FLT_MAX;
+    h[k] = -FLT_MAX;
+  }
+  for (int64_t i = s + threadIdx.x; i < e; i += 64)
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      const float v = soa[k * stride + i];
+      l[k] = fminf(l[k], v);
+      h[k] = fmaxf(h[k], v);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      l[k] = fminf(l[k], __shfl_xor(l[k], o, 64));
+      h[k] = fmaxf(h[k], __shfl_xor(h[k], o, 64));
+    }
+  float c[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) c[k] = 0.5f * (l[k] + h[k]);
+  float r2 = 0.0f;
+  for (int64_t i = s + threadIdx.x; i < ep; i += 64) {
+    float q = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      const float v = i < e ? soa[k * stride + i] - c[k] : 0.0f;
+      off[k * stride + i] = v;
+      q = __builtin_fmaf(v, v, q);
+    }
+    r2 = fmaxf(r2, q);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) r2 = fmaxf(r2, __shfl_xor(r2, o, 64));
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ctr[J * 4 + k] = k < D ? c[k] : 0.0f;
+    ctr[J * 4 + 3] = sqrtf(r2) * (1.0f + 0x1p-20f);
+  }
+}
+
+// h'_j = log2 w_j + lam pot_j - kappa ||off_j||^2 in fp64 (-inf for a
+// massless point).
+__device__ __forceinline__ double frame_term(const float* __restrict__ off, int64_t stride, int32_t d,
+                                             const float* __restrict__ w,
+                                             const float* __restrict__ pot, int64_t i, double lam,
+                                             double kappa) {
+  const double wi = (double)w[i];
+  if (!(wi > 0.0)) return -INFINITY;
+  double q = 0.0;
+  for (int k = 0; k < d; ++k) {
+    const double v = (double)off[k * stride + i];
+    q = fma(v, v, q);
+  }
+  return log2(wi) + lam * (double)pot[i] - kappa * q;
+}
+
+// Tile-local frame, per half-step: one wave per block; m_J = max h'_j and the
+// weights 2^(h'_j - m_J) (fp64 exp2, rounded once to fp32); 0 on padding and
+// for every point of a block without mass (m_J = -inf).
+__global__ __launch_bounds__(64) void k_frame_weights(const float* __restrict__ off, int64_t stride,
+                                                      int32_t d, const float* __restrict__ w,
+                                                      const float* __restrict__ pot, int64_t count,
+                                                      int32_t B, double lam, double kappa,
+                                                      float* __restrict__ wt, double* __restrict__ mx) {
+  const int64_t J = blockIdx.x;
+  const int64_t s = J * B;
+  const int64_t e = s + B < count ? s + B : count;
+  const int64_t ep = s + B < stride ? s + B : stride;
+  double m = -INFINITY;
+  for (int64_t i = s + threadIdx.x; i < e; i += 64)
+    m = fmax(m, frame_term(off, stride, d, w, pot, i, lam, kappa));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+  const bool live = m > -INFINITY;
+  for (int64_t i = s + threadIdx.x; i < ep; i += 64)
+    wt[i] = (live && i < e) ? (float)exp2(frame_term(off, stride, d, w, pot, i, lam, kappa) - m) : 0.0f;
+  if (threadIdx.x == 0) mx[J] = m;
+}
+
 // One wave per block: min / max of each axis and the max weight.
 __global__ __launch_bounds__(64) void k_block_static(const float* __restrict__ soa, int64_t stride,
                                                      int32_t d, const float* __restrict__ w,
@@ -232,8 +326,130 @@ struct SparseArgs {
   int32_t* tile_flag;      // [tiles] tiles left for the exact recompute
   const int32_t* order;    // [tiles] tile of each workgroup (heaviest first), or null: in order
   int32_t fallback;        // 1: exact recompute of the flagged tiles only
+  // shifted mode, tile-local expanded form (null off: every tile in the
+  // difference form)
+  const float* off;        // [D][qstride] column offsets from their block centres
+  const float* wt;         // [qstride] column weights 2^(h'_j - m_J)
+  const float* ctr;        // [column blocks][4] block centre (first D slots) and radius
+  const double* mx;        // [column blocks] m_J
+  float two_kappa;         // 2 kappa
+  double kappa;            // kappa (fp64)
+  float guard2;            // a tile takes the expanded form when every row of the
+                           // wave has |x_i - o_J|^2 R_J^2 <= guard2 = (kGuard / 2 kappa)^2
   RowFinal F;
 };
+
+// Largest |exponent| of a pair term in the expanded form, 2 kappa |x - o| R:
+// keeps 128 weighted terms of a tile far inside the fp32 range and the
+// exponent's rounding near 2^-24 of it.
+constexpr float kGuard = 96.0f;
+
+// v * 2^s for an fp64 exponent s clamped to [-1000, 1000]: the fraction
+// through v_exp_f32, the integer part exactly by v_ldexp.
+__device__ __forceinline__ float scale2(float v, double s) {
+  s = fmin(fmax(s, -1000.0), 1000.0);
+  const double fl = floor(s);
+  return ldexpf(v * ex2((float)(s - fl)), (int)fl);
+}
+
+// The tile (row tile against column block J, chunks c0 .. c1) in the
+// tile-local expanded form, for the lane's kR rows; false (nothing done) when
+// some row of the wave fails the range guard. With a_i = x_i - o_J and the
+// column offsets dy_j = y_j - o_J,
+//   z_ij - c_i = log2 w'_j + 2 kappa a_i . dy_j + s_i,
+//   s_i = m_J - kappa ||a_i||^2 - c_i,  w'_j = 2^(h'_j - m_J),
+// so a pair costs 1 mul + 2 fma (d = 3) for the dot product, the exp2 and
+// 1 fma into the tile sum T_i = sum_j w'_j 2^(2 kappa a_i . dy_j); the tile
+// then adds T_i 2^(s_i) to the row sum (fp64 exponent). A tile whose
+// contribution passes 2^64 raises the row's shift to it first.
+template <int D>
+__device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
+                                           const float* __restrict__ off,
+                                           const float* __restrict__ wt, const float (&x)[kR][D],
+                                           int64_t J, int64_t c0, int64_t c1) {
+  const float* ct = A.ctr + J * 4;
+  float o[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) o[k] = ct[k];
+  const float RJ = ct[3];
+  float a[kR][D];
+  double n2[kR];
+  bool ok = true;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    float q = 0.0f;
+    double qd = 0.0;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      a[r][k] = x[r][k] - o[k];
+      q = __builtin_fmaf(a[r][k], a[r][k], q);
+      qd = fma((double)a[r][k], (double)a[r][k], qd);
+    }
+    n2[r] = qd;
+    ok = ok && (q * (RJ * RJ) <= A.guard2);
+  }
+  if (__builtin_amdgcn_ballot_w64(!ok) != 0) return false;
+  float ap[kR][D];
+#pragma unroll
+  for (int r = 0; r < kR; ++r)
+#pragma unroll
+    for (int k = 0; k < D; ++k) ap[r][k] = a[r][k] * A.two_kappa;
+  float T0[kR], T1[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) T0[r] = T1[r] = 0.0f;
+  const int64_t qs = A.qstride;
+  const float* oc = off + c0 * kChunk;
+  const float* wc = wt + c0 * kChunk;
+  for (int64_t c = c0; c < c1; ++c, oc += kChunk, wc += kChunk) {
+    float dv[D][kChunk];
+    float wv[kChunk];
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) dv[k][jj] = oc[k * qs + jj];
+#pragma unroll
+    for (int jj = 0; jj < kChunk; ++jj) wv[jj] = wc[jj];
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) {
+        float pz = ap[r][D - 1] * dv[D - 1][jj];
+#pragma unroll
+        for (int k = D - 2; k >= 0; --k) pz = __builtin_fmaf(ap[r][k], dv[k][jj], pz);
+        if (jj & 1)
+          T1[r] = __builtin_fmaf(wv[jj], ex2(pz), T1[r]);
+        else
+          T0[r] = __builtin_fmaf(wv[jj], ex2(pz), T0[r]);
+      }
+  }
+  const double mJ = A.mx[J];
+  const double kd = -(double)A.nkappa;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const float T = T0[r] + T1[r];
+    const double sr = mJ - A.kappa * n2[r] - R.Md[r];
+    const float cval = scale2(T, sr);
+    const bool big = !(cval <= kBig);
+    if (__builtin_amdgcn_ballot_w64(big) != 0) {
+      if (big) {
+        // the row's shift moves up to this tile's scale (the same fp32 u /
+        // fp64 kappa u pair as the difference form keeps)
+        const double t = sr + (double)__log2f(T);
+        const float un = (float)((R.Md[r] + t) / kd);
+        const double Mn = kd * (double)un;
+        const double delta = Mn - R.Md[r];
+        R.u[r] = un;
+        R.Md[r] = Mn;
+        R.S[r] = scale2(R.S[r], -delta) + scale2(T, sr - delta);
+      } else {
+        R.S[r] += cval;
+      }
+    } else {
+      R.S[r] += cval;
+    }
+  }
+  return true;
+}
 
 // Workgroup = one 128-row tile of row block I = tile * 128 / B; its waves
 // share out the admitted column blocks (or, for an empty list, all column
@@ -245,9 +461,12 @@ struct SparseArgs {
 // residual partial, so the order leaves the results unchanged.
 template <int D, bool SHIFT>
 __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const float* __restrict__ Q,
-                                                        const float* __restrict__ H) {
+                                                        const float* __restrict__ H,
+                                                        const float* __restrict__ off,
+                                                        const float* __restrict__ wt) {
   __shared__ TileLds L;
   const int64_t tile = A.order ? (int64_t)A.order[blockIdx.x] : (int64_t)blockIdx.x;
+  if (tile < 0) return;                                         // an empty slot (uniform)
   if (!SHIFT && A.fallback && A.tile_flag[tile] == 0) return;  // uniform
   const int64_t I = tile * kRowsPerTile / A.B;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -270,6 +489,9 @@ __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const flo
       const int64_t J = A.idx[q];
       const int64_t c0 = J * cpb;
       const int64_t c1 = c0 + cpb < A.nchunks ? c0 + cpb : A.nchunks;
+      if constexpr (SHIFT) {
+        if (A.off != nullptr && local_tile<D>(R, A, off, wt, x, J, c0, c1)) continue;
+      }
       pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, c0, c1, 1);
     }
   } else {
@@ -374,6 +596,49 @@ void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, B
   SK_LAUNCH_CHECK();
 }
 
+void LocalFrame::release() {
+  dev_free(off);
+  dev_free(wt);
+  dev_free(ctr);
+  dev_free(mx);
+  off = wt = ctr = nullptr;
+  mx = nullptr;
+  nb = 0;
+}
+
+void frame_build(sinkhorn_problem* p, const Side& s, int32_t B, LocalFrame& out) {
+  if (p->d > 3) fail(SINKHORN_ERR_UNSUPPORTED, "tile-local frames need d <= 3");
+  if (B < 1) fail(SINKHORN_ERR_INVALID_ARG, "block size must be >= 1");
+  out.release();
+  out.nb = (s.count + B - 1) / B;
+  out.B = B;
+  out.stride = s.padded;
+  out.off = (float*)dev_alloc(sizeof(float) * p->d * s.padded);
+  out.wt = (float*)dev_alloc(sizeof(float) * s.padded);
+  out.ctr = (float*)dev_alloc(sizeof(float) * 4 * out.nb);
+  out.mx = (double*)dev_alloc(sizeof(double) * out.nb);
+  switch (p->d) {
+#define SK_FRAME(Dv)                                                                              \
+  case Dv:                                                                                        \
+    hipLaunchKernelGGL(k_frame_build<Dv>, grid1(out.nb, 64), dim3(64), 0, p->stream, s.soa,      \
+                       s.padded, s.count, B, out.off, out.ctr);                                   \
+    break;
+    SK_FRAME(1)
+    SK_FRAME(2)
+    SK_FRAME(3)
+#undef SK_FRAME
+  }
+  SK_LAUNCH_CHECK();
+}
+
+void frame_weights(sinkhorn_problem* p, const Side& s, const float* pot, double eps, LocalFrame& fr) {
+  const double lam = kLog2e / eps;
+  const double kappa = p->scale * kLog2e / eps;
+  hipLaunchKernelGGL(k_frame_weights, grid1(fr.nb, 64), dim3(64), 0, p->stream, fr.off, fr.stride,
+                     p->d, s.w, pot, s.count, fr.B, lam, kappa, fr.wt, fr.mx);
+  SK_LAUNCH_CHECK();
+}
+
 // Row-major list of the tiles admitted between `rows` and `cols` summaries.
 // ptr [rows.nb + 1] is always written; idx only when the count fits cap.
 // Returns the count. counts_tmp must hold rows.nb + 1 int64.
@@ -450,29 +715,90 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr) {
 }
 
 // ---------------------------------------------------------------- sparse half-step
-// Sort key of each row tile: the bit length of its row block's list of
-// admitted column blocks (lists within a factor of two share a key; an
-// empty list means a pass over all columns: the largest key, 63).
-constexpr int kKeyBits = 6;
-__global__ __launch_bounds__(256) void k_tile_keys(const int64_t* __restrict__ ptr, int64_t tiles,
-                                                   int32_t B, uint32_t* __restrict__ key,
-                                                   int32_t* __restrict__ val) {
+// Work of each row tile: its row block's list length in column blocks, or
+// all `dense` column blocks for an empty list (a dense pass).
+__global__ __launch_bounds__(256) void k_tile_work(const int64_t* __restrict__ ptr, int64_t tiles,
+                                                   int32_t B, int64_t dense,
+                                                   int64_t* __restrict__ work) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= tiles) return;
   const int64_t I = t * kRowsPerTile / B;
   const int64_t c = ptr[I + 1] - ptr[I];
-  key[t] = c > 0 ? 64u - (uint32_t)__clzll((unsigned long long)c) : (1u << kKeyBits) - 1;
+  work[t] = c > 0 ? c : (dense > 0 ? dense : 1);
+}
+
+// Sort key of each row tile: its XCD segment (row tiles cut, in order, into
+// kXcds runs of about equal total work) above the bit length of its work
+// (lists within a factor of two share a length key), so that a descending
+// sort puts segment 0 first and, within a segment, the longest lists first;
+// counts the tiles of each segment.
+constexpr int kXcds = 8;
+constexpr int kLenBits = 6;
+constexpr int kKeyBits = kLenBits + 3;
+__global__ __launch_bounds__(256) void k_tile_keys(const int64_t* __restrict__ work,
+                                                   const int64_t* __restrict__ pre, int64_t tiles,
+                                                   uint32_t* __restrict__ key,
+                                                   int32_t* __restrict__ val,
+                                                   uint32_t* __restrict__ seg_count) {
+  __shared__ uint32_t cnt[kXcds];
+  if (threadIdx.x < kXcds) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < tiles) {
+    const int64_t total = pre[tiles - 1];
+    const int64_t before = pre[t] - work[t];
+    int64_t seg = before * kXcds / total;
+    if (seg > kXcds - 1) seg = kXcds - 1;
+    const uint32_t len = 64u - (uint32_t)__clzll((unsigned long long)work[t]);
+    key[t] = ((uint32_t)(kXcds - 1 - seg) << kLenBits) | len;
+    val[t] = (int32_t)t;
+    atomicAdd(&cnt[seg], 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < kXcds && cnt[threadIdx.x]) atomicAdd(&seg_count[threadIdx.x], cnt[threadIdx.x]);
+}
+
+// Length keys alone (the fallback order when the XCD runs are very uneven).
+__global__ __launch_bounds__(256) void k_len_only(const int64_t* __restrict__ work, int64_t tiles,
+                                                  uint32_t* __restrict__ key,
+                                                  int32_t* __restrict__ val) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= tiles) return;
+  key[t] = 64u - (uint32_t)__clzll((unsigned long long)work[t]);
   val[t] = (int32_t)t;
 }
 
-// The row tiles of a sparse half-step, longest lists first by powers of two
-// and in tile order within a power (a stable radix sort of the bit lengths):
-// the rare lists tens of times the average no longer start late and run
-// alone at the end, while the workgroups running together still take
-// neighbouring row blocks, whose column blocks overlap in L2. Measured at
-// 2^24: 798 ms per launch in tile order, 778 ms with the exact lengths
-// sorted, 765 ms so; on verified lists 446, 460 and 446 ms.
-const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B) {
+struct SegTable {
+  int64_t start[kXcds];
+  int64_t count[kXcds];
+};
+
+// Workgroup w runs on XCD w mod kXcds (workgroups are dealt to the XCDs in
+// turn), so slot w takes the (w / kXcds)-th tile of segment w mod kXcds, or
+// -1 (the workgroup exits) past the segment's end.
+__global__ __launch_bounds__(256) void k_xcd_slots(const int32_t* __restrict__ sorted, SegTable S,
+                                                   int64_t slots, int32_t* __restrict__ out) {
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= slots) return;
+  const int seg = (int)(w % kXcds);
+  const int64_t i = w / kXcds;
+  out[w] = i < S.count[seg] ? sorted[S.start[seg] + i] : -1;
+}
+
+// Dispatch order of the row tiles of a sparse launch. The tiles are cut, in
+// row order, into one run per XCD of about equal total work, and each XCD
+// takes its own run, longest lists first by powers of two and in tile order
+// within a power (a stable radix sort). Neighbouring row blocks (Morton
+// order) share most of their column blocks, so a run keeps its column reads
+// in its own XCD's L2; the rare lists tens of times the average start first
+// instead of running alone at the end. Returns the slot table (a tile index
+// or -1 per workgroup) and its length in *slots; a table more than twice the
+// tile count (very uneven runs) falls back to one sequence, the longest lists
+// first, with *slots = tiles. Synchronizes the stream (the segment counts).
+// Measured at 2^24 before the XCD runs: 798 ms per launch in tile order,
+// 778 ms with the exact lengths sorted, 765 ms by powers of two.
+const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B,
+                           int64_t dense_work, int64_t* slots) {
   hipStream_t st = p->stream;
   if (tiles > p->order_cap) {
     SK_HIP(hipStreamSynchronize(st));
@@ -489,8 +815,31 @@ const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tile
   uint32_t* kout = p->order_key + p->order_cap;
   int32_t* vin = p->order_val;
   int32_t* vout = p->order_val + p->order_cap;
-  hipLaunchKernelGGL(k_tile_keys, grid1(((tiles + 255) / 256), 256), dim3(256), 0, st, ptr, tiles,
-                     B, kin, vin);
+  struct Tmp {
+    int64_t* work = nullptr;
+    uint32_t* cnt = nullptr;
+    void* scan = nullptr;
+    ~Tmp() {
+      dev_free(work);
+      dev_free(cnt);
+      dev_free(scan);
+    }
+  } tmp;
+  tmp.work = (int64_t*)dev_alloc(sizeof(int64_t) * 2 * tiles);
+  int64_t* pre = tmp.work + tiles;
+  tmp.cnt = (uint32_t*)dev_alloc(sizeof(uint32_t) * kXcds);
+  zero_i32((int32_t*)tmp.cnt, kXcds, st);
+  hipLaunchKernelGGL(k_tile_work, grid1(((tiles + 255) / 256), 256), dim3(256), 0, st, ptr, tiles, B,
+                     dense_work, tmp.work);
+  SK_LAUNCH_CHECK();
+  size_t scan_bytes = 0;
+  SK_HIP(rocprim::inclusive_scan(nullptr, scan_bytes, tmp.work, pre, (size_t)tiles,
+                                 rocprim::plus<int64_t>(), st));
+  tmp.scan = dev_alloc(scan_bytes);
+  SK_HIP(rocprim::inclusive_scan(tmp.scan, scan_bytes, tmp.work, pre, (size_t)tiles,
+                                 rocprim::plus<int64_t>(), st));
+  hipLaunchKernelGGL(k_tile_keys, grid1(((tiles + 255) / 256), 256), dim3(256), 0, st, tmp.work, pre,
+                     tiles, kin, vin, tmp.cnt);
   SK_LAUNCH_CHECK();
   size_t need = 0;
   SK_HIP(rocprim::radix_sort_pairs_desc(nullptr, need, kin, kout, vin, vout, (size_t)tiles, 0,
@@ -505,18 +854,48 @@ const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tile
   }
   SK_HIP(rocprim::radix_sort_pairs_desc(p->order_temp, need, kin, kout, vin, vout, (size_t)tiles, 0,
                                         kKeyBits, st));
-  return vout;
+  uint32_t cnt[kXcds];
+  SK_HIP(hipMemcpyAsync(cnt, tmp.cnt, sizeof(cnt), hipMemcpyDeviceToHost, st));
+  SK_HIP(hipStreamSynchronize(st));
+  SegTable S;
+  int64_t most = 0, at = 0;
+  for (int k = 0; k < kXcds; ++k) {
+    S.start[k] = at;
+    S.count[k] = cnt[k];
+    at += cnt[k];
+    most = cnt[k] > most ? cnt[k] : most;
+  }
+  if (at != tiles) fail(SINKHORN_ERR_HIP, "tile segments do not add up");
+  const int64_t n_slots = most * kXcds;
+  if (n_slots > 2 * tiles) {
+    // one sequence: the length keys alone, longest first (segments ignored)
+    *slots = tiles;
+    hipLaunchKernelGGL(k_len_only, grid1(((tiles + 255) / 256), 256), dim3(256), 0, st, tmp.work,
+                       tiles, kin, vin);
+    SK_LAUNCH_CHECK();
+    SK_HIP(rocprim::radix_sort_pairs_desc(p->order_temp, need, kin, kout, vin, vout, (size_t)tiles, 0,
+                                          kKeyBits, st));
+    return vout;
+  }
+  // the slot table reuses the key buffers (2 * order_cap entries >= n_slots)
+  int32_t* out = (int32_t*)p->order_key;
+  hipLaunchKernelGGL(k_xcd_slots, grid1(((n_slots + 255) / 256), 256), dim3(256), 0, st, vout, S,
+                     n_slots, out);
+  SK_LAUNCH_CHECK();
+  *slots = n_slots;
+  return out;
 }
 
+// `tiles` workgroups: one per entry of A.order when given, else per row tile.
 template <int D>
 void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool shifted,
                    const ProfEv& pe) {
   if (shifted)
     hipExtLaunchKernelGGL((k_lse_sparse<D, true>), grid1(tiles, kThreads), dim3(kThreads), 0, p->stream,
-                          pe.start, pe.stop, 0, A, A.Q, A.H);
+                          pe.start, pe.stop, 0, A, A.Q, A.H, A.off, A.wt);
   else
     hipExtLaunchKernelGGL((k_lse_sparse<D, false>), grid1(tiles, kThreads), dim3(kThreads), 0,
-                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H);
+                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H, A.off, A.wt);
   SK_LAUNCH_CHECK();
 }
 
@@ -545,13 +924,35 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
   A.inv_kappa = (float)(1.0 / kappa);
   A.tile_flag = p->tile_flag;
   A.fallback = 0;
-  A.order = heavy_first(p, ptr, tiles, B);
+  int64_t slots = tiles;
+  A.order = heavy_first(p, ptr, tiles, B, (cols.count + B - 1) / B, &slots);
+  A.off = nullptr;
+  A.wt = nullptr;
+  A.ctr = nullptr;
+  A.mx = nullptr;
+  A.two_kappa = (float)(2.0 * kappa);
+  A.kappa = kappa;
+  {
+    const double g = (double)kGuard / (2.0 * kappa);
+    A.guard2 = (float)(g * g);
+  }
+  if (shifted && hs.frame && hs.cols_pot) {
+    LocalFrame& fr = *hs.frame;
+    if (fr.B != B || fr.stride != cols.padded || fr.nb != (cols.count + B - 1) / B)
+      fail(SINKHORN_ERR_INVALID_ARG, "tile-local frame built for another side or block size");
+    frame_weights(p, cols, hs.cols_pot, hs.eps, fr);
+    A.off = fr.off;
+    A.wt = fr.wt;
+    A.ctr = fr.ctr;
+    A.mx = fr.mx;
+  }
   A.F = make_rowfinal(p, hs);
   auto launch = [&](const SparseArgs& a, bool sh, const ProfEv& pe) {
+    const int64_t wg = a.order ? slots : tiles;
     switch (p->d) {
-      case 1: launch_sparse<1>(p, a, tiles, sh, pe); break;
-      case 2: launch_sparse<2>(p, a, tiles, sh, pe); break;
-      case 3: launch_sparse<3>(p, a, tiles, sh, pe); break;
+      case 1: launch_sparse<1>(p, a, wg, sh, pe); break;
+      case 2: launch_sparse<2>(p, a, wg, sh, pe); break;
+      case 3: launch_sparse<3>(p, a, wg, sh, pe); break;
       default: fail(SINKHORN_ERR_UNSUPPORTED, "sparse half-steps need d <= 3");
     }
   };
@@ -584,6 +985,12 @@ void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_
 using namespace sk;
 
 namespace {
+
+// A tile-local frame released when the call returns or throws.
+struct FrameHold {
+  LocalFrame f;
+  ~FrameHold() { f.release(); }
+};
 
 template <class F>
 int guarded(F&& body) {
@@ -661,6 +1068,12 @@ int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, 
     reset_nonfinite(p);
     HalfStep hs{&p->X, &p->Y, p->Y.H, f_out, f_prev, nullptr, eps, eps, f_prev && row_l1};
     hs.shift_pot = f_prev;  // the previous potential estimates the row shifts
+    FrameHold fr;
+    if (f_prev) {  // shifted mode: the tile-local frame of the columns for this call
+      frame_build(p, p->Y, B, fr.f);
+      hs.frame = &fr.f;
+      hs.cols_pot = g;
+    }
     sparse_halfstep(p, hs, B, ptr, idx, 0.0);
     double v = 0.0;
     int32_t bad = 0;
@@ -685,6 +1098,12 @@ int sinkhorn_sparse_halfstep_g(sinkhorn_problem* p, double eps, const float* f, 
     reset_nonfinite(p);
     HalfStep hs{&p->Y, &p->X, p->X.H, g_out, g_prev, nullptr, eps, eps, g_prev && col_l1};
     hs.shift_pot = g_prev;
+    FrameHold fr;
+    if (g_prev) {
+      frame_build(p, p->X, B, fr.f);
+      hs.frame = &fr.f;
+      hs.cols_pot = f;
+    }
     sparse_halfstep(p, hs, B, ptr, idx, 0.0);
     double v = 0.0;
     int32_t bad = 0;

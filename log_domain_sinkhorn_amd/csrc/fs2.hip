@@ -389,7 +389,10 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
   int32_t* perm[2] = {nullptr, nullptr};
   float* pot[10] = {};
   BlockSummary sx, sy;
+  LocalFrame lx, ly;
   auto cleanup = [&]() {
+    lx.release();
+    ly.release();
     free_side(Xs);
     free_side(Ys);
     free_side(Cx);
@@ -594,6 +597,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
     // ---- fine loop on the block-pair mask
     block_static(p, Xs, P.B, sx);
     block_static(p, Ys, P.B, sy);
+    frame_build(p, Xs, P.B, lx);
+    frame_build(p, Ys, P.B, ly);
     TileList rowL, colL;
     VerifiedList rowV, colV;
     VerifyScratch vscr;
@@ -637,7 +642,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       // sparse f-step at (f, g); its fused residual is R_A,row of (f, g)
       reset_nonfinite(p);
       prep_column_term(p, Ys, gs[cg], eps, Ys.H);
-      sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true, fs[cf]},
+      sparse_halfstep(p, HalfStep{&Xs, &Ys, Ys.H, fs[1 - cf], fs[cf], nullptr, eps, eps, true, fs[cf],
+                                  &ly, gs[cg]},
                       P.B, rptr, ridx, row_pairs);
       int32_t bad = 0;
       read_reduction(p, &Rrow, &bad);
@@ -646,7 +652,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       Rcol = NAN;
       if (Rrow + omega <= P.tol) {
         prep_column_term(p, Xs, fs[cf], eps, Xs.H);
-        sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true, gs[cg]},
+        sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], gs[cg], nullptr, eps, eps, true, gs[cg],
+                                    &lx, fs[cf]},
                         P.B, cptr, cidx, col_pairs);
         read_reduction(p, &Rcol, nullptr);
         R.pairs_evaluated += col_pairs;
@@ -662,7 +669,8 @@ extern "C" int sinkhorn_solve_multiscale(sinkhorn_problem* p, const sinkhorn_mul
       if (R.fine_updates >= P.max_fine) break;
       cf = 1 - cf;  // accept the f-step
       prep_column_term(p, Xs, fs[cf], eps, Xs.H);
-      sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false, gs[cg]},
+      sparse_halfstep(p, HalfStep{&Ys, &Xs, Xs.H, gs[1 - cg], nullptr, nullptr, eps, eps, false, gs[cg],
+                                  &lx, fs[cf]},
                       P.B, cptr, cidx, col_pairs);
       R.pairs_evaluated += col_pairs;
       cg = 1 - cg;

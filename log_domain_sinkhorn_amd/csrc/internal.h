@@ -93,6 +93,8 @@ struct Ctl {
   int32_t pad;
 };
 
+struct LocalFrame;
+
 // Per-launch description of one dense half-step "rows against columns".
 struct HalfStep {
   const Side* rows;
@@ -107,6 +109,11 @@ struct HalfStep {
   // previous potential of the row side: enables the shifted pair loop (its
   // fixed per-row shift is estimated from it); null runs the exact loop
   const float* shift_pot = nullptr;
+  // sparse half-steps in shifted mode: the column side's tile-local frame
+  // (built for the same B) and the column side's potentials, from which the
+  // frame's weights are refreshed; null runs every tile in the difference form
+  LocalFrame* frame = nullptr;
+  const float* cols_pot = nullptr;
 };
 
 // One dense half-step with fp64 potentials, column terms and pair
@@ -259,6 +266,26 @@ struct BlockSummary {
   void release();
 };
 void block_static(sinkhorn_problem* p, const Side& s, int32_t B, BlockSummary& out);
+
+// Tile-local frame of one side for the shifted sparse half-steps (d <= 3).
+// Static per side and B: the centre o_J of each block's bounding box, the
+// radius R_J of the block about it, and every point's offset y_j - o_J
+// (fp32). Refreshed before each half-step from the side's potentials, in
+// fp64: h'_j = log2 w_j + lam pot_j - kappa ||y_j - o_J||^2, its block maximum
+// m_J and the point's weight 2^(h'_j - m_J) rounded to fp32 (0 for massless
+// points and padding; m_J = -inf for a block without mass).
+struct LocalFrame {
+  int64_t nb = 0;          // blocks
+  int32_t B = 0;           // points per block
+  int64_t stride = 0;      // the side's padded count
+  float* off = nullptr;    // [d][stride] offsets from the block centre, 0 on padding
+  float* wt = nullptr;     // [stride] weights, 0 on padding
+  float* ctr = nullptr;    // [nb][4]: o_J in the first d slots, R_J in slot 3
+  double* mx = nullptr;    // [nb] m_J
+  void release();
+};
+void frame_build(sinkhorn_problem* p, const Side& s, int32_t B, LocalFrame& out);
+void frame_weights(sinkhorn_problem* p, const Side& s, const float* pot, double eps, LocalFrame& fr);
 void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, BlockSummary& s);
 int64_t screen_tiles(sinkhorn_problem* p, const BlockSummary& rows, const BlockSummary& cols,
                      double eps, double delta_rel, int64_t* ptr, int32_t* idx, int64_t cap,
@@ -267,9 +294,11 @@ int64_t count_empty_rows(sinkhorn_problem* p, const int64_t* ptr, int64_t nr);
 void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const int64_t* ptr,
                      const int32_t* idx, double pairs);
 void check_csr(sinkhorn_problem* p, const int64_t* ptr, int64_t nr, const int32_t* idx, int64_t nc);
-// row tiles (128 rows) of a sparse list with block size B, longest lists
-// first (device array of `tiles` indices in the handle's scratch)
-const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B);
+// dispatch order of the row tiles (128 rows) of a sparse list with block
+// size B: one entry per workgroup (*slots of them), a tile index or -1, in the
+// handle's scratch; one run of tiles per XCD, longest lists first in each
+const int32_t* heavy_first(sinkhorn_problem* p, const int64_t* ptr, int64_t tiles, int32_t B,
+                           int64_t dense_work, int64_t* slots);
 
 // api.hip: annealed dense solve between two sides (X rows, Y columns), f/g
 // in/out, F/G scratch pairs; stall_window > 0 adds the stall stop rule

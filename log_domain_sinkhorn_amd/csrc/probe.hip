@@ -11,7 +11,11 @@
 //        row shift folded into the first), v_fma_f32 (exponent with the
 //        scalar column term), v_exp_f32, v_add_f32 (sum): 8 VALU + 1 exp;
 //   fp64: 3 v_add_f64, 3 v_fma_f64, v_fma_f64, v_cvt_f32_f64, v_exp_f32,
-//        v_add_f32: 9 VALU + 1 exp.
+//        v_add_f32: 9 VALU + 1 exp;
+//   tile-local expanded form (the column's offset from its block origin
+//        and its weight in SGPRs): v_mul_f32 + 2 v_fmac_f32 (the row's
+//        scaled offset dotted with the column's), v_exp_f32, v_fmac_f32
+//        (weighted sum): 4 VALU + 1 exp.
 // No result is meaningful; the probes only take time. A transcendental's
 // result is read no earlier than three instructions after it is written.
 #include "internal.h"
@@ -208,6 +212,41 @@ __device__ __forceinline__ void body_pair_f64(const double (&x)[2][3], const dou
         [y0] "s"(y0), [y1] "s"(y1), [y2] "s"(y2), [h] "s"(h));
 }
 
+// One pair of the tile-local expanded form for each of 4 rows against one
+// column: p = a2 dy2 + a1 dy1 + a0 dy0 (the row's scaled offsets a in
+// VGPRs, the column's offsets dy in SGPRs), T += w exp2(p) (w in an SGPR).
+__device__ __forceinline__ void body_pair_tile(const float (&a)[4][3], float (&acc)[4], float dy0,
+                                               float dy1, float dy2, float w) {
+  float p[4];
+  asm volatile(
+      "v_mul_f32 %[p0], %[y2], %[a02]\n"
+      "v_mul_f32 %[p1], %[y2], %[a12]\n"
+      "v_mul_f32 %[p2], %[y2], %[a22]\n"
+      "v_mul_f32 %[p3], %[y2], %[a32]\n"
+      "v_fmac_f32 %[p0], %[y1], %[a01]\n"
+      "v_fmac_f32 %[p1], %[y1], %[a11]\n"
+      "v_fmac_f32 %[p2], %[y1], %[a21]\n"
+      "v_fmac_f32 %[p3], %[y1], %[a31]\n"
+      "v_fmac_f32 %[p0], %[y0], %[a00]\n"
+      "v_fmac_f32 %[p1], %[y0], %[a10]\n"
+      "v_fmac_f32 %[p2], %[y0], %[a20]\n"
+      "v_fmac_f32 %[p3], %[y0], %[a30]\n"
+      "v_exp_f32 %[p0], %[p0]\n"
+      "v_exp_f32 %[p1], %[p1]\n"
+      "v_exp_f32 %[p2], %[p2]\n"
+      "v_exp_f32 %[p3], %[p3]\n"
+      "v_fmac_f32 %[s0], %[w], %[p0]\n"
+      "v_fmac_f32 %[s1], %[w], %[p1]\n"
+      "v_fmac_f32 %[s2], %[w], %[p2]\n"
+      "v_fmac_f32 %[s3], %[w], %[p3]\n"
+      : [p0] "=&v"(p[0]), [p1] "=&v"(p[1]), [p2] "=&v"(p[2]), [p3] "=&v"(p[3]),
+        [s0] "+v"(acc[0]), [s1] "+v"(acc[1]), [s2] "+v"(acc[2]), [s3] "+v"(acc[3])
+      : [a00] "v"(a[0][0]), [a01] "v"(a[0][1]), [a02] "v"(a[0][2]), [a10] "v"(a[1][0]),
+        [a11] "v"(a[1][1]), [a12] "v"(a[1][2]), [a20] "v"(a[2][0]), [a21] "v"(a[2][1]),
+        [a22] "v"(a[2][2]), [a30] "v"(a[3][0]), [a31] "v"(a[3][1]), [a32] "v"(a[3][2]),
+        [y0] "s"(dy0), [y1] "s"(dy1), [y2] "s"(dy2), [w] "s"(w));
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out, int32_t iters,
                                                         float s0, float s1, float s2, float s3,
@@ -247,6 +286,13 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out
     }
     for (int32_t i = 0; i < iters; ++i)
       body_pair_f32<KIND == SINKHORN_PROBE_PAIR_F32>(x, u, acc, -1.0f, s0, s1, s2, s3);
+  } else if constexpr (KIND == SINKHORN_PROBE_PAIR_TILE_F32) {
+    float a[4][3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) a[r][k] = t + 0.25f * (float)(r + k);
+    for (int32_t i = 0; i < iters; ++i) body_pair_tile(a, acc, s0, s1, s2, s3);
   } else if constexpr (KIND == SINKHORN_PROBE_PAIR_F64) {
     double x[2][3], u[2];
     float a2[2] = {acc[0], acc[1]};
@@ -279,6 +325,7 @@ void probe_counts(int32_t kind, double* valu, double* pairs) {
     case SINKHORN_PROBE_FMAC_F32: *valu = 4; *pairs = 0; break;
     case SINKHORN_PROBE_ADD_F64: *valu = 4; *pairs = 0; break;
     case SINKHORN_PROBE_CVT_F32_F64: *valu = 4; *pairs = 0; break;
+    case SINKHORN_PROBE_PAIR_TILE_F32: *valu = 16; *pairs = 4; break;
     default: fail(SINKHORN_ERR_INVALID_ARG, "unknown probe kind");
   }
 }
@@ -324,6 +371,7 @@ extern "C" int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stre
           SK_PROBE(SINKHORN_PROBE_FMAC_F32)
           SK_PROBE(SINKHORN_PROBE_ADD_F64)
           SK_PROBE(SINKHORN_PROBE_CVT_F32_F64)
+          SK_PROBE(SINKHORN_PROBE_PAIR_TILE_F32)
 #undef SK_PROBE
         }
         SK_LAUNCH_CHECK();

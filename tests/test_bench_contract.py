@@ -27,8 +27,12 @@ def test_multiscale_options_are_refused_elsewhere():
     assert r.returncode == 2 and "workload (5) only" in r.stderr
 
 
-def test_ops_per_pair_counts_the_shifted_loop():
-    assert bench.ops_per_pair(3) == 8 and bench.ops_per_pair(1) == 4
+def test_slots_per_pair_count_each_pair_form():
+    # fp32 difference form: 8 VALU + exp2 at 4 slots; fp64: 7 fp64 VALU at 2,
+    # the conversion at 2, the add and the exp2; tile-local: 4 VALU + exp2
+    assert bench.slots_per_pair(3, "f32") == 12 and bench.slots_per_pair(1, "f32") == 8
+    assert bench.slots_per_pair(3, "f64") == 21
+    assert bench.slots_per_pair(3, "local") == 8 and bench.slots_per_pair(1, "local") == 6
 
 
 def test_traffic_records_match_their_kernel_and_sources(tmp_path, monkeypatch):

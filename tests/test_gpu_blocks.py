@@ -189,6 +189,37 @@ def test_sparse_halfsteps_match_oracle(sk, n, B, eps, prev):
         assert r is None and rc is None
 
 
+@pytest.mark.parametrize("offset", [0.0, 300.0, -300.0, "mixed"])
+@pytest.mark.parametrize("eps", [1e-2, 1e-3])
+def test_sparse_shifted_loop_matches_oracle_for_any_shift_estimate(sk, eps, offset):
+    """The shifted sparse loop takes most tiles in the tile-local expanded
+    form at these eps (the rest in the difference form). Its per-row shift
+    comes from the previous potential: a good estimate, one far too low (tile
+    sums pass 2^64: the shift moves up), one far too high (row sums underflow:
+    exact recompute of the tile) and a mixture must all give the oracle's
+    potentials within 1e-5 max(eps, |f|)."""
+    n, B = 16384, 128
+    x, y, a, b = _sorted_problem(5, n)
+    rng = np.random.default_rng(17)
+    f, g = _near_plan_potentials(n, eps, rng)
+    NB = n // B
+    delta = 1e-3 / NB
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    f_ref = oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B)
+    if offset == "mixed":
+        prev = f_ref + rng.choice([-300.0, 0.0, 300.0], n) * eps
+    else:
+        prev = f_ref + offset * eps
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        fo, _ = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)),
+                                    f_prev=_t(prev.astype(np.float32)))
+    got = fo.cpu().numpy().astype(np.float64)
+    err = np.abs(got - f_ref) / np.maximum(eps, np.abs(f_ref))
+    assert err.max() <= 1e-5, err.max()
+
+
 def _gauge_close(f, g, fr, gr, tol):
     """Potentials equal up to the common shift (f + c, g - c), which leaves the
     plan unchanged (FlashSinkhorn 2, §A.3) and which fp32 rounding walks."""
