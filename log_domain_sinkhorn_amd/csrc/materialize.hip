@@ -113,6 +113,15 @@ __global__ __launch_bounds__(256) void k_materialize_valu(
   }
 }
 
+// max of two floats in one v_max_f32: fmaxf would first copy each operand
+// through v_max(x, x) to quiet a signalling NaN, and neither operand can be
+// one here (MFMA results and maxima of them)
+__device__ __forceinline__ float vmax_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // MFMA path (9 <= d <= 63): A = selected x rows scaled by 2 kappa (slot d :=
 // 2 kappa, slot KP - 1 := the fp32 part P_hi of the row term), B = column
 // tile of y from LDS (slot d = H'_j, slot KP - 1 = 1), so the chain yields
@@ -202,9 +211,14 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
     if (more) gload(t + 1);
     v16f acc = (v16f){};
     const float* ys = &sY[buf][l32 * LW + kh];
+    float yb[KH];
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) yb[kk] = ys[2 * kk];
+    // all B fragments in flight before the first MFMA waits on one
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[kk], ys[2 * kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ax[kk], yb[kk], acc, 0, 0, 0);
     const int64_t j = t * 32 + l32;
     if (Tw) {
       float* Tj = Tw + j;
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(256) void k_materialize_mfma(
     }
     // padding columns give -inf (their column term), absent rows are not read
 #pragma unroll
-    for (int r = 0; r < 16; ++r) emax[r] = fmaxf(emax[r], acc[r]);
+    for (int r = 0; r < 16; ++r) emax[r] = vmax_f32(emax[r], acc[r]);
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
