@@ -287,7 +287,13 @@ int sinkhorn_verify_tiles(sinkhorn_problem* p, double eps, const float* f, const
 /* Sparse f-step on a row-major tile list (FlashSinkhorn 2, §3.2: log-sum-exp
  * over admitted tiles only; a block with no admitted tile takes a dense
  * update). Same outputs as sinkhorn_halfstep_f, with the residual (when
- * f_prev and row_l1 are given) taken over the same support. */
+ * f_prev and row_l1 are given) taken over the same support. With f_prev the
+ * rows carry shifts from it and each admitted tile is evaluated about its
+ * column block's bounding-box centre (per-column weights and per-tile scales
+ * in fp64, the pair terms in fp32; a tile whose rows lie too far from the
+ * block for the fp32 range takes the plain difference form): the call then
+ * holds 16 B of device memory per column point and 24 B per column block
+ * until it returns. Synchronizes the handle's stream. */
 int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, int32_t B,
                                const int64_t* ptr, const int32_t* idx, float* f_out,
                                const float* f_prev, double* row_l1);
@@ -415,8 +421,9 @@ int sinkhorn_barycentric(sinkhorn_problem* p, double eps, const float* g, const 
 /* The same on the block mask (FlashSinkhorn 2, §A.4, masked gradient): row
  * block I of B stored points averages over the columns of its admitted tiles
  * (ptr/idx as from sinkhorn_block_screen; all columns for a block with none).
- * B a multiple of 128 (at most 1024), d <= 3. Asynchronous on the handle's
- * stream (the tile-list check synchronizes it first). */
+ * B a multiple of 128 (at most 1024), d <= 3. The launches are asynchronous
+ * on the handle's stream; before them the tile-list check and the dispatch
+ * plan (the list lengths per XCD run) synchronize it. */
 int sinkhorn_sparse_barycentric(sinkhorn_problem* p, double eps, const float* g,
                                 const float* f_hint, int32_t B, const int64_t* ptr,
                                 const int32_t* idx, float* T, float* grad);
