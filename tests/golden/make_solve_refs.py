@@ -27,6 +27,9 @@ CASES = {
     "w3_n1500_tol": (3, 1500, 1800, dict(eps_start=0.05, eps_target=0.05, tol=1e-3, max_iters=5000), "mean"),
     # the full 20000 x 20000 workload (a few hours of fp64 numpy on a few cores)
     "w2_full_tol": (2, None, None, dict(eps_start=1.0, eps_target=1e-3, tol=1e-3, max_iters=5000), "one"),
+    # the full 50000 x 60000, d = 50 workload, a fixed budget of 10 iterations
+    # (about 12 minutes of fp64 numpy per iteration on 8 cores)
+    "w3_full_fixed10": (3, None, None, dict(eps_start=0.05, eps_target=0.05, fixed_iters=10), "mean"),
 }
 
 

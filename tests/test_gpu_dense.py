@@ -261,8 +261,10 @@ def _potentials_close(f, g, ref, eps, name):
 
 
 SOLVE_GOLDENS = ["w1_full_fixed200", "w2_n1000_tol", "w4_n1000_tol", "w3_n1500_tol"]
-if os.path.exists(os.path.join(GOLDEN, "solve_w2_full_tol.npz")):
-    SOLVE_GOLDENS.append("w2_full_tol")
+# full-size goldens (hours of fp64 numpy to write)
+for _name in ("w2_full_tol", "w3_full_fixed10"):
+    if os.path.exists(os.path.join(GOLDEN, f"solve_{_name}.npz")):
+        SOLVE_GOLDENS.append(_name)
 
 
 @pytest.mark.parametrize("name", SOLVE_GOLDENS)
