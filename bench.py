@@ -91,14 +91,19 @@ def slots_per_pair(d: int, form: str) -> int:
     """form: 'f32' (the shifted difference form: d sub, d fma, 1 fma for the
     exponent, 1 add, 1 exp2), 'f64' (the same in fp64 up to the exponent: d
     add, d + 1 fma in fp64, 1 conversion, then the exp2 and the fp32 add),
-    'local' (the tile-local expanded form of the sparse half-step: 1 mul and
-    d - 1 fma for the dot product, the exp2, 1 fma into the tile sum)."""
+    'split' (the precise dense default: the squared distance in fp32, the
+    integer column term minus the integer row shift, 1 fma for the exponent,
+    the exp2 and 1 fma of the column weight into the sum), 'local' (the
+    tile-local expanded form of the sparse half-step: 1 mul and d - 1 fma for
+    the dot product, the exp2, 1 fma into the tile sum)."""
     if form == "f32":
         return (2 * d + 2) + 4
     if form == "f64":
         return 2 * (2 * d + 1) + 2 + 1 + 4
     if form == "local":
         return (d + 1) + 4
+    if form == "split":
+        return (2 * d + 3) + 4
     raise ValueError(form)
 
 
@@ -106,6 +111,7 @@ SLOT_TEXT = {
     "f32": "2d+2 fp32 VALU + 1 exp2 (4 slots) per pair",
     "f64": "2d+1 fp64 VALU (2 slots each) + 1 fp64-to-fp32 conversion (2) + 1 fp32 add + 1 exp2 (4) per pair",
     "local": "d+1 fp32 VALU + 1 exp2 (4 slots) per pair",
+    "split": "2d+3 fp32 VALU (d sub, 1 mul + d-1 fma, 1 sub, 1 fma, 1 fma into the sum) + 1 exp2 (4 slots) per pair",
 }
 
 
@@ -194,7 +200,7 @@ def cpu_baseline(c, eps, scale=1.0, budget_s=12.0):
 
 
 PROBES = ("FMA_F32", "SUB_F32", "FMAC_F32", "EXP_F32", "PAIR_F32", "PAIR_F32_NOEXP", "FMA_F64",
-          "ADD_F64", "CVT_F32_F64", "PAIR_F64", "PAIR_TILE_F32")
+          "ADD_F64", "CVT_F32_F64", "PAIR_F64", "PAIR_TILE_F32", "PAIR_SPLIT_F32")
 
 
 def issue_rates(kinds=PROBES, iters=200000):
@@ -441,7 +447,8 @@ def main():
                      "one full iteration at eps_target from the solved potentials" if continuing
                      else "one solve from zero potentials to the stop test"
                      + (", then all plan rows materialized and min_row" if batch else "")),
-            "pair_arithmetic": "fp64 up to the exponent (d <= 3)" if fp64 else "fp32",
+            "pair_arithmetic": ("fp32 pair terms, integer/fp64 split of the column term and shift, fp64 "
+                                "potentials (d <= 3)") if fp64 else "fp32",
         },
         "wall_time_to_residual_s": wall,
         "halfsteps_timed": halfsteps,
@@ -477,11 +484,11 @@ def main():
                                "flops_per_pair": flops, "kernel": f"k_lse_mfma<{kp}>"}
         else:
             kname = (f"k_lse_sparse<{c.d},true>" if multiscale else
-                     f"k_lse_valu64<{c.d}>" if fp64 else f"k_lse_valu<{c.d},true>")
-            form = "local" if multiscale else "f64" if fp64 else "f32"
+                     f"k_lse_split<{c.d}>" if fp64 else f"k_lse_valu<{c.d},true>")
+            form = "local" if multiscale else "split" if fp64 else "f32"
             out["roofline"] = alu_roofline(kname, pairs, ms, c.d, form, args.workload)
             # the same instruction mix measured by the probe kernels
-            name = "PAIR_TILE_F32" if multiscale else "PAIR_F64" if fp64 else "PAIR_F32"
+            name = "PAIR_TILE_F32" if multiscale else "PAIR_SPLIT_F32" if fp64 else "PAIR_F32"
             pr = issue_rates((name,))
             out["issue_ceiling"] = {"probe": name, "pairs_per_s": pr[name]["pairs_per_s"],
                                     "kernel_over_probe": (pairs / (ms * 1e-3)) / pr[name]["pairs_per_s"]}

@@ -482,6 +482,11 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
  *                                 v_mul_f32 + 2 v_fmac_f32 (scalar column
  *                                 offsets), v_exp_f32, v_fmac_f32 (scalar
  *                                 column weight); counts the 4 non-exp
+ *   SINKHORN_PROBE_PAIR_SPLIT_F32 one pair of the dense split form: 3
+ *                                 v_sub_f32, v_mul_f32 + 2 v_fmac_f32,
+ *                                 v_sub_f32 (scalar integer column term),
+ *                                 v_fmac_f32, v_exp_f32, v_fmac_f32 (scalar
+ *                                 weight); counts the 9 non-exp
  * Synchronizes `stream`. */
 #define SINKHORN_PROBE_FMA_F32 0
 #define SINKHORN_PROBE_EXP_F32 1
@@ -494,6 +499,7 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
 #define SINKHORN_PROBE_ADD_F64 8
 #define SINKHORN_PROBE_CVT_F32_F64 9
 #define SINKHORN_PROBE_PAIR_TILE_F32 10
+#define SINKHORN_PROBE_PAIR_SPLIT_F32 11
 int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stream, double* lane_instr_per_s,
                               double* pairs_per_s, double* kernel_ms);
 

@@ -44,6 +44,15 @@ struct LseArgs64 {
   const double* shift_pot;  // previous potential of the row side (shifted mode)
   double shift_mul;         // shift c = pot * shift_mul + shift_add (log2 units)
   double shift_add;
+  // split form of the shifted pass: fp32 coordinates and the column term
+  // split into an integer and a weight (see pair_pass_split)
+  const float* P32;         // row side fp32 SoA [D][pstride]
+  const float* Q32;         // column side fp32 SoA [D][qstride]
+  const float* Hhi;
+  const float* Wlo;
+  float nkappa32;           // -kappa rounded to fp32
+  int64_t nchunks32;        // column chunks of kChunk points
+  int64_t cps32;            // chunks of kChunk per split
   RowFinal64 F;
 };
 
@@ -116,6 +125,75 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu64(LseArgs64 A, const doub
     Mp[(int64_t)gs * A.F.np + i] = mx;
     Sp[(int64_t)gs * A.F.np + i] = (float)sum;
   }
+}
+
+// Shifted pair kernel in split form (pair_pass_split): workgroup w works on
+// tile w / G, column split w % G; writes the same partials as k_lse_valu64
+// (fp64 shift, fp32 sum). A row's integer shift is its estimated LSE less the
+// headroom, rounded down; beyond 2^22 in magnitude the integer is rounded to
+// fp32 and the form keeps only fp32 accuracy.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_lse_split(LseArgs64 A, const float* __restrict__ Q,
+                                                       const float* __restrict__ Hhi,
+                                                       const float* __restrict__ Wlo,
+                                                       double* __restrict__ Mp,
+                                                       float* __restrict__ Sp) {
+  __shared__ TileLds L;
+  const int32_t gs = (int32_t)(blockIdx.x & (uint32_t)(A.G - 1));
+  const int64_t tile = blockIdx.x >> A.glog;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  float x[kR][D];
+  load_rows<D>(A.P32, A.pstride, tile, lane, x);
+  RowAccS R;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int64_t i = tile * kRowsPerTile + lane + 64 * r;
+    const double c = (i < A.F.np ? A.shift_pot[i] : 0.0) * A.shift_mul + A.shift_add;
+    R.c[r] = isfinite(c) ? (float)floor(c) : 0.0f;
+    R.S[r] = 0.0f;
+  }
+  const int64_t g0 = (int64_t)gs * A.cps32;
+  const int64_t g1 = g0 + A.cps32 < A.nchunks32 ? g0 + A.cps32 : A.nchunks32;
+  pair_pass_split<D>(R, Q, Hhi, Wlo, A.qstride, A.nkappa32, x, g0 + wave, g1, kW);
+  // merge the waves' (shift, sum) through LDS in wave order (as merge_waves64)
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    L.M[wave][lane + 64 * r] = (double)R.c[r];
+    L.S[wave][lane + 64 * r] = R.S[r];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t i = tile * kRowsPerTile + t;
+  if (t < kRowsPerTile && i < A.F.np) {
+    double mx = -DBL_MAX, sum = 0.0;
+#pragma unroll
+    for (int v = 0; v < kW; ++v) mx = fmax(mx, L.M[v][t]);
+#pragma unroll
+    for (int v = 0; v < kW; ++v) sum += (double)L.S[v][t] * (double)ex2((float)(L.M[v][t] - mx));
+    Mp[(int64_t)gs * A.F.np + i] = mx;
+    Sp[(int64_t)gs * A.F.np + i] = (float)sum;
+  }
+}
+
+// Split of the fp64 column term for the split form: Hhi = the integer below
+// H, Wlo = 2^(H - Hhi) (fp64 exp2, one rounding); |H| >= 2^22: Hhi = H rounded
+// to fp32 and Wlo the remainder's weight; padding and massless points: -inf
+// and 0.
+__global__ __launch_bounds__(256) void k_split_terms(const double* __restrict__ H, int64_t n,
+                                                     float* __restrict__ Hhi,
+                                                     float* __restrict__ Wlo) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  const double h = H[j];
+  if (!isfinite(h)) {
+    Hhi[j] = (float)h;
+    Wlo[j] = 0.0f;
+    return;
+  }
+  const double hi = fabs(h) < 0x1p22 ? floor(h) : (double)(float)h;
+  Hhi[j] = (float)hi;
+  Wlo[j] = (float)exp2(h - hi);
 }
 
 // Merge of the G splits of each row of a tile (as k_merge in dense.hip), the
@@ -224,9 +302,22 @@ void run64(sinkhorn_problem* p, const HalfStep64& hs, LseArgs64& A, double pairs
   if (shifted) {
     if (2 * (int64_t)A.G * hs.rows->count > p->part_cap)
       fail(SINKHORN_ERR_HIP, "partial buffer too small");
+    const Side& cols = *hs.cols;
+    // the column term's split for this half-step, then the split-form pass
+    // over the same G column splits, cut in chunks of kChunk columns
+    hipLaunchKernelGGL(k_split_terms, grid1((cols.padded + 255) / 256, 256), dim3(256), 0, p->stream,
+                       A.H, cols.padded, cols.Hhi, cols.Wlo);
+    SK_LAUNCH_CHECK();
+    A.P32 = hs.rows->soa;
+    A.Q32 = cols.soa;
+    A.Hhi = cols.Hhi;
+    A.Wlo = cols.Wlo;
+    A.nkappa32 = (float)A.nkappa;
+    A.nchunks32 = (cols.count + kChunk - 1) / kChunk;
+    A.cps32 = (A.nchunks32 + A.G - 1) / A.G;
     const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
-    hipExtLaunchKernelGGL((k_lse_valu64<D>), grid1(A.tiles * A.G, kThreads), dim3(kThreads), 0,
-                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H, A.Mp, A.Sp);
+    hipExtLaunchKernelGGL((k_lse_split<D>), grid1(A.tiles * A.G, kThreads), dim3(kThreads), 0,
+                          p->stream, pe.start, pe.stop, 0, A, A.Q32, A.Hhi, A.Wlo, A.Mp, A.Sp);
     SK_LAUNCH_CHECK();
     prof_done(p, SINKHORN_PROF_DENSE, pairs);
     hipLaunchKernelGGL(k_merge64<D>, grid1(A.tiles, kThreads), dim3(kThreads), 0, p->stream, A);

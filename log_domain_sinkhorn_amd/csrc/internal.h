@@ -83,6 +83,8 @@ struct Side {
   float* H = nullptr;      // [padded] column term of this side, -inf padding
   double* soa64 = nullptr; // [d][padded] coordinates widened to fp64 (fp64 half-steps, d <= 3)
   double* H64 = nullptr;   // [padded] fp64 column term, -inf padding (fp64 half-steps)
+  float* Hhi = nullptr;    // [padded] H64 split for the shifted precise loop: an integer ...
+  float* Wlo = nullptr;    // [padded] ... and the weight 2^(H64 - Hhi) (fp32)
   double wsum = 0.0;
 };
 

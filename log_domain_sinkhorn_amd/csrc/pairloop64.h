@@ -114,6 +114,87 @@ __device__ __forceinline__ void pair_pass64(RowAcc64& R, const double* __restric
   }
 }
 
+// The shifted pass in split form: the same sum as pair_pass64 with fp32
+// arithmetic whose only iterate-dependent roundings are small. The column
+// term is split as h_j = Hhi_j + log2 Wlo_j with Hhi_j an integer, and each
+// row's shift c_i is an integer: both are exact in fp32 below 2^22 in
+// magnitude, so t = Hhi_j - c_i is exact, and
+//   z_ij = RN(t - kappa32 q_ij),  q_ij = ||x_i - y_j||^2 in fp32,
+//   S_i += Wlo_j exp2(z_ij).
+// q and kappa32 (kappa rounded to fp32 once) depend on the clouds and eps
+// only, a fixed perturbation of the cost; what depends on the iterate is
+// rounded once, at the magnitude of z itself (small for the pairs that carry
+// the sum) or of Wlo (near 1). Per pair: d sub, 1 mul + (d - 1) fma, 1 sub,
+// 1 fma, the exp2 and 1 fma. A chunk whose sum passes 2^64 is redone with the
+// shift raised by the integer part of its largest exponent.
+struct RowAccS {
+  float S[kR];
+  float c[kR];  // integer shift (log2 units), exact in fp32
+};
+
+template <int D>
+__device__ __forceinline__ void pair_pass_split(RowAccS& R, const float* __restrict__ Q,
+                                                const float* __restrict__ Hhi,
+                                                const float* __restrict__ Wlo, int64_t qs, float nk,
+                                                const float (&x)[kR][D], int64_t c0, int64_t c1,
+                                                int64_t step) {
+  const float nkv = in_vgpr(nk);
+  const int32_t niter = c1 > c0 ? (int32_t)((c1 - c0 + step - 1) / step) : 0;
+  const float* qc = Q + c0 * kChunk;
+  const float* hc = Hhi + c0 * kChunk;
+  const float* wc = Wlo + c0 * kChunk;
+  const int64_t adv = step * kChunk;
+  for (int32_t it = 0; it < niter; ++it, qc += adv, hc += adv, wc += adv) {
+    float yv[D][kChunk];
+    float hv[kChunk];
+    float wv[kChunk];
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = qc[k * qs + jj];
+#pragma unroll
+    for (int jj = 0; jj < kChunk; ++jj) {
+      hv[jj] = hc[jj];
+      wv[jj] = wc[jj];
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      float z[kChunk];
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) {
+        float dd = x[r][0] - yv[0][jj];
+        float q = dd * dd;
+#pragma unroll
+        for (int k = 1; k < D; ++k) {
+          dd = x[r][k] - yv[k][jj];
+          q = __builtin_fmaf(dd, dd, q);
+        }
+        z[jj] = __builtin_fmaf(q, nkv, hv[jj] - R.c[r]);
+      }
+      float acc = wv[0] * ex2(z[0]);
+#pragma unroll
+      for (int jj = 1; jj < kChunk; ++jj) acc = __builtin_fmaf(wv[jj], ex2(z[jj]), acc);
+      const bool big = !(acc <= kBig);
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        float cm = z[0];
+#pragma unroll
+        for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
+        float delta = 0.0f;
+        if (big) {
+          delta = floorf(cm);  // an integer: c stays exact
+          R.c[r] += delta;
+        }
+        float acc2 = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < kChunk; ++jj) acc2 = __builtin_fmaf(wv[jj], ex2(z[jj] - delta), acc2);
+        R.S[r] = big ? __builtin_fmaf(R.S[r], ex2(-delta), acc2) : R.S[r] + acc;
+      } else {
+        R.S[r] += acc;
+      }
+    }
+  }
+}
+
 // Row maxima of z_ij = h_j - kappa ||x_i - y_j||^2 over the chunks c0, c0 +
 // step, ... < c1 (fp64), folded into mx.
 template <int D>

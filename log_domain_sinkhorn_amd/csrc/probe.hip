@@ -15,7 +15,11 @@
 //   tile-local expanded form (the column's offset from its block origin
 //        and its weight in SGPRs): v_mul_f32 + 2 v_fmac_f32 (the row's
 //        scaled offset dotted with the column's), v_exp_f32, v_fmac_f32
-//        (weighted sum): 4 VALU + 1 exp.
+//        (weighted sum): 4 VALU + 1 exp;
+//   split form (the precise dense default): 3 v_sub_f32, v_mul_f32 +
+//        2 v_fmac_f32 (squared distance), v_sub_f32 (integer column term
+//        minus the row's integer shift), v_fmac_f32 (exponent), v_exp_f32,
+//        v_fmac_f32 (weighted sum): 9 VALU + 1 exp.
 // No result is meaningful; the probes only take time. A transcendental's
 // result is read no earlier than three instructions after it is written.
 #include "internal.h"
@@ -247,6 +251,64 @@ __device__ __forceinline__ void body_pair_tile(const float (&a)[4][3], float (&a
         [y0] "s"(dy0), [y1] "s"(dy1), [y2] "s"(dy2), [w] "s"(w));
 }
 
+// One pair of the split form for each of 4 rows against one column (y0, y1,
+// y2, the integer column term h and the weight w in SGPRs; the rows' integer
+// shifts c and -kappa in VGPRs).
+__device__ __forceinline__ void body_pair_split(const float (&x)[4][3], const float (&c)[4],
+                                                float (&acc)[4], float nk, float y0, float y1,
+                                                float y2, float h, float w) {
+  float q[4], t[4];
+  asm volatile(
+      "v_sub_f32 %[q0], %[y0], %[x00]\n"
+      "v_sub_f32 %[q1], %[y0], %[x10]\n"
+      "v_sub_f32 %[q2], %[y0], %[x20]\n"
+      "v_sub_f32 %[q3], %[y0], %[x30]\n"
+      "v_mul_f32 %[q0], %[q0], %[q0]\n"
+      "v_mul_f32 %[q1], %[q1], %[q1]\n"
+      "v_mul_f32 %[q2], %[q2], %[q2]\n"
+      "v_mul_f32 %[q3], %[q3], %[q3]\n"
+      "v_sub_f32 %[t0], %[y1], %[x01]\n"
+      "v_sub_f32 %[t1], %[y1], %[x11]\n"
+      "v_sub_f32 %[t2], %[y1], %[x21]\n"
+      "v_sub_f32 %[t3], %[y1], %[x31]\n"
+      "v_fmac_f32 %[q0], %[t0], %[t0]\n"
+      "v_fmac_f32 %[q1], %[t1], %[t1]\n"
+      "v_fmac_f32 %[q2], %[t2], %[t2]\n"
+      "v_fmac_f32 %[q3], %[t3], %[t3]\n"
+      "v_sub_f32 %[t0], %[y2], %[x02]\n"
+      "v_sub_f32 %[t1], %[y2], %[x12]\n"
+      "v_sub_f32 %[t2], %[y2], %[x22]\n"
+      "v_sub_f32 %[t3], %[y2], %[x32]\n"
+      "v_fmac_f32 %[q0], %[t0], %[t0]\n"
+      "v_fmac_f32 %[q1], %[t1], %[t1]\n"
+      "v_fmac_f32 %[q2], %[t2], %[t2]\n"
+      "v_fmac_f32 %[q3], %[t3], %[t3]\n"
+      "v_sub_f32 %[t0], %[h], %[c0]\n"
+      "v_sub_f32 %[t1], %[h], %[c1]\n"
+      "v_sub_f32 %[t2], %[h], %[c2]\n"
+      "v_sub_f32 %[t3], %[h], %[c3]\n"
+      "v_fmac_f32 %[t0], %[q0], %[nk]\n"
+      "v_fmac_f32 %[t1], %[q1], %[nk]\n"
+      "v_fmac_f32 %[t2], %[q2], %[nk]\n"
+      "v_fmac_f32 %[t3], %[q3], %[nk]\n"
+      "v_exp_f32 %[t0], %[t0]\n"
+      "v_exp_f32 %[t1], %[t1]\n"
+      "v_exp_f32 %[t2], %[t2]\n"
+      "v_exp_f32 %[t3], %[t3]\n"
+      "v_fmac_f32 %[s0], %[w], %[t0]\n"
+      "v_fmac_f32 %[s1], %[w], %[t1]\n"
+      "v_fmac_f32 %[s2], %[w], %[t2]\n"
+      "v_fmac_f32 %[s3], %[w], %[t3]\n"
+      : [q0] "=&v"(q[0]), [q1] "=&v"(q[1]), [q2] "=&v"(q[2]), [q3] "=&v"(q[3]),
+        [t0] "=&v"(t[0]), [t1] "=&v"(t[1]), [t2] "=&v"(t[2]), [t3] "=&v"(t[3]),
+        [s0] "+v"(acc[0]), [s1] "+v"(acc[1]), [s2] "+v"(acc[2]), [s3] "+v"(acc[3])
+      : [x00] "v"(x[0][0]), [x01] "v"(x[0][1]), [x02] "v"(x[0][2]), [x10] "v"(x[1][0]),
+        [x11] "v"(x[1][1]), [x12] "v"(x[1][2]), [x20] "v"(x[2][0]), [x21] "v"(x[2][1]),
+        [x22] "v"(x[2][2]), [x30] "v"(x[3][0]), [x31] "v"(x[3][1]), [x32] "v"(x[3][2]),
+        [c0] "v"(c[0]), [c1] "v"(c[1]), [c2] "v"(c[2]), [c3] "v"(c[3]), [nk] "v"(nk),
+        [y0] "s"(y0), [y1] "s"(y1), [y2] "s"(y2), [h] "s"(h), [w] "s"(w));
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out, int32_t iters,
                                                         float s0, float s1, float s2, float s3,
@@ -293,6 +355,15 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out
 #pragma unroll
       for (int k = 0; k < 3; ++k) a[r][k] = t + 0.25f * (float)(r + k);
     for (int32_t i = 0; i < iters; ++i) body_pair_tile(a, acc, s0, s1, s2, s3);
+  } else if constexpr (KIND == SINKHORN_PROBE_PAIR_SPLIT_F32) {
+    float x[4][3], c[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c[r] = (float)(r + 3);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) x[r][k] = t + 0.25f * (float)(r + k);
+    }
+    for (int32_t i = 0; i < iters; ++i) body_pair_split(x, c, acc, -1.0f, s0, s1, s2, s3, 0.5f);
   } else if constexpr (KIND == SINKHORN_PROBE_PAIR_F64) {
     double x[2][3], u[2];
     float a2[2] = {acc[0], acc[1]};
@@ -326,6 +397,7 @@ void probe_counts(int32_t kind, double* valu, double* pairs) {
     case SINKHORN_PROBE_ADD_F64: *valu = 4; *pairs = 0; break;
     case SINKHORN_PROBE_CVT_F32_F64: *valu = 4; *pairs = 0; break;
     case SINKHORN_PROBE_PAIR_TILE_F32: *valu = 16; *pairs = 4; break;
+    case SINKHORN_PROBE_PAIR_SPLIT_F32: *valu = 36; *pairs = 4; break;
     default: fail(SINKHORN_ERR_INVALID_ARG, "unknown probe kind");
   }
 }
@@ -372,6 +444,7 @@ extern "C" int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stre
           SK_PROBE(SINKHORN_PROBE_ADD_F64)
           SK_PROBE(SINKHORN_PROBE_CVT_F32_F64)
           SK_PROBE(SINKHORN_PROBE_PAIR_TILE_F32)
+          SK_PROBE(SINKHORN_PROBE_PAIR_SPLIT_F32)
 #undef SK_PROBE
         }
         SK_LAUNCH_CHECK();

@@ -304,6 +304,8 @@ void side_init(sinkhorn_problem* p, Side& s, const float* pts, const float* w, i
       widen_f32(s.soa, (int64_t)d * s.padded, s.soa64, st);
       s.H64 = (double*)dev_alloc(sizeof(double) * s.padded);
       fill_f64(s.H64, s.padded, -INFINITY, st);
+      s.Hhi = (float*)dev_alloc(sizeof(float) * s.padded);
+      s.Wlo = (float*)dev_alloc(sizeof(float) * s.padded);
     }
   }
   // weight sum and finiteness of coordinates and weights
@@ -333,6 +335,8 @@ void side_free(Side& s) {
   dev_free(s.soa);
   dev_free(s.soa64);
   dev_free(s.H64);
+  dev_free(s.Hhi);
+  dev_free(s.Wlo);
   dev_free(s.rowmaj);
   dev_free(s.norm2);
   dev_free(s.w);

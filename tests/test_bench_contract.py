@@ -33,6 +33,7 @@ def test_slots_per_pair_count_each_pair_form():
     assert bench.slots_per_pair(3, "f32") == 12 and bench.slots_per_pair(1, "f32") == 8
     assert bench.slots_per_pair(3, "f64") == 21
     assert bench.slots_per_pair(3, "local") == 8 and bench.slots_per_pair(1, "local") == 6
+    assert bench.slots_per_pair(3, "split") == 13
 
 
 def test_traffic_records_match_their_kernel_and_sources(tmp_path, monkeypatch):

@@ -305,7 +305,10 @@ def test_solve_stops_at_the_oracles_iteration(sk, name):
 def test_small_eps_long_solve_matches_at_plan_level(sk):
     """eps = 1e-4 after 2229 iterations (|f| up to 0.045 = 450 eps): besides
     the potentials (checked above within 1e-3 eps), the oracle's exact marginal
-    residuals of the GPU potentials and the transport cost <pi, C> agree."""
+    residuals of the GPU potentials stay at the tolerance and the transport
+    cost <pi, C> moves no more than the potentials allow: every plan entry
+    changes by a factor within exp(+-(max|df| + max|dg|)/eps), so the cost
+    by at most that factor minus one (relative)."""
     ref = _golden("w4_n1000_tol")
     eps = float(ref["eps_target"])
     c, P = _golden_problem(sk, ref)
@@ -319,7 +322,9 @@ def test_small_eps_long_solve_matches_at_plan_level(sk):
     C = oracle.cost_rows(c.x, c.y, 1.0)
     cost = float((oracle.plan_rows(c.x, c.y, c.a, c.b, f, g, eps, 1.0) * C).sum())
     cost_ref = float((oracle.plan_rows(c.x, c.y, c.a, c.b, ref["f"], ref["g"], eps, 1.0) * C).sum())
-    assert cost == pytest.approx(cost_ref, rel=1e-6)
+    shift = (np.abs(f - ref["f"]).max() + np.abs(g - ref["g"]).max()) / eps
+    assert shift <= 2e-3, shift
+    assert abs(cost - cost_ref) <= math.expm1(shift) * cost_ref, (cost, cost_ref, shift)
 
 
 def test_solve_not_converged_returns_valid_potentials(sk):
