@@ -1,4 +1,4 @@
-// Dense online half-step for d <= 3 with fp64 pair arithmetic (pairloop64.h).
+// Dense online half-step for d <= 3 with fp64 solve state (pairloop64.h).
 //
 // FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport, §2.1: the
 // streaming tiled log-sum-exp over all pairs; §A.1 on how the precision of
@@ -7,9 +7,11 @@
 // are hundreds of log2 units, and an fp32 rounding of either, or of the
 // potentials themselves, moves each half-step by ~1e-5 eps in a way that
 // depends on the iterate; Sinkhorn's slow modes integrate that over thousands
-// of iterations. Here the potentials, the column terms and the pair
-// arithmetic up to the exponent are fp64; only the small shifted exponent is
-// rounded to fp32 for the exp2.
+// of iterations. Here the potentials, the column terms and the row shifts are
+// fp64. The shifted pass (pair_pass_split) keeps them exact in fp32 as an
+// integer plus a small remainder, so its pair arithmetic is fp32 with only
+// small iterate-dependent roundings; the exact two-pass recompute is fp64
+// throughout.
 //
 // Mapping as the fp32 kernels (dense.hip): a lane owns 2 rows, a workgroup of
 // 8 waves shares a 128-row tile, G workgroups per tile split the columns
@@ -51,8 +53,8 @@ struct LseArgs64 {
   const float* Hhi;
   const float* Wlo;
   float nkappa32;           // -kappa rounded to fp32
-  int64_t nchunks32;        // column chunks of kChunk points
-  int64_t cps32;            // chunks of kChunk per split
+  int64_t nchunks32;        // column chunks of kChunkS points
+  int64_t cps32;            // chunks of kChunkS per split
   RowFinal64 F;
 };
 
@@ -93,43 +95,10 @@ __device__ void exact_tile64(const LseArgs64& A, TileLds& L, int64_t tile, doubl
   merge_waves64(L, wave, lane, R, mx, sum);
 }
 
-// Shifted pair kernel: workgroup w works on tile w / G, column split w % G.
-// Q, H, Mp and Sp come as separate no-alias arguments (scalar column loads).
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_lse_valu64(LseArgs64 A, const double* __restrict__ Q,
-                                                        const double* __restrict__ H,
-                                                        double* __restrict__ Mp,
-                                                        float* __restrict__ Sp) {
-  __shared__ TileLds L;
-  const int32_t gs = (int32_t)(blockIdx.x & (uint32_t)(A.G - 1));
-  const int64_t tile = blockIdx.x >> A.glog;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  double x[kR][D];
-  load_rows64<D>(A.P, A.pstride, tile, lane, x);
-  double c[kR];
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int64_t i = tile * kRowsPerTile + lane + 64 * r;
-    c[r] = (i < A.F.np ? A.shift_pot[i] : 0.0) * A.shift_mul + A.shift_add;
-  }
-  RowAcc64 R;
-  init_shift64(R, c, A.inv_kappa);
-  const int64_t g0 = (int64_t)gs * A.cps;
-  const int64_t g1 = g0 + A.cps < A.nchunks ? g0 + A.cps : A.nchunks;
-  pair_pass64<D>(R, Q, H, A.qstride, A.nkappa, A.inv_kappa, x, g0 + wave, g1, kW);
-  double mx, sum;
-  merge_waves64(L, wave, lane, R, mx, sum);
-  const int64_t i = tile * kRowsPerTile + threadIdx.x;
-  if (threadIdx.x < kRowsPerTile && i < A.F.np) {
-    Mp[(int64_t)gs * A.F.np + i] = mx;
-    Sp[(int64_t)gs * A.F.np + i] = (float)sum;
-  }
-}
-
 // Shifted pair kernel in split form (pair_pass_split): workgroup w works on
-// tile w / G, column split w % G; writes the same partials as k_lse_valu64
-// (fp64 shift, fp32 sum). A row's integer shift is its estimated LSE less the
+// tile w / G, column split w % G, and writes the split's partials (fp64
+// shift, fp32 sum) for k_merge64. Q, Hhi, Wlo, Mp and Sp come as separate
+// no-alias arguments (scalar column loads). A row's integer shift is its estimated LSE less the
 // headroom, rounded down; beyond 2^22 in magnitude the integer is rounded to
 // fp32 and the form keeps only fp32 accuracy.
 template <int D>
@@ -272,7 +241,7 @@ template <int D>
 int64_t resident_slots64(sinkhorn_problem* p) {
   static const int per_cu = [] {
     int nb = 0;
-    SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_valu64<D>, kThreads, 0));
+    SK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_lse_split<D>, kThreads, 0));
     return nb > 0 ? nb : 1;
   }();
   return (int64_t)per_cu * p->num_cu;
@@ -304,7 +273,7 @@ void run64(sinkhorn_problem* p, const HalfStep64& hs, LseArgs64& A, double pairs
       fail(SINKHORN_ERR_HIP, "partial buffer too small");
     const Side& cols = *hs.cols;
     // the column term's split for this half-step, then the split-form pass
-    // over the same G column splits, cut in chunks of kChunk columns
+    // over the same G column splits, cut in chunks of kChunkS columns
     hipLaunchKernelGGL(k_split_terms, grid1((cols.padded + 255) / 256, 256), dim3(256), 0, p->stream,
                        A.H, cols.padded, cols.Hhi, cols.Wlo);
     SK_LAUNCH_CHECK();
@@ -313,7 +282,7 @@ void run64(sinkhorn_problem* p, const HalfStep64& hs, LseArgs64& A, double pairs
     A.Hhi = cols.Hhi;
     A.Wlo = cols.Wlo;
     A.nkappa32 = (float)A.nkappa;
-    A.nchunks32 = (cols.count + kChunk - 1) / kChunk;
+    A.nchunks32 = (cols.count + kChunkS - 1) / kChunkS;
     A.cps32 = (A.nchunks32 + A.G - 1) / A.G;
     const ProfEv pe = prof_events(p, SINKHORN_PROF_DENSE);
     hipExtLaunchKernelGGL((k_lse_split<D>), grid1(A.tiles * A.G, kThreads), dim3(kThreads), 0,

@@ -127,6 +127,11 @@ __device__ __forceinline__ void pair_pass64(RowAcc64& R, const double* __restric
 // the sum) or of Wlo (near 1). Per pair: d sub, 1 mul + (d - 1) fma, 1 sub,
 // 1 fma, the exp2 and 1 fma. A chunk whose sum passes 2^64 is redone with the
 // shift raised by the integer part of its largest exponent.
+// 16 columns per chunk. The chunk's D + 2 floats per column take 80 scalar
+// registers, which caps the kernel at 3 workgroups per CU; 8-column chunks
+// reach 4, but their per-chunk overhead makes the pass 3-7% slower on MI355X
+constexpr int kChunkS = 16;
+
 struct RowAccS {
   float S[kR];
   float c[kR];  // integer shift (log2 units), exact in fp32
@@ -140,28 +145,28 @@ __device__ __forceinline__ void pair_pass_split(RowAccS& R, const float* __restr
                                                 int64_t step) {
   const float nkv = in_vgpr(nk);
   const int32_t niter = c1 > c0 ? (int32_t)((c1 - c0 + step - 1) / step) : 0;
-  const float* qc = Q + c0 * kChunk;
-  const float* hc = Hhi + c0 * kChunk;
-  const float* wc = Wlo + c0 * kChunk;
-  const int64_t adv = step * kChunk;
+  const float* qc = Q + c0 * kChunkS;
+  const float* hc = Hhi + c0 * kChunkS;
+  const float* wc = Wlo + c0 * kChunkS;
+  const int64_t adv = step * kChunkS;
   for (int32_t it = 0; it < niter; ++it, qc += adv, hc += adv, wc += adv) {
-    float yv[D][kChunk];
-    float hv[kChunk];
-    float wv[kChunk];
+    float yv[D][kChunkS];
+    float hv[kChunkS];
+    float wv[kChunkS];
 #pragma unroll
     for (int k = 0; k < D; ++k)
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) yv[k][jj] = qc[k * qs + jj];
+      for (int jj = 0; jj < kChunkS; ++jj) yv[k][jj] = qc[k * qs + jj];
 #pragma unroll
-    for (int jj = 0; jj < kChunk; ++jj) {
+    for (int jj = 0; jj < kChunkS; ++jj) {
       hv[jj] = hc[jj];
       wv[jj] = wc[jj];
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-      float z[kChunk];
+      float z[kChunkS];
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) {
+      for (int jj = 0; jj < kChunkS; ++jj) {
         float dd = x[r][0] - yv[0][jj];
         float q = dd * dd;
 #pragma unroll
@@ -173,12 +178,12 @@ __device__ __forceinline__ void pair_pass_split(RowAccS& R, const float* __restr
       }
       float acc = wv[0] * ex2(z[0]);
 #pragma unroll
-      for (int jj = 1; jj < kChunk; ++jj) acc = __builtin_fmaf(wv[jj], ex2(z[jj]), acc);
+      for (int jj = 1; jj < kChunkS; ++jj) acc = __builtin_fmaf(wv[jj], ex2(z[jj]), acc);
       const bool big = !(acc <= kBig);
       if (__builtin_amdgcn_ballot_w64(big) != 0) {
         float cm = z[0];
 #pragma unroll
-        for (int jj = 1; jj < kChunk; ++jj) cm = fmaxf(cm, z[jj]);
+        for (int jj = 1; jj < kChunkS; ++jj) cm = fmaxf(cm, z[jj]);
         float delta = 0.0f;
         if (big) {
           delta = floorf(cm);  // an integer: c stays exact
@@ -186,7 +191,7 @@ __device__ __forceinline__ void pair_pass_split(RowAccS& R, const float* __restr
         }
         float acc2 = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < kChunk; ++jj) acc2 = __builtin_fmaf(wv[jj], ex2(z[jj] - delta), acc2);
+        for (int jj = 0; jj < kChunkS; ++jj) acc2 = __builtin_fmaf(wv[jj], ex2(z[jj] - delta), acc2);
         R.S[r] = big ? __builtin_fmaf(R.S[r], ex2(-delta), acc2) : R.S[r] + acc;
       } else {
         R.S[r] += acc;
