@@ -94,8 +94,12 @@ def slots_per_pair(d: int, form: str) -> int:
     'split' (the precise dense default: the squared distance in fp32, the
     integer column term minus the integer row shift, 1 fma for the exponent,
     the exp2 and 1 fma of the column weight into the sum), 'local' (the
-    tile-local expanded form of the sparse half-step: 1 mul and d - 1 fma for
-    the dot product, the exp2, 1 fma into the tile sum)."""
+    tile-local expanded form on the vector ALU: 1 mul and d - 1 fma for the
+    dot product, the exp2, 1 fma into the tile sum), 'local_mfma' (the same
+    form with the dot products on the matrix cores, as the sparse half-step
+    runs it: d K = 1 MFMA steps, 2d flops at the fp32 MFMA rate, which is
+    twice the fp32 lane rate, so d slots, plus the exp2 and 1 fma; the
+    matrix and vector pipes do not overlap on a SIMD, so the slots add)."""
     if form == "f32":
         return (2 * d + 2) + 4
     if form == "f64":
@@ -104,6 +108,8 @@ def slots_per_pair(d: int, form: str) -> int:
         return (d + 1) + 4
     if form == "split":
         return (2 * d + 3) + 4
+    if form == "local_mfma":
+        return d + 1 + 4
     raise ValueError(form)
 
 
@@ -112,6 +118,9 @@ SLOT_TEXT = {
     "f64": "2d+1 fp64 VALU (2 slots each) + 1 fp64-to-fp32 conversion (2) + 1 fp32 add + 1 exp2 (4) per pair",
     "local": "d+1 fp32 VALU + 1 exp2 (4 slots) per pair",
     "split": "2d+3 fp32 VALU (d sub, 1 mul + d-1 fma, 1 sub, 1 fma, 1 fma into the sum) + 1 exp2 (4 slots) per pair",
+    "local_mfma": ("d K = 1 steps of v_mfma_f32_4x4x1_16b_f32 (2d flops at the fp32 MFMA rate = d slots; "
+                   "the matrix and vector pipes do not overlap on a SIMD) + 1 exp2 (4 slots) + 1 fp32 fma "
+                   "per pair"),
 }
 
 
@@ -200,7 +209,7 @@ def cpu_baseline(c, eps, scale=1.0, budget_s=12.0):
 
 
 PROBES = ("FMA_F32", "SUB_F32", "FMAC_F32", "EXP_F32", "PAIR_F32", "PAIR_F32_NOEXP", "FMA_F64",
-          "ADD_F64", "CVT_F32_F64", "PAIR_F64", "PAIR_TILE_F32", "PAIR_SPLIT_F32")
+          "ADD_F64", "CVT_F32_F64", "PAIR_F64", "PAIR_TILE_F32", "PAIR_SPLIT_F32", "PAIR_TILE_MFMA")
 
 
 def issue_rates(kinds=PROBES, iters=200000):
@@ -485,10 +494,10 @@ def main():
         else:
             kname = (f"k_lse_sparse<{c.d},true>" if multiscale else
                      f"k_lse_split<{c.d}>" if fp64 else f"k_lse_valu<{c.d},true>")
-            form = "local" if multiscale else "split" if fp64 else "f32"
+            form = "local_mfma" if multiscale else "split" if fp64 else "f32"
             out["roofline"] = alu_roofline(kname, pairs, ms, c.d, form, args.workload)
             # the same instruction mix measured by the probe kernels
-            name = "PAIR_TILE_F32" if multiscale else "PAIR_SPLIT_F32" if fp64 else "PAIR_F32"
+            name = "PAIR_TILE_MFMA" if multiscale else "PAIR_SPLIT_F32" if fp64 else "PAIR_F32"
             pr = issue_rates((name,))
             out["issue_ceiling"] = {"probe": name, "pairs_per_s": pr[name]["pairs_per_s"],
                                     "kernel_over_probe": (pairs / (ms * 1e-3)) / pr[name]["pairs_per_s"]}

@@ -487,6 +487,12 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
  *                                 v_sub_f32 (scalar integer column term),
  *                                 v_fmac_f32, v_exp_f32, v_fmac_f32 (scalar
  *                                 weight); counts the 9 non-exp
+ *   SINKHORN_PROBE_PAIR_TILE_MFMA the same form with the cross terms on the
+ *                                 matrix cores, as the sparse half-step
+ *                                 runs it: per wave four 16 x 16 pair
+ *                                 blocks, each 3 v_mfma_f32_4x4x1_16b_f32
+ *                                 (one per coordinate), then v_exp_f32 and
+ *                                 v_fmac_f32 per pair; counts the 1 fmac
  * Synchronizes `stream`. */
 #define SINKHORN_PROBE_FMA_F32 0
 #define SINKHORN_PROBE_EXP_F32 1
@@ -500,6 +506,7 @@ int sinkhorn_profile_read(sinkhorn_problem* p, double* kernel_ms, int64_t* launc
 #define SINKHORN_PROBE_CVT_F32_F64 9
 #define SINKHORN_PROBE_PAIR_TILE_F32 10
 #define SINKHORN_PROBE_PAIR_SPLIT_F32 11
+#define SINKHORN_PROBE_PAIR_TILE_MFMA 12
 int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stream, double* lane_instr_per_s,
                               double* pairs_per_s, double* kernel_ms);
 

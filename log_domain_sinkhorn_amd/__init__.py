@@ -328,7 +328,7 @@ def morton_order(x: torch.Tensor, y: torch.Tensor):
 
 (PROBE_FMA_F32, PROBE_EXP_F32, PROBE_FMA_F64, PROBE_PAIR_F32, PROBE_PAIR_F32_NOEXP, PROBE_PAIR_F64,
  PROBE_SUB_F32, PROBE_FMAC_F32, PROBE_ADD_F64, PROBE_CVT_F32_F64, PROBE_PAIR_TILE_F32,
- PROBE_PAIR_SPLIT_F32) = range(12)
+ PROBE_PAIR_SPLIT_F32, PROBE_PAIR_TILE_MFMA) = range(13)
 FLAG_FP32_PAIRS = 1
 
 

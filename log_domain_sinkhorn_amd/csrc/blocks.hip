@@ -352,27 +352,41 @@ __device__ __forceinline__ float scale2(float v, double s) {
   return ldexpf(v * ex2((float)(s - fl)), (int)fl);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // The tile (row tile against column block J, chunks c0 .. c1) in the
 // tile-local expanded form, for the lane's kR rows; false (nothing done) when
 // some row of the wave fails the range guard. With a_i = x_i - o_J and the
 // column offsets dy_j = y_j - o_J,
 //   z_ij - c_i = log2 w'_j + 2 kappa a_i . dy_j + s_i,
 //   s_i = m_J - kappa ||a_i||^2 - c_i,  w'_j = 2^(h'_j - m_J),
-// so a pair costs 1 mul + 2 fma (d = 3) for the dot product, the exp2 and
-// 1 fma into the tile sum T_i = sum_j w'_j 2^(2 kappa a_i . dy_j); the tile
-// then adds T_i 2^(s_i) to the row sum (fp64 exponent). A tile whose
-// contribution passes 2^64 raises the row's shift to it first.
+// and the tile sum T_i = sum_j w'_j 2^(2 kappa a_i . dy_j) is then added as
+// T_i 2^(s_i) to the row sum (fp64 exponent). A tile whose contribution
+// passes 2^64 raises the row's shift to it first.
+//
+// The cross terms 2 kappa a_i . dy_j of a 16-column chunk and 16 rows are D
+// v_mfma_f32_4x4x1_16b_f32 steps, one per coordinate (on this part the
+// matrix and vector pipes do not overlap, so the K = 1 blocks, which spend no
+// cycles on a padded coordinate, are the cheapest shape). Block b pairs the
+// column quad b / 4 with the row quad b % 4; lane l = 4 b + j then holds
+// row l % 16 and columns 4 (l / 16) + v in its four results v. A pair costs
+// 3/4 of an MFMA cycle per lane-group, the exp2 and 1 fma. Each lane keeps
+// one partial T per 16-row block; at the end of the tile the four lane groups
+// of a row add their partials (two exchange steps), which leaves each lane
+// the whole T of rows l and l + 64, its two rows in RowAcc.
 template <int D>
 __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
                                            const float* __restrict__ off,
                                            const float* __restrict__ wt, const float (&x)[kR][D],
-                                           int64_t J, int64_t c0, int64_t c1) {
+                                           int lane, int64_t J, int64_t c0, int64_t c1) {
+  static_assert(kR == 2 && kRowsPerTile == 128 && kChunk == 16, "layout of the exchanges below");
+  constexpr int NB = kRowsPerTile / 16;
   const float* ct = A.ctr + J * 4;
   float o[D];
 #pragma unroll
   for (int k = 0; k < D; ++k) o[k] = ct[k];
   const float RJ = ct[3];
-  float a[kR][D];
+  float ap[kR][D];
   double n2[kR];
   bool ok = true;
 #pragma unroll
@@ -381,52 +395,75 @@ __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
     double qd = 0.0;
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      a[r][k] = x[r][k] - o[k];
-      q = __builtin_fmaf(a[r][k], a[r][k], q);
-      qd = fma((double)a[r][k], (double)a[r][k], qd);
+      const float a = x[r][k] - o[k];
+      q = __builtin_fmaf(a, a, q);
+      qd = fma((double)a, (double)a, qd);
+      ap[r][k] = a * A.two_kappa;
     }
     n2[r] = qd;
     ok = ok && (q * (RJ * RJ) <= A.guard2);
   }
   if (__builtin_amdgcn_ballot_w64(!ok) != 0) return false;
-  float ap[kR][D];
+  // row operand of block rb: 2 kappa a of row 16 rb + l % 16, which RowAcc
+  // keeps in lane 16 (rb % 4) + l % 16, slot rb / 4
+  float bop[NB][D];
 #pragma unroll
-  for (int r = 0; r < kR; ++r)
+  for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-    for (int k = 0; k < D; ++k) ap[r][k] = a[r][k] * A.two_kappa;
-  float T0[kR], T1[kR];
+    for (int k = 0; k < D; ++k) bop[rb][k] = __shfl(ap[rb / 4][k], 16 * (rb % 4) + (lane & 15), 64);
+  float T[NB];
 #pragma unroll
-  for (int r = 0; r < kR; ++r) T0[r] = T1[r] = 0.0f;
+  for (int rb = 0; rb < NB; ++rb) T[rb] = 0.0f;
+  const int g = lane >> 4;
   const int64_t qs = A.qstride;
-  const float* oc = off + c0 * kChunk;
-  const float* wc = wt + c0 * kChunk;
+  const float* oc = off + c0 * kChunk + 4 * g + (lane & 3);
+  const float* wc = wt + c0 * kChunk + 4 * g;
   for (int64_t c = c0; c < c1; ++c, oc += kChunk, wc += kChunk) {
-    float dv[D][kChunk];
-    float wv[kChunk];
+    float av[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k)
+    for (int k = 0; k < D; ++k) av[k] = oc[k * qs];
+    const v4f wv = *(const v4f*)wc;
+    v4f z[NB];
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) dv[k][jj] = oc[k * qs + jj];
+    for (int rb = 0; rb < NB; ++rb)
+      z[rb] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[0], bop[rb][0], (v4f){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-    for (int jj = 0; jj < kChunk; ++jj) wv[jj] = wc[jj];
+    for (int k = 1; k < D; ++k)
 #pragma unroll
-    for (int r = 0; r < kR; ++r)
+      for (int rb = 0; rb < NB; ++rb) z[rb] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[k], bop[rb][k], z[rb], 0, 0, 0);
 #pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) {
-        float pz = ap[r][D - 1] * dv[D - 1][jj];
+    for (int rb = 0; rb < NB; ++rb)
 #pragma unroll
-        for (int k = D - 2; k >= 0; --k) pz = __builtin_fmaf(ap[r][k], dv[k][jj], pz);
-        if (jj & 1)
-          T1[r] = __builtin_fmaf(wv[jj], ex2(pz), T1[r]);
-        else
-          T0[r] = __builtin_fmaf(wv[jj], ex2(pz), T0[r]);
-      }
+      for (int v = 0; v < 4; ++v) T[rb] = __builtin_fmaf(wv[v], ex2(z[rb][v]), T[rb]);
+  }
+  // lane groups g and g ^ 2 (lanes l and l ^ 32): keep the blocks rb with
+  // rb & 2 == g & 2 and add the partner's; then g and g ^ 1 (l ^ 16): keep
+  // rb & 1 == g & 1. What is left is block g (row l) and block g + 4 (row
+  // l + 64).
+  const bool g2 = (g & 2) != 0;
+  float keep[4], send[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      keep[2 * h + e] = g2 ? T[4 * h + 2 + e] : T[4 * h + e];
+      send[2 * h + e] = g2 ? T[4 * h + e] : T[4 * h + 2 + e];
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) keep[t] += __shfl_xor(send[t], 32, 64);
+  const bool g1 = (g & 1) != 0;
+  float Tr[kR];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float mine = g1 ? keep[2 * h + 1] : keep[2 * h];
+    const float other = g1 ? keep[2 * h] : keep[2 * h + 1];
+    Tr[h] = mine + __shfl_xor(other, 16, 64);
   }
   const double mJ = A.mx[J];
   const double kd = -(double)A.nkappa;
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-    const float T = T0[r] + T1[r];
+    const float T = Tr[r];
     const double sr = mJ - A.kappa * n2[r] - R.Md[r];
     const float cval = scale2(T, sr);
     const bool big = !(cval <= kBig);
@@ -490,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const flo
       const int64_t c0 = J * cpb;
       const int64_t c1 = c0 + cpb < A.nchunks ? c0 + cpb : A.nchunks;
       if constexpr (SHIFT) {
-        if (A.off != nullptr && local_tile<D>(R, A, off, wt, x, J, c0, c1)) continue;
+        if (A.off != nullptr && local_tile<D>(R, A, off, wt, x, lane, J, c0, c1)) continue;
       }
       pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, c0, c1, 1);
     }

@@ -309,6 +309,32 @@ __device__ __forceinline__ void body_pair_split(const float (&x)[4][3], const fl
         [y0] "s"(y0), [y1] "s"(y1), [y2] "s"(y2), [h] "s"(h), [w] "s"(w));
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The tile-local expanded form with the cross terms on the matrix cores, as
+// the sparse half-step runs it: four 16 x 16 pair blocks, each a chain of 3
+// v_mfma_f32_4x4x1_16b_f32 (one per coordinate), then per lane 4 v_exp_f32
+// and 4 v_fmac_f32 (the column weights) per block. The empty asm statements
+// make the row operands opaque to the compiler each iteration, so the chains
+// stay in the loop; they emit no instructions.
+__device__ __forceinline__ void body_pair_tile_mfma(float (&b)[4][3], float (&acc)[4],
+                                                    const float (&a)[3], const v4f& w) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) asm volatile("" : "+v"(b[rb][0]), "+v"(b[rb][1]), "+v"(b[rb][2]));
+  v4f z[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    z[rb] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[0], b[rb][0], (v4f){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+  for (int k = 1; k < 3; ++k)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) z[rb] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[k], b[rb][k], z[rb], 0, 0, 0);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[rb] = __builtin_fmaf(w[v], __builtin_amdgcn_exp2f(z[rb][v]), acc[rb]);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out, int32_t iters,
                                                         float s0, float s1, float s2, float s3,
@@ -355,6 +381,15 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe(float* __restrict__ out
 #pragma unroll
       for (int k = 0; k < 3; ++k) a[r][k] = t + 0.25f * (float)(r + k);
     for (int32_t i = 0; i < iters; ++i) body_pair_tile(a, acc, s0, s1, s2, s3);
+  } else if constexpr (KIND == SINKHORN_PROBE_PAIR_TILE_MFMA) {
+    float b[4][3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) b[r][k] = 4.0f * t + 0.125f * (float)(r + k);
+    const float a[3] = {0.5f * t, 0.25f - t, 0.125f + t};
+    const v4f w = {0.5f, 0.25f, 0.125f, 0.0625f};
+    for (int32_t i = 0; i < iters; ++i) body_pair_tile_mfma(b, acc, a, w);
   } else if constexpr (KIND == SINKHORN_PROBE_PAIR_SPLIT_F32) {
     float x[4][3], c[4];
 #pragma unroll
@@ -398,6 +433,8 @@ void probe_counts(int32_t kind, double* valu, double* pairs) {
     case SINKHORN_PROBE_CVT_F32_F64: *valu = 4; *pairs = 0; break;
     case SINKHORN_PROBE_PAIR_TILE_F32: *valu = 16; *pairs = 4; break;
     case SINKHORN_PROBE_PAIR_SPLIT_F32: *valu = 36; *pairs = 4; break;
+    // a wave's 4 blocks of 16 x 16 pairs: 16 pairs and 16 fmas per lane
+    case SINKHORN_PROBE_PAIR_TILE_MFMA: *valu = 16; *pairs = 16; break;
     default: fail(SINKHORN_ERR_INVALID_ARG, "unknown probe kind");
   }
 }
@@ -445,6 +482,7 @@ extern "C" int sinkhorn_probe_issue_rate(int32_t kind, int32_t iters, void* stre
           SK_PROBE(SINKHORN_PROBE_CVT_F32_F64)
           SK_PROBE(SINKHORN_PROBE_PAIR_TILE_F32)
           SK_PROBE(SINKHORN_PROBE_PAIR_SPLIT_F32)
+          SK_PROBE(SINKHORN_PROBE_PAIR_TILE_MFMA)
 #undef SK_PROBE
         }
         SK_LAUNCH_CHECK();

@@ -29,11 +29,14 @@ def test_multiscale_options_are_refused_elsewhere():
 
 def test_slots_per_pair_count_each_pair_form():
     # fp32 difference form: 8 VALU + exp2 at 4 slots; fp64: 7 fp64 VALU at 2,
-    # the conversion at 2, the add and the exp2; tile-local: 4 VALU + exp2
+    # the conversion at 2, the add and the exp2; tile-local: 4 VALU + exp2;
+    # tile-local on the matrix cores: d K = 1 MFMA steps (2d flops at twice
+    # the lane rate: d slots) + exp2 + 1 fma
     assert bench.slots_per_pair(3, "f32") == 12 and bench.slots_per_pair(1, "f32") == 8
     assert bench.slots_per_pair(3, "f64") == 21
     assert bench.slots_per_pair(3, "local") == 8 and bench.slots_per_pair(1, "local") == 6
     assert bench.slots_per_pair(3, "split") == 13
+    assert bench.slots_per_pair(3, "local_mfma") == 8 and bench.slots_per_pair(2, "local_mfma") == 7
 
 
 def test_traffic_records_match_their_kernel_and_sources(tmp_path, monkeypatch):

@@ -9,9 +9,11 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 # counted (non-transcendental) lane-instructions per pair of each pair probe
-PAIR_COUNTS = {"PAIR_F32": 8, "PAIR_F32_NOEXP": 8, "PAIR_F64": 9, "PAIR_TILE_F32": 4, "PAIR_SPLIT_F32": 9}
+PAIR_COUNTS = {"PAIR_F32": 8, "PAIR_F32_NOEXP": 8, "PAIR_F64": 9, "PAIR_TILE_F32": 4, "PAIR_SPLIT_F32": 9,
+               "PAIR_TILE_MFMA": 1}
 KINDS = ("FMA_F32", "EXP_F32", "FMA_F64", "PAIR_F32", "PAIR_F32_NOEXP", "PAIR_F64", "SUB_F32",
-         "FMAC_F32", "ADD_F64", "CVT_F32_F64", "PAIR_TILE_F32", "PAIR_SPLIT_F32")
+         "FMAC_F32", "ADD_F64", "CVT_F32_F64", "PAIR_TILE_F32", "PAIR_SPLIT_F32",
+         "PAIR_TILE_MFMA")
 
 
 @pytest.fixture(scope="module")
