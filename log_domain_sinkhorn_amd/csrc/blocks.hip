@@ -104,7 +104,11 @@ __device__ __forceinline__ double frame_term(const float* __restrict__ off, int6
 
 // Tile-local frame, per half-step: one wave per block; m_J = max h'_j and the
 // weights 2^(h'_j - m_J) (fp64 exp2, rounded once to fp32); 0 on padding and
-// for every point of a block without mass (m_J = -inf).
+// for every point of a block without mass (m_J = -inf). A block whose weights
+// span more than the normal fp32 range (some h'_j - m_J < -126: that weight
+// would be flushed or lose bits, and the range guard alone does not make its
+// terms negligible) gets m_J = NaN, which sends its tiles to the difference
+// form.
 __global__ __launch_bounds__(64) void k_frame_weights(const float* __restrict__ off, int64_t stride,
                                                       int32_t d, const float* __restrict__ w,
                                                       const float* __restrict__ pot, int64_t count,
@@ -120,9 +124,15 @@ __global__ __launch_bounds__(64) void k_frame_weights(const float* __restrict__ 
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
   const bool live = m > -INFINITY;
-  for (int64_t i = s + threadIdx.x; i < ep; i += 64)
-    wt[i] = (live && i < e) ? (float)exp2(frame_term(off, stride, d, w, pot, i, lam, kappa) - m) : 0.0f;
-  if (threadIdx.x == 0) mx[J] = m;
+  double lo = 0.0;
+  for (int64_t i = s + threadIdx.x; i < ep; i += 64) {
+    const double t = (live && i < e) ? frame_term(off, stride, d, w, pot, i, lam, kappa) - m : -INFINITY;
+    if (t > -INFINITY) lo = fmin(lo, t);
+    wt[i] = (float)exp2(t);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lo = fmin(lo, __shfl_xor(lo, o, 64));
+  if (threadIdx.x == 0) mx[J] = lo < -126.0 ? (double)NAN : m;
 }
 
 // One wave per block: min / max of each axis and the max weight.
@@ -356,7 +366,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 // The tile (row tile against column block J, chunks c0 .. c1) in the
 // tile-local expanded form, for the lane's kR rows; false (nothing done) when
-// some row of the wave fails the range guard. With a_i = x_i - o_J and the
+// some row of the wave fails the range guard or the block's weights do not
+// fit fp32 (m_J = NaN). With a_i = x_i - o_J and the
 // column offsets dy_j = y_j - o_J,
 //   z_ij - c_i = log2 w'_j + 2 kappa a_i . dy_j + s_i,
 //   s_i = m_J - kappa ||a_i||^2 - c_i,  w'_j = 2^(h'_j - m_J),
@@ -381,6 +392,8 @@ __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
                                            int lane, int64_t J, int64_t c0, int64_t c1) {
   static_assert(kR == 2 && kRowsPerTile == 128 && kChunk == 16, "layout of the exchanges below");
   constexpr int NB = kRowsPerTile / 16;
+  const double mJ = A.mx[J];
+  if (isnan(mJ)) return false;  // uniform: weights beyond the fp32 range
   const float* ct = A.ctr + J * 4;
   float o[D];
 #pragma unroll
@@ -459,7 +472,6 @@ __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
     const float other = g1 ? keep[2 * h] : keep[2 * h + 1];
     Tr[h] = mine + __shfl_xor(other, 16, 64);
   }
-  const double mJ = A.mx[J];
   const double kd = -(double)A.nkappa;
 #pragma unroll
   for (int r = 0; r < kR; ++r) {

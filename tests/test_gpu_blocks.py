@@ -153,6 +153,30 @@ def test_block_screen_capacity_overflow_reports_the_needed_count(sk):
         assert b"capacity" in sk.lib().sinkhorn_strerror(code)
 
 
+def test_sparse_halfstep_with_weights_beyond_fp32_range(sk):
+    """Column weights 2^-130 below the rest (subnormal in fp32): a block whose
+    tile-local weights would leave the normal fp32 range takes the difference
+    form, and the shifted sparse f-step still matches the oracle."""
+    n, B, eps = 16384, 128, 1e-3
+    x, y, a, b = _sorted_problem(5, n)
+    b = b.astype(np.float64)
+    b[5::97] *= 2.0 ** -130
+    b = (b * (a.astype(np.float64).sum() / b.sum())).astype(np.float32)  # balanced masses
+    assert (b > 0).all() and (b[5::97] < np.finfo(np.float32).tiny).all()
+    rng = np.random.default_rng(4)
+    f, g = _near_plan_potentials(n, eps, rng)
+    NB = (n + B - 1) // B
+    delta = 1e-3 / NB
+    sx = oracle.block_summaries(x, a, f, B)
+    sy = oracle.block_summaries(y, b, g, B)
+    ptr, col = oracle.screen(sx, sy, eps, 1.0, delta)
+    with sk.Problem(_t(x), _t(y), _t(a), _t(b), 1.0) as P:
+        fo, _ = P.sparse_halfstep_f(eps, _t(g), B, _t(ptr), _t(col.astype(np.int32)), f_prev=_t(f))
+    ref = oracle.sparse_halfstep_f(x, y, b, g, eps, 1.0, ptr, col, B)
+    err = np.abs(fo.cpu().numpy().astype(np.float64) - ref) / np.maximum(eps, np.abs(ref))
+    assert err.max() <= 1e-5, err.max()
+
+
 @pytest.mark.parametrize("prev", [True, False], ids=["shifted", "exact"])
 @pytest.mark.parametrize("n,B,eps", [(16384, 128, 1e-4), (16384, 256, 1e-3), (5000, 128, 1e-3)])
 def test_sparse_halfsteps_match_oracle(sk, n, B, eps, prev):
