@@ -133,9 +133,9 @@ SPARSE_SOURCES = ("blocks.hip", "pairloop.h", "rowfinal.h", "internal.h", "launc
 # summary and the sources that kernel is built from (the figure is used only
 # while their digest matches the one recorded with the counters)
 PMC_RECORDS = {
-    2: ("k_lse_valu64_w2_n20000_d3_pmc.md", KERNEL_SOURCES_64),
+    2: ("k_lse_split_w2_n20000_d3_pmc.md", KERNEL_SOURCES_64),
     3: ("k_lse_mfma_w3_n50000_m60000_d50_pmc.md", ("mfma.hip", "rowfinal.h", "internal.h")),
-    4: ("k_lse_valu64_w4_n1000000_d3.md", KERNEL_SOURCES_64),
+    4: ("k_lse_split_w4_n1000000_d3.md", KERNEL_SOURCES_64),
     5: ("k_lse_sparse_w5_n16777216_eps1e-4_pmc.md", SPARSE_SOURCES),
 }
 
