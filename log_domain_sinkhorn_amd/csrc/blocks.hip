@@ -31,6 +31,13 @@
 namespace sk {
 namespace {
 
+// Frame record of a side: per 16-point chunk, d rows of 16 offsets and then
+// 16 weights, so that one chunk of the tile-local loop is one contiguous
+// (d + 1) x 64-byte record. Slot k of point i (k = d: its weight).
+__host__ __device__ __forceinline__ int64_t rec_at(int64_t i, int k, int d) {
+  return (i >> 4) * ((int64_t)(d + 1) << 4) + ((int64_t)k << 4) + (i & 15);
+}
+
 // Tile-local frame, static part: one wave per block of B points; the block
 // centre o = (lo + hi) / 2 per axis (fp32), every point's offset from it and
 // the block radius max |y_j - o| (rounded up by 2^-20 relative), zero offsets
@@ -39,6 +46,7 @@ template <int D>
 __global__ __launch_bounds__(64) void k_frame_build(const float* __restrict__ soa, int64_t stride,
                                                     int64_t count, int32_t B, float* __restrict__ off,
                                                     float* __restrict__ ctr) {
+  // off: the frame record (rec_at); this kernel writes the offset rows
   const int64_t J = blockIdx.x;
   const int64_t s = J * B;
   const int64_t e = s + B < count ? s + B : count;
@@ -72,7 +80,7 @@ __global__ __launch_bounds__(64) void k_frame_build(const float* __restrict__ so
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       const float v = i < e ? soa[k * stride + i] - c[k] : 0.0f;
-      off[k * stride + i] = v;
+      off[rec_at(i, k, D)] = v;
       q = __builtin_fmaf(v, v, q);
     }
     r2 = fmaxf(r2, q);
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(64) void k_frame_build(const float* __restrict__ so
 
 // h'_j = log2 w_j + lam pot_j - kappa ||off_j||^2 in fp64 (-inf for a
 // massless point).
-__device__ __forceinline__ double frame_term(const float* __restrict__ off, int64_t stride, int32_t d,
+__device__ __forceinline__ double frame_term(const float* __restrict__ rec, int32_t d,
                                              const float* __restrict__ w,
                                              const float* __restrict__ pot, int64_t i, double lam,
                                              double kappa) {
@@ -96,39 +104,46 @@ __device__ __forceinline__ double frame_term(const float* __restrict__ off, int6
   if (!(wi > 0.0)) return -INFINITY;
   double q = 0.0;
   for (int k = 0; k < d; ++k) {
-    const double v = (double)off[k * stride + i];
+    const double v = (double)rec[rec_at(i, k, d)];
     q = fma(v, v, q);
   }
   return log2(wi) + lam * (double)pot[i] - kappa * q;
 }
 
+// Largest |exponent| of a pair term in the expanded form, 2 kappa |x - o| R:
+// keeps 128 weighted terms of a tile far inside the fp32 range and the
+// exponent's rounding near 2^-24 of it.
+constexpr float kGuard = 96.0f;
+
 // Tile-local frame, per half-step: one wave per block; m_J = max h'_j and the
 // weights 2^(h'_j - m_J) (fp64 exp2, rounded once to fp32); 0 on padding and
-// for every point of a block without mass (m_J = -inf). A block whose weights
-// span more than the normal fp32 range (some h'_j - m_J < -126: that weight
-// would be flushed or lose bits, and the range guard alone does not make its
-// terms negligible) gets m_J = NaN, which sends its tiles to the difference
-// form.
-__global__ __launch_bounds__(64) void k_frame_weights(const float* __restrict__ off, int64_t stride,
+// for every point of a block without mass (m_J = -inf). The tile-local form
+// sums w'_j 2^z with |z| <= kGuard in fp32. The column with w'_j = 1 keeps
+// every row's tile sum at 2^-kGuard or more, so a term that falls below the
+// normal fp32 range is below 2^-30 of it and negligible; but a weight below
+// 2^-126 is itself flushed or short of bits while its term can still be the
+// largest of the tile, so such a block gets m_J = NaN, which sends its tiles
+// to the difference form.
+__global__ __launch_bounds__(64) void k_frame_weights(float* __restrict__ rec, int64_t stride,
                                                       int32_t d, const float* __restrict__ w,
                                                       const float* __restrict__ pot, int64_t count,
                                                       int32_t B, double lam, double kappa,
-                                                      float* __restrict__ wt, double* __restrict__ mx) {
+                                                      double* __restrict__ mx) {
   const int64_t J = blockIdx.x;
   const int64_t s = J * B;
   const int64_t e = s + B < count ? s + B : count;
   const int64_t ep = s + B < stride ? s + B : stride;
   double m = -INFINITY;
   for (int64_t i = s + threadIdx.x; i < e; i += 64)
-    m = fmax(m, frame_term(off, stride, d, w, pot, i, lam, kappa));
+    m = fmax(m, frame_term(rec, d, w, pot, i, lam, kappa));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
   const bool live = m > -INFINITY;
   double lo = 0.0;
   for (int64_t i = s + threadIdx.x; i < ep; i += 64) {
-    const double t = (live && i < e) ? frame_term(off, stride, d, w, pot, i, lam, kappa) - m : -INFINITY;
+    const double t = (live && i < e) ? frame_term(rec, d, w, pot, i, lam, kappa) - m : -INFINITY;
     if (t > -INFINITY) lo = fmin(lo, t);
-    wt[i] = (float)exp2(t);
+    rec[rec_at(i, d, d)] = (float)exp2(t);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lo = fmin(lo, __shfl_xor(lo, o, 64));
@@ -338,8 +353,9 @@ struct SparseArgs {
   int32_t fallback;        // 1: exact recompute of the flagged tiles only
   // shifted mode, tile-local expanded form (null off: every tile in the
   // difference form)
-  const float* off;        // [D][qstride] column offsets from their block centres
-  const float* wt;         // [qstride] column weights 2^(h'_j - m_J)
+  const float* rec;        // column frame records: per 16-point chunk D rows of
+                           // offsets from the block centre, then the weights
+                           // 2^(h'_j - m_J)
   const float* ctr;        // [column blocks][4] block centre (first D slots) and radius
   const double* mx;        // [column blocks] m_J
   float two_kappa;         // 2 kappa
@@ -348,11 +364,6 @@ struct SparseArgs {
                            // wave has |x_i - o_J|^2 R_J^2 <= guard2 = (kGuard / 2 kappa)^2
   RowFinal F;
 };
-
-// Largest |exponent| of a pair term in the expanded form, 2 kappa |x - o| R:
-// keeps 128 weighted terms of a tile far inside the fp32 range and the
-// exponent's rounding near 2^-24 of it.
-constexpr float kGuard = 96.0f;
 
 // v * 2^s for an fp64 exponent s clamped to [-1000, 1000]: the fraction
 // through v_exp_f32, the integer part exactly by v_ldexp.
@@ -387,8 +398,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // the whole T of rows l and l + 64, its two rows in RowAcc.
 template <int D>
 __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
-                                           const float* __restrict__ off,
-                                           const float* __restrict__ wt, const float (&x)[kR][D],
+                                           const float* __restrict__ rec, const float (&x)[kR][D],
                                            int lane, int64_t J, int64_t c0, int64_t c1) {
   static_assert(kR == 2 && kRowsPerTile == 128 && kChunk == 16, "layout of the exchanges below");
   constexpr int NB = kRowsPerTile / 16;
@@ -428,14 +438,17 @@ __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) T[rb] = 0.0f;
   const int g = lane >> 4;
-  const int64_t qs = A.qstride;
-  const float* oc = off + c0 * kChunk + 4 * g + (lane & 3);
-  const float* wc = wt + c0 * kChunk + 4 * g;
-  for (int64_t c = c0; c < c1; ++c, oc += kChunk, wc += kChunk) {
+  // one contiguous record per chunk: a uniform base and this lane's offsets
+  // within it (its column 4 g + l % 4, and the weights of columns 4 g .. + 3)
+  const int32_t ao = 4 * g + (lane & 3);
+  const int32_t wo = D * kChunk + 4 * g;
+  const int32_t nc = (int32_t)(c1 - c0);
+  const float* base = rec + c0 * (D + 1) * kChunk;
+  for (int32_t c = 0; c < nc; ++c, base += (D + 1) * kChunk) {
     float av[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) av[k] = oc[k * qs];
-    const v4f wv = *(const v4f*)wc;
+    for (int k = 0; k < D; ++k) av[k] = base[ao + k * kChunk];
+    const v4f wv = *(const v4f*)(base + wo);
     v4f z[NB];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb)
@@ -511,8 +524,7 @@ __device__ __forceinline__ bool local_tile(RowAcc<true>& R, const SparseArgs& A,
 template <int D, bool SHIFT>
 __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const float* __restrict__ Q,
                                                         const float* __restrict__ H,
-                                                        const float* __restrict__ off,
-                                                        const float* __restrict__ wt) {
+                                                        const float* __restrict__ rec) {
   __shared__ TileLds L;
   const int64_t tile = A.order ? (int64_t)A.order[blockIdx.x] : (int64_t)blockIdx.x;
   if (tile < 0) return;                                         // an empty slot (uniform)
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_sparse(SparseArgs A, const flo
       const int64_t c0 = J * cpb;
       const int64_t c1 = c0 + cpb < A.nchunks ? c0 + cpb : A.nchunks;
       if constexpr (SHIFT) {
-        if (A.off != nullptr && local_tile<D>(R, A, off, wt, x, lane, J, c0, c1)) continue;
+        if (A.rec != nullptr && local_tile<D>(R, A, rec, x, lane, J, c0, c1)) continue;
       }
       pair_pass<D, SHIFT>(R, Q, H, A.qstride, A.nkappa, x, c0, c1, 1);
     }
@@ -646,11 +658,10 @@ void block_potential_max(sinkhorn_problem* p, const float* pot, int64_t count, B
 }
 
 void LocalFrame::release() {
-  dev_free(off);
-  dev_free(wt);
+  dev_free(rec);
   dev_free(ctr);
   dev_free(mx);
-  off = wt = ctr = nullptr;
+  rec = ctr = nullptr;
   mx = nullptr;
   nb = 0;
 }
@@ -662,15 +673,14 @@ void frame_build(sinkhorn_problem* p, const Side& s, int32_t B, LocalFrame& out)
   out.nb = (s.count + B - 1) / B;
   out.B = B;
   out.stride = s.padded;
-  out.off = (float*)dev_alloc(sizeof(float) * p->d * s.padded);
-  out.wt = (float*)dev_alloc(sizeof(float) * s.padded);
+  out.rec = (float*)dev_alloc(sizeof(float) * (p->d + 1) * s.padded);
   out.ctr = (float*)dev_alloc(sizeof(float) * 4 * out.nb);
   out.mx = (double*)dev_alloc(sizeof(double) * out.nb);
   switch (p->d) {
 #define SK_FRAME(Dv)                                                                              \
   case Dv:                                                                                        \
     hipLaunchKernelGGL(k_frame_build<Dv>, grid1(out.nb, 64), dim3(64), 0, p->stream, s.soa,      \
-                       s.padded, s.count, B, out.off, out.ctr);                                   \
+                       s.padded, s.count, B, out.rec, out.ctr);                                   \
     break;
     SK_FRAME(1)
     SK_FRAME(2)
@@ -683,8 +693,8 @@ void frame_build(sinkhorn_problem* p, const Side& s, int32_t B, LocalFrame& out)
 void frame_weights(sinkhorn_problem* p, const Side& s, const float* pot, double eps, LocalFrame& fr) {
   const double lam = kLog2e / eps;
   const double kappa = p->scale * kLog2e / eps;
-  hipLaunchKernelGGL(k_frame_weights, grid1(fr.nb, 64), dim3(64), 0, p->stream, fr.off, fr.stride,
-                     p->d, s.w, pot, s.count, fr.B, lam, kappa, fr.wt, fr.mx);
+  hipLaunchKernelGGL(k_frame_weights, grid1(fr.nb, 64), dim3(64), 0, p->stream, fr.rec, fr.stride,
+                     p->d, s.w, pot, s.count, fr.B, lam, kappa, fr.mx);
   SK_LAUNCH_CHECK();
 }
 
@@ -941,10 +951,10 @@ void launch_sparse(sinkhorn_problem* p, const SparseArgs& A, int64_t tiles, bool
                    const ProfEv& pe) {
   if (shifted)
     hipExtLaunchKernelGGL((k_lse_sparse<D, true>), grid1(tiles, kThreads), dim3(kThreads), 0, p->stream,
-                          pe.start, pe.stop, 0, A, A.Q, A.H, A.off, A.wt);
+                          pe.start, pe.stop, 0, A, A.Q, A.H, A.rec);
   else
     hipExtLaunchKernelGGL((k_lse_sparse<D, false>), grid1(tiles, kThreads), dim3(kThreads), 0,
-                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H, A.off, A.wt);
+                          p->stream, pe.start, pe.stop, 0, A, A.Q, A.H, A.rec);
   SK_LAUNCH_CHECK();
 }
 
@@ -975,8 +985,7 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
   A.fallback = 0;
   int64_t slots = tiles;
   A.order = heavy_first(p, ptr, tiles, B, (cols.count + B - 1) / B, &slots);
-  A.off = nullptr;
-  A.wt = nullptr;
+  A.rec = nullptr;
   A.ctr = nullptr;
   A.mx = nullptr;
   A.two_kappa = (float)(2.0 * kappa);
@@ -990,8 +999,7 @@ void sparse_halfstep(sinkhorn_problem* p, const HalfStep& hs, int32_t B, const i
     if (fr.B != B || fr.stride != cols.padded || fr.nb != (cols.count + B - 1) / B)
       fail(SINKHORN_ERR_INVALID_ARG, "tile-local frame built for another side or block size");
     frame_weights(p, cols, hs.cols_pot, hs.eps, fr);
-    A.off = fr.off;
-    A.wt = fr.wt;
+    A.rec = fr.rec;
     A.ctr = fr.ctr;
     A.mx = fr.mx;
   }

@@ -280,8 +280,8 @@ struct LocalFrame {
   int64_t nb = 0;          // blocks
   int32_t B = 0;           // points per block
   int64_t stride = 0;      // the side's padded count
-  float* off = nullptr;    // [d][stride] offsets from the block centre, 0 on padding
-  float* wt = nullptr;     // [stride] weights, 0 on padding
+  float* rec = nullptr;    // per 16-point chunk d rows of 16 offsets from the block
+                           // centre, then 16 weights; 0 on padding
   float* ctr = nullptr;    // [nb][4]: o_J in the first d slots, R_J in slot 3
   double* mx = nullptr;    // [nb] m_J
   void release();
