@@ -361,6 +361,26 @@ def test_shifted_pair_loop_matches_oracle_for_any_shift_estimate(sk, offset):
         _assert_halfstep(g.cpu().numpy(), g_ref, eps, f"shifted g-step offset={offset}")
 
 
+def test_split_form_column_terms_beyond_two_to_the_22(sk):
+    """Potentials near 3 at eps = 1e-6 put every column term
+    h_j = log2 b_j + g_j log2(e) / eps near 4.3e6, past 2^22, where the split
+    takes the fp32 rounding of h_j as its integer part and keeps the rest in
+    the weight: the shifted f-step stays within eps of the oracle (the fp32
+    output itself rounds to about 0.12 eps at |f| = 3)."""
+    c = synth.make(2, n=700, m=900)
+    eps = 1e-6
+    rng = np.random.default_rng(23)
+    g0 = (3.0 + rng.normal(0, 1, c.m) * eps).astype(np.float32)
+    h = np.log2(c.b.astype(np.float64)) + g0.astype(np.float64) * (1.0 / math.log(2.0)) / eps
+    assert (np.abs(h) > 2.0 ** 22).all()
+    f_ref = oracle.halfstep_f(c.x, c.y, c.b, g0, eps, 1.0)
+    with _problem(sk, c) as P:
+        f, _ = P.halfstep_f(eps, _t(g0), f_prev=_t(f_ref.astype(np.float32)))
+    f = f.cpu().numpy().astype(np.float64)
+    _assert_halfstep(f, f_ref, eps, "split form, |h| > 2^22")
+    assert np.abs(f - f_ref).max() <= eps, np.abs(f - f_ref).max() / eps
+
+
 def test_shifted_full_size_workload4_sampled_rows(sk):
     c = synth.make(4)
     eps = 1e-4
