@@ -289,11 +289,13 @@ int sinkhorn_verify_tiles(sinkhorn_problem* p, double eps, const float* f, const
  * update). Same outputs as sinkhorn_halfstep_f, with the residual (when
  * f_prev and row_l1 are given) taken over the same support. With f_prev the
  * rows carry shifts from it and each admitted tile is evaluated about its
- * column block's bounding-box centre (per-column weights and per-tile scales
- * in fp64, the pair terms in fp32; a tile whose rows lie too far from the
- * block for the fp32 range takes the plain difference form): the call then
- * holds 16 B of device memory per column point and 24 B per column block
- * until it returns. Synchronizes the handle's stream. */
+ * column block's bounding-box centre: per-column weights and per-tile scales
+ * in fp64 (rounded once), the cross terms of each 16 x 16 pair block on the
+ * matrix cores in fp32. A tile whose rows lie too far from the block for the
+ * fp32 range, or whose block's weights span more than the normal fp32 range,
+ * takes the plain difference form. The call then holds (4 d + 4) B of device
+ * memory per column point and 24 B per column block until it returns.
+ * Synchronizes the handle's stream. */
 int sinkhorn_sparse_halfstep_f(sinkhorn_problem* p, double eps, const float* g, int32_t B,
                                const int64_t* ptr, const int32_t* idx, float* f_out,
                                const float* f_prev, double* row_l1);

@@ -351,13 +351,13 @@ struct SparseArgs {
   int32_t* tile_flag;      // [tiles] tiles left for the exact recompute
   const int32_t* order;    // [tiles] tile of each workgroup (heaviest first), or null: in order
   int32_t fallback;        // 1: exact recompute of the flagged tiles only
-  // shifted mode, tile-local expanded form (null off: every tile in the
+  // shifted mode, tile-local expanded form (null rec: every tile in the
   // difference form)
   const float* rec;        // column frame records: per 16-point chunk D rows of
                            // offsets from the block centre, then the weights
                            // 2^(h'_j - m_J)
   const float* ctr;        // [column blocks][4] block centre (first D slots) and radius
-  const double* mx;        // [column blocks] m_J
+  const double* mx;        // [column blocks] m_J (NaN: weights beyond the fp32 range)
   float two_kappa;         // 2 kappa
   double kappa;            // kappa (fp64)
   float guard2;            // a tile takes the expanded form when every row of the

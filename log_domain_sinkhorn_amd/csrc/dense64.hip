@@ -98,9 +98,10 @@ __device__ void exact_tile64(const LseArgs64& A, TileLds& L, int64_t tile, doubl
 // Shifted pair kernel in split form (pair_pass_split): workgroup w works on
 // tile w / G, column split w % G, and writes the split's partials (fp64
 // shift, fp32 sum) for k_merge64. Q, Hhi, Wlo, Mp and Sp come as separate
-// no-alias arguments (scalar column loads). A row's integer shift is its estimated LSE less the
-// headroom, rounded down; beyond 2^22 in magnitude the integer is rounded to
-// fp32 and the form keeps only fp32 accuracy.
+// no-alias arguments (scalar column loads). A row's shift is its estimated
+// LSE less the headroom, rounded down to an integer and then to fp32 (exact
+// below 2^24 in magnitude; beyond, the fp32 value is the shift, and the merge
+// takes that same value).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_lse_split(LseArgs64 A, const float* __restrict__ Q,
                                                        const float* __restrict__ Hhi,
@@ -147,8 +148,8 @@ __global__ __launch_bounds__(kThreads) void k_lse_split(LseArgs64 A, const float
 
 // Split of the fp64 column term for the split form: Hhi = the integer below
 // H, Wlo = 2^(H - Hhi) (fp64 exp2, one rounding); |H| >= 2^22: Hhi = H rounded
-// to fp32 and Wlo the remainder's weight; padding and massless points: -inf
-// and 0.
+// to fp32 (a multiple of its ulp) and Wlo = 2^(H - Hhi), so the split is as
+// exact there; padding and massless points: -inf and 0.
 __global__ __launch_bounds__(256) void k_split_terms(const double* __restrict__ H, int64_t n,
                                                      float* __restrict__ Hhi,
                                                      float* __restrict__ Wlo) {

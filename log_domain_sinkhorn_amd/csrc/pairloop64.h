@@ -116,9 +116,11 @@ __device__ __forceinline__ void pair_pass64(RowAcc64& R, const double* __restric
 
 // The shifted pass in split form: the same sum as pair_pass64 with fp32
 // arithmetic whose only iterate-dependent roundings are small. The column
-// term is split as h_j = Hhi_j + log2 Wlo_j with Hhi_j an integer, and each
-// row's shift c_i is an integer: both are exact in fp32 below 2^22 in
-// magnitude, so t = Hhi_j - c_i is exact, and
+// term is split as h_j = Hhi_j + log2 Wlo_j with Hhi_j an integer (beyond
+// 2^22 in magnitude, the fp32 rounding of h_j), and each row's shift c_i is
+// an fp32 integer. Then t = Hhi_j - c_i is exact: below 2^24 in magnitude
+// both are integers, and beyond, for the pairs that carry the sum, they are
+// within a factor 2 of each other (Sterbenz); and
 //   z_ij = RN(t - kappa32 q_ij),  q_ij = ||x_i - y_j||^2 in fp32,
 //   S_i += Wlo_j exp2(z_ij).
 // q and kappa32 (kappa rounded to fp32 once) depend on the clouds and eps
